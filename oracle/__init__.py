@@ -1,0 +1,184 @@
+"""The oracle: plain double-precision CPU reference of the four Gaussian map-reductions.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  The GPU library
+(``geometric_map_reduce_amd``) never imports it and shares no code with it.
+
+The arithmetic lives in ``keops_oracle.c`` (plain C, double precision, OpenMP
+over independent rows); this module only builds it with gcc and marshals numpy
+arrays.  Each function cites the passage of the KeOps pages it follows:
+
+* ``gauss_sum``   -- "Kernel Operations on the GPU, with Autodiff, without
+  Memory Overflows", §1 "Target operation" (a_i = sum_j k(x_i, y_j) b_j with a
+  Gaussian k of deviation sigma); KeOps README PyTorch example (K_ij.sum).
+* ``gauss_lse``   -- same paper, §2 reductions list (log-sum-exp); README
+  ``.logsumexp()``.
+* ``gauss_grad_x``-- same paper, §2 "Performance and differentiation"
+  (autodiff); README ``torch.autograd.grad((a_i ** 2).sum(), [x])``.
+* ``kmin``        -- same paper, §2 (argmin, argKmin); README feature list
+  (ArgMin, K-min reductions).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "keops_oracle.c")
+_LIB = os.path.join(_HERE, "_build", "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def compile_source(src: str, out: str) -> str:
+    """gcc -O2 -fopenmp, no fast-math and no FMA contraction; returns ``out``."""
+    os.makedirs(os.path.dirname(out) or ".", exist_ok=True)
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-fopenmp", "-fno-fast-math", "-ffp-contract=off", "-std=c11",
+           "-fPIC", "-shared", "-Wall", "-o", tmp, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = True) -> str:
+    """Compile keops_oracle.c into oracle/_build/liboracle.so."""
+    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(SOURCE):
+        return _LIB
+    return compile_source(SOURCE, _LIB)
+
+
+def open_library(path: str):
+    """ctypes handle on an oracle library built from keops_oracle.c (or a copy of it)."""
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    i64, i32, f64 = ctypes.c_int64, ctypes.c_int, ctypes.c_double
+    lib.oracle_gauss_sum.argtypes = [P, P, P, i64, i64, i32, i32, f64, P, i64, P, P]
+    lib.oracle_gauss_lse.argtypes = [P, P, P, i64, i64, i32, i32, f64, P, i64, P]
+    lib.oracle_gauss_grad_x.argtypes = [P, P, P, P, i64, i64, i32, i32, f64, P, i64, P, P]
+    lib.oracle_kmin.argtypes = [P, P, i64, i64, i32, i32, P, i64, P, P]
+    lib.oracle_sq_dist_pairs.argtypes = [P, P, i32, P, P, i64, P]
+    for f in ("oracle_gauss_sum", "oracle_gauss_lse", "oracle_gauss_grad_x",
+              "oracle_kmin", "oracle_sq_dist_pairs", "oracle_num_threads"):
+        getattr(lib, f).restype = ctypes.c_int
+    return lib
+
+
+def _load():
+    """The library built from the committed source (``lib=`` arguments below accept another
+    handle from ``open_library``, e.g. one built from a deliberately broken copy in a test)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            _lib = open_library(build(force=False))
+    return _lib
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle uses (OMP_NUM_THREADS, else all host cores)."""
+    return int(_load().oracle_num_threads())
+
+
+def _f32(a, ndim):
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    if a.ndim == 1 and ndim == 2:
+        a = a.reshape(-1, 1)
+    assert a.ndim == ndim
+    return a
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
+
+
+def _rows(rows, M):
+    if rows is None:
+        return None, M
+    r = np.ascontiguousarray(rows, dtype=np.int64)
+    return r, r.shape[0]
+
+
+def _check(rc, name):
+    if rc != 0:
+        raise ValueError(f"oracle {name}: invalid argument")
+
+
+def gauss_sum(x, y, b, sigma, rows=None, lib=None):
+    """a[r, e] = sum_j exp(-|x_i - y_j|^2 / sigma^2) b[j, e]  for i = rows[r].
+
+    Returns (a, norm) in float64, norm[r, e] = sum_j |K_ij b_je|.
+    """
+    x, y, b = _f32(x, 2), _f32(y, 2), _f32(b, 2)
+    M, D = x.shape
+    N, E = b.shape
+    assert y.shape == (N, D)
+    r, n = _rows(rows, M)
+    out = np.empty((n, E), np.float64)
+    nrm = np.empty((n, E), np.float64)
+    _check((lib or _load()).oracle_gauss_sum(_ptr(x), _ptr(y), _ptr(b), M, N, D, E, float(sigma),
+                                    _ptr(r), n, _ptr(out), _ptr(nrm)), "gauss_sum")
+    return out, nrm
+
+
+def gauss_lse(x, y, b, sigma, rows=None, lib=None):
+    """l[r, e] = log sum_j exp(-|x_i - y_j|^2 / sigma^2 + b[j, e]) in float64 (two-pass)."""
+    x, y, b = _f32(x, 2), _f32(y, 2), _f32(b, 2)
+    M, D = x.shape
+    N, E = b.shape
+    assert y.shape == (N, D)
+    r, n = _rows(rows, M)
+    out = np.empty((n, E), np.float64)
+    _check((lib or _load()).oracle_gauss_lse(_ptr(x), _ptr(y), _ptr(b), M, N, D, E, float(sigma),
+                                    _ptr(r), n, _ptr(out)), "gauss_lse")
+    return out
+
+
+def gauss_grad_x(x, y, b, g, sigma, rows=None, lib=None):
+    """G[r, d] = sum_j (-2/sigma^2) K_ij <g_i, b_j> (x_id - y_jd)  for i = rows[r].
+
+    ``g`` is the full [M, E] cotangent dL/da.  Returns (G, nu) in float64 with
+    nu[r, d] = sum_j |(2/sigma^2) K_ij <g_i, b_j> (x_id - y_jd)|.
+    """
+    x, y, b, g = _f32(x, 2), _f32(y, 2), _f32(b, 2), _f32(g, 2)
+    M, D = x.shape
+    N, E = b.shape
+    assert y.shape == (N, D) and g.shape == (M, E)
+    r, n = _rows(rows, M)
+    out = np.empty((n, D), np.float64)
+    nu = np.empty((n, D), np.float64)
+    _check((lib or _load()).oracle_gauss_grad_x(_ptr(x), _ptr(y), _ptr(b), _ptr(g), M, N, D, E,
+                                       float(sigma), _ptr(r), n, _ptr(out), _ptr(nu)),
+           "gauss_grad_x")
+    return out, nu
+
+
+def kmin(x, y, K, rows=None, lib=None):
+    """K smallest |x_i - y_j|^2 (float64) and their int64 indices, ascending by (d^2, j)."""
+    x, y = _f32(x, 2), _f32(y, 2)
+    M, D = x.shape
+    N = y.shape[0]
+    assert y.shape == (N, D)
+    r, n = _rows(rows, M)
+    out_d = np.empty((n, K), np.float64)
+    out_i = np.empty((n, K), np.int64)
+    _check((lib or _load()).oracle_kmin(_ptr(x), _ptr(y), M, N, D, int(K), _ptr(r), n,
+                               _ptr(out_d), _ptr(out_i)), "kmin")
+    return out_d, out_i
+
+
+def sq_dist_pairs(x, y, ii, jj, lib=None):
+    """|x_ii[p] - y_jj[p]|^2 in float64 for each pair p."""
+    x, y = _f32(x, 2), _f32(y, 2)
+    ii = np.ascontiguousarray(ii, dtype=np.int64).ravel()
+    jj = np.ascontiguousarray(jj, dtype=np.int64).ravel()
+    assert ii.shape == jj.shape
+    assert ii.size == 0 or (ii.min() >= 0 and ii.max() < x.shape[0])
+    assert jj.size == 0 or (jj.min() >= 0 and jj.max() < y.shape[0])
+    out = np.empty(ii.shape[0], np.float64)
+    _check((lib or _load()).oracle_sq_dist_pairs(_ptr(x), _ptr(y), x.shape[1], _ptr(ii), _ptr(jj),
+                                        ii.shape[0], _ptr(out)), "sq_dist_pairs")
+    return out

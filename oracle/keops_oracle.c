@@ -1,0 +1,216 @@
+/*
+ * keops_oracle.c -- the ORACLE: a plain, slow, double-precision CPU
+ * implementation of the four Gaussian map-reductions.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
+ * baseline leg of the benchmark may load this library.  The GPU library shares
+ * no code, header, table or helper with it, and neither calls the other.
+ *
+ * Every function is the textbook definition written out, in double precision,
+ * with inputs given as the same fp32 arrays the GPU receives (each element is
+ * widened to double exactly).  There is no blocking, no fusion and no
+ * reordering: one output row at a time, a sequential loop over j, plain
+ * summation.  Rows are independent, so an OpenMP loop over rows changes no
+ * row's arithmetic.
+ *
+ * Sources (web pages about the KeOps library):
+ *  [KO-GPU]  "Kernel Operations on the GPU, with Autodiff, without Memory
+ *            Overflows" (paper summary page), §1 "Target operation",
+ *            §2 "Generic reduction framework", "Performance and
+ *            differentiation".
+ *  [README]  KeOps README (PyTorch example: squared distances D_ij, Gaussian
+ *            K_ij = exp(-D_ij), reductions .sum(), .logsumexp(), .argmin(),
+ *            and autograd of (a**2).sum()); feature list "Sum, LogSumExp,
+ *            Min, Max but also ArgMin, ArgMax or K-min reductions".
+ *
+ * Conventions (readings where the pages leave the step open):
+ *  - Gaussian kernel with deviation sigma:  k(x,y) = exp(-|x-y|^2 / sigma^2).
+ *    sigma = 1 gives the README's exp(-D_ij).
+ *  - LogSumExp of row i, column e:  log sum_j exp(-|x_i-y_j|^2/sigma^2 + b_je).
+ *  - grad_x is the vector-Jacobian product of a = sum-reduction with a given
+ *    cotangent g[M,E] = dL/da (the README differentiates (a**2).sum(), i.e.
+ *    g = 2a).
+ *  - K-min: the K smallest squared distances of row i with their indices, in
+ *    ascending (distance, index) lexicographic order.
+ *
+ * All arrays are dense row-major.  `rows` selects which output rows to
+ * compute (NULL = rows 0..nrows-1); outputs are written for the selected rows
+ * in order.  Return value: 0 on success, -1 on an invalid argument.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* |x_i - y_j|^2 in double: [README] D_ij = ((x_i - y_j)**2).sum(dim=2). */
+static double sq_dist(const float *xi, const float *yj, int D) {
+    double s = 0.0;
+    for (int d = 0; d < D; ++d) {
+        double t = (double)xi[d] - (double)yj[d];
+        s += t * t;
+    }
+    return s;
+}
+
+static int check_common(int64_t M, int64_t N, int D, int64_t nrows, const int64_t *rows) {
+    if (M < 0 || N < 0 || D < 1 || nrows < 0) return -1;
+    if (!rows && nrows > M) return -1;
+    if (rows)
+        for (int64_t r = 0; r < nrows; ++r)
+            if (rows[r] < 0 || rows[r] >= M) return -1;
+    return 0;
+}
+
+/*
+ * Gaussian kernel sum  a_ie = sum_j exp(-|x_i - y_j|^2 / sigma^2) * b_je
+ * ([KO-GPU] §1 "Target operation": a_i = sum_j k(x_i, y_j) b_j with a Gaussian
+ * k of deviation sigma > 0; [README] a_i = K_ij.sum(dim=1)).
+ * Also returns the normaliser  norm_ie = sum_j |K_ij * b_je|  used by the
+ * per-row relative tolerance.
+ */
+int oracle_gauss_sum(const float *x, const float *y, const float *b,
+                     int64_t M, int64_t N, int D, int E, double sigma,
+                     const int64_t *rows, int64_t nrows,
+                     double *out, double *norm) {
+    if (check_common(M, N, D, nrows, rows) || E < 1 || !(sigma > 0.0)) return -1;
+    const double inv_s2 = 1.0 / (sigma * sigma);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t i = rows ? rows[r] : r;
+        double *o = out + r * E, *nm = norm ? norm + r * E : NULL;
+        for (int e = 0; e < E; ++e) { o[e] = 0.0; if (nm) nm[e] = 0.0; }
+        for (int64_t j = 0; j < N; ++j) {
+            const double k = exp(-sq_dist(x + i * D, y + j * D, D) * inv_s2);
+            for (int e = 0; e < E; ++e) {
+                const double t = k * (double)b[j * E + e];
+                o[e] += t;
+                if (nm) nm[e] += fabs(t);
+            }
+        }
+    }
+    return 0;
+}
+
+/*
+ * LogSumExp reduction  l_ie = log sum_j exp(v_ije),  v_ije = -|x_i-y_j|^2/sigma^2 + b_je
+ * ([KO-GPU] §2 reductions "sum, max, argmin, and log-sum-exp"; [README]
+ * .logsumexp()).  Textbook two-pass form: m = max_j v, then
+ * l = m + log sum_j exp(v - m).  N = 0 gives -inf.
+ */
+int oracle_gauss_lse(const float *x, const float *y, const float *b,
+                     int64_t M, int64_t N, int D, int E, double sigma,
+                     const int64_t *rows, int64_t nrows, double *out) {
+    if (check_common(M, N, D, nrows, rows) || E < 1 || !(sigma > 0.0)) return -1;
+    const double inv_s2 = 1.0 / (sigma * sigma);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t i = rows ? rows[r] : r;
+        for (int e = 0; e < E; ++e) {
+            double m = -INFINITY;
+            for (int64_t j = 0; j < N; ++j) {
+                const double v = -sq_dist(x + i * D, y + j * D, D) * inv_s2 + (double)b[j * E + e];
+                if (v > m) m = v;
+            }
+            double s = 0.0;
+            if (m > -INFINITY) {
+                for (int64_t j = 0; j < N; ++j) {
+                    const double v = -sq_dist(x + i * D, y + j * D, D) * inv_s2 + (double)b[j * E + e];
+                    s += exp(v - m);
+                }
+                out[r * E + e] = m + log(s);
+            } else {
+                out[r * E + e] = -INFINITY;
+            }
+        }
+    }
+    return 0;
+}
+
+/*
+ * Gradient of L with respect to x, given the cotangent g = dL/da of the sum
+ * reduction ([KO-GPU] §2 "Performance and differentiation": autodiff through
+ * torch.autograd; [README] torch.autograd.grad((a_i ** 2).sum(), [x])).
+ * Differentiating a_ie = sum_j exp(-|x_i-y_j|^2/sigma^2) b_je with respect to
+ * x_id gives
+ *   G_id = sum_j (-2/sigma^2) K_ij <g_i, b_j> (x_id - y_jd).
+ * Also returns  nu_id = sum_j |(2/sigma^2) K_ij <g_i, b_j> (x_id - y_jd)|.
+ */
+int oracle_gauss_grad_x(const float *x, const float *y, const float *b, const float *g,
+                        int64_t M, int64_t N, int D, int E, double sigma,
+                        const int64_t *rows, int64_t nrows,
+                        double *out, double *nu) {
+    if (check_common(M, N, D, nrows, rows) || E < 1 || !(sigma > 0.0)) return -1;
+    const double inv_s2 = 1.0 / (sigma * sigma);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t i = rows ? rows[r] : r;
+        double *o = out + r * D, *n = nu ? nu + r * D : NULL;
+        for (int d = 0; d < D; ++d) { o[d] = 0.0; if (n) n[d] = 0.0; }
+        for (int64_t j = 0; j < N; ++j) {
+            const double k = exp(-sq_dist(x + i * D, y + j * D, D) * inv_s2);
+            double gb = 0.0;
+            for (int e = 0; e < E; ++e) gb += (double)g[i * E + e] * (double)b[j * E + e];
+            for (int d = 0; d < D; ++d) {
+                const double t = -2.0 * inv_s2 * k * gb * ((double)x[i * D + d] - (double)y[j * D + d]);
+                o[d] += t;
+                if (n) n[d] += fabs(t);
+            }
+        }
+    }
+    return 0;
+}
+
+/*
+ * K-min reduction with indices ([KO-GPU] §2 "argmin, and argKmin"; [README]
+ * "ArgMin, ArgMax or K-min reductions").  For row i: the K smallest values of
+ * delta_ij = |x_i - y_j|^2 (double), ordered by (delta, j) lexicographically,
+ * ascending.  Kept as a sorted list of length K into which each j is inserted
+ * when it precedes the current K-th entry.  Requires 1 <= K <= N.
+ */
+int oracle_kmin(const float *x, const float *y,
+                int64_t M, int64_t N, int D, int K,
+                const int64_t *rows, int64_t nrows,
+                double *out_d, int64_t *out_idx) {
+    if (check_common(M, N, D, nrows, rows) || K < 1 || (int64_t)K > N) return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t i = rows ? rows[r] : r;
+        double *bd = out_d + r * K;
+        int64_t *bj = out_idx + r * K;
+        int count = 0;
+        for (int64_t j = 0; j < N; ++j) {
+            const double dj = sq_dist(x + i * D, y + j * D, D);
+            /* does (dj, j) precede the last kept entry? */
+            if (count == K && !(dj < bd[K - 1] || (dj == bd[K - 1] && j < bj[K - 1]))) continue;
+            int pos = (count < K) ? count : K - 1;
+            while (pos > 0 && (dj < bd[pos - 1] || (dj == bd[pos - 1] && j < bj[pos - 1]))) {
+                bd[pos] = bd[pos - 1];
+                bj[pos] = bj[pos - 1];
+                --pos;
+            }
+            bd[pos] = dj;
+            bj[pos] = j;
+            if (count < K) ++count;
+        }
+    }
+    return 0;
+}
+
+/* delta(i, j) = |x_i - y_j|^2 in double for a list of (i, j) pairs, to judge
+ * the GPU's K-min picks one by one. */
+int oracle_sq_dist_pairs(const float *x, const float *y, int D,
+                         const int64_t *ii, const int64_t *jj, int64_t npairs, double *out) {
+    if (D < 1 || npairs < 0) return -1;
+    for (int64_t p = 0; p < npairs; ++p) out[p] = sq_dist(x + ii[p] * D, y + jj[p] * D, D);
+    return 0;
+}

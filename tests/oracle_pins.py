@@ -1,0 +1,332 @@
+"""Pins of the oracle against facts that do not come from the oracle itself.
+
+Each ``pin_*`` function takes an optional ``lib`` (a handle from
+``oracle.open_library``) and raises AssertionError when the oracle disagrees
+with brute force (an explicitly materialised matrix evaluated with numpy,
+scipy or torch float64 autograd), a closed form, a limit or an invariant.
+``tests/test_oracle.py`` runs them on the committed oracle;
+``tests/test_oracle_mutants.py`` runs them on deliberately broken copies of
+the oracle source and checks that every planted mistake is caught.
+
+Passages (KeOps pages): "Kernel Operations on the GPU, with Autodiff, without
+Memory Overflows" §1 "Target operation" (Gaussian kernel sum), §2 reductions
+list and autodiff; KeOps README PyTorch example (D_ij, K_ij = exp(-D_ij),
+.sum, .logsumexp, .argmin, grad of (a**2).sum()).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import scipy.special
+import torch
+
+import oracle
+
+
+# --------------------------------------------------------------------------- helpers
+def dyadic(rng, shape, lo=-4.0, hi=4.0, step=1 / 64):
+    """float32 values on a grid of spacing ``step`` (sums/products stay exact in fp32)."""
+    n = int(round((hi - lo) / step))
+    return (lo + step * rng.integers(0, n + 1, size=shape)).astype(np.float32)
+
+
+def brute_sqdist(x, y):
+    """Materialised |x_i - y_j|^2 in float64, summed over d in index order."""
+    x = x.astype(np.float64)
+    y = y.astype(np.float64)
+    out = np.zeros((x.shape[0], y.shape[0]))
+    for d in range(x.shape[1]):
+        out += (x[:, None, d] - y[None, :, d]) ** 2
+    return out
+
+
+def brute_K(x, y, sigma):
+    return np.exp(-brute_sqdist(x, y) / float(sigma) ** 2)
+
+
+def rel_close(a, b, rtol, atol=0.0):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    assert a.shape == b.shape, (a.shape, b.shape)
+    err = np.abs(a - b)
+    bad = err > rtol * np.abs(b) + atol
+    assert not bad.any(), f"max err {err.max():.3e} at {np.argwhere(bad)[:3].tolist()}"
+
+
+SHAPES = [(1, 1, 1, 1), (5, 7, 2, 1), (17, 33, 3, 1), (16, 9, 3, 3), (8, 64, 5, 2),
+          (12, 20, 32, 1), (6, 11, 50, 1), (9, 13, 64, 3)]
+
+
+# --------------------------------------------------------------------------- sum
+def pin_sum_brute(lib=None):
+    """Sum and its normaliser equal the materialised K @ b (numpy float64)."""
+    rng = np.random.default_rng(11)
+    for (M, N, D, E) in SHAPES:
+        for sigma in (0.7, 1.0, 2.5 * math.sqrt(D)):
+            x = rng.standard_normal((M, D)).astype(np.float32)
+            y = rng.standard_normal((N, D)).astype(np.float32)
+            b = rng.standard_normal((N, E)).astype(np.float32)
+            a, n = oracle.gauss_sum(x, y, b, np.float32(sigma), lib=lib)
+            K = brute_K(x, y, np.float32(sigma))
+            rel_close(a, K @ b.astype(np.float64), 1e-12, 1e-300)
+            rel_close(n, np.abs(K[:, :, None] * b.astype(np.float64)[None]).sum(1), 1e-12, 1e-300)
+            rows = np.array(sorted(rng.choice(M, min(M, 3), replace=False)), np.int64)
+            a2, _ = oracle.gauss_sum(x, y, b, np.float32(sigma), rows=rows, lib=lib)
+            assert np.array_equal(a2, a[rows])
+
+
+def pin_sum_single_point(lib=None):
+    """M = N = 1 and x = y: K = exp(0) = 1, so a = b exactly."""
+    rng = np.random.default_rng(3)
+    for D in (1, 3, 64):
+        for E in (1, 4):
+            x = rng.standard_normal((1, D)).astype(np.float32)
+            b = rng.standard_normal((1, E)).astype(np.float32)
+            a, n = oracle.gauss_sum(x, x.copy(), b, 0.3, lib=lib)
+            assert np.array_equal(a, b.astype(np.float64))
+            assert np.array_equal(n, np.abs(b.astype(np.float64)))
+
+
+def pin_sum_sigma_infinite(lib=None):
+    """sigma -> infinity: every K_ij -> 1, so a_i -> sum_j b_j."""
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((6, 3)).astype(np.float32)
+    y = rng.standard_normal((40, 3)).astype(np.float32)
+    b = rng.standard_normal((40, 2)).astype(np.float32)
+    a, _ = oracle.gauss_sum(x, y, b, 1e8, lib=lib)
+    expect = np.broadcast_to(b.astype(np.float64).sum(0), a.shape)
+    rel_close(a, expect, 1e-12, 1e-12)
+
+
+def pin_sum_sigma_zero(lib=None):
+    """sigma -> 0: a_i -> sum of b_j over the y_j equal to x_i (others vanish)."""
+    rng = np.random.default_rng(5)
+    x = dyadic(rng, (10, 3), step=1 / 8)
+    y = np.concatenate([x[[1, 4, 4, 7]], dyadic(rng, (30, 3), step=1 / 8) + np.float32(0.0625)])
+    b = rng.standard_normal((y.shape[0], 1)).astype(np.float32)
+    a, _ = oracle.gauss_sum(x, y, b, 1e-3, lib=lib)
+    expect = np.zeros((10, 1))
+    for j in range(y.shape[0]):
+        for i in range(10):
+            if np.array_equal(x[i], y[j]):
+                expect[i, 0] += float(b[j, 0])
+    rel_close(a, expect, 1e-12, 1e-300)
+
+
+def pin_sum_separable_grid(lib=None):
+    """y on a Cartesian grid G1 x G2 x G3 with b = 1: a_i is a product of 1-D sums."""
+    rng = np.random.default_rng(6)
+    grids = [np.float32([-1.0, 0.0, 0.5, 2.0]), np.float32([-0.75, 0.25, 1.0, 1.5, 3.0]),
+             np.float32([0.0, 1.0, -2.0])]
+    y = np.array([[g0, g1, g2] for g0 in grids[0] for g1 in grids[1] for g2 in grids[2]],
+                 np.float32)
+    b = np.ones((y.shape[0], 1), np.float32)
+    x = rng.standard_normal((7, 3)).astype(np.float32)
+    sigma = 0.8
+    a, _ = oracle.gauss_sum(x, y, b, sigma, lib=lib)
+    for i in range(7):
+        prod = 1.0
+        for d in range(3):
+            prod *= sum(math.exp(-((float(x[i, d]) - float(g)) ** 2) / sigma ** 2)
+                        for g in grids[d])
+        assert abs(a[i, 0] - prod) <= 1e-12 * prod, (i, a[i, 0], prod)
+
+
+def pin_sum_translation(lib=None):
+    """Shifting x and y by the same vector leaves a unchanged (inputs exact on a dyadic grid)."""
+    rng = np.random.default_rng(7)
+    x = dyadic(rng, (9, 3))
+    y = dyadic(rng, (25, 3))
+    b = rng.standard_normal((25, 1)).astype(np.float32)
+    shift = np.float32([8.0, -4.0, 2.0])
+    a1, _ = oracle.gauss_sum(x, y, b, 1.3, lib=lib)
+    a2, _ = oracle.gauss_sum(x + shift, y + shift, b, 1.3, lib=lib)
+    n1, _ = oracle.gauss_sum(x, y, np.abs(b), 1.3, lib=lib)
+    assert np.all(np.abs(a1 - a2) <= 1e-13 * n1)
+
+
+def pin_sum_columns_independent(lib=None):
+    """Column e of a depends only on column e of b (E=3 equals three E=1 calls)."""
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((5, 4)).astype(np.float32)
+    y = rng.standard_normal((12, 4)).astype(np.float32)
+    b = rng.standard_normal((12, 3)).astype(np.float32)
+    a, _ = oracle.gauss_sum(x, y, b, 1.1, lib=lib)
+    for e in range(3):
+        ae, _ = oracle.gauss_sum(x, y, b[:, e:e + 1], 1.1, lib=lib)
+        assert np.array_equal(ae[:, 0], a[:, e])
+
+
+def pin_sum_empty(lib=None):
+    """N = 0: empty sums are 0; M = 0 gives an empty output."""
+    x = np.ones((3, 2), np.float32)
+    a, n = oracle.gauss_sum(x, np.zeros((0, 2), np.float32), np.zeros((0, 1), np.float32), 1.0,
+                            lib=lib)
+    assert a.shape == (3, 1) and not a.any() and not n.any()
+    a, n = oracle.gauss_sum(np.zeros((0, 2), np.float32), x, np.ones((3, 1), np.float32), 1.0,
+                            lib=lib)
+    assert a.shape == (0, 1)
+
+
+# --------------------------------------------------------------------------- lse
+def pin_lse_brute(lib=None):
+    """LSE equals scipy.special.logsumexp of the materialised -D_ij/sigma^2 + b_j."""
+    rng = np.random.default_rng(21)
+    for (M, N, D, E) in SHAPES:
+        for sigma in (0.2, 1.0, 3.0):
+            x = rng.standard_normal((M, D)).astype(np.float32)
+            y = rng.standard_normal((N, D)).astype(np.float32)
+            b = (3 * rng.standard_normal((N, E))).astype(np.float32)
+            l = oracle.gauss_lse(x, y, b, np.float32(sigma), lib=lib)
+            s2 = float(np.float32(sigma)) ** 2
+            V = -brute_sqdist(x, y)[:, :, None] / s2 + b.astype(np.float64)[None]
+            ref = scipy.special.logsumexp(V, axis=1)
+            rel_close(l, ref, 1e-12, 1e-12)
+
+
+def pin_lse_naive(lib=None):
+    """On moderate values LSE equals log(sum(exp(v))) written out naively."""
+    rng = np.random.default_rng(22)
+    x = rng.standard_normal((6, 3)).astype(np.float32)
+    y = rng.standard_normal((15, 3)).astype(np.float32)
+    b = rng.standard_normal((15, 1)).astype(np.float32)
+    l = oracle.gauss_lse(x, y, b, 1.5, lib=lib)
+    for i in range(6):
+        s = 0.0
+        for j in range(15):
+            d2 = sum((float(x[i, d]) - float(y[j, d])) ** 2 for d in range(3))
+            s += math.exp(-d2 / 2.25 + float(b[j, 0]))
+        assert abs(l[i, 0] - math.log(s)) <= 1e-12 * (1 + abs(math.log(s)))
+
+
+def pin_lse_shift_and_sum(lib=None):
+    """b -> b + c shifts LSE by c; with b = log w, LSE = log(sum with weights w)."""
+    rng = np.random.default_rng(23)
+    x = rng.standard_normal((8, 3)).astype(np.float32)
+    y = rng.standard_normal((30, 3)).astype(np.float32)
+    b = dyadic(rng, (30, 2), lo=-2, hi=2, step=1 / 32)
+    l0 = oracle.gauss_lse(x, y, b, 0.9, lib=lib)
+    l1 = oracle.gauss_lse(x, y, b + np.float32(40.0), 0.9, lib=lib)
+    rel_close(l1 - 40.0, l0, 0, 1e-12)
+    w = np.exp(b.astype(np.float64)).astype(np.float32)   # fp32 weights: rounding <= 6e-8 rel
+    a, _ = oracle.gauss_sum(x, y, w, 0.9, lib=lib)
+    rel_close(l0, np.log(a), 0, 2e-7)
+
+
+def pin_lse_large_offsets(lib=None):
+    """Huge |b| and tiny sigma do not overflow: the max is factored out."""
+    rng = np.random.default_rng(24)
+    x = rng.standard_normal((4, 2)).astype(np.float32)
+    y = rng.standard_normal((20, 2)).astype(np.float32)
+    b = (rng.standard_normal((20, 1)) * 3 + 800.0).astype(np.float32)
+    l = oracle.gauss_lse(x, y, b, np.float32(0.01), lib=lib)
+    V = -brute_sqdist(x, y) / float(np.float32(0.01)) ** 2 + b.astype(np.float64)[:, 0][None]
+    rel_close(l[:, 0], scipy.special.logsumexp(V, axis=1), 1e-13, 0)
+    assert np.isfinite(l).all()
+
+
+def pin_lse_empty(lib=None):
+    """N = 0: the log of an empty sum is -inf."""
+    l = oracle.gauss_lse(np.ones((2, 3), np.float32), np.zeros((0, 3), np.float32),
+                         np.zeros((0, 1), np.float32), 1.0, lib=lib)
+    assert np.all(np.isneginf(l))
+
+
+# --------------------------------------------------------------------------- grad_x
+def pin_grad_autograd(lib=None):
+    """grad_x equals torch float64 autograd of sum(g * a) on the materialised matrix."""
+    rng = np.random.default_rng(31)
+    for (M, N, D, E) in SHAPES:
+        sigma = np.float32(0.9 * math.sqrt(D))
+        x = rng.standard_normal((M, D)).astype(np.float32)
+        y = rng.standard_normal((N, D)).astype(np.float32)
+        b = rng.standard_normal((N, E)).astype(np.float32)
+        g = rng.standard_normal((M, E)).astype(np.float32)
+        G, nu = oracle.gauss_grad_x(x, y, b, g, sigma, lib=lib)
+        xt = torch.tensor(x, dtype=torch.float64, requires_grad=True)
+        yt = torch.tensor(y, dtype=torch.float64)
+        d2 = ((xt[:, None, :] - yt[None, :, :]) ** 2).sum(-1)
+        a = torch.exp(-d2 / float(sigma) ** 2) @ torch.tensor(b, dtype=torch.float64)
+        (ref,) = torch.autograd.grad((a * torch.tensor(g, dtype=torch.float64)).sum(), [xt])
+        rel_close(G, ref.numpy(), 0, 1e-12 * (1 + nu.max()))
+        assert np.all(np.abs(G) <= nu * (1 + 1e-12))
+
+
+def pin_grad_finite_differences(lib=None):
+    """Central differences of L(x) = sum_ie g_ie a_ie(x), all in double, match grad_x."""
+    rng = np.random.default_rng(32)
+    M, N, D, E = 4, 25, 3, 2
+    x = dyadic(rng, (M, D), lo=-1, hi=1, step=1 / 16)
+    y = rng.standard_normal((N, D)).astype(np.float32)
+    b = rng.standard_normal((N, E)).astype(np.float32)
+    g = rng.standard_normal((M, E)).astype(np.float32)
+    sigma = 1.25
+    G, nu = oracle.gauss_grad_x(x, y, b, g, sigma, lib=lib)
+    h = np.float32(2.0 ** -10)            # x +- h stays exact in fp32
+    for i in range(M):
+        for d in range(D):
+            xp, xm = x.copy(), x.copy()
+            xp[i, d] += h
+            xm[i, d] -= h
+            ap, _ = oracle.gauss_sum(xp, y, b, sigma, lib=lib)
+            am, _ = oracle.gauss_sum(xm, y, b, sigma, lib=lib)
+            fd = ((ap - am) * g.astype(np.float64)).sum() / (2 * float(h))
+            assert abs(fd - G[i, d]) <= 1e-5 * nu[i, d] + 1e-12, (i, d, fd, G[i, d], nu[i, d])
+
+
+def pin_grad_identity(lib=None):
+    """E = 1: G_i = (-2/sigma^2) g_i (x_i a_i - sum_j K_ij b_j y_j), from sum-oracle calls."""
+    rng = np.random.default_rng(33)
+    M, N, D = 6, 40, 3
+    x = dyadic(rng, (M, D), step=1 / 16)
+    y = dyadic(rng, (N, D), step=1 / 16)
+    b = dyadic(rng, (N, 1), step=1 / 16)
+    g = dyadic(rng, (M, 1), step=1 / 16)
+    sigma = 1.5
+    G, nu = oracle.gauss_grad_x(x, y, b, g, sigma, lib=lib)
+    a, _ = oracle.gauss_sum(x, y, b, sigma, lib=lib)
+    by = (b * y).astype(np.float32)       # exact: few mantissa bits on each side
+    assert np.array_equal(by.astype(np.float64), b.astype(np.float64) * y.astype(np.float64))
+    s, _ = oracle.gauss_sum(x, y, by, sigma, lib=lib)
+    expect = (-2 / sigma ** 2) * g.astype(np.float64) * (x.astype(np.float64) * a - s)
+    rel_close(G, expect, 0, 1e-12 * (1 + nu.max()))
+
+
+# --------------------------------------------------------------------------- kmin
+def pin_kmin_argsort(lib=None):
+    """K-min equals a stable argsort of the materialised distances (ties -> smaller j)."""
+    rng = np.random.default_rng(41)
+    for (M, N, D, _) in SHAPES:
+        for K in sorted({1, min(N, 3), min(N, 10), N}):
+            x = rng.standard_normal((M, D)).astype(np.float32)
+            y = rng.standard_normal((N, D)).astype(np.float32)
+            if N >= 4:                     # exact duplicates force distance ties
+                y[N - 1] = y[1]
+                y[N - 2] = y[0]
+            d, idx = oracle.kmin(x, y, K, lib=lib)
+            D2 = brute_sqdist(x, y)
+            order = np.argsort(D2, axis=1, kind="stable")[:, :K]
+            assert np.array_equal(idx, order), (M, N, D, K)
+            assert np.array_equal(d, np.take_along_axis(D2, order, 1))
+
+
+def pin_kmin_invariants(lib=None):
+    """K = 1 is argmin; K = N is a permutation; returned distances recompute exactly."""
+    rng = np.random.default_rng(42)
+    x = rng.standard_normal((10, 3)).astype(np.float32)
+    y = rng.standard_normal((50, 3)).astype(np.float32)
+    d1, i1 = oracle.kmin(x, y, 1, lib=lib)
+    D2 = brute_sqdist(x, y)
+    assert np.array_equal(i1[:, 0], D2.argmin(1))
+    dN, iN = oracle.kmin(x, y, 50, lib=lib)
+    assert all(sorted(r) == list(range(50)) for r in iN.tolist())
+    assert np.all(np.diff(dN, axis=1) >= 0)
+    ii = np.repeat(np.arange(10), 50)
+    again = oracle.sq_dist_pairs(x, y, ii, iN.ravel(), lib=lib)
+    assert np.array_equal(again, dN.ravel())
+    # x = y: the self-match is rank 0 at distance 0
+    d0, i0 = oracle.kmin(y, y, 3, lib=lib)
+    assert np.array_equal(i0[:, 0], np.arange(50)) and not d0[:, 0].any()
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

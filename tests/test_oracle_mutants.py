@@ -1,0 +1,62 @@
+"""Plant plausible mistakes in copies of the oracle source; the pins must catch each one.
+
+Every mutant is a one-token edit of keops_oracle.c (a dropped term, a flipped
+sign, a wrong index, a broken tie-break).  The copy is compiled to a temporary
+library and the full pin set runs against it; the test passes only if at
+least one pin fails.  The committed oracle is never modified.
+"""
+import os
+
+import pytest
+
+import oracle
+import oracle_pins
+
+MUTANTS = {
+    "sqdist_no_square": ("s += t * t;", "s += t;"),
+    "sqdist_abs": ("s += t * t;", "s += t * (t < 0 ? -t : t);"),
+    "kernel_sign": ("const double k = exp(-sq_dist(x + i * D, y + j * D, D) * inv_s2);\n"
+                    "            for (int e = 0; e < E; ++e) {",
+                    "const double k = exp(sq_dist(x + i * D, y + j * D, D) * inv_s2 - 1.0);\n"
+                    "            for (int e = 0; e < E; ++e) {"),
+    "sigma_not_squared": ("const double inv_s2 = 1.0 / (sigma * sigma);\n#pragma omp parallel for schedule(dynamic, 1)\n"
+                          "    for (int64_t r = 0; r < nrows; ++r) {\n        const int64_t i = rows ? rows[r] : r;\n"
+                          "        double *o = out + r * E,",
+                          "const double inv_s2 = 1.0 / (2.0 * sigma * sigma);\n#pragma omp parallel for schedule(dynamic, 1)\n"
+                          "    for (int64_t r = 0; r < nrows; ++r) {\n        const int64_t i = rows ? rows[r] : r;\n"
+                          "        double *o = out + r * E,"),
+    "sum_b_column": ("const double t = k * (double)b[j * E + e];", "const double t = k * (double)b[j * E];"),
+    "sum_row_index": ("const int64_t i = rows ? rows[r] : r;\n        double *o = out + r * E,",
+                      "const int64_t i = r;\n        double *o = out + r * E,"),
+    "lse_drop_max": ("out[r * E + e] = m + log(s);", "out[r * E + e] = log(s);"),
+    "lse_b_sign": ("* inv_s2 + (double)b[j * E + e];\n                    s += exp(v - m);",
+                   "* inv_s2 - (double)b[j * E + e];\n                    s += exp(v - m);"),
+    "grad_factor": ("const double t = -2.0 * inv_s2 * k * gb", "const double t = -1.0 * inv_s2 * k * gb"),
+    "grad_sign": ("((double)x[i * D + d] - (double)y[j * D + d]);\n                o[d] += t;",
+                  "((double)y[j * D + d] - (double)x[i * D + d]);\n                o[d] += t;"),
+    "grad_g_index": ("gb += (double)g[i * E + e] * (double)b[j * E + e];",
+                     "gb += (double)g[e] * (double)b[j * E + e];"),
+    "grad_transposed_gb": ("gb += (double)g[i * E + e] * (double)b[j * E + e];",
+                           "gb += (double)g[i * E + (E - 1 - e)] * (double)b[j * E + e];"),
+    "kmin_tie_break": ("(dj == bd[pos - 1] && j < bj[pos - 1])", "(dj == bd[pos - 1] && j > bj[pos - 1])"),
+    "kmin_keep_last": ("if (count == K && !(dj < bd[K - 1]", "if (count == K && !(dj <= bd[K - 1]"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(oracle.SOURCE).read()
+    assert src.count(old) >= 1, f"mutation site for {name} not found"
+    mutated = src.replace(old, new, 1)
+    path = os.path.join(str(tmp_path), "mutant.c")
+    with open(path, "w") as f:
+        f.write(mutated)
+    lib = oracle.open_library(oracle.compile_source(path, os.path.join(str(tmp_path), "libm.so")))
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(lib=lib)
+        except (AssertionError, ValueError, FloatingPointError):
+            caught.append(pin.__name__)
+    assert caught, f"mutant {name} survived every pin"
