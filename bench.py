@@ -1,0 +1,223 @@
+#!/usr/bin/env python
+"""Benchmark of the Gaussian kernel mat-vec on one MI355X.
+
+Default workload (one "step" = one call of the whole hot path on resident
+inputs): the Gaussian kernel sum a_i = sum_j exp(-|x_i - y_j|^2 / sigma^2) b_j
+at M = N = 1,000,000, D = 3, E = 1, sigma = 0.1, x, y ~ U[0,1)^3,
+b ~ N(0, 1), seed 0 -- the shape of the KeOps paper's benchmark (M = N
+points in dimension 3; timings quoted up to N = 1M).
+
+Prints ONE JSON line:
+  value         G pair-evaluations per second (M*N / time per step)
+  roofline      fp32 VALU roofline of the pair-evaluation kernel: algorithmic
+                flops per launch (12 per pair at D = 3, E = 1) / the kernel's
+                average duration, measured here with HIP events recorded by
+                the library around each launch on the call's stream;
+                traffic = HBM bytes per launch from the recorded rocprofv3
+                counter runs (null when the kernel sources changed since)
+  cpu_baseline  the float64 oracle timed on this host's cores over a bounded
+                sample of rows (each row over all N), scaled to pair-evals/s
+Other workloads (--workload) print the same fields for their own op.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Gaussian kernel mat-vec G pair-evals/s @ M=N=1M,D=3; % fp32 VALU peak"
+PEAK_FP32_TFLOPS = 157.3          # MI355X fp32 vector (and fp32 MFMA) peak
+PAGES_PAIRS_PER_S_1M = 1e12 / 1.38  # the pages' KeOps timing at N = 1M (hardware not stated)
+
+# (op, workload name, algorithmic flops per pair)
+#  sum: 3D + 1 + 2E (D subtractions, D squares, D-1 adds, 1 scale, 1 exp, E multiply-adds)
+#  lse: 3D + 5 (distance 3D-1, scale, +b, max, -m, exp, add)
+#  grad: 5D + 2E + 1;  kmin: 3D (distance 3D-1, compare)
+BENCHES = {
+    "sum": ("sum", "sum_lse_1M"),
+    "lse": ("lse", "sum_lse_1M"),
+    "grad": ("grad_x", "sum_grad_10k"),
+    "sum10k": ("sum", "sum_grad_10k"),
+    "sum1k": ("sum", "sum_1k"),
+    "solver": ("sum", "solver_matvec_100k_x_10M"),
+    "kmin3": ("kmin", "kmin10_1M_d3"),
+    "kmin64": ("kmin", "kmin10_1M_d64"),
+}
+
+
+def flops_per_pair(op, D, E):
+    return {"sum": 3 * D + 1 + 2 * E, "lse": 3 * D + 5, "grad_x": 5 * D + 2 * E + 1, "kmin": 3 * D}[op]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "geometric_map_reduce_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(bench_name):
+    """HBM bytes per launch from profiles/traffic_<bench>.json if it matches the current sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{bench_name}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_sources_sha256") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def run_op(gm, op, X, Y, B, G, sigma, K, out):
+    if op == "sum":
+        return gm.keops_gauss_sum(X, Y, B, sigma, out=out)
+    if op == "lse":
+        return gm.keops_gauss_lse(X, Y, B, sigma, out=out)
+    if op == "grad_x":
+        return gm.keops_gauss_grad_x(X, Y, B, G, sigma, out=out)
+    return gm.keops_kmin(X, Y, K, out_d=out[0], out_idx=out[1])
+
+
+def cpu_baseline(op, w, x, y, b, g, target_s, gpu_out):
+    import numpy as np
+
+    import oracle
+    from geometric_map_reduce_amd import workloads
+
+    def call(rows):
+        t0 = time.perf_counter()
+        if op == "sum":
+            res = oracle.gauss_sum(x, y, b, w.sigma, rows=rows)
+        elif op == "lse":
+            res = oracle.gauss_lse(x, y, b, w.sigma, rows=rows)
+        elif op == "grad_x":
+            res = oracle.gauss_grad_x(x, y, b, g, w.sigma, rows=rows)
+        else:
+            res = oracle.kmin(x, y, w.K, rows=rows)
+        return time.perf_counter() - t0, res
+
+    probe = workloads.sample_rows(w.M, min(w.M, 64), seed=2)
+    t_probe, _ = call(probe)
+    per_row = max(t_probe / len(probe), 1e-9)
+    n = int(min(w.M, max(64, target_s / per_row)))
+    rows = workloads.sample_rows(w.M, n, seed=1)
+    t, res = call(rows)
+    pairs = len(rows) * w.N
+    base = {"value": pairs / t / 1e9, "unit": "G pair-evals/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{len(rows)} seeded rows x all {w.N} j (float64 C/OpenMP oracle), {t:.1f} s"}
+    # the same rows double as a spot check of the GPU result
+    check = None
+    if op in ("sum", "grad_x"):
+        ref, nrm = res
+        gpu = gpu_out[rows].reshape(ref.shape).astype(np.float64)
+        check = {"rows": len(rows), "max_err_over_norm": float(np.max(np.abs(gpu - ref) / np.maximum(nrm, 1e-300)))}
+    elif op == "lse":
+        check = {"rows": len(rows), "max_abs_err": float(np.max(np.abs(gpu_out[rows].astype(np.float64) - res)))}
+    return base, check
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="sum", choices=sorted(BENCHES))
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}): this engine "
+              "has no multi-GPU path; the one-GPU throughput is the reported value.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import geometric_map_reduce_amd as gm
+    from geometric_map_reduce_amd import workloads
+
+    op, wname = BENCHES[args.workload]
+    w = workloads.WORKLOADS[wname]
+    x, y, b = workloads.make_inputs(w)
+    dev = torch.device("cuda:0")
+    X, Y = torch.from_numpy(x).to(dev), torch.from_numpy(y).to(dev)
+    B = torch.from_numpy(b).to(dev) if b is not None else None
+    g = None
+    G = None
+    if op == "grad_x":
+        g = np.random.default_rng(3).standard_normal((w.M, w.E)).astype(np.float32)
+        G = torch.from_numpy(g).to(dev)
+    if op == "kmin":
+        out = (torch.empty((w.M, w.K), device=dev), torch.empty((w.M, w.K), device=dev, dtype=torch.int64))
+    else:
+        out = torch.empty((w.M, w.D if op == "grad_x" else w.E), device=dev)
+
+    for _ in range(args.warmup):
+        run_op(gm, op, X, Y, B, G, w.sigma, w.K, out)
+    torch.cuda.synchronize()
+
+    gm.keops_set_option(gm.KEOPS_OPT_PROFILE, 1)
+    gm.keops_profile_read()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        run_op(gm, op, X, Y, B, G, w.sigma, w.K, out)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gm.keops_set_option(gm.KEOPS_OPT_PROFILE, 0)
+    kern_ms, launches = gm.keops_profile_read()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+
+    pairs = w.M * w.N
+    value = pairs / (ms_step * 1e-3) / 1e9
+    fpp = flops_per_pair(op, w.D, w.E)
+    kern_avg_ms = kern_ms / max(launches, 1)
+    achieved = fpp * pairs / (kern_avg_ms * 1e-3) / 1e12
+    traffic = recorded_traffic(args.workload)
+
+    res = {
+        "metric": METRIC if args.workload == "sum" else f"{op} G pair-evals/s @ {w.name}",
+        "value": round(value, 3),
+        "unit": "G pair-evals/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(value / (PAGES_PAIRS_PER_S_1M / 1e9), 3) if args.workload == "sum" else None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": dict(w.describe(), op=op, seed=0),
+        "roofline": {"bound": "alu", "achieved": round(achieved, 3), "peak": PEAK_FP32_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_TFLOPS, 4), "traffic": traffic},
+        "kernel": {"name": f"gauss_valu_kernel<{op}>" if op != "kmin" else "kmin_valu_kernel",
+                   "avg_ms": round(kern_avg_ms, 4), "launches": launches, "flops_per_pair": fpp},
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        gpu_out = (out[0] if op == "kmin" else out).cpu().numpy()
+        base, check = cpu_baseline(op, w, x, y, b, g, args.cpu_seconds, gpu_out)
+        res["cpu_baseline"] = base
+        if check is not None:
+            res["check"] = check
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,1 +1,17 @@
-"""MI355X (gfx950) engine for KeOps-style Gaussian map-reductions (placeholder; binding below)."""
+"""MI355X (gfx950) engine for KeOps-style Gaussian map-reductions.
+
+Four reductions over the symbolic matrix K_ij = exp(-|x_i - y_j|^2 / sigma^2),
+never stored, run as hand-written gfx950 HIP kernels behind the C ABI of
+``include/keops_mi355x.h`` (library ``libkeops_mi355x.so``, built by
+``geometric_map_reduce_amd.build``):
+
+* ``keops_gauss_sum``    -- a_i = sum_j K_ij b_j
+* ``keops_gauss_lse``    -- log sum_j exp(-|x_i - y_j|^2/sigma^2 + b_j)
+* ``keops_gauss_grad_x`` -- gradient of the sum with respect to x
+* ``keops_kmin``         -- K nearest neighbours with indices
+
+PyTorch supplies device memory and streams only.
+"""
+from .binding import (KEOPS_OPT_FORM, KEOPS_OPT_PROFILE, KEOPS_OPT_ROWS, KEOPS_OPT_SPLIT_J,  # noqa: F401
+                      KeopsError, keops_gauss_grad_x, keops_gauss_lse, keops_gauss_sum, keops_kmin,
+                      keops_profile_read, keops_set_option, keops_version, lib, status_string)

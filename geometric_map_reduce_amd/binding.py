@@ -1,0 +1,179 @@
+"""Thin ctypes binding of the C ABI in include/keops_mi355x.h.
+
+Argument marshalling only: every step of the computation runs in the gfx950
+kernels of ``libkeops_mi355x.so``.  Tensors must be CUDA (HIP) float32 tensors
+on one device; outputs may be passed in (``out=``, the caller-allocated
+output of the "Transparent interface for billion-scale matrices" issue) or are
+allocated here with ``torch.empty``.  Calls are enqueued on the current torch
+stream of the tensors' device unless ``stream`` is given.  ctypes releases the
+Python lock for the duration of each call.
+
+If the library has not been built the first call raises: there is no CPU
+fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkeops_mi355x.so")
+
+KEOPS_OK = 0
+KEOPS_ERR_INVALID_ARG = -1
+KEOPS_ERR_UNSUPPORTED = -2
+KEOPS_ERR_ALLOC = -3
+KEOPS_ERR_HIP = -4
+KEOPS_OPT_SPLIT_J = 1
+KEOPS_OPT_FORM = 2
+KEOPS_OPT_ROWS = 3
+KEOPS_OPT_PROFILE = 4
+
+_lock = threading.Lock()
+_lib = None
+
+
+class KeopsError(RuntimeError):
+    def __init__(self, name: str, status: int, msg: str):
+        super().__init__(f"{name}: {msg} (status {status})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    f"{LIB_PATH} is missing: build the gfx950 library first "
+                    "(python -m geometric_map_reduce_amd.build); there is no CPU fallback")
+            L = ctypes.CDLL(LIB_PATH)
+            P, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+            L.keops_gauss_sum.argtypes = [P, P, P, i64, i64, i32, i32, f32, P, P]
+            L.keops_gauss_lse.argtypes = [P, P, P, i64, i64, i32, i32, f32, P, P]
+            L.keops_gauss_grad_x.argtypes = [P, P, P, P, i64, i64, i32, i32, f32, P, P]
+            L.keops_kmin.argtypes = [P, P, i64, i64, i32, i32, P, P, P]
+            L.keops_set_option.argtypes = [ctypes.c_int, i64]
+            L.keops_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
+            L.keops_status_string.argtypes = [ctypes.c_int]
+            L.keops_status_string.restype = ctypes.c_char_p
+            for f in ("keops_gauss_sum", "keops_gauss_lse", "keops_gauss_grad_x", "keops_kmin",
+                      "keops_set_option", "keops_version", "keops_profile_read"):
+                getattr(L, f).restype = ctypes.c_int
+            _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().keops_status_string(int(status)).decode()
+
+
+def _check(name, rc):
+    if rc != KEOPS_OK:
+        raise KeopsError(name, rc, status_string(rc))
+
+
+def _mat(t, name, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dim() == 1:
+        t = t.view(-1, 1)
+    if t.dim() != 2 or t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous 2-D float32 CUDA tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    return t
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else None
+
+
+def _stream(stream, device):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _out(out, shape, device, dtype=torch.float32, name="out"):
+    if out is None:
+        return torch.empty(shape, device=device, dtype=dtype)
+    if tuple(out.shape) != tuple(shape) or out.dtype != dtype or out.device != device or not out.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} on {device}")
+    return out
+
+
+def _gauss(fn_name, x, y, b, sigma, out, stream, g=None):
+    x = _mat(x, "x")
+    dev = x.device
+    y, b = _mat(y, "y", dev), _mat(b, "b", dev)
+    M, D = x.shape
+    N, E = b.shape
+    if y.shape != (N, D):
+        raise ValueError(f"y must be [N, D] = [{N}, {D}], got {tuple(y.shape)}")
+    args = [_ptr(x), _ptr(y), _ptr(b)]
+    if g is not None:
+        g = _mat(g, "g", dev)
+        if g.shape != (M, E):
+            raise ValueError(f"g must be [M, E] = [{M}, {E}]")
+        args.append(_ptr(g))
+    out = _out(out, (M, D if g is not None else E), dev)
+    with torch.cuda.device(dev):
+        rc = getattr(lib(), fn_name)(*args, M, N, D, E, float(sigma), _ptr(out), _stream(stream, dev))
+    _check(fn_name, rc)
+    return out
+
+
+def keops_gauss_sum(x, y, b, sigma, out=None, stream=None):
+    """out[i, e] = sum_j exp(-|x_i - y_j|^2 / sigma^2) b[j, e]   (x [M,D], y [N,D], b [N,E])."""
+    return _gauss("keops_gauss_sum", x, y, b, sigma, out, stream)
+
+
+def keops_gauss_lse(x, y, b, sigma, out=None, stream=None):
+    """out[i, e] = log sum_j exp(-|x_i - y_j|^2 / sigma^2 + b[j, e])."""
+    return _gauss("keops_gauss_lse", x, y, b, sigma, out, stream)
+
+
+def keops_gauss_grad_x(x, y, b, g, sigma, out=None, stream=None):
+    """out[i, d] = sum_j (-2/sigma^2) K_ij <g_i, b_j> (x_id - y_jd), the VJP of the sum with cotangent g."""
+    return _gauss("keops_gauss_grad_x", x, y, b, sigma, out, stream, g=g)
+
+
+def keops_kmin(x, y, K, out_d=None, out_idx=None, stream=None):
+    """K smallest |x_i - y_j|^2 per row (ascending, ties by smaller j) and their int64 indices."""
+    x = _mat(x, "x")
+    dev = x.device
+    y = _mat(y, "y", dev)
+    M, D = x.shape
+    N = y.shape[0]
+    if y.shape[1] != D:
+        raise ValueError("x and y must have the same number of columns")
+    out_d = _out(out_d, (M, K), dev, name="out_d")
+    out_idx = _out(out_idx, (M, K), dev, dtype=torch.int64, name="out_idx")
+    with torch.cuda.device(dev):
+        rc = lib().keops_kmin(_ptr(x), _ptr(y), M, N, D, int(K), _ptr(out_d), _ptr(out_idx),
+                              _stream(stream, dev))
+    _check("keops_kmin", rc)
+    return out_d, out_idx
+
+
+def keops_set_option(option: int, value: int) -> None:
+    """Process-wide scheduling switch (KEOPS_OPT_*); 0 restores the automatic choice."""
+    _check("keops_set_option", lib().keops_set_option(int(option), int(value)))
+
+
+def keops_profile_read() -> tuple[float, int]:
+    """(summed pass-1 kernel milliseconds, launches) recorded while KEOPS_OPT_PROFILE was 1."""
+    ms, n = ctypes.c_double(0.0), ctypes.c_int64(0)
+    _check("keops_profile_read", lib().keops_profile_read(ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
+
+
+def keops_version() -> int:
+    return int(lib().keops_version())

@@ -1,0 +1,105 @@
+// combine.hip -- pass 2 of the split-j reductions and the empty-N fills.
+//
+// With S splits of the j range, pass 1 leaves S partial results per row:
+//   sum / grad_x : partial sums,               combined as  sum_s p_s
+//   LogSumExp    : (m_s, s_s) in log2 units,   combined as  m = max_s m_s,
+//                  s = sum_s s_s 2^(m_s - m),  out = ln2 (m + log2 s)
+//   K-min        : sorted (d^2, j) lists,      merged by (d^2, j) order.
+// Splits are visited in order, so results do not depend on scheduling.
+#include "common.h"
+#include "launch.h"
+
+namespace kmi {
+
+__global__ __launch_bounds__(kThreads) void sum_combine_kernel(const float *__restrict__ ws, int nsplit,
+                                                               int64_t count, float *__restrict__ out) {
+  const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (t >= count) return;
+  float s = 0.0f;
+  for (int k = 0; k < nsplit; ++k) s += ws[(int64_t)k * count + t];
+  out[t] = s;
+}
+
+__global__ __launch_bounds__(kThreads) void lse_combine_kernel(const float *__restrict__ ws, int nsplit,
+                                                               int64_t M, int E, float *__restrict__ out) {
+  const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (t >= M * E) return;
+  const int64_t i = t / E;
+  const int e = (int)(t - i * E);
+  const int64_t stride = M * 2 * E;
+  const float *p = ws + i * 2 * E + 2 * e;
+  float m = -3.0e38f;
+  for (int k = 0; k < nsplit; ++k) m = fmaxf(m, p[k * stride]);
+  float s = 0.0f;
+  for (int k = 0; k < nsplit; ++k) s += p[k * stride + 1] * exp2f(p[k * stride] - m);
+  out[t] = kLn2 * (m + log2f(s));
+}
+
+template <int K>
+__global__ __launch_bounds__(kThreads) void kmin_combine_kernel(const float *__restrict__ pd, const int32_t *__restrict__ pi,
+                                                                int nsplit, int64_t M, float *__restrict__ out_d,
+                                                                int64_t *__restrict__ out_i) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= M) return;
+  float bd[K];
+  int bi[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) { bd[k] = INFINITY; bi[k] = 0x7fffffff; }
+  for (int s = 0; s < nsplit; ++s) {
+    const int64_t base = ((int64_t)s * M + i) * K;
+    for (int q = 0; q < K; ++q) {
+      const float v = pd[base + q];
+      const int j = pi[base + q];
+      if (j < 0) break;                              // rest of this list is empty
+      if (!(v < bd[K - 1] || (v == bd[K - 1] && j < bi[K - 1]))) break;   // lists are sorted
+#pragma unroll
+      for (int k = K - 1; k > 0; --k) {
+        const bool shift = v < bd[k - 1] || (v == bd[k - 1] && j < bi[k - 1]);
+        const bool here = v < bd[k] || (v == bd[k] && j < bi[k]);
+        const float nd = shift ? bd[k - 1] : (here ? v : bd[k]);
+        const int ni = shift ? bi[k - 1] : (here ? j : bi[k]);
+        bd[k] = nd;
+        bi[k] = ni;
+      }
+      if (v < bd[0] || (v == bd[0] && j < bi[0])) { bd[0] = v; bi[0] = j; }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    out_d[i * K + k] = bd[k];
+    out_i[i * K + k] = bi[k] == 0x7fffffff ? -1 : (int64_t)bi[k];
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void fill_kernel(float *__restrict__ out, int64_t count, float v) {
+  const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (t < count) out[t] = v;
+}
+
+static inline unsigned blocks_for(int64_t n) { return (unsigned)((n + kThreads - 1) / kThreads); }
+
+void launch_sum_combine(const float *ws, int nsplit, int64_t count, float *out, hipStream_t st) {
+  if (count > 0) hipLaunchKernelGGL(sum_combine_kernel, dim3(blocks_for(count)), dim3(kThreads), 0, st, ws, nsplit, count, out);
+}
+
+void launch_lse_combine(const float *ws, int nsplit, int64_t M, int E, float *out, hipStream_t st) {
+  if (M * E > 0) hipLaunchKernelGGL(lse_combine_kernel, dim3(blocks_for(M * E)), dim3(kThreads), 0, st, ws, nsplit, M, E, out);
+}
+
+int launch_kmin_combine(const float *pd, const int32_t *pi, int nsplit, int64_t M, int K, float *out_d,
+                        int64_t *out_i, hipStream_t st) {
+  if (M == 0) return 0;
+  const dim3 g(blocks_for(M)), b(kThreads);
+  switch (K) {
+#define KC(KK) case KK: hipLaunchKernelGGL((kmin_combine_kernel<KK>), g, b, 0, st, pd, pi, nsplit, M, out_d, out_i); return 0;
+    KC(1) KC(2) KC(3) KC(4) KC(5) KC(6) KC(7) KC(8) KC(9) KC(10) KC(11) KC(12) KC(13) KC(14) KC(15) KC(16) KC(32)
+#undef KC
+    default: return -2;
+  }
+}
+
+void launch_fill(float *out, int64_t count, float v, hipStream_t st) {
+  if (count > 0) hipLaunchKernelGGL(fill_kernel, dim3(blocks_for(count)), dim3(kThreads), 0, st, out, count, v);
+}
+
+}  // namespace kmi

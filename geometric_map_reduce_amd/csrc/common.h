@@ -1,0 +1,126 @@
+// common.h -- internal definitions shared by the gfx950 kernels and the host
+// launcher of the Gaussian map-reduce engine (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kmi {
+
+constexpr int kThreads = 256;           // work-group: four wave64
+constexpr int kWave = 64;
+constexpr int kTileJ = 256;             // j rows staged in LDS per tile (one per thread)
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2 = 0.69314718055994530942f;
+// Largest |x'_i|^2 (scaled, centred, log2 units) for which the expanded form
+// exp2(2<x',y'> - |y'|^2 - G) keeps both range and precision; see the design doc.
+constexpr float kFastR2 = 128.0f;
+// Exponent offset (log2 units) of the direct form's sums and gradients.
+constexpr float kDirectOffset = 64.0f;
+
+enum Op : int { OP_SUM = 0, OP_LSE = 1, OP_GRAD = 2 };
+enum Form : int { FORM_AUTO = 0, FORM_DIRECT = 1 };
+
+// Arguments of the sum / LSE / grad_x pass-1 kernels.
+struct GaussArgs {
+  const float *x, *y, *b, *g;
+  int64_t M, N;
+  float scale;          // sqrt(log2 e) / sigma: exp(-d^2/sigma^2) = exp2(-|scale*(x-y)|^2)
+  float grad_coef;      // -(2 / sigma^2) / scale  (expanded form: scaled coordinates)
+  float grad_coef_direct;  // -(2 / sigma^2)        (direct form: raw coordinates)
+  float *out;           // final output when nsplit == 1, else partials [nsplit][M][W]
+  int64_t j_per_split;  // multiple of kTileJ
+  int nsplit;
+  int form;             // Form
+};
+
+// Arguments of the K-min pass-1 kernel.
+struct KminArgs {
+  const float *x, *y;
+  int64_t M, N;
+  float *out_d;         // [M][K] when nsplit == 1, else partial distances [nsplit][M][K]
+  int64_t *out_idx;     // [M][K] when nsplit == 1
+  int32_t *part_idx;    // partial indices [nsplit][M][K] when nsplit > 1
+  int64_t j_per_split;
+  int nsplit;
+};
+
+// ---------------------------------------------------------------- wave / block reductions
+// Cross-lane steps use DPP inside 16-lane rows and a swizzle/bpermute across rows.
+__device__ __forceinline__ float dpp_quad_xor1(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_quad_xor2(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_row_half_mirror(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_row_mirror(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+}
+
+// Every lane of each 16-lane row receives the row's sum.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_quad_xor1(v);
+  v += dpp_quad_xor2(v);
+  v += dpp_row_half_mirror(v);
+  v += dpp_row_mirror(v);
+  return v;
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_quad_xor1(v));
+  v = fmaxf(v, dpp_quad_xor2(v));
+  v = fmaxf(v, dpp_row_half_mirror(v));
+  v = fmaxf(v, dpp_row_mirror(v));
+  return v;
+}
+__device__ __forceinline__ float row16_min(float v) {
+  v = fminf(v, dpp_quad_xor1(v));
+  v = fminf(v, dpp_quad_xor2(v));
+  v = fminf(v, dpp_row_half_mirror(v));
+  v = fminf(v, dpp_row_mirror(v));
+  return v;
+}
+// Whole-wave reductions: rows of 16 by DPP, then the four row results by xor-shuffles.
+__device__ __forceinline__ float wave_max(float v) {
+  v = row16_max(v);
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+__device__ __forceinline__ float wave_min(float v) {
+  v = row16_min(v);
+  v = fminf(v, __shfl_xor(v, 16));
+  v = fminf(v, __shfl_xor(v, 32));
+  return v;
+}
+
+// Work-group max / min of one value per thread; `red` holds kThreads/kWave floats.
+// Contains barriers: every thread of the work-group must call it.
+__device__ __forceinline__ float block_max(float v, float *red) {
+  v = wave_max(v);
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) red[w] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int k = 1; k < kThreads / kWave; ++k) r = fmaxf(r, red[k]);
+  return r;
+}
+__device__ __forceinline__ float block_min(float v, float *red) {
+  v = wave_min(v);
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) red[w] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int k = 1; k < kThreads / kWave; ++k) r = fminf(r, red[k]);
+  return r;
+}
+
+__device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
+
+}  // namespace kmi

@@ -1,0 +1,451 @@
+// gauss_kernel.h -- pass-1 kernel of the Gaussian sum, LogSumExp and grad_x
+// reductions on gfx950 VALU (the D < 32 hot path; also the reference VALU
+// path at large D).
+//
+// Operation (KeOps pages: "Kernel Operations on the GPU, with Autodiff,
+// without Memory Overflows" §1 "Target operation" and §2; KeOps README
+// example): for each row i, reduce over j the Gaussian coefficients
+// K_ij = exp(-|x_i - y_j|^2 / sigma^2) without storing them.
+//
+// Layout of one work-group (256 threads = 4 wave64):
+//   * rows: thread t owns rows i = row0 + r*256 + t, r < R, held in VGPRs;
+//   * j-tiles: TJ rows of y (and b) are read from HBM with coalesced loads,
+//     transformed once per work-group and stored in LDS as one record per j;
+//     all lanes then read the same record (broadcast ds_read_b128);
+//   * double-buffered LDS: the next tile's global loads are in flight while
+//     the current tile is reduced; one barrier per tile;
+//   * per-tile partial sums, folded into the row accumulators at the end of
+//     each tile, so that a long j range does not round small terms away;
+//   * split-j: blockIdx.y selects a j-range; partial results go to a
+//     workspace that a second kernel combines.
+//
+// Two forms of the pair map, chosen once per work-group:
+//   EXPANDED: coordinates centred on the work-group's bounding-box centre c
+//            and scaled by s = sqrt(log2 e)/sigma (x' = s(x - c)), so that
+//            K_ij = exp2(<x'_i, 2y'_j> + c_j) * exp2(G - |x'_i|^2) with
+//            c_j = -|y'_j|^2 - G.  Three FMAs and one v_exp_f32 per pair at
+//            D = 3; the row factor is applied once per row at the end.  Used
+//            when max_i |x'_i|^2 <= kFastR2 over the work-group, which bounds
+//            both the exponent range (|exponent| <= 64 + |x'-y'|^2) and the
+//            rounding of the expansion (about 1e-5 relative in K_ij).
+//   DIRECT  : K_ij = exp2(-s^2 sum_k (x_k - y_k)^2) from raw coordinates (the
+//            difference is taken first, so far-apart or far-from-origin
+//            points keep full relative precision); the fallback.  Sums and
+//            gradients evaluate exp2(64 - s^2 |x - y|^2) and scale the row by
+//            2^-64 at the end, which moves the flush-to-zero floor of
+//            v_exp_f32 from 2^-126 to 2^-190 (a gradient multiplies tiny
+//            K_ij by (2/sigma^2)|x - y| and can lift them into range).
+#pragma once
+
+#include "common.h"
+
+namespace kmi {
+
+template <int OP, int D, int E>
+struct GaussShape {
+  static constexpr int NV = (D + 1 + 3) / 4;                              // float4 per j record
+  static constexpr int PAY = E;                                           // payload floats per j (b)
+  // per-row accumulators: sum E; LSE (max, sum) per column; grad D
+  static constexpr int NACC = (OP == OP_GRAD) ? D : (OP == OP_LSE ? 2 * E : E);
+  // per-tile partial sums: sum E; LSE E; grad D
+  static constexpr int NPART = (OP == OP_GRAD) ? D : E;
+  static constexpr int BYTES_PER_J = NV * 16 + PAY * 4;
+  static constexpr int TJ = (2 * 256 * BYTES_PER_J <= 49152) ? 256
+                          : (2 * 128 * BYTES_PER_J <= 49152) ? 128
+                          : (2 * 64 * BYTES_PER_J <= 49152) ? 64
+                          : (2 * 32 * BYTES_PER_J <= 49152) ? 32 : 16;
+};
+
+// Record of one j (NV float4 from LDS) into registers.
+template <int NV>
+__device__ __forceinline__ void load_rec(const float4 *rec, int j, float (&yv)[4 * NV]) {
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const float4 t = rec[j * NV + v];
+    yv[4 * v] = t.x; yv[4 * v + 1] = t.y; yv[4 * v + 2] = t.z; yv[4 * v + 3] = t.w;
+  }
+}
+
+__device__ __forceinline__ float lane4(const float4 &v, int u) {
+  return u == 0 ? v.x : (u == 1 ? v.y : (u == 2 ? v.z : v.w));
+}
+
+// Exponent (log2 units) of the pair map for R rows and one j record, phase by
+// phase over the rows so that the R chains are independent.
+//   EXPANDED: q_r = <x'_r, 2y'> + c_j      (xs = x', record = (2y', c_j))
+//   DIRECT  : q_r = off - s^2 |x_r - y|^2  (xs = raw x, record = raw y); the
+//             differences are kept in d for the grad_x accumulation.
+template <bool FAST, int R, int D, int NV4>
+__device__ __forceinline__ void pair_exponent(const float (&xs)[R][D], const float (&yv)[NV4], float s2, float off,
+                                              float (&q)[R], float (&d)[FAST ? 1 : R][D]) {
+  if (FAST) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) q[r] = yv[D];
+#pragma unroll
+    for (int k = 0; k < D; ++k)
+#pragma unroll
+      for (int r = 0; r < R; ++r) q[r] = fmaf(xs[r][k], yv[k], q[r]);
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int k = 0; k < D; ++k) d[FAST ? 0 : r][k] = xs[r][k] - yv[k];
+#pragma unroll
+    for (int r = 0; r < R; ++r) q[r] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < D; ++k)
+#pragma unroll
+      for (int r = 0; r < R; ++r) q[r] = fmaf(d[FAST ? 0 : r][k], d[FAST ? 0 : r][k], q[r]);
+#pragma unroll
+    for (int r = 0; r < R; ++r) q[r] = fmaf(-s2, q[r], off);
+  }
+}
+
+// The j loop of one work-group for a fixed form (FAST = expanded distance).
+template <int OP, int D, int E, int R, bool FAST>
+__device__ __forceinline__ void gauss_jloop(const GaussArgs &a,
+                                            float4 (*sRec)[GaussShape<OP, D, E>::TJ * GaussShape<OP, D, E>::NV],
+                                            float (*sPay)[GaussShape<OP, D, E>::PAY * GaussShape<OP, D, E>::TJ],
+                                            const float (&xs)[R][D], const float (&gr)[R][E], const float (&cen)[D],
+                                            float G, float (&acc)[R][GaussShape<OP, D, E>::NACC]) {
+  using S = GaussShape<OP, D, E>;
+  constexpr int NV = S::NV, PAY = S::PAY, TJ = S::TJ, NP = S::NPART;
+  const int tid = threadIdx.x;
+  const int64_t N = a.N;
+  const int64_t jb = (int64_t)blockIdx.y * a.j_per_split;
+  const int64_t je = (jb + a.j_per_split < N) ? jb + a.j_per_split : N;
+  const float s2 = a.scale * a.scale;
+  // exponent offset of the direct form (see the file comment); LSE tracks its own max
+  const float off = (FAST || OP == OP_LSE) ? 0.0f : kDirectOffset;
+
+  // raw tile registers (one j per thread for tid < TJ)
+  float ry[D], rb[E];
+  auto load_raw = [&](int64_t jt) {
+    const int64_t j = jt + tid;
+    const bool ok = (tid < TJ) && (j < je);
+#pragma unroll
+    for (int k = 0; k < D; ++k) ry[k] = ok ? a.y[j * D + k] : 0.0f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) rb[e] = ok ? a.b[j * E + e] : 0.0f;
+    return ok;
+  };
+  // Transform the staged raw j rows into LDS records and payloads.  Padded j
+  // (beyond je) get records whose contribution is exactly zero.
+  auto stage = [&](int buf, bool ok) {
+    if (tid >= TJ) return;
+    float rec[4 * NV];
+#pragma unroll
+    for (int q = 0; q < 4 * NV; ++q) rec[q] = 0.0f;
+    if (FAST) {
+      float ny = 0.0f;
+#pragma unroll
+      for (int k = 0; k < D; ++k) {
+        const float yp = a.scale * (ry[k] - cen[k]);
+        rec[k] = 2.0f * yp;
+        ny = fmaf(yp, yp, ny);
+      }
+      float cj = -ny - G;
+      if (OP == OP_LSE && E == 1) cj += kLog2e * rb[0];
+      rec[D] = ok ? cj : -INFINITY;
+    } else {
+#pragma unroll
+      for (int k = 0; k < D; ++k) rec[k] = ry[k];
+    }
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+      sRec[buf][tid * NV + v] = make_float4(rec[4 * v], rec[4 * v + 1], rec[4 * v + 2], rec[4 * v + 3]);
+    if (OP == OP_SUM) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) sPay[buf][e * TJ + tid] = ok ? rb[e] : 0.0f;
+    } else if (OP == OP_LSE) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) sPay[buf][e * TJ + tid] = ok ? kLog2e * rb[e] : -INFINITY;
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) sPay[buf][e * TJ + tid] = ok ? rb[e] : 0.0f;
+    }
+  };
+
+  if (jb < je) {
+    const bool ok = load_raw(jb);
+    stage(0, ok);
+  }
+  __syncthreads();
+  int buf = 0;
+  for (int64_t jt = jb; jt < je; jt += TJ) {
+    const bool has_next = jt + TJ < je;
+    bool ok_next = false;
+    if (has_next) ok_next = load_raw(jt + TJ);
+    const int cnt = (int)(((je - jt < TJ ? je - jt : TJ) + 3) & ~3);
+    const float4 *rec = sRec[buf];
+    const float *pay = sPay[buf];
+
+    float part[R][NP];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int q = 0; q < NP; ++q) part[r][q] = 0.0f;
+
+    for (int jj = 0; jj < cnt; jj += 4) {
+      float4 pq[PAY];
+#pragma unroll
+      for (int p = 0; p < PAY; ++p) pq[p] = *reinterpret_cast<const float4 *>(pay + p * TJ + jj);
+
+      if (OP == OP_LSE) {
+        // online LogSumExp in log2 units: four exponents per row, raise the
+        // running max when one exceeds it (rescaling the sums), accumulate.
+        float uu[4][R][E];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          float yv[4 * NV];
+          load_rec<NV>(rec, jj + u, yv);
+          float q[R], dd[FAST ? 1 : R][D];
+          pair_exponent<FAST>(xs, yv, s2, off, q, dd);
+#pragma unroll
+          for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int e = 0; e < E; ++e) uu[u][r][e] = (FAST && E == 1) ? q[r] : q[r] + lane4(pq[e], u);
+        }
+        bool up = false;
+        float mn[R][E];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            mn[r][e] = fmaxf(fmaxf(acc[r][2 * e], uu[0][r][e]), uu[1][r][e]);
+            mn[r][e] = fmaxf(fmaxf(mn[r][e], uu[2][r][e]), uu[3][r][e]);
+            up |= mn[r][e] > acc[r][2 * e];
+          }
+        if (up) {
+#pragma unroll
+          for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+              const float f = fast_exp2(acc[r][2 * e] - mn[r][e]);
+              acc[r][2 * e + 1] *= f;
+              part[r][e] *= f;
+              acc[r][2 * e] = mn[r][e];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          float ex[R][E];
+#pragma unroll
+          for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int e = 0; e < E; ++e) ex[r][e] = uu[u][r][e] - acc[r][2 * e];
+#pragma unroll
+          for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int e = 0; e < E; ++e) ex[r][e] = fast_exp2(ex[r][e]);
+#pragma unroll
+          for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int e = 0; e < E; ++e) part[r][e] += ex[r][e];
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          float yv[4 * NV];
+          load_rec<NV>(rec, jj + u, yv);
+          float ex[R], dd[FAST ? 1 : R][D];
+          pair_exponent<FAST>(xs, yv, s2, off, ex, dd);
+#pragma unroll
+          for (int r = 0; r < R; ++r) ex[r] = fast_exp2(ex[r]);
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            if (OP == OP_SUM) {
+#pragma unroll
+              for (int e = 0; e < E; ++e) part[r][e] = fmaf(ex[r], lane4(pq[e], u), part[r][e]);
+            } else {
+              // grad: A_k += K <g_i, b_j> (x_k - y_k), the difference taken per pair
+              // (never as x * sum - sum * y, which cancels for near neighbours)
+              float gb;
+              if (E == 1) {
+                gb = lane4(pq[0], u);
+              } else {
+                gb = 0.0f;
+#pragma unroll
+                for (int e = 0; e < E; ++e) gb = fmaf(gr[r][e], lane4(pq[e], u), gb);
+              }
+              const float w = ex[r] * gb;
+#pragma unroll
+              for (int k = 0; k < D; ++k) {
+                // expanded form: x'_k - y'_k = x'_k - (2y'_k)/2, one rounding
+                const float dk = FAST ? fmaf(yv[k], -0.5f, xs[r][k]) : dd[FAST ? 0 : r][k];
+                part[r][k] = fmaf(w, dk, part[r][k]);
+              }
+            }
+          }
+        }
+      }
+    }
+    // fold the tile's partial sums into the row accumulators
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (OP == OP_LSE) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[r][2 * e + 1] += part[r][e];
+      } else {
+#pragma unroll
+        for (int q = 0; q < NP; ++q) acc[r][q] += part[r][q];
+      }
+    }
+    if (has_next) stage(buf ^ 1, ok_next);
+    __syncthreads();
+    buf ^= 1;
+  }
+}
+
+template <int OP, int D, int E, int R>
+__global__ __launch_bounds__(kThreads) void gauss_valu_kernel(GaussArgs a) {
+  using S = GaussShape<OP, D, E>;
+  constexpr int NV = S::NV, PAY = S::PAY, TJ = S::TJ;
+  __shared__ float4 sRec[2][TJ * NV];
+  __shared__ __attribute__((aligned(16))) float sPay[2][PAY * TJ];
+  __shared__ float sRed[2 * D * (kThreads / kWave) + 8];
+
+  const int tid = threadIdx.x;
+  const int wid = tid / kWave, lane = tid & (kWave - 1);
+  const int64_t row0 = (int64_t)blockIdx.x * (kThreads * R);
+  const int64_t M = a.M;
+
+  // ---- rows (raw), bounding-box centre of the work-group
+  float xs[R][D];
+  bool valid[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t i = row0 + (int64_t)r * kThreads + tid;
+    valid[r] = i < M;
+#pragma unroll
+    for (int k = 0; k < D; ++k) xs[r][k] = valid[r] ? a.x[i * D + k] : 0.0f;
+  }
+  float cen[D];
+  {
+    float lo[D], hi[D];
+#pragma unroll
+    for (int k = 0; k < D; ++k) {
+      lo[k] = INFINITY;
+      hi[k] = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (valid[r]) { lo[k] = fminf(lo[k], xs[r][k]); hi[k] = fmaxf(hi[k], xs[r][k]); }
+      lo[k] = wave_min(lo[k]);
+      hi[k] = wave_max(hi[k]);
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int k = 0; k < D; ++k) { sRed[(2 * k) * 4 + wid] = lo[k]; sRed[(2 * k + 1) * 4 + wid] = hi[k]; }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < D; ++k) {
+      float l = sRed[(2 * k) * 4], h = sRed[(2 * k + 1) * 4];
+#pragma unroll
+      for (int w = 1; w < kThreads / kWave; ++w) {
+        l = fminf(l, sRed[(2 * k) * 4 + w]);
+        h = fmaxf(h, sRed[(2 * k + 1) * 4 + w]);
+      }
+      cen[k] = 0.5f * l + 0.5f * h;
+    }
+  }
+  // ---- |x'|^2 of every row and the work-group radius that selects the form
+  float nx[R];
+  float r2 = 0.0f;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float n = 0.0f;
+#pragma unroll
+    for (int k = 0; k < D; ++k) {
+      const float t = a.scale * (xs[r][k] - cen[k]);
+      n = fmaf(t, t, n);
+    }
+    nx[r] = n;
+    if (valid[r]) r2 = fmaxf(r2, n);
+  }
+  r2 = block_max(r2, sRed + 2 * D * (kThreads / kWave));
+  const bool fast = a.form == FORM_AUTO && r2 <= kFastR2;
+  // Offset folded into every j constant so that exp2 stays within range: the
+  // largest exponent is r2 - G and the smallest row factor exponent is -G.
+  const float G = (OP == OP_LSE || !fast) ? 0.0f : 0.5f * r2;
+  if (fast) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int k = 0; k < D; ++k) xs[r][k] = a.scale * (xs[r][k] - cen[k]);
+  }
+
+  float gr[R][E];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t i = row0 + (int64_t)r * kThreads + tid;
+#pragma unroll
+    for (int e = 0; e < E; ++e) gr[r][e] = (OP == OP_GRAD && valid[r]) ? a.g[i * E + e] : 0.0f;
+  }
+
+  // ---- accumulators
+  float acc[R][S::NACC];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int q = 0; q < S::NACC; ++q) acc[r][q] = 0.0f;
+  if (OP == OP_LSE) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[r][2 * e] = -3.0e38f;   // running max (finite: keeps u - m defined)
+  }
+
+  // ---- the j loop, specialised on the form (uniform across the work-group)
+  if (fast) gauss_jloop<OP, D, E, R, true>(a, sRec, sPay, xs, gr, cen, G, acc);
+  else gauss_jloop<OP, D, E, R, false>(a, sRec, sPay, xs, gr, cen, G, acc);
+
+  // ---- finalise and store
+  const bool partial = a.nsplit > 1;
+  constexpr int W = (OP == OP_SUM) ? E : (OP == OP_LSE ? (2 * E) : D);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (!valid[r]) continue;
+    const int64_t i = row0 + (int64_t)r * kThreads + tid;
+    float res[W];
+    if (OP == OP_SUM) {
+      const float f = fast ? exp2f(G - nx[r]) : exp2f(-kDirectOffset);
+#pragma unroll
+      for (int e = 0; e < E; ++e) res[e] = acc[r][e] * f;
+    } else if (OP == OP_LSE) {
+      const float off = fast ? nx[r] : 0.0f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) { res[2 * e] = acc[r][2 * e] - off; res[2 * e + 1] = acc[r][2 * e + 1]; }
+    } else {
+      // expanded: G_k = -(2/sigma^2) (1/s) exp2(G - |x'|^2) sum_j K' <g, b> (x'_k - y'_k)
+      // direct:   G_k = -(2/sigma^2) sum_j K <g, b> (x_k - y_k)
+      const float f = (fast ? exp2f(G - nx[r]) * a.grad_coef : a.grad_coef_direct) * (E == 1 ? gr[r][0] : 1.0f);
+      const float f2 = fast ? 1.0f : exp2f(-kDirectOffset);
+#pragma unroll
+      for (int k = 0; k < D; ++k) res[k] = (f * acc[r][k]) * f2;
+    }
+    if (partial) {
+      float *dst = a.out + ((int64_t)blockIdx.y * M + i) * W;
+#pragma unroll
+      for (int w = 0; w < W; ++w) dst[w] = res[w];
+    } else if (OP == OP_LSE) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) a.out[i * E + e] = kLn2 * (res[2 * e] + log2f(res[2 * e + 1]));
+    } else {
+#pragma unroll
+      for (int w = 0; w < W; ++w) a.out[i * W + w] = res[w];
+    }
+  }
+}
+
+// Rows per lane of the "wide" variant (large M); the narrow variant holds 1.
+__host__ __device__ constexpr int gauss_rows_wide(int op, int D, int E) {
+  return D <= 4 ? (op == OP_SUM ? 8 : 4) : (D <= 8 ? (E <= 2 ? 4 : 2) : (D <= 16 ? 2 : 1));
+}
+
+template <int OP, int D, int E, int R>
+void launch_gauss_t(dim3 grid, const GaussArgs &a, hipStream_t st) {
+  hipLaunchKernelGGL((gauss_valu_kernel<OP, D, E, R>), grid, dim3(kThreads), 0, st, a);
+}
+
+}  // namespace kmi

@@ -1,0 +1,353 @@
+// keops_api.cpp -- the C ABI of include/keops_mi355x.h: argument validation,
+// the launch plan (rows per lane, j-splits), stream-ordered workspace and
+// kernel dispatch.  No HIP call is made before the arguments are validated,
+// so argument errors never touch the device.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "keops_mi355x.h"
+#include "launch.h"
+
+namespace kmi {
+namespace {
+
+std::atomic<int64_t> g_opt_split{0}, g_opt_form{0}, g_opt_rows{0}, g_opt_profile{0};
+
+// ---- pass-1 timing (KEOPS_OPT_PROFILE)
+struct EventPair { hipEvent_t start, stop; };
+std::mutex g_prof_mu;
+std::vector<EventPair> g_prof_events;
+constexpr size_t kMaxProfiled = 4096;
+
+// Records the start event when profiling is on; returns the pair index or -1.
+int prof_begin(hipStream_t st) {
+  if (g_opt_profile.load(std::memory_order_relaxed) != 1) return -1;
+  EventPair e{};
+  if (hipEventCreate(&e.start) != hipSuccess) return -1;
+  if (hipEventCreate(&e.stop) != hipSuccess) { (void)hipEventDestroy(e.start); return -1; }
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (g_prof_events.size() >= kMaxProfiled) {
+    (void)hipEventDestroy(e.start);
+    (void)hipEventDestroy(e.stop);
+    return -1;
+  }
+  (void)hipEventRecord(e.start, st);
+  g_prof_events.push_back(e);
+  return (int)g_prof_events.size() - 1;
+}
+
+void prof_end(int idx, hipStream_t st) {
+  if (idx < 0) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if ((size_t)idx < g_prof_events.size()) (void)hipEventRecord(g_prof_events[idx].stop, st);
+}
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+std::once_flag g_pool_once[kMaxDevices];
+
+// Compute units of the current device (cached).  Also raises the release
+// threshold of the device's default memory pool once, so that stream-ordered
+// workspace allocations are served from the pool instead of the driver.
+int device_setup(int *cus) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KEOPS_ERR_HIP;
+  int c = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (c <= 0) {
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
+      return KEOPS_ERR_HIP;
+    g_cu_count[dev].store(c, std::memory_order_relaxed);
+  }
+  std::call_once(g_pool_once[dev], [dev] {
+    hipMemPool_t pool;
+    if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
+      uint64_t thr = UINT64_MAX;
+      (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &thr);
+    }
+  });
+  *cus = c;
+  return KEOPS_OK;
+}
+
+bool overlaps(const void *a, int64_t abytes, const void *b, int64_t bbytes) {
+  if (!a || !b || abytes <= 0 || bbytes <= 0) return false;
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
+
+using GaussDispatch = int (*)(int, int, int, VariantInfo *, dim3, const GaussArgs *, hipStream_t);
+using KminDispatch = int (*)(int, int, VariantInfo *, dim3, const KminArgs *, hipStream_t);
+
+const GaussDispatch kGaussUnits[3][2] = {
+    {gauss_dispatch_sum_small, gauss_dispatch_sum_large},
+    {gauss_dispatch_lse_small, gauss_dispatch_lse_large},
+    {gauss_dispatch_grad_small, gauss_dispatch_grad_large},
+};
+const KminDispatch kKminUnits[3] = {kmin_dispatch_d1_4, kmin_dispatch_d5_8, kmin_dispatch_large};
+
+int gauss_find(int op, int D, int E, int wide, VariantInfo *info, GaussDispatch *fn) {
+  for (GaussDispatch f : kGaussUnits[op])
+    if (f(D, E, wide, info, dim3(), nullptr, nullptr) == 0) { *fn = f; return 0; }
+  return KEOPS_ERR_UNSUPPORTED;
+}
+
+int kmin_find(int D, int K, VariantInfo *info, KminDispatch *fn) {
+  for (KminDispatch f : kKminUnits)
+    if (f(D, K, info, dim3(), nullptr, nullptr) == 0) { *fn = f; return 0; }
+  return KEOPS_ERR_UNSUPPORTED;
+}
+
+struct Plan {
+  int wide;
+  int rows;        // rows per lane
+  int tile_j;
+  int64_t nblk;    // work-groups along i
+  int nsplit;      // j-splits
+  int64_t jps;     // j per split (multiple of tile_j)
+};
+
+// Work-groups along i and splits along j.  The split count is chosen so that
+// the grid offers at least `kWaveTarget` waves per SIMD, with at least two
+// tiles per split.
+Plan make_plan(int64_t M, int64_t N, int cus, int rows_wide, int rows_narrow, int tile_j) {
+  constexpr int kWaveTarget = 4;
+  const int64_t want_wgs = (int64_t)cus * kWaveTarget;        // 4 waves per WG, 4 SIMDs per CU
+  Plan p{};
+  const int64_t opt_rows = g_opt_rows.load();
+  p.wide = opt_rows == 1 ? 0 : (opt_rows == 2 ? 1 : (M >= (int64_t)kThreads * rows_wide * cus));
+  p.rows = p.wide ? rows_wide : rows_narrow;
+  p.tile_j = tile_j;
+  p.nblk = (M + (int64_t)kThreads * p.rows - 1) / ((int64_t)kThreads * p.rows);
+  const int64_t ntiles = (N + tile_j - 1) / tile_j;
+  int64_t s = 1;
+  const int64_t forced = g_opt_split.load();
+  if (forced > 0) {
+    s = forced;
+  } else if (p.nblk < want_wgs) {
+    s = (want_wgs + p.nblk - 1) / p.nblk;
+    const int64_t max_s = ntiles / 2 > 1 ? ntiles / 2 : 1;
+    if (s > max_s) s = max_s;
+  }
+  if (s > ntiles) s = ntiles;
+  if (s < 1) s = 1;
+  if (s > 65535) s = 65535;
+  const int64_t tiles_per = (ntiles + s - 1) / s;
+  p.jps = tiles_per * tile_j;
+  p.nsplit = (int)((N + p.jps - 1) / p.jps);
+  return p;
+}
+
+int check_launch() { return hipGetLastError() == hipSuccess ? KEOPS_OK : KEOPS_ERR_HIP; }
+
+int gauss_entry(int op, const float *x, const float *y, const float *b, const float *g, int64_t M, int64_t N,
+                int32_t D, int32_t E, float sigma, float *out, void *stream) {
+  // ---- validation (host only)
+  if (M < 0 || N < 0 || D < 1 || E < 1) return KEOPS_ERR_INVALID_ARG;
+  if (!std::isfinite(sigma) || !(sigma > 0.0f)) return KEOPS_ERR_INVALID_ARG;
+  if (M > 0 && (!x || !out)) return KEOPS_ERR_INVALID_ARG;
+  if (N > 0 && (!y || !b)) return KEOPS_ERR_INVALID_ARG;
+  if (op == OP_GRAD && M > 0 && !g) return KEOPS_ERR_INVALID_ARG;
+  for (const void *p : {(const void *)x, (const void *)y, (const void *)b, (const void *)g, (const void *)out})
+    if (p && !aligned4(p)) return KEOPS_ERR_INVALID_ARG;
+  const int W = op == OP_GRAD ? D : E;
+  if (M > 0) {
+    const int64_t ob = M * W * 4;
+    if (overlaps(out, ob, x, M * D * 4) || overlaps(out, ob, y, N * D * 4) || overlaps(out, ob, b, N * E * 4) ||
+        (op == OP_GRAD && overlaps(out, ob, g, M * E * 4)))
+      return KEOPS_ERR_INVALID_ARG;
+  }
+  VariantInfo wide_info{}, narrow_info{};
+  GaussDispatch fn = nullptr;
+  if (gauss_find(op, D, E, 1, &wide_info, &fn) || gauss_find(op, D, E, 0, &narrow_info, &fn))
+    return KEOPS_ERR_UNSUPPORTED;
+  if (M == 0) return KEOPS_OK;
+
+  // ---- device work
+  hipStream_t st = (hipStream_t)stream;
+  (void)hipGetLastError();
+  if (N == 0) {
+    launch_fill(out, M * W, op == OP_LSE ? -INFINITY : 0.0f, st);
+    return check_launch();
+  }
+  int cus = 0;
+  if (int rc = device_setup(&cus)) return rc;
+  const Plan p = make_plan(M, N, cus, wide_info.rows, narrow_info.rows, wide_info.tile_j);
+
+  const double s2 = (double)sigma * (double)sigma;
+  const double scale = std::sqrt(1.4426950408889634 / s2);
+  GaussArgs a{};
+  a.x = x; a.y = y; a.b = b; a.g = g;
+  a.M = M; a.N = N;
+  a.scale = (float)scale;
+  a.grad_coef = (float)(-2.0 / s2 / scale);
+  a.grad_coef_direct = (float)(-2.0 / s2);
+  a.j_per_split = p.jps;
+  a.nsplit = p.nsplit;
+  const int64_t form = g_opt_form.load();
+  a.form = form == 1 ? FORM_DIRECT : FORM_AUTO;
+
+  float *ws = nullptr;
+  const int PW = op == OP_SUM ? E : (op == OP_LSE ? 2 * E : D);
+  if (p.nsplit > 1) {
+    if (hipMallocAsync((void **)&ws, (size_t)p.nsplit * M * PW * sizeof(float), st) != hipSuccess || !ws) {
+      (void)hipGetLastError();
+      return KEOPS_ERR_ALLOC;
+    }
+    a.out = ws;
+  } else {
+    a.out = out;
+  }
+  const dim3 grid((unsigned)p.nblk, (unsigned)p.nsplit);
+  const int prof = prof_begin(st);
+  fn(D, E, p.wide, nullptr, grid, &a, st);
+  prof_end(prof, st);
+  if (p.nsplit > 1) {
+    if (op == OP_LSE) launch_lse_combine(ws, p.nsplit, M, E, out, st);
+    else launch_sum_combine(ws, p.nsplit, M * PW, out, st);
+    (void)hipFreeAsync(ws, st);
+  }
+  return check_launch();
+}
+
+}  // namespace
+}  // namespace kmi
+
+using namespace kmi;
+
+extern "C" {
+
+int keops_gauss_sum(const float *x, const float *y, const float *b, int64_t M, int64_t N, int32_t D, int32_t E,
+                    float sigma, float *out, void *stream) {
+  return gauss_entry(OP_SUM, x, y, b, nullptr, M, N, D, E, sigma, out, stream);
+}
+
+int keops_gauss_lse(const float *x, const float *y, const float *b, int64_t M, int64_t N, int32_t D, int32_t E,
+                    float sigma, float *out, void *stream) {
+  return gauss_entry(OP_LSE, x, y, b, nullptr, M, N, D, E, sigma, out, stream);
+}
+
+int keops_gauss_grad_x(const float *x, const float *y, const float *b, const float *g, int64_t M, int64_t N,
+                       int32_t D, int32_t E, float sigma, float *out, void *stream) {
+  return gauss_entry(OP_GRAD, x, y, b, g, M, N, D, E, sigma, out, stream);
+}
+
+int keops_kmin(const float *x, const float *y, int64_t M, int64_t N, int32_t D, int32_t K, float *out_d,
+               int64_t *out_idx, void *stream) {
+  if (M < 0 || N < 0 || D < 1 || K < 1) return KEOPS_ERR_INVALID_ARG;
+  if ((int64_t)K > N) return KEOPS_ERR_INVALID_ARG;
+  if (M > 0 && (!x || !out_d || !out_idx)) return KEOPS_ERR_INVALID_ARG;
+  if (!y) return KEOPS_ERR_INVALID_ARG;   // N >= K >= 1
+  for (const void *p : {(const void *)x, (const void *)y, (const void *)out_d})
+    if (p && !aligned4(p)) return KEOPS_ERR_INVALID_ARG;
+  if (out_idx && ((uintptr_t)out_idx & 7u)) return KEOPS_ERR_INVALID_ARG;
+  if (M > 0) {
+    const int64_t db = M * K * 4, ib = M * K * 8;
+    if (overlaps(out_d, db, x, M * D * 4) || overlaps(out_d, db, y, N * D * 4) || overlaps(out_idx, ib, x, M * D * 4) ||
+        overlaps(out_idx, ib, y, N * D * 4) || overlaps(out_d, db, out_idx, ib))
+      return KEOPS_ERR_INVALID_ARG;
+  }
+  if (N >= ((int64_t)1 << 31)) return KEOPS_ERR_UNSUPPORTED;
+  VariantInfo info{};
+  KminDispatch fn = nullptr;
+  if (kmin_find(D, K, &info, &fn)) return KEOPS_ERR_UNSUPPORTED;
+  if (M == 0) return KEOPS_OK;
+
+  hipStream_t st = (hipStream_t)stream;
+  (void)hipGetLastError();
+  int cus = 0;
+  if (int rc = device_setup(&cus)) return rc;
+  const Plan p = make_plan(M, N, cus, info.rows, info.rows, info.tile_j);
+  KminArgs a{};
+  a.x = x; a.y = y; a.M = M; a.N = N;
+  a.j_per_split = p.jps;
+  a.nsplit = p.nsplit;
+  void *ws = nullptr;
+  if (p.nsplit > 1) {
+    const size_t n = (size_t)p.nsplit * M * K;
+    if (hipMallocAsync(&ws, n * (sizeof(float) + sizeof(int32_t)), st) != hipSuccess || !ws) {
+      (void)hipGetLastError();
+      return KEOPS_ERR_ALLOC;
+    }
+    a.out_d = (float *)ws;
+    a.part_idx = (int32_t *)((float *)ws + n);
+  } else {
+    a.out_d = out_d;
+    a.out_idx = out_idx;
+  }
+  const int prof = prof_begin(st);
+  fn(D, K, nullptr, dim3((unsigned)p.nblk, (unsigned)p.nsplit), &a, st);
+  prof_end(prof, st);
+  if (p.nsplit > 1) {
+    launch_kmin_combine(a.out_d, a.part_idx, p.nsplit, M, K, out_d, out_idx, st);
+    (void)hipFreeAsync(ws, st);
+  }
+  return check_launch();
+}
+
+const char *keops_status_string(int status) {
+  switch (status) {
+    case KEOPS_OK: return "ok";
+    case KEOPS_ERR_INVALID_ARG: return "invalid argument";
+    case KEOPS_ERR_UNSUPPORTED: return "unsupported D, E or K";
+    case KEOPS_ERR_ALLOC: return "workspace allocation failed";
+    case KEOPS_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+int keops_set_option(int option, int64_t value) {
+  switch (option) {
+    case KEOPS_OPT_SPLIT_J:
+      if (value < 0 || value > 65535) return KEOPS_ERR_INVALID_ARG;
+      g_opt_split.store(value);
+      return KEOPS_OK;
+    case KEOPS_OPT_FORM:
+      if (value < 0 || value > 1) return KEOPS_ERR_INVALID_ARG;
+      g_opt_form.store(value);
+      return KEOPS_OK;
+    case KEOPS_OPT_ROWS:
+      if (value < 0 || value > 2) return KEOPS_ERR_INVALID_ARG;
+      g_opt_rows.store(value);
+      return KEOPS_OK;
+    case KEOPS_OPT_PROFILE:
+      if (value < 0 || value > 1) return KEOPS_ERR_INVALID_ARG;
+      g_opt_profile.store(value);
+      return KEOPS_OK;
+    default:
+      return KEOPS_ERR_INVALID_ARG;
+  }
+}
+
+int keops_profile_read(double *total_ms, int64_t *launches) {
+  if (!total_ms || !launches) return KEOPS_ERR_INVALID_ARG;
+  std::vector<EventPair> ev;
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    ev.swap(g_prof_events);
+  }
+  double tot = 0.0;
+  int rc = KEOPS_OK;
+  for (const EventPair &e : ev) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(e.stop) != hipSuccess || hipEventElapsedTime(&ms, e.start, e.stop) != hipSuccess)
+      rc = KEOPS_ERR_HIP;
+    tot += ms;
+    (void)hipEventDestroy(e.start);
+    (void)hipEventDestroy(e.stop);
+  }
+  *total_ms = tot;
+  *launches = (int64_t)ev.size();
+  return rc;
+}
+
+int keops_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,39 @@
+// launch.h -- host-side entry points of the kernel translation units.
+#pragma once
+
+#include "common.h"
+
+namespace kmi {
+
+// Shape facts of a compiled variant, filled when `info` is non-null.
+struct VariantInfo {
+  int rows;     // rows per lane
+  int tile_j;   // j rows per LDS tile (the j-split granularity)
+};
+
+// Each dispatcher returns 0 when it owns (D, E[, K]) -- launching the kernel,
+// or only describing it when `info` is non-null -- and -2 otherwise.
+#define KMI_DECLARE_GAUSS(NAME) \
+  int NAME(int D, int E, int wide, VariantInfo *info, dim3 grid, const GaussArgs *args, hipStream_t st);
+KMI_DECLARE_GAUSS(gauss_dispatch_sum_small)
+KMI_DECLARE_GAUSS(gauss_dispatch_sum_large)
+KMI_DECLARE_GAUSS(gauss_dispatch_lse_small)
+KMI_DECLARE_GAUSS(gauss_dispatch_lse_large)
+KMI_DECLARE_GAUSS(gauss_dispatch_grad_small)
+KMI_DECLARE_GAUSS(gauss_dispatch_grad_large)
+#undef KMI_DECLARE_GAUSS
+
+#define KMI_DECLARE_KMIN(NAME) \
+  int NAME(int D, int K, VariantInfo *info, dim3 grid, const KminArgs *args, hipStream_t st);
+KMI_DECLARE_KMIN(kmin_dispatch_d1_4)
+KMI_DECLARE_KMIN(kmin_dispatch_d5_8)
+KMI_DECLARE_KMIN(kmin_dispatch_large)
+#undef KMI_DECLARE_KMIN
+
+void launch_sum_combine(const float *ws, int nsplit, int64_t count, float *out, hipStream_t st);
+void launch_lse_combine(const float *ws, int nsplit, int64_t M, int E, float *out, hipStream_t st);
+int launch_kmin_combine(const float *pd, const int32_t *pi, int nsplit, int64_t M, int K, float *out_d,
+                        int64_t *out_i, hipStream_t st);
+void launch_fill(float *out, int64_t count, float v, hipStream_t st);
+
+}  // namespace kmi

@@ -1,0 +1,142 @@
+/*
+ * keops_mi355x.h -- C ABI of the MI355X (gfx950) Gaussian map-reduce engine.
+ *
+ * The engine evaluates reductions over a symbolic matrix M_ij = F(x_i, y_j)
+ * that is never stored: coefficients are computed on the fly, tile by tile,
+ * with memory linear in M + N.  Sources (web pages about the KeOps library):
+ *
+ *  [KO-GPU]  "Kernel Operations on the GPU, with Autodiff, without Memory
+ *            Overflows" (paper summary page): §1 "Target operation" (the
+ *            Gaussian kernel product a_i = sum_j k(x_i, y_j) b_j, x_i, y_j in
+ *            R^D, Gaussian k of deviation sigma > 0, M and N up to a billion);
+ *            §2 "Generic reduction framework" (sum, max, argmin, log-sum-exp
+ *            reductions of formulas over i- and j-variables), "Performance and
+ *            differentiation" (argKmin; autodiff); §4 (D <= 100).
+ *  [README]  KeOps README: "symbolic matrices" paragraph (c) (formula
+ *            evaluated on the fly on data arrays x_i, y_j); PyTorch example
+ *            (D_ij = sum of squared differences, K_ij = exp(-D_ij), .sum(),
+ *            .logsumexp(), .argmin(), grad of (a**2).sum()).
+ *  [ISSUE]   GitHub issue "Transparent interface for billion-scale matrices":
+ *            an output parameter so that the user allocates the result
+ *            tensor, and calls made without holding the Python lock.
+ *
+ * Common conventions for every entry point
+ * ----------------------------------------
+ *  Memory:    every array pointer is a DEVICE pointer on the HIP device that is
+ *             current on the calling thread.  Arrays are dense, row-major,
+ *             fp32 (indices int64), at least 4-byte aligned.
+ *  Ownership: the caller allocates every input and output ([ISSUE], item 1).
+ *             The library keeps no reference after returning, except through
+ *             work queued on `stream`; the caller keeps the buffers alive
+ *             until the stream has passed that work.  Outputs must not overlap
+ *             inputs.  Split-j workspace is allocated by the library in
+ *             stream order (hipMallocAsync / hipFreeAsync on `stream`).
+ *  Stream:    `stream` is a hipStream_t passed as void* (NULL = the default
+ *             stream).  Calls only enqueue work and never synchronise; kernel
+ *             faults surface at the caller's next synchronisation.
+ *  Threads:   reentrant; may be called concurrently from several host
+ *             threads on different streams.  Calls running concurrently on
+ *             one GPU do not share memory.
+ *  Errors:    0 = KEOPS_OK, negative = error (see below); no exception ever
+ *             crosses the ABI, and on an error nothing has been enqueued.
+ *  Sizes:     M = 0 is a no-op.  N = 0: sums and gradients are 0, LogSumExp
+ *             is -inf; K-min needs 1 <= K <= N.
+ *  Supported: D in 1..8, 16, 32, 50, 64, 100; E in 1..4; K in 1..16 or 32.
+ *             Other values return KEOPS_ERR_UNSUPPORTED.
+ *  Kernel:    k(x, y) = exp(-|x - y|^2 / sigma^2)   (sigma finite, > 0)
+ *             (sigma = 1 is the README's exp(-D_ij)).
+ */
+#ifndef KEOPS_MI355X_H
+#define KEOPS_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KEOPS_OK 0
+#define KEOPS_ERR_INVALID_ARG (-1)  /* null pointer with non-zero size, negative size,
+                                       sigma not finite or <= 0, K > N, overlap  */
+#define KEOPS_ERR_UNSUPPORTED (-2)  /* D, E or K outside the compiled set; N >= 2^31 for K-min */
+#define KEOPS_ERR_ALLOC (-3)        /* workspace allocation failed                 */
+#define KEOPS_ERR_HIP (-4)          /* a HIP call or kernel launch failed          */
+
+/*
+ * Gaussian kernel sum ([KO-GPU] §1 "Target operation"; [README] K_ij.sum(dim=1)):
+ *   out[i, e] = sum_j exp(-|x_i - y_j|^2 / sigma^2) * b[j, e]
+ * x: [M, D], y: [N, D], b: [N, E], out: [M, E].
+ */
+int keops_gauss_sum(const float *x, const float *y, const float *b,
+                    int64_t M, int64_t N, int32_t D, int32_t E, float sigma,
+                    float *out, void *stream);
+
+/*
+ * LogSumExp reduction ([KO-GPU] §2 reductions list; [README] .logsumexp()):
+ *   out[i, e] = log sum_j exp(-|x_i - y_j|^2 / sigma^2 + b[j, e])
+ * b enters additively in the exponent.  Shapes as keops_gauss_sum.
+ */
+int keops_gauss_lse(const float *x, const float *y, const float *b,
+                    int64_t M, int64_t N, int32_t D, int32_t E, float sigma,
+                    float *out, void *stream);
+
+/*
+ * Gradient of the kernel sum with respect to x ([KO-GPU] §2 "Performance and
+ * differentiation"; [README] torch.autograd.grad((a_i ** 2).sum(), [x])), as
+ * the vector-Jacobian product with the cotangent g = dL/da:
+ *   out[i, d] = sum_j (-2/sigma^2) exp(-|x_i-y_j|^2/sigma^2) <g_i, b_j> (x[i,d] - y[j,d])
+ * g: [M, E]; out: [M, D].  For L = sum_i |a_i|^2 pass g = 2a.
+ */
+int keops_gauss_grad_x(const float *x, const float *y, const float *b, const float *g,
+                       int64_t M, int64_t N, int32_t D, int32_t E, float sigma,
+                       float *out, void *stream);
+
+/*
+ * K-min reduction with indices ([KO-GPU] §2 argmin / argKmin; [README] ArgMin,
+ * K-min reductions): for each row i, the K smallest squared distances
+ * |x_i - y_j|^2, ascending, and their indices j; equal distances are ordered
+ * by smaller j first.  K = 1 is ArgMin.
+ * out_d: [M, K] fp32; out_idx: [M, K] int64.  Requires 1 <= K <= N < 2^31.
+ */
+int keops_kmin(const float *x, const float *y,
+               int64_t M, int64_t N, int32_t D, int32_t K,
+               float *out_d, int64_t *out_idx, void *stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *keops_status_string(int status);
+
+/*
+ * Process-wide tuning and test switches (0 = automatic for each).  They change
+ * how the work is scheduled, never what is computed beyond fp32 rounding:
+ *   KEOPS_OPT_SPLIT_J   -- force this many j-splits (pass 1 partials + pass 2)
+ *   KEOPS_OPT_FORM      -- 1 = use the direct distance form everywhere (the
+ *                          expanded form is otherwise used wherever its range
+ *                          condition holds)
+ *   KEOPS_OPT_ROWS      -- 1 = one row per lane, 2 = the wide variant (several
+ *                          rows per lane, for large M)
+ * Returns KEOPS_OK, or KEOPS_ERR_INVALID_ARG for an unknown option or value.
+ */
+#define KEOPS_OPT_SPLIT_J 1
+#define KEOPS_OPT_FORM 2
+#define KEOPS_OPT_ROWS 3
+#define KEOPS_OPT_PROFILE 4   /* 1 = record HIP events around each pass-1 launch */
+int keops_set_option(int option, int64_t value);
+
+/*
+ * Duration of the pass-1 (pair-evaluation) kernels, for benchmarks.  While
+ * KEOPS_OPT_PROFILE is 1, every call records a HIP event pair around its
+ * pass-1 launch on the call's stream (at most 4096 pairs are kept).  This
+ * waits for the recorded events, returns the summed duration in milliseconds
+ * and the number of launches since the previous read, and forgets them.
+ * total_ms and launches must be valid host pointers.
+ */
+int keops_profile_read(double *total_ms, int64_t *launches);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int keops_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KEOPS_MI355X_H */

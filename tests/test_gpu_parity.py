@@ -1,0 +1,272 @@
+"""GPU parity: the gfx950 kernels (through the C ABI) against the float64 oracle.
+
+Small cases compare every output element and span several tiles, ragged
+tails, both distance forms, forced j-splits and both row layouts.  The named
+workloads run at full size in the launch configuration the library picks and
+compare seeded samples of rows (each sampled row is exact: the oracle
+evaluates it over all N).
+"""
+from __future__ import annotations
+
+import json
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import check_grad, check_kmin, check_lse, check_sum, dev, host
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import geometric_map_reduce_amd as gm
+    from geometric_map_reduce_amd import workloads
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(autouse=True)
+def _options():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    for o in (gm.KEOPS_OPT_SPLIT_J, gm.KEOPS_OPT_FORM, gm.KEOPS_OPT_ROWS):
+        gm.keops_set_option(o, 0)
+    yield
+    for o in (gm.KEOPS_OPT_SPLIT_J, gm.KEOPS_OPT_FORM, gm.KEOPS_OPT_ROWS):
+        gm.keops_set_option(o, 0)
+
+
+def rand_case(seed, M, N, D, E, scale=1.0):
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((M, D)) * scale).astype(np.float32)
+    y = (rng.standard_normal((N, D)) * scale).astype(np.float32)
+    b = rng.standard_normal((N, E)).astype(np.float32)
+    g = rng.standard_normal((M, E)).astype(np.float32)
+    return x, y, b, g
+
+
+# (M, N, D, E, sigma): tiles of 256 j, ragged tails, every compiled D group
+SMALL = [
+    (1, 1, 1, 1, 1.0), (2, 3, 3, 1, 0.7), (63, 65, 3, 1, 0.5), (64, 64, 2, 2, 1.0),
+    (65, 257, 3, 1, 0.3), (255, 513, 5, 3, 1.5), (257, 1000, 8, 4, 2.0), (1000, 3001, 16, 1, 3.0),
+    (300, 700, 4, 2, 0.8), (129, 600, 32, 1, 4.0), (70, 300, 50, 1, 5.0), (33, 250, 64, 2, 6.0),
+    (20, 130, 100, 1, 8.0), (700, 1100, 6, 1, 1.2), (513, 2000, 7, 2, 0.9),
+]
+
+
+def _run_all(x, y, b, g, sigma):
+    X, Y, B, G = dev(x), dev(y), dev(b), dev(g)
+    a = gm.keops_gauss_sum(X, Y, B, sigma)
+    l = gm.keops_gauss_lse(X, Y, B, sigma)
+    gx = gm.keops_gauss_grad_x(X, Y, B, G, sigma)
+    torch.cuda.synchronize()
+    return host(a), host(l), host(gx)
+
+
+def _check_all(x, y, b, g, sigma, res):
+    a, l, gx = res
+    a_ref, n_ref = oracle.gauss_sum(x, y, b, sigma)
+    check_sum(a, a_ref, n_ref)
+    check_lse(l, oracle.gauss_lse(x, y, b, sigma))
+    G_ref, nu_ref = oracle.gauss_grad_x(x, y, b, g, sigma)
+    check_grad(gx, G_ref, nu_ref)
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "M%d_N%d_D%d_E%d_s%g" % c)
+def test_small_all_ops(case):
+    M, N, D, E, sigma = case
+    say(f"small case M={M} N={N} D={D} E={E} sigma={sigma}")
+    x, y, b, g = rand_case(1000 + M + N + D, M, N, D, E)
+    sigma = float(np.float32(sigma))
+    _check_all(x, y, b, g, sigma, _run_all(x, y, b, g, sigma))
+
+
+@pytest.mark.parametrize("form", [0, 1], ids=["auto", "direct"])
+@pytest.mark.parametrize("split", [0, 1, 3, 7])
+@pytest.mark.parametrize("rows", [1, 2], ids=["narrow", "wide"])
+def test_forms_splits_layouts(form, split, rows):
+    say(f"forced form={form} split={split} rows={rows}")
+    # sigma = 0.4: one work-group beyond the expanded form's range (direct), one within
+    for (M, N, D, E, sigma) in [(2100, 1900, 3, 1, 0.4), (600, 2500, 5, 2, 1.1), (3000, 700, 3, 1, 1.5)]:
+        gm.keops_set_option(gm.KEOPS_OPT_FORM, form)
+        gm.keops_set_option(gm.KEOPS_OPT_SPLIT_J, split)
+        gm.keops_set_option(gm.KEOPS_OPT_ROWS, rows)
+        x, y, b, g = rand_case(7 + D, M, N, D, E)
+        _check_all(x, y, b, g, sigma, _run_all(x, y, b, g, sigma))
+
+
+def test_far_from_origin_and_spread():
+    """Data far from the origin (centring) and spread out (direct-form fallback)."""
+    say("far/spread")
+    rng = np.random.default_rng(5)
+    for shift, scale, sigma in [(1000.0, 1.0, 0.5), (0.0, 30.0, 0.5), (-50.0, 5.0, 0.05)]:
+        x = (rng.standard_normal((900, 3)) * scale + shift).astype(np.float32)
+        y = np.concatenate([x[::3] + np.float32(0.01) * rng.standard_normal((300, 3)).astype(np.float32),
+                            (rng.standard_normal((700, 3)) * scale + shift).astype(np.float32)])
+        b = rng.standard_normal((y.shape[0], 1)).astype(np.float32)
+        g = rng.standard_normal((900, 1)).astype(np.float32)
+        _check_all(x, y, b, g, sigma, _run_all(x, y, b, g, sigma))
+
+
+KMIN_SMALL = [(1, 1, 1, 1), (5, 40, 3, 10), (300, 1000, 3, 10), (257, 513, 2, 16), (100, 3000, 4, 32),
+              (70, 600, 8, 7), (64, 300, 16, 5), (40, 500, 32, 10), (30, 200, 50, 3), (25, 300, 64, 10),
+              (10, 128, 100, 2), (200, 900, 5, 1), (129, 129, 3, 12)]
+
+
+@pytest.mark.parametrize("case", KMIN_SMALL, ids=lambda c: "M%d_N%d_D%d_K%d" % c)
+def test_kmin_small(case):
+    M, N, D, K = case
+    say(f"kmin M={M} N={N} D={D} K={K}")
+    rng = np.random.default_rng(M * 7 + N + D)
+    x = rng.standard_normal((M, D)).astype(np.float32)
+    y = rng.standard_normal((N, D)).astype(np.float32)
+    if N > 4:
+        y[N - 1] = y[0]                       # an exact distance tie: smaller index first
+    for split in (0, 3):
+        gm.keops_set_option(gm.KEOPS_OPT_SPLIT_J, split)
+        d, i = gm.keops_kmin(dev(x), dev(y), K)
+        torch.cuda.synchronize()
+        d_ref, i_ref = oracle.kmin(x, y, K)
+        check_kmin(x, y, np.arange(M), host(d), host(i), d_ref, i_ref)
+
+
+def test_kmin_self_and_permutation():
+    say("kmin self-match and K = N")
+    rng = np.random.default_rng(9)
+    y = rng.standard_normal((16, 3)).astype(np.float32)
+    d, i = gm.keops_kmin(dev(y), dev(y), 16)
+    torch.cuda.synchronize()
+    d, i = host(d), host(i)
+    assert (i[:, 0] == np.arange(16)).all() and (d[:, 0] == 0).all()
+    assert all(sorted(r) == list(range(16)) for r in i.tolist())
+
+
+def test_empty_and_degenerate():
+    say("empty / degenerate sizes")
+    x = dev(np.ones((5, 3), np.float32))
+    y0 = torch.empty((0, 3), device="cuda")
+    b0 = torch.empty((0, 2), device="cuda")
+    assert (host(gm.keops_gauss_sum(x, y0, b0, 1.0)) == 0).all()
+    assert np.isneginf(host(gm.keops_gauss_lse(x, y0, b0, 1.0))).all()
+    g = dev(np.ones((5, 2), np.float32))
+    assert (host(gm.keops_gauss_grad_x(x, y0, b0, g, 1.0)) == 0).all()
+    x0 = torch.empty((0, 3), device="cuda")
+    out = gm.keops_gauss_sum(x0, dev(np.ones((4, 3), np.float32)), dev(np.ones((4, 1), np.float32)), 1.0)
+    assert out.shape == (0, 1)
+    with pytest.raises(gm.KeopsError):
+        gm.keops_kmin(x, dev(np.ones((3, 3), np.float32)), 4)         # K > N
+    with pytest.raises(gm.KeopsError):
+        gm.keops_gauss_sum(x, dev(np.ones((4, 3), np.float32)), dev(np.ones((4, 1), np.float32)), 0.0)
+    with pytest.raises(gm.KeopsError):
+        gm.keops_gauss_sum(dev(np.ones((5, 9), np.float32)), dev(np.ones((4, 9), np.float32)),
+                           dev(np.ones((4, 1), np.float32)), 1.0)      # D = 9 not compiled
+
+
+def test_single_point_identity():
+    """M = N = 1, x = y: a = b (K = 1) and LSE = b."""
+    say("single point")
+    x = dev(np.float32([[0.3, -1.2, 2.5]]))
+    b = dev(np.float32([[1.75]]))
+    assert host(gm.keops_gauss_sum(x, x.clone(), b, 0.37))[0, 0] == np.float32(1.75)
+    assert abs(host(gm.keops_gauss_lse(x, x.clone(), b, 0.37))[0, 0] - 1.75) <= 1e-6
+
+
+def test_determinism_stream_and_out():
+    """Bitwise-equal reruns; a non-default stream; caller-owned out and offset views."""
+    say("determinism / stream / out")
+    x, y, b, g = rand_case(3, 3000, 5000, 3, 1)
+    X, Y, B = dev(x), dev(y), dev(b)
+    a1 = host(gm.keops_gauss_sum(X, Y, B, 0.3))
+    a2 = host(gm.keops_gauss_sum(X, Y, B, 0.3))
+    assert np.array_equal(a1, a2)
+    s = torch.cuda.Stream()
+    out = torch.full((3000, 1), float("nan"), device="cuda")
+    with torch.cuda.stream(s):
+        gm.keops_gauss_sum(X, Y, B, 0.3, out=out)
+    s.synchronize()
+    assert np.array_equal(host(out), a1)
+    # views whose data pointer is 4-byte but not 16-byte aligned
+    Xv = torch.cat([torch.zeros(1, device="cuda"), X.ravel()])[1:].view(3000, 3)
+    assert Xv.data_ptr() % 16 != 0
+    a3 = host(gm.keops_gauss_sum(Xv, Y, B, 0.3))
+    assert np.array_equal(a3, a1)
+
+
+# ----------------------------------------------------------------------------- named workloads
+def _sample(M, n):
+    return workloads.sample_rows(M, n)
+
+
+def test_workload_sum_1k():
+    w = workloads.WORKLOADS["sum_1k"]
+    say(f"workload {w.name}")
+    x, y, b = workloads.make_inputs(w)
+    a = host(gm.keops_gauss_sum(dev(x), dev(y), dev(b), w.sigma))
+    a_ref, n_ref = oracle.gauss_sum(x, y, b, w.sigma)
+    check_sum(a, a_ref, n_ref)
+
+
+def test_workload_sum_grad_10k():
+    w = workloads.WORKLOADS["sum_grad_10k"]
+    say(f"workload {w.name}")
+    x, y, b = workloads.make_inputs(w)
+    X, Y, B = dev(x), dev(y), dev(b)
+    a = gm.keops_gauss_sum(X, Y, B, w.sigma)
+    a_ref, n_ref = oracle.gauss_sum(x, y, b, w.sigma)
+    check_sum(host(a), a_ref, n_ref)
+    # gated grad: both sides get the same fp32 cotangent g = 2 a_oracle
+    g = (2.0 * a_ref).astype(np.float32)
+    G = host(gm.keops_gauss_grad_x(X, Y, B, dev(g), w.sigma))
+    G_ref, nu_ref = oracle.gauss_grad_x(x, y, b, g, w.sigma)
+    check_grad(G, G_ref, nu_ref)
+    # end-to-end chain g = 2 a_gpu (as autograd of (a**2).sum() would produce)
+    G2 = host(gm.keops_gauss_grad_x(X, Y, B, 2.0 * a, w.sigma))
+    G2_ref, nu2 = oracle.gauss_grad_x(x, y, b, (2.0 * host(a)).astype(np.float32), w.sigma)
+    check_grad(G2, G2_ref, nu2)
+
+
+def test_workload_sum_lse_1M():
+    w = workloads.WORKLOADS["sum_lse_1M"]
+    say(f"workload {w.name}")
+    x, y, b = workloads.make_inputs(w)
+    X, Y, B = dev(x), dev(y), dev(b)
+    rows = _sample(w.M, 2048)
+    a = host(gm.keops_gauss_sum(X, Y, B, w.sigma))
+    a_ref, n_ref = oracle.gauss_sum(x, y, b, w.sigma, rows=rows)
+    err_sum = check_sum(a[rows], a_ref, n_ref)
+    l = host(gm.keops_gauss_lse(X, Y, B, w.sigma))
+    err_lse = check_lse(l[rows], oracle.gauss_lse(x, y, b, w.sigma, rows=rows))
+    say(json.dumps({"workload": w.name, "sum_max_norm_err": err_sum, "lse_max_abs_err": err_lse}))
+
+
+def test_workload_solver_matvec():
+    w = workloads.WORKLOADS["solver_matvec_100k_x_10M"]
+    say(f"workload {w.name}")
+    x, y, b = workloads.make_inputs(w)
+    X, Y, B = dev(x), dev(y), dev(b)
+    a = host(gm.keops_gauss_sum(X, Y, B, w.sigma))
+    del X, Y, B
+    torch.cuda.empty_cache()
+    rows = _sample(w.M, 96)
+    a_ref, n_ref = oracle.gauss_sum(x, y, b, w.sigma, rows=rows)
+    err = check_sum(a[rows], a_ref, n_ref)
+    say(json.dumps({"workload": w.name, "sum_max_norm_err": err}))
+
+
+@pytest.mark.parametrize("name", ["kmin10_1M_d3", "kmin10_1M_d64"])
+def test_workload_kmin(name):
+    w = workloads.WORKLOADS[name]
+    say(f"workload {w.name}")
+    x, y, _ = workloads.make_inputs(w)
+    d, i = gm.keops_kmin(dev(x), dev(y), w.K)
+    d, i = host(d), host(i)
+    rows = _sample(w.M, 2048 if w.D <= 8 else 256)
+    d_ref, i_ref = oracle.kmin(x, y, w.K, rows=rows)
+    nswap = check_kmin(x, y, rows, d[rows], i[rows], d_ref, i_ref)
+    say(json.dumps({"workload": w.name, "rows_checked": len(rows), "near_tie_swaps": nswap}))
