@@ -55,22 +55,33 @@ def flops_per_pair(op, D, E):
     return {"sum": 3 * D + 1 + 2 * E, "lse": 3 * D + 5, "grad_x": 5 * D + 2 * E + 1, "kmin": 3 * D}[op]
 
 
-def kernel_source_hash():
+# sources that define each benchmarked kernel and its launch plan
+_COMMON_SRC = ["common.h", "launch.h", "keops_api.cpp"]
+KERNEL_SOURCES = {
+    "sum": ["gauss_kernel.h", "dispatch_gauss.h", "gauss_sum_small.hip"],
+    "lse": ["gauss_kernel.h", "dispatch_gauss.h", "gauss_lse_small.hip"],
+    "grad_x": ["gauss_kernel.h", "dispatch_gauss.h", "gauss_grad_small.hip"],
+    "kmin": ["kmin_kernel.h", "dispatch_kmin.h", "kmin_d1_4.hip"],
+}
+
+
+def kernel_source_hash(op):
+    """sha256 over the sources of one op's pass-1 kernel (traffic is void once they change)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "geometric_map_reduce_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in sorted(_COMMON_SRC + KERNEL_SOURCES[op]):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()
 
 
-def recorded_traffic(bench_name):
+def recorded_traffic(bench_name, op):
     """HBM bytes per launch from profiles/traffic_<bench>.json if it matches the current sources."""
     path = os.path.join(ROOT, "profiles", f"traffic_{bench_name}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("kernel_sources_sha256") != kernel_source_hash():
+    if rec.get("kernel_sources_sha256") != kernel_source_hash(op):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -124,12 +135,25 @@ def cpu_baseline(op, w, x, y, b, g, target_s, gpu_out):
     return base, check
 
 
+def copy_calibration(torch, args):
+    """A plain streaming kernel of known traffic (read 256 MiB, write 256 MiB), run under the
+    same rocprofv3 counters as the hot kernel to scale FETCH_SIZE / WRITE_SIZE into bytes."""
+    n = 64 << 20
+    src = torch.ones(n, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup + args.steps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"workload": "copycal", "kernel": "torch neg (elementwise)", "launches": args.warmup + args.steps,
+                      "read_bytes_per_launch": 4 * n, "write_bytes_per_launch": 4 * n}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="sum", choices=sorted(BENCHES))
+    ap.add_argument("--workload", default="sum", choices=sorted(BENCHES) + ["copycal"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -142,6 +166,10 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.workload == "copycal":
+        copy_calibration(torch, args)
+        return
 
     import geometric_map_reduce_amd as gm
     from geometric_map_reduce_amd import workloads
@@ -186,7 +214,7 @@ def main():
     fpp = flops_per_pair(op, w.D, w.E)
     kern_avg_ms = kern_ms / max(launches, 1)
     achieved = fpp * pairs / (kern_avg_ms * 1e-3) / 1e12
-    traffic = recorded_traffic(args.workload)
+    traffic = recorded_traffic(args.workload, op)
 
     res = {
         "metric": METRIC if args.workload == "sum" else f"{op} G pair-evals/s @ {w.name}",

@@ -178,34 +178,47 @@ __global__ __launch_bounds__(kThreads) void kmin_valu_kernel(KminArgs a) {
     const float4 *rec = sRec[buf];
     const float4 *raw = sRaw[buf];
     for (int jj = 0; jj < cnt; jj += 4) {
+      // prefilter 4 j x R rows; one wave-level branch for the whole group
+      float t[4][R];
+      float lowest = INFINITY;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         float yv[4 * NV];
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
-          const float4 t = rec[(jj + u) * NV + v];
-          yv[4 * v] = t.x; yv[4 * v + 1] = t.y; yv[4 * v + 2] = t.z; yv[4 * v + 3] = t.w;
+          const float4 q = rec[(jj + u) * NV + v];
+          yv[4 * v] = q.x; yv[4 * v + 1] = q.y; yv[4 * v + 2] = q.z; yv[4 * v + 3] = q.w;
         }
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          float t = yv[D];
+        for (int r = 0; r < R; ++r) t[u][r] = yv[D];
 #pragma unroll
-          for (int k = 0; k < D; ++k) t = fmaf(xm[r][k], yv[k], t);
-          if (t < thr[r]) {
-            float yr[4 * NR];
+        for (int k = 0; k < D; ++k)
 #pragma unroll
-            for (int v = 0; v < NR; ++v) {
-              const float4 q = raw[(jj + u) * NR + v];
-              yr[4 * v] = q.x; yr[4 * v + 1] = q.y; yr[4 * v + 2] = q.z; yr[4 * v + 3] = q.w;
-            }
-            float d2 = 0.0f;
+          for (int r = 0; r < R; ++r) t[u][r] = fmaf(xm[r][k], yv[k], t[u][r]);
 #pragma unroll
-            for (int k = 0; k < D; ++k) { const float d = xr[r][k] - yr[k]; d2 = fmaf(d, d, d2); }
-            if (d2 < bd[r][K - 1]) {
-              kmin_insert<K>(bd[r], bi[r], d2, (int)(jt + jj + u));
-              const float kth = bd[r][K - 1];
-              const float s = 2.0f * ax[r] + sqrtf(kth);
-              thr[r] = (kth - nx[r]) + mcoef * s * s;   // +inf while the list is not full
+        for (int r = 0; r < R; ++r) lowest = fminf(lowest, t[u][r] - thr[r]);
+      }
+      if (lowest < 0.0f) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            if (t[u][r] < thr[r]) {
+              float yr[4 * NR];
+#pragma unroll
+              for (int v = 0; v < NR; ++v) {
+                const float4 q = raw[(jj + u) * NR + v];
+                yr[4 * v] = q.x; yr[4 * v + 1] = q.y; yr[4 * v + 2] = q.z; yr[4 * v + 3] = q.w;
+              }
+              float d2 = 0.0f;
+#pragma unroll
+              for (int k = 0; k < D; ++k) { const float d = xr[r][k] - yr[k]; d2 = fmaf(d, d, d2); }
+              if (d2 < bd[r][K - 1]) {
+                kmin_insert<K>(bd[r], bi[r], d2, (int)(jt + jj + u));
+                const float kth = bd[r][K - 1];
+                const float s = 2.0f * ax[r] + sqrtf(kth);
+                thr[r] = (kth - nx[r]) + mcoef * s * s;   // +inf while the list is not full
+              }
             }
           }
         }
