@@ -32,6 +32,9 @@ struct GaussArgs {
   int64_t j_per_split;  // multiple of kTileJ
   int nsplit;
   int form;             // Form
+  // Per row-block form decisions of the MFMA kernel (1 = done there); when set,
+  // the VALU kernel skips those blocks.  Null otherwise.
+  int *wg_flags;
 };
 
 // Arguments of the K-min pass-1 kernel.

@@ -305,6 +305,9 @@ __global__ __launch_bounds__(kThreads) void gauss_valu_kernel(GaussArgs a) {
   __shared__ __attribute__((aligned(16))) float sPay[2][PAY * TJ];
   __shared__ float sRed[2 * D * (kThreads / kWave) + 8];
 
+  // row blocks already computed by the MFMA kernel (uniform across the work-group)
+  if (a.wg_flags && a.wg_flags[blockIdx.x]) return;
+
   const int tid = threadIdx.x;
   const int wid = tid / kWave, lane = tid & (kWave - 1);
   const int64_t row0 = (int64_t)blockIdx.x * (kThreads * R);

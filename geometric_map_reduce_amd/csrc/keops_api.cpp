@@ -4,6 +4,7 @@
 // so argument errors never touch the device.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
@@ -164,10 +165,14 @@ int gauss_entry(int op, const float *x, const float *y, const float *b, const fl
         (op == OP_GRAD && overlaps(out, ob, g, M * E * 4)))
       return KEOPS_ERR_INVALID_ARG;
   }
-  VariantInfo wide_info{}, narrow_info{};
+  VariantInfo wide_info{}, narrow_info{}, mfma_info{};
   GaussDispatch fn = nullptr;
   if (gauss_find(op, D, E, 1, &wide_info, &fn) || gauss_find(op, D, E, 0, &narrow_info, &fn))
     return KEOPS_ERR_UNSUPPORTED;
+  // fp32-MFMA cross term where the contraction is large enough (D >= 32)
+  const int64_t form = g_opt_form.load();
+  const bool use_mfma = op == OP_SUM && D >= 32 && form == 0 &&
+                        gauss_dispatch_sum_mfma(D, E, 0, &mfma_info, dim3(), nullptr, nullptr) == 0;
   if (M == 0) return KEOPS_OK;
 
   // ---- device work
@@ -179,7 +184,10 @@ int gauss_entry(int op, const float *x, const float *y, const float *b, const fl
   }
   int cus = 0;
   if (int rc = device_setup(&cus)) return rc;
-  const Plan p = make_plan(M, N, cus, wide_info.rows, narrow_info.rows, wide_info.tile_j);
+  // The MFMA kernel and its direct-form companion both use 256-row work-groups
+  // (the narrow VALU variant) and j-splits on the larger of the two tiles.
+  const Plan p = use_mfma ? make_plan(M, N, cus, 1, 1, std::max(mfma_info.tile_j, narrow_info.tile_j))
+                          : make_plan(M, N, cus, wide_info.rows, narrow_info.rows, wide_info.tile_j);
 
   const double s2 = (double)sigma * (double)sigma;
   const double scale = std::sqrt(1.4426950408889634 / s2);
@@ -191,29 +199,39 @@ int gauss_entry(int op, const float *x, const float *y, const float *b, const fl
   a.grad_coef_direct = (float)(-2.0 / s2);
   a.j_per_split = p.jps;
   a.nsplit = p.nsplit;
-  const int64_t form = g_opt_form.load();
   a.form = form == 1 ? FORM_DIRECT : FORM_AUTO;
+  a.wg_flags = nullptr;
 
+  // workspace: split-j partials, then (MFMA path) one form flag per row block
   float *ws = nullptr;
   const int PW = op == OP_SUM ? E : (op == OP_LSE ? 2 * E : D);
-  if (p.nsplit > 1) {
-    if (hipMallocAsync((void **)&ws, (size_t)p.nsplit * M * PW * sizeof(float), st) != hipSuccess || !ws) {
+  const size_t part_bytes = p.nsplit > 1 ? ((size_t)p.nsplit * M * PW * sizeof(float) + 255) / 256 * 256 : 0;
+  const size_t flag_bytes = use_mfma ? (size_t)p.nblk * sizeof(int) : 0;
+  if (part_bytes + flag_bytes > 0) {
+    if (hipMallocAsync((void **)&ws, part_bytes + flag_bytes, st) != hipSuccess || !ws) {
       (void)hipGetLastError();
       return KEOPS_ERR_ALLOC;
     }
-    a.out = ws;
-  } else {
-    a.out = out;
   }
+  a.out = p.nsplit > 1 ? ws : out;
   const dim3 grid((unsigned)p.nblk, (unsigned)p.nsplit);
   const int prof = prof_begin(st);
-  fn(D, E, p.wide, nullptr, grid, &a, st);
-  prof_end(prof, st);
+  if (use_mfma) {
+    a.wg_flags = (int *)((char *)ws + part_bytes);
+    gauss_dispatch_sum_mfma(D, E, 0, nullptr, grid, &a, st);
+    prof_end(prof, st);
+    GaussArgs b2 = a;            // direct-form VALU pass over the blocks the MFMA kernel left
+    b2.form = FORM_DIRECT;
+    fn(D, E, 0, nullptr, grid, &b2, st);
+  } else {
+    fn(D, E, p.wide, nullptr, grid, &a, st);
+    prof_end(prof, st);
+  }
   if (p.nsplit > 1) {
     if (op == OP_LSE) launch_lse_combine(ws, p.nsplit, M, E, out, st);
     else launch_sum_combine(ws, p.nsplit, M * PW, out, st);
-    (void)hipFreeAsync(ws, st);
   }
+  if (ws) (void)hipFreeAsync(ws, st);
   return check_launch();
 }
 

@@ -21,6 +21,7 @@ KMI_DECLARE_GAUSS(gauss_dispatch_lse_small)
 KMI_DECLARE_GAUSS(gauss_dispatch_lse_large)
 KMI_DECLARE_GAUSS(gauss_dispatch_grad_small)
 KMI_DECLARE_GAUSS(gauss_dispatch_grad_large)
+KMI_DECLARE_GAUSS(gauss_dispatch_sum_mfma)
 #undef KMI_DECLARE_GAUSS
 
 #define KMI_DECLARE_KMIN(NAME) \

@@ -270,3 +270,41 @@ def test_workload_kmin(name):
     d_ref, i_ref = oracle.kmin(x, y, w.K, rows=rows)
     nswap = check_kmin(x, y, rows, d[rows], i[rows], d_ref, i_ref)
     say(json.dumps({"workload": w.name, "rows_checked": len(rows), "near_tie_swaps": nswap}))
+
+
+# ----------------------------------------------------------------------------- MFMA path
+@pytest.mark.parametrize("D", [32, 50, 64, 100])
+@pytest.mark.parametrize("E", [1, 3])
+def test_mfma_vs_valu(D, E):
+    """fp32-MFMA cross term (automatic at D >= 32) and the VALU direct form (forced)
+    both match the oracle; the deviation between the two paths is reported."""
+    M, N, sigma = 700, 2300, 0.9 * np.sqrt(D / 3.0)
+    say(f"mfma vs valu D={D} E={E}")
+    x, y, b, _ = rand_case(50 + D + E, M, N, D, E, scale=1.0)
+    X, Y, B = dev(x), dev(y), dev(b)
+    a_ref, n_ref = oracle.gauss_sum(x, y, b, float(np.float32(sigma)))
+    a_mfma = host(gm.keops_gauss_sum(X, Y, B, sigma))
+    gm.keops_set_option(gm.KEOPS_OPT_FORM, 1)
+    a_valu = host(gm.keops_gauss_sum(X, Y, B, sigma))
+    e1 = check_sum(a_mfma, a_ref, n_ref, what="sum (mfma)")
+    e2 = check_sum(a_valu, a_ref, n_ref, what="sum (valu)")
+    dev_paths = float(np.max(np.abs(a_mfma - a_valu) / np.maximum(n_ref, 1e-300)))
+    say(json.dumps({"D": D, "E": E, "mfma_err": e1, "valu_err": e2, "mfma_vs_valu": dev_paths}))
+
+
+@pytest.mark.parametrize("split", [0, 1, 4])
+def test_mfma_mixed_blocks(split):
+    """Row blocks within the expansion's range run on MFMA, the others on the direct-form
+    VALU kernel, in one call (256-row blocks: the second block is spread out)."""
+    say(f"mfma mixed blocks split={split}")
+    rng = np.random.default_rng(77)
+    D, sigma = 50, 0.6
+    x = (rng.standard_normal((700, D)) * 0.05).astype(np.float32)
+    x[256:512] *= np.float32(40.0)                 # second row block: far beyond the range bound
+    y = np.concatenate([x[::2] + np.float32(0.01) * rng.standard_normal((350, D)).astype(np.float32),
+                        (rng.standard_normal((900, D)) * 0.05).astype(np.float32)])
+    b = rng.standard_normal((y.shape[0], 2)).astype(np.float32)
+    gm.keops_set_option(gm.KEOPS_OPT_SPLIT_J, split)
+    a = host(gm.keops_gauss_sum(dev(x), dev(y), dev(b), sigma))
+    a_ref, n_ref = oracle.gauss_sum(x, y, b, float(np.float32(sigma)))
+    check_sum(a, a_ref, n_ref)
