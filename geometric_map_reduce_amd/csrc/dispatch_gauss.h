@@ -8,7 +8,7 @@
   if (D == DD && E == EE) {                                                              \
     constexpr int RW = ::kmi::gauss_rows_wide(OP, DD, EE);                               \
     if (info) {                                                                          \
-      info->rows = wide ? RW : 1;                                                        \
+      info->rows_per_wg = ::kmi::kThreads * (wide ? RW : 1);                             \
       info->tile_j = ::kmi::GaussShape<OP, DD, EE>::TJ;                                  \
       return 0;                                                                          \
     }                                                                                    \

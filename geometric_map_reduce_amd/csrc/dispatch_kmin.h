@@ -7,7 +7,7 @@
 #define KMI_KMIN_CASE(DD, KK)                                                            \
   if (D == DD && K == KK) {                                                              \
     if (info) {                                                                          \
-      info->rows = ::kmi::KminShape<DD, KK>::R;                                          \
+      info->rows_per_wg = ::kmi::kThreads * ::kmi::KminShape<DD, KK>::R;                 \
       info->tile_j = ::kmi::KminShape<DD, KK>::TJ;                                       \
       return 0;                                                                          \
     }                                                                                    \

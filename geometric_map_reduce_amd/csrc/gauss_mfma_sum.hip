@@ -10,7 +10,7 @@ int gauss_dispatch_sum_mfma(int D, int E, int wide, VariantInfo *info, dim3 grid
 #define KMI_MFMA_CASE(DD, EE)                                          \
   if (D == DD && E == EE) {                                            \
     if (info) {                                                        \
-      info->rows = MfmaShape<DD>::ROWS_WG / kThreads;                  \
+      info->rows_per_wg = MfmaShape<DD>::ROWS_WG;                      \
       info->tile_j = MfmaShape<DD>::TJ;                                \
       return 0;                                                        \
     }                                                                  \

@@ -108,7 +108,7 @@ int kmin_find(int D, int K, VariantInfo *info, KminDispatch *fn) {
 
 struct Plan {
   int wide;
-  int rows;        // rows per lane
+  int64_t rows_wg; // rows per work-group
   int tile_j;
   int64_t nblk;    // work-groups along i
   int nsplit;      // j-splits
@@ -118,15 +118,18 @@ struct Plan {
 // Work-groups along i and splits along j.  The split count is chosen so that
 // the grid offers at least `kWaveTarget` waves per SIMD, with at least two
 // tiles per split.
-Plan make_plan(int64_t M, int64_t N, int cus, int rows_wide, int rows_narrow, int tile_j) {
+Plan make_plan(int64_t M, int64_t N, int cus, int64_t rows_wide, int64_t rows_narrow, int tile_j) {
   constexpr int kWaveTarget = 4;
+  if (rows_wide < 1) rows_wide = 1;
+  if (rows_narrow < 1) rows_narrow = 1;
+  if (tile_j < 1) tile_j = 1;
   const int64_t want_wgs = (int64_t)cus * kWaveTarget;        // 4 waves per WG, 4 SIMDs per CU
   Plan p{};
   const int64_t opt_rows = g_opt_rows.load();
-  p.wide = opt_rows == 1 ? 0 : (opt_rows == 2 ? 1 : (M >= (int64_t)kThreads * rows_wide * cus));
-  p.rows = p.wide ? rows_wide : rows_narrow;
+  p.wide = opt_rows == 1 ? 0 : (opt_rows == 2 ? 1 : (M >= rows_wide * cus));
+  p.rows_wg = p.wide ? rows_wide : rows_narrow;
   p.tile_j = tile_j;
-  p.nblk = (M + (int64_t)kThreads * p.rows - 1) / ((int64_t)kThreads * p.rows);
+  p.nblk = (M + p.rows_wg - 1) / p.rows_wg;
   const int64_t ntiles = (N + tile_j - 1) / tile_j;
   int64_t s = 1;
   const int64_t forced = g_opt_split.load();
@@ -186,8 +189,9 @@ int gauss_entry(int op, const float *x, const float *y, const float *b, const fl
   if (int rc = device_setup(&cus)) return rc;
   // The MFMA kernel and its direct-form companion both use 256-row work-groups
   // (the narrow VALU variant) and j-splits on the larger of the two tiles.
-  const Plan p = use_mfma ? make_plan(M, N, cus, 1, 1, std::max(mfma_info.tile_j, narrow_info.tile_j))
-                          : make_plan(M, N, cus, wide_info.rows, narrow_info.rows, wide_info.tile_j);
+  const Plan p = use_mfma ? make_plan(M, N, cus, mfma_info.rows_per_wg, mfma_info.rows_per_wg,
+                                      std::max(mfma_info.tile_j, narrow_info.tile_j))
+                          : make_plan(M, N, cus, wide_info.rows_per_wg, narrow_info.rows_per_wg, wide_info.tile_j);
 
   const double s2 = (double)sigma * (double)sigma;
   const double scale = std::sqrt(1.4426950408889634 / s2);
@@ -276,13 +280,19 @@ int keops_kmin(const float *x, const float *y, int64_t M, int64_t N, int32_t D, 
   VariantInfo info{};
   KminDispatch fn = nullptr;
   if (kmin_find(D, K, &info, &fn)) return KEOPS_ERR_UNSUPPORTED;
+  // fp32-MFMA prefilter at D >= 32 (the result is the same direct-form K-min)
+  VariantInfo mfma_info{};
+  if (D >= 32 && g_opt_form.load() == 0 && kmin_dispatch_mfma(D, K, &mfma_info, dim3(), nullptr, nullptr) == 0) {
+    fn = kmin_dispatch_mfma;
+    info = mfma_info;
+  }
   if (M == 0) return KEOPS_OK;
 
   hipStream_t st = (hipStream_t)stream;
   (void)hipGetLastError();
   int cus = 0;
   if (int rc = device_setup(&cus)) return rc;
-  const Plan p = make_plan(M, N, cus, info.rows, info.rows, info.tile_j);
+  const Plan p = make_plan(M, N, cus, info.rows_per_wg, info.rows_per_wg, info.tile_j);
   KminArgs a{};
   a.x = x; a.y = y; a.M = M; a.N = N;
   a.j_per_split = p.jps;

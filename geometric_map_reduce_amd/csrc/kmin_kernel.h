@@ -39,7 +39,8 @@ __device__ __forceinline__ float kmin_margin_coef(int D) { return (4.0f * D + 32
 
 template <int K>
 __device__ __forceinline__ void kmin_insert(float (&bd)[K], int (&bi)[K], float v, int j) {
-  // new list = first K of (old list with (v, j) inserted after every entry <= v)
+  // new list = first K of (old list with (v, j) inserted after every entry <= v);
+  // pure selects, no branches
 #pragma unroll
   for (int k = K - 1; k > 0; --k) {
     const bool shift = v < bd[k - 1];
@@ -49,7 +50,32 @@ __device__ __forceinline__ void kmin_insert(float (&bd)[K], int (&bi)[K], float 
     bd[k] = nd;
     bi[k] = ni;
   }
-  if (v < bd[0]) { bd[0] = v; bi[0] = j; }
+  const bool first = v < bd[0];
+  bd[0] = first ? v : bd[0];
+  bi[0] = first ? j : bi[0];
+}
+
+// Insertion by (d, j) lexicographic order into a sorted list whose empty slots
+// carry j < 0 and rank last; an entry with j < 0 is not inserted.  Used to merge
+// lists built over disjoint j sets.  Pure selects over bitwise boolean logic (a
+// short-circuit formulation of the K = 1 case was lowered with the partner's
+// values lost on this toolchain).
+template <int K>
+__device__ __forceinline__ void kmin_insert_lex(float (&bd)[K], int (&bi)[K], float v, int j) {
+  const bool invalid = j < 0;   // ranks after every slot, so nothing moves
+  bool before[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k)
+    before[k] = invalid | ((bi[k] >= 0) & ((bd[k] < v) | ((bd[k] == v) & (bi[k] < j))));
+#pragma unroll
+  for (int k = K - 1; k > 0; --k) {
+    const float nd = !before[k - 1] ? bd[k - 1] : (!before[k] ? v : bd[k]);
+    const int ni = !before[k - 1] ? bi[k - 1] : (!before[k] ? j : bi[k]);
+    bd[k] = nd;
+    bi[k] = ni;
+  }
+  bd[0] = before[0] ? bd[0] : v;
+  bi[0] = before[0] ? bi[0] : j;
 }
 
 template <int D, int K, int R>

@@ -7,8 +7,8 @@ namespace kmi {
 
 // Shape facts of a compiled variant, filled when `info` is non-null.
 struct VariantInfo {
-  int rows;     // rows per lane
-  int tile_j;   // j rows per LDS tile (the j-split granularity)
+  int rows_per_wg;  // output rows per work-group
+  int tile_j;       // j rows per LDS tile (the j-split granularity)
 };
 
 // Each dispatcher returns 0 when it owns (D, E[, K]) -- launching the kernel,
@@ -29,6 +29,7 @@ KMI_DECLARE_GAUSS(gauss_dispatch_sum_mfma)
 KMI_DECLARE_KMIN(kmin_dispatch_d1_4)
 KMI_DECLARE_KMIN(kmin_dispatch_d5_8)
 KMI_DECLARE_KMIN(kmin_dispatch_large)
+KMI_DECLARE_KMIN(kmin_dispatch_mfma)
 #undef KMI_DECLARE_KMIN
 
 void launch_sum_combine(const float *ws, int nsplit, int64_t count, float *out, hipStream_t st);

@@ -308,3 +308,25 @@ def test_mfma_mixed_blocks(split):
     a = host(gm.keops_gauss_sum(dev(x), dev(y), dev(b), sigma))
     a_ref, n_ref = oracle.gauss_sum(x, y, b, float(np.float32(sigma)))
     check_sum(a, a_ref, n_ref)
+
+
+@pytest.mark.parametrize("D,K", [(32, 10), (50, 3), (64, 10), (64, 16), (100, 1), (100, 10), (64, 1), (64, 32)])
+def test_kmin_mfma_equals_valu(D, K):
+    """The MFMA-prefiltered K-min and the VALU K-min both return the direct-form fp32
+    K-min: identical indices and bitwise-identical distances; both match the oracle."""
+    say(f"kmin mfma == valu D={D} K={K}")
+    rng = np.random.default_rng(D * 100 + K)
+    centres = rng.uniform(-5, 5, (16, D))
+    x = (centres[rng.integers(0, 16, 600)] + 0.5 * rng.standard_normal((600, D))).astype(np.float32)
+    y = (centres[rng.integers(0, 16, 3000)] + 0.5 * rng.standard_normal((3000, D))).astype(np.float32)
+    y[2999] = y[5]                                   # an exact tie
+    X, Y = dev(x), dev(y)
+    d1, i1 = gm.keops_kmin(X, Y, K)
+    gm.keops_set_option(gm.KEOPS_OPT_FORM, 1)        # forces the VALU kernel
+    d2, i2 = gm.keops_kmin(X, Y, K)
+    d1, i1, d2, i2 = host(d1), host(i1), host(d2), host(i2)
+    d_ref, i_ref = oracle.kmin(x, y, K)
+    check_kmin(x, y, np.arange(600), d2, i2, d_ref, i_ref)   # VALU path
+    check_kmin(x, y, np.arange(600), d1, i1, d_ref, i_ref)   # MFMA path
+    assert np.array_equal(i1, i2)
+    assert np.array_equal(d1.view(np.int32), d2.view(np.int32))
