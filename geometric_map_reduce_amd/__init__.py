@@ -12,6 +12,6 @@ never stored, run as hand-written gfx950 HIP kernels behind the C ABI of
 
 PyTorch supplies device memory and streams only.
 """
-from .binding import (KEOPS_OPT_FORM, KEOPS_OPT_PROFILE, KEOPS_OPT_ROWS, KEOPS_OPT_SPLIT_J,  # noqa: F401
+from .binding import (KEOPS_OPT_FORM, KEOPS_OPT_PROFILE, KEOPS_OPT_ROWS, KEOPS_OPT_SPLIT_J, KEOPS_OPT_WG_TARGET,  # noqa: F401
                       KeopsError, keops_gauss_grad_x, keops_gauss_lse, keops_gauss_sum, keops_kmin,
                       keops_profile_read, keops_set_option, keops_version, lib, status_string)

@@ -18,7 +18,7 @@
 namespace kmi {
 namespace {
 
-std::atomic<int64_t> g_opt_split{0}, g_opt_form{0}, g_opt_rows{0}, g_opt_profile{0};
+std::atomic<int64_t> g_opt_split{0}, g_opt_form{0}, g_opt_rows{0}, g_opt_profile{0}, g_opt_wg_target{0};
 
 // ---- pass-1 timing (KEOPS_OPT_PROFILE)
 struct EventPair { hipEvent_t start, stop; };
@@ -106,6 +106,15 @@ int kmin_find(int D, int K, VariantInfo *info, KminDispatch *fn) {
   return KEOPS_ERR_UNSUPPORTED;
 }
 
+// Default work-groups per CU for each kernel family, from sweeps at the
+// 1M x 1M (D = 3), 100k x 10M (D = 50) and 1M x 1M K-min shapes: the VALU sum,
+// LSE and grad gain 7-8 % going from 4 to 24, the MFMA sum 7 % from 4 to 16;
+// K-min's partial lists are larger, and more splits cost about what they balance.
+constexpr int64_t kGaussWgsPerCu = 24;
+constexpr int64_t kMfmaSumWgsPerCu = 16;
+constexpr int64_t kKminWgsPerCu = 8;
+constexpr int64_t kKminMfmaWgsPerCu = 4;
+
 struct Plan {
   int wide;
   int64_t rows_wg; // rows per work-group
@@ -116,14 +125,19 @@ struct Plan {
 };
 
 // Work-groups along i and splits along j.  The split count is chosen so that
-// the grid offers at least `kWaveTarget` waves per SIMD, with at least two
-// tiles per split.
-Plan make_plan(int64_t M, int64_t N, int cus, int64_t rows_wide, int64_t rows_narrow, int tile_j) {
-  constexpr int kWaveTarget = 4;
+// the grid holds about `wgs_per_cu` work-groups per CU (each of four waves), with
+// at least two tiles per split.  Many short work-groups let the hardware
+// dispatcher even out the CUs' finishing times: the last round of a grid whose
+// size is not a multiple of the resident capacity leaves CUs idle, and at a
+// handful of work-groups per CU that tail costs several per cent.
+Plan make_plan(int64_t M, int64_t N, int cus, int64_t rows_wide, int64_t rows_narrow, int tile_j,
+               int64_t wgs_per_cu) {
+  const int64_t target = g_opt_wg_target.load();
+  if (target > 0) wgs_per_cu = target;
   if (rows_wide < 1) rows_wide = 1;
   if (rows_narrow < 1) rows_narrow = 1;
   if (tile_j < 1) tile_j = 1;
-  const int64_t want_wgs = (int64_t)cus * kWaveTarget;        // 4 waves per WG, 4 SIMDs per CU
+  const int64_t want_wgs = (int64_t)cus * (wgs_per_cu > 0 ? wgs_per_cu : 1);
   Plan p{};
   const int64_t opt_rows = g_opt_rows.load();
   p.wide = opt_rows == 1 ? 0 : (opt_rows == 2 ? 1 : (M >= rows_wide * cus));
@@ -190,8 +204,9 @@ int gauss_entry(int op, const float *x, const float *y, const float *b, const fl
   // The MFMA kernel and its direct-form companion both use 256-row work-groups
   // (the narrow VALU variant) and j-splits on the larger of the two tiles.
   const Plan p = use_mfma ? make_plan(M, N, cus, mfma_info.rows_per_wg, mfma_info.rows_per_wg,
-                                      std::max(mfma_info.tile_j, narrow_info.tile_j))
-                          : make_plan(M, N, cus, wide_info.rows_per_wg, narrow_info.rows_per_wg, wide_info.tile_j);
+                                      std::max(mfma_info.tile_j, narrow_info.tile_j), kMfmaSumWgsPerCu)
+                          : make_plan(M, N, cus, wide_info.rows_per_wg, narrow_info.rows_per_wg, wide_info.tile_j,
+                                      kGaussWgsPerCu);
 
   const double s2 = (double)sigma * (double)sigma;
   const double scale = std::sqrt(1.4426950408889634 / s2);
@@ -292,7 +307,8 @@ int keops_kmin(const float *x, const float *y, int64_t M, int64_t N, int32_t D, 
   (void)hipGetLastError();
   int cus = 0;
   if (int rc = device_setup(&cus)) return rc;
-  const Plan p = make_plan(M, N, cus, info.rows_per_wg, info.rows_per_wg, info.tile_j);
+  const Plan p = make_plan(M, N, cus, info.rows_per_wg, info.rows_per_wg, info.tile_j,
+                           fn == kmin_dispatch_mfma ? kKminMfmaWgsPerCu : kKminWgsPerCu);
   KminArgs a{};
   a.x = x; a.y = y; a.M = M; a.N = N;
   a.j_per_split = p.jps;
@@ -348,6 +364,10 @@ int keops_set_option(int option, int64_t value) {
     case KEOPS_OPT_PROFILE:
       if (value < 0 || value > 1) return KEOPS_ERR_INVALID_ARG;
       g_opt_profile.store(value);
+      return KEOPS_OK;
+    case KEOPS_OPT_WG_TARGET:
+      if (value < 0 || value > 4096) return KEOPS_ERR_INVALID_ARG;
+      g_opt_wg_target.store(value);
       return KEOPS_OK;
     default:
       return KEOPS_ERR_INVALID_ARG;

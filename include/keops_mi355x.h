@@ -114,12 +114,15 @@ const char *keops_status_string(int status);
  *                          condition holds)
  *   KEOPS_OPT_ROWS      -- 1 = one row per lane, 2 = the wide variant (several
  *                          rows per lane, for large M)
+ *   KEOPS_OPT_WG_TARGET -- work-groups per CU the automatic j-split aims for
+ *                          (1..4096; ignored when KEOPS_OPT_SPLIT_J is set)
  * Returns KEOPS_OK, or KEOPS_ERR_INVALID_ARG for an unknown option or value.
  */
 #define KEOPS_OPT_SPLIT_J 1
 #define KEOPS_OPT_FORM 2
 #define KEOPS_OPT_ROWS 3
 #define KEOPS_OPT_PROFILE 4   /* 1 = record HIP events around each pass-1 launch */
+#define KEOPS_OPT_WG_TARGET 5
 int keops_set_option(int option, int64_t value);
 
 /*

@@ -96,6 +96,9 @@ def test_options(L):
     assert L.keops_set_option(1, -1) == -1
     assert L.keops_set_option(2, 2) == -1
     assert L.keops_set_option(3, 3) == -1
-    for opt in (1, 2, 3):
+    assert L.keops_set_option(5, -1) == -1
+    assert L.keops_set_option(5, 4097) == -1
+    assert L.keops_set_option(5, 16) == 0
+    for opt in (1, 2, 3, 5):
         assert L.keops_set_option(opt, 0) == 0
     assert L.keops_version() >= 100

@@ -35,10 +35,10 @@ def say(msg):
 def _options():
     if not torch.cuda.is_available():
         pytest.skip("needs a GPU")
-    for o in (gm.KEOPS_OPT_SPLIT_J, gm.KEOPS_OPT_FORM, gm.KEOPS_OPT_ROWS):
+    for o in (gm.KEOPS_OPT_SPLIT_J, gm.KEOPS_OPT_FORM, gm.KEOPS_OPT_ROWS, gm.KEOPS_OPT_WG_TARGET):
         gm.keops_set_option(o, 0)
     yield
-    for o in (gm.KEOPS_OPT_SPLIT_J, gm.KEOPS_OPT_FORM, gm.KEOPS_OPT_ROWS):
+    for o in (gm.KEOPS_OPT_SPLIT_J, gm.KEOPS_OPT_FORM, gm.KEOPS_OPT_ROWS, gm.KEOPS_OPT_WG_TARGET):
         gm.keops_set_option(o, 0)
 
 
