@@ -17,7 +17,9 @@ Prints ONE JSON line:
                 counter runs (null when the kernel sources changed since)
   cpu_baseline  the float64 oracle timed on this host's cores over a bounded
                 sample of rows (each row over all N), scaled to pair-evals/s
-Other workloads (--workload) print the same fields for their own op.
+Other workloads (--workload) print the same fields for their own op; the
+few-rows sum (--workload stream: 16 rows against 1e8 points) is bound by
+streaming y and b from HBM and reports its roofline in GB/s against 8 TB/s.
 """
 from __future__ import annotations
 
@@ -48,7 +50,10 @@ BENCHES = {
     "solver": ("sum", "solver_matvec_100k_x_10M"),
     "kmin3": ("kmin", "kmin10_1M_d3"),
     "kmin64": ("kmin", "kmin10_1M_d64"),
+    "stream": ("sum", "stream_16_x_100M"),
 }
+PEAK_HBM_GBS = 8000.0             # MI355X HBM3E peak
+STREAM_MAX_ROWS = 64              # the library's few-rows layout (j per lane) for the sum
 
 
 def flops_per_pair(op, D, E):
@@ -60,14 +65,27 @@ def uses_mfma(op, D):
     return D >= 32 and op in ("sum", "kmin")
 
 
-def roofline_of(op, D, E):
-    """(bound, algorithmic flops per pair, kernel name) of the dominant pass-1 kernel.
+def is_stream(op, M, D):
+    """The sum at few rows runs the j-per-lane kernel, bound by streaming y and b from HBM."""
+    return op == "sum" and M <= STREAM_MAX_ROWS and D <= 8
+
+
+def roofline_of(op, M, D, E):
+    """(bound, algorithmic units per pair, kernel name) of the dominant pass-1 kernel.
     MFMA path: the contraction <x~, y~> of 2D flops per pair against the fp32 matrix peak
-    (the per-pair exp and accumulate are VALU work on top)."""
+    (the per-pair exp and accumulate are VALU work on top).  Few-rows sum: HBM bytes,
+    priced per launch (y and b read once) rather than per pair."""
+    if is_stream(op, M, D):
+        return "hbm", None, "gauss_stream_kernel"
     if uses_mfma(op, D):
         return "mfma", 2 * D, ("gauss_mfma_sum_kernel" if op == "sum" else "kmin_mfma_kernel")
     name = "kmin_valu_kernel" if op == "kmin" else f"gauss_valu_kernel<{op}>"
     return "alu", flops_per_pair(op, D, E), name
+
+
+def stream_bytes(w):
+    """Algorithmic HBM bytes of one few-rows sum launch: x, y, b read once, out written once."""
+    return 4 * (w.N * (w.D + w.E) + w.M * w.D + w.M * w.E)
 
 
 # sources that define each benchmarked kernel and its launch plan
@@ -77,6 +95,7 @@ KERNEL_SOURCES = {
     "lse": ["gauss_kernel.h", "dispatch_gauss.h", "gauss_lse_small.hip"],
     "grad_x": ["gauss_kernel.h", "dispatch_gauss.h", "gauss_grad_small.hip"],
     "kmin": ["kmin_kernel.h", "dispatch_kmin.h", "kmin_d1_4.hip"],
+    "stream": ["gauss_stream.h", "gauss_stream.hip"],
 }
 
 
@@ -226,10 +245,20 @@ def main():
 
     pairs = w.M * w.N
     value = pairs / (ms_step * 1e-3) / 1e9
-    bound, fpp, kname = roofline_of(op, w.D, w.E)
+    bound, fpp, kname = roofline_of(op, w.M, w.D, w.E)
     kern_avg_ms = kern_ms / max(launches, 1)
-    achieved = fpp * pairs / (kern_avg_ms * 1e-3) / 1e12
-    traffic = recorded_traffic(args.workload, op)
+    src_key = "stream" if bound == "hbm" else op
+    traffic = recorded_traffic(args.workload, src_key)
+    if bound == "hbm":
+        achieved = stream_bytes(w) / (kern_avg_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic}
+        kinfo = {"bytes_per_launch": stream_bytes(w)}
+    else:
+        achieved = fpp * pairs / (kern_avg_ms * 1e-3) / 1e12
+        roof = {"bound": bound, "achieved": round(achieved, 3), "peak": PEAK_FP32_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_TFLOPS, 4), "traffic": traffic}
+        kinfo = {"flops_per_pair": fpp}
 
     res = {
         "metric": METRIC if args.workload == "sum" else f"{op} G pair-evals/s @ {w.name}",
@@ -245,10 +274,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": dict(w.describe(), op=op, seed=0),
-        "roofline": {"bound": bound, "achieved": round(achieved, 3), "peak": PEAK_FP32_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_TFLOPS, 4), "traffic": traffic},
-        "kernel": {"name": kname,
-                   "avg_ms": round(kern_avg_ms, 4), "launches": launches, "flops_per_pair": fpp},
+        "roofline": roof,
+        "kernel": dict({"name": kname, "avg_ms": round(kern_avg_ms, 4), "launches": launches}, **kinfo),
         "wall_s_timed": round(wall, 3),
     }
     if not args.no_cpu_baseline:

@@ -37,6 +37,16 @@ struct GaussArgs {
   int *wg_flags;
 };
 
+// Arguments of the few-rows sum kernel (j per lane, rows in LDS).
+struct StreamArgs {
+  const float *x, *y, *b;
+  int64_t M, N;
+  float scale;          // sqrt(log2 e) / sigma
+  int64_t j_per_wg;     // multiple of the kernel's step (kThreads * j per lane)
+  float *part;          // [gridDim.x][M][E] partial sums
+  int form;             // Form
+};
+
 // Arguments of the K-min pass-1 kernel.
 struct KminArgs {
   const float *x, *y;

@@ -165,6 +165,50 @@ Plan make_plan(int64_t M, int64_t N, int cus, int64_t rows_wide, int64_t rows_na
 
 int check_launch() { return hipGetLastError() == hipSuccess ? KEOPS_OK : KEOPS_ERR_HIP; }
 
+// Few rows, many j: lanes own j, rows sit in LDS (M <= kStreamMaxRows by default).
+// Work-groups along j: about kStreamWgsPerCu per CU over all row groups, between
+// 4 and kStreamMaxSteps steps each (the latter bounds the terms one lane adds up).
+constexpr int64_t kStreamMaxRows = 64;
+constexpr int64_t kStreamWgsPerCu = 8;
+constexpr int64_t kStreamMaxSteps = 128;
+
+int gauss_stream_entry(const float *x, const float *y, const float *b, int64_t M, int64_t N, int D, int E,
+                       float sigma, float *out, hipStream_t st, int cus, const VariantInfo &info, int form) {
+  const int64_t step = info.tile_j;
+  const int64_t groups = (M + info.rows_per_wg - 1) / info.rows_per_wg;
+  const int64_t nsteps = (N + step - 1) / step;
+  const int64_t target = g_opt_wg_target.load() > 0 ? g_opt_wg_target.load() : kStreamWgsPerCu;
+  int64_t wgs = ((int64_t)cus * target + groups - 1) / groups;
+  const int64_t lo = (nsteps + kStreamMaxSteps - 1) / kStreamMaxSteps;
+  const int64_t hi = std::max<int64_t>(1, nsteps / 4);
+  wgs = std::max(lo, std::min(wgs, hi));
+  if (wgs > nsteps) wgs = nsteps;
+  if (wgs < 1) wgs = 1;
+  if (wgs > 0x7fffffff || groups > 65535) return KEOPS_ERR_UNSUPPORTED;
+  const int64_t jpw = (nsteps + wgs - 1) / wgs * step;
+  wgs = (N + jpw - 1) / jpw;
+
+  float *ws = nullptr;
+  const size_t bytes = (size_t)wgs * M * E * sizeof(float);
+  if (hipMallocAsync((void **)&ws, bytes, st) != hipSuccess || !ws) {
+    (void)hipGetLastError();
+    return KEOPS_ERR_ALLOC;
+  }
+  StreamArgs a{};
+  a.x = x; a.y = y; a.b = b;
+  a.M = M; a.N = N;
+  a.scale = (float)std::sqrt(1.4426950408889634 / ((double)sigma * (double)sigma));
+  a.j_per_wg = jpw;
+  a.part = ws;
+  a.form = form == 1 ? FORM_DIRECT : FORM_AUTO;
+  const int prof = prof_begin(st);
+  gauss_dispatch_sum_stream(D, E, info.rows_per_wg, nullptr, dim3((unsigned)wgs, (unsigned)groups), &a, st);
+  prof_end(prof, st);
+  launch_stream_combine(ws, (int)wgs, M * E, out, st);
+  (void)hipFreeAsync(ws, st);
+  return check_launch();
+}
+
 int gauss_entry(int op, const float *x, const float *y, const float *b, const float *g, int64_t M, int64_t N,
                 int32_t D, int32_t E, float sigma, float *out, void *stream) {
   // ---- validation (host only)
@@ -201,6 +245,15 @@ int gauss_entry(int op, const float *x, const float *y, const float *b, const fl
   }
   int cus = 0;
   if (int rc = device_setup(&cus)) return rc;
+  if (op == OP_SUM && !use_mfma) {
+    VariantInfo sinfo{};
+    const int64_t rows_opt = g_opt_rows.load();
+    const int mr = M <= 4 ? 4 : stream_rows_large(D, E);
+    if ((rows_opt == 3 || (rows_opt == 0 && M <= kStreamMaxRows)) &&
+        gauss_dispatch_sum_stream(D, E, mr, &sinfo, dim3(), nullptr, nullptr) == 0 &&
+        (M + sinfo.rows_per_wg - 1) / sinfo.rows_per_wg <= 65535)
+      return gauss_stream_entry(x, y, b, M, N, D, E, sigma, out, st, cus, sinfo, (int)form);
+  }
   // The MFMA kernel and its direct-form companion both use 256-row work-groups
   // (the narrow VALU variant) and j-splits on the larger of the two tiles.
   const Plan p = use_mfma ? make_plan(M, N, cus, mfma_info.rows_per_wg, mfma_info.rows_per_wg,
@@ -358,7 +411,7 @@ int keops_set_option(int option, int64_t value) {
       g_opt_form.store(value);
       return KEOPS_OK;
     case KEOPS_OPT_ROWS:
-      if (value < 0 || value > 2) return KEOPS_ERR_INVALID_ARG;
+      if (value < 0 || value > 3) return KEOPS_ERR_INVALID_ARG;
       g_opt_rows.store(value);
       return KEOPS_OK;
     case KEOPS_OPT_PROFILE:

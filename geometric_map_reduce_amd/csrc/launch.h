@@ -24,6 +24,14 @@ KMI_DECLARE_GAUSS(gauss_dispatch_grad_large)
 KMI_DECLARE_GAUSS(gauss_dispatch_sum_mfma)
 #undef KMI_DECLARE_GAUSS
 
+// Few-rows sum with row groups of mr = 4 or stream_rows_large(D, E) rows (rows_per_wg =
+// mr, tile_j = j per work-group step).
+constexpr int stream_rows_large(int D, int E) {
+  return D <= 4 ? (E == 1 ? 16 : (E == 2 ? 8 : 4)) : (E == 1 ? 8 : 4);
+}
+int gauss_dispatch_sum_stream(int D, int E, int mr, VariantInfo *info, dim3 grid, const StreamArgs *args,
+                              hipStream_t st);
+
 #define KMI_DECLARE_KMIN(NAME) \
   int NAME(int D, int K, VariantInfo *info, dim3 grid, const KminArgs *args, hipStream_t st);
 KMI_DECLARE_KMIN(kmin_dispatch_d1_4)
@@ -37,5 +45,6 @@ void launch_lse_combine(const float *ws, int nsplit, int64_t M, int E, float *ou
 int launch_kmin_combine(const float *pd, const int32_t *pi, int nsplit, int64_t M, int K, float *out_d,
                         int64_t *out_i, hipStream_t st);
 void launch_fill(float *out, int64_t count, float v, hipStream_t st);
+void launch_stream_combine(const float *part, int nparts, int64_t count, float *out, hipStream_t st);
 
 }  // namespace kmi

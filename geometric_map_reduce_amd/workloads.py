@@ -22,7 +22,12 @@ sum_lse_1M                 1e6       1e6       3    E=1     0.1    x, y ~ U[0,1)
 solver_matvec_100k_x_10M   1e5       1e7       50   E=1     1.0    x, y ~ N(0, I/50), b ~ N(0,1)
 kmin10_1M_d3               1e6       1e6       3    K=10    --     16-component mixture
 kmin10_1M_d64              1e6       1e6       64   K=10    --     16-component mixture
+stream_16_x_100M           16        1e8       3    E=1     0.1    x, y ~ U[0,1)^3, b ~ N(0,1)
 =========================  ========  ========  ===  ======  =====  =========================
+
+stream_16_x_100M is the few-rows, many-j case (the Falkon issue's M << N taken
+to its end): 16 rows against 1e8 points, where streaming y and b from HBM
+once, not arithmetic, bounds the time.
 
 Mixture recipe: centres ~ U[-5, 5)^D (16 of them, drawn first), then for x:
 labels ~ U{0..15}, x = centres[label] + 0.5 * N(0, I); then the same for y.
@@ -73,6 +78,8 @@ WORKLOADS = {
                  ops=("kmin",)),
         Workload("kmin10_1M_d64", 1_000_000, 1_000_000, 64, K=10, dist="mixture16",
                  ops=("kmin",)),
+        Workload("stream_16_x_100M", 16, 100_000_000, 3, E=1, sigma=0.1, dist="uniform",
+                 ops=("sum",)),
     ]
 }
 

@@ -113,7 +113,9 @@ const char *keops_status_string(int status);
  *                          expanded form is otherwise used wherever its range
  *                          condition holds)
  *   KEOPS_OPT_ROWS      -- 1 = one row per lane, 2 = the wide variant (several
- *                          rows per lane, for large M)
+ *                          rows per lane, for large M), 3 = the few-rows layout
+ *                          of the sum (j per lane, rows in LDS; chosen
+ *                          automatically for M <= 64 at D <= 8)
  *   KEOPS_OPT_WG_TARGET -- work-groups per CU the automatic j-split aims for
  *                          (1..4096; ignored when KEOPS_OPT_SPLIT_J is set)
  * Returns KEOPS_OK, or KEOPS_ERR_INVALID_ARG for an unknown option or value.

@@ -95,7 +95,7 @@ def test_options(L):
     assert L.keops_set_option(99, 1) == -1
     assert L.keops_set_option(1, -1) == -1
     assert L.keops_set_option(2, 2) == -1
-    assert L.keops_set_option(3, 3) == -1
+    assert L.keops_set_option(3, 4) == -1
     assert L.keops_set_option(5, -1) == -1
     assert L.keops_set_option(5, 4097) == -1
     assert L.keops_set_option(5, 16) == 0

@@ -101,6 +101,32 @@ def test_forms_splits_layouts(form, split, rows):
         _check_all(x, y, b, g, sigma, _run_all(x, y, b, g, sigma))
 
 
+# few-rows layout (j per lane, rows in LDS): row groups of 16 with a ragged last
+# group, steps of 1024 j with ragged tails, sigma = 0.05 puts the row group beyond
+# the expanded form's range (direct-form fallback under the automatic form)
+STREAM = [(1, 1, 3, 1, 1.0), (1, 5000, 3, 1, 0.3), (5, 1025, 1, 2, 0.7), (16, 3000, 3, 1, 0.1),
+          (16, 3000, 3, 1, 0.05), (17, 4097, 8, 4, 1.5), (40, 10000, 5, 3, 0.9), (64, 2049, 2, 1, 2.0),
+          (100, 3000, 3, 1, 0.5), (33, 70000, 4, 1, 0.2)]
+
+
+@pytest.mark.parametrize("form", [0, 1], ids=["auto", "direct"])
+@pytest.mark.parametrize("case", STREAM, ids=lambda c: "M%d_N%d_D%d_E%d_s%g" % c)
+def test_stream_layout(case, form):
+    M, N, D, E, sigma = case
+    say(f"stream layout M={M} N={N} D={D} E={E} sigma={sigma} form={form}")
+    x, y, b, _ = rand_case(300 + M + D, M, N, D, E)
+    sigma = float(np.float32(sigma))
+    a_ref, n_ref = oracle.gauss_sum(x, y, b, sigma)
+    X, Y, B = dev(x), dev(y), dev(b)
+    gm.keops_set_option(gm.KEOPS_OPT_ROWS, 3)
+    gm.keops_set_option(gm.KEOPS_OPT_FORM, form)
+    for target in (0, 1, 64):                 # one long j range per work-group, the default, many short
+        gm.keops_set_option(gm.KEOPS_OPT_WG_TARGET, target)
+        a = gm.keops_gauss_sum(X, Y, B, sigma)
+        torch.cuda.synchronize()
+        check_sum(host(a), a_ref, n_ref)
+
+
 def test_far_from_origin_and_spread():
     """Data far from the origin (centring) and spread out (direct-form fallback)."""
     say("far/spread")
@@ -257,6 +283,18 @@ def test_workload_solver_matvec():
     a_ref, n_ref = oracle.gauss_sum(x, y, b, w.sigma, rows=rows)
     err = check_sum(a[rows], a_ref, n_ref)
     say(json.dumps({"workload": w.name, "sum_max_norm_err": err}))
+
+
+def test_workload_stream_16_x_100M():
+    """Few rows, 1e8 j: every row against the oracle, in the launch the library picks."""
+    w = workloads.WORKLOADS["stream_16_x_100M"]
+    say(f"workload {w.name}")
+    x, y, b = workloads.make_inputs(w)
+    a = gm.keops_gauss_sum(dev(x), dev(y), dev(b), w.sigma)
+    torch.cuda.synchronize()
+    a_ref, n_ref = oracle.gauss_sum(x, y, b, w.sigma)
+    err = check_sum(host(a), a_ref, n_ref)
+    say(f"  max err / norm {err:.3g}")
 
 
 @pytest.mark.parametrize("name", ["kmin10_1M_d3", "kmin10_1M_d64"])
