@@ -60,10 +60,12 @@ def open_library(path: str):
     lib.oracle_gauss_sum.argtypes = [P, P, P, i64, i64, i32, i32, f64, P, i64, P, P]
     lib.oracle_gauss_lse.argtypes = [P, P, P, i64, i64, i32, i32, f64, P, i64, P]
     lib.oracle_gauss_grad_x.argtypes = [P, P, P, P, i64, i64, i32, i32, f64, P, i64, P, P]
+    lib.oracle_gauss_grad_y.argtypes = [P, P, P, P, i64, i64, i32, i32, f64, P, i64, P, P]
+    lib.oracle_gauss_grad_b.argtypes = [P, P, P, i64, i64, i32, i32, f64, P, i64, P, P]
     lib.oracle_kmin.argtypes = [P, P, i64, i64, i32, i32, P, i64, P, P]
     lib.oracle_sq_dist_pairs.argtypes = [P, P, i32, P, P, i64, P]
-    for f in ("oracle_gauss_sum", "oracle_gauss_lse", "oracle_gauss_grad_x",
-              "oracle_kmin", "oracle_sq_dist_pairs", "oracle_num_threads"):
+    for f in ("oracle_gauss_sum", "oracle_gauss_lse", "oracle_gauss_grad_x", "oracle_gauss_grad_y",
+              "oracle_gauss_grad_b", "oracle_kmin", "oracle_sq_dist_pairs", "oracle_num_threads"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -153,6 +155,39 @@ def gauss_grad_x(x, y, b, g, sigma, rows=None, lib=None):
     _check((lib or _load()).oracle_gauss_grad_x(_ptr(x), _ptr(y), _ptr(b), _ptr(g), M, N, D, E,
                                        float(sigma), _ptr(r), n, _ptr(out), _ptr(nu)),
            "gauss_grad_x")
+    return out, nu
+
+
+def gauss_grad_y(x, y, b, g, sigma, cols=None, lib=None):
+    """Gy[c, d] = sum_i (2/sigma^2) K_ij <g_i, b_j> (x_id - y_jd)  for j = cols[c]:
+    dL/dy of L = sum g * a.  Returns (Gy, nu) in float64, nu the sum of the terms' moduli."""
+    x, y, b, g = _f32(x, 2), _f32(y, 2), _f32(b, 2), _f32(g, 2)
+    M, D = x.shape
+    N, E = b.shape
+    assert y.shape == (N, D) and g.shape == (M, E)
+    c, n = _rows(cols, N)
+    out = np.empty((n, D), np.float64)
+    nu = np.empty((n, D), np.float64)
+    _check((lib or _load()).oracle_gauss_grad_y(_ptr(x), _ptr(y), _ptr(b), _ptr(g), M, N, D, E,
+                                       float(sigma), _ptr(c), n, _ptr(out), _ptr(nu)),
+           "gauss_grad_y")
+    return out, nu
+
+
+def gauss_grad_b(x, y, g, sigma, cols=None, lib=None):
+    """Gb[c, e] = sum_i K_ij g_ie  for j = cols[c]: dL/db of L = sum g * a.
+    Returns (Gb, nu) in float64, nu[c, e] = sum_i |K_ij g_ie|."""
+    x, y, g = _f32(x, 2), _f32(y, 2), _f32(g, 2)
+    M, D = x.shape
+    N = y.shape[0]
+    E = g.shape[1]
+    assert y.shape == (N, D) and g.shape == (M, E)
+    c, n = _rows(cols, N)
+    out = np.empty((n, E), np.float64)
+    nu = np.empty((n, E), np.float64)
+    _check((lib or _load()).oracle_gauss_grad_b(_ptr(x), _ptr(y), _ptr(g), M, N, D, E,
+                                       float(sigma), _ptr(c), n, _ptr(out), _ptr(nu)),
+           "gauss_grad_b")
     return out, nu
 
 

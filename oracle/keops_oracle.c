@@ -1,6 +1,6 @@
 /*
  * keops_oracle.c -- the ORACLE: a plain, slow, double-precision CPU
- * implementation of the four Gaussian map-reductions.
+ * implementation of the Gaussian map-reductions and their gradients.
  *
  * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
  * baseline leg of the benchmark may load this library.  The GPU library shares
@@ -30,6 +30,8 @@
  *  - grad_x is the vector-Jacobian product of a = sum-reduction with a given
  *    cotangent g[M,E] = dL/da (the README differentiates (a**2).sum(), i.e.
  *    g = 2a).
+ *  - grad_y and grad_b are the vector-Jacobian products of the same sum in y
+ *    and b (reductions over i, one output per point y_j).
  *  - K-min: the K smallest squared distances of row i with their indices, in
  *    ascending (distance, index) lexicographic order.
  *
@@ -164,6 +166,70 @@ int oracle_gauss_grad_x(const float *x, const float *y, const float *b, const fl
                 const double t = -2.0 * inv_s2 * k * gb * ((double)x[i * D + d] - (double)y[j * D + d]);
                 o[d] += t;
                 if (n) n[d] += fabs(t);
+            }
+        }
+    }
+    return 0;
+}
+
+/*
+ * Gradient of L = sum_ie g_ie a_ie with respect to y (the transposed
+ * reduction: one output per point y_j, summed over the rows i).  [KO-GPU] §2
+ * "Performance and differentiation": the reductions are differentiable with
+ * respect to every input variable; differentiating
+ * a_ie = sum_j exp(-|x_i - y_j|^2/sigma^2) b_je in y_jd gives
+ *   Gy_jd = sum_i (2/sigma^2) K_ij <g_i, b_j> (x_id - y_jd).
+ * `cols` selects which points j to compute (NULL = 0..ncols-1).  Also returns
+ * nu_jd = sum_i |(2/sigma^2) K_ij <g_i, b_j> (x_id - y_jd)|.
+ */
+int oracle_gauss_grad_y(const float *x, const float *y, const float *b, const float *g,
+                        int64_t M, int64_t N, int D, int E, double sigma,
+                        const int64_t *cols, int64_t ncols,
+                        double *out, double *nu) {
+    if (check_common(N, M, D, ncols, cols) || E < 1 || !(sigma > 0.0)) return -1;
+    const double inv_s2 = 1.0 / (sigma * sigma);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t c = 0; c < ncols; ++c) {
+        const int64_t j = cols ? cols[c] : c;
+        double *o = out + c * D, *n = nu ? nu + c * D : NULL;
+        for (int d = 0; d < D; ++d) { o[d] = 0.0; if (n) n[d] = 0.0; }
+        for (int64_t i = 0; i < M; ++i) {
+            const double k = exp(-sq_dist(x + i * D, y + j * D, D) * inv_s2);
+            double gb = 0.0;
+            for (int e = 0; e < E; ++e) gb += (double)g[i * E + e] * (double)b[j * E + e];
+            for (int d = 0; d < D; ++d) {
+                const double t = 2.0 * inv_s2 * k * gb * ((double)x[i * D + d] - (double)y[j * D + d]);
+                o[d] += t;
+                if (n) n[d] += fabs(t);
+            }
+        }
+    }
+    return 0;
+}
+
+/*
+ * Gradient of L = sum_ie g_ie a_ie with respect to b (same passage): a is
+ * linear in b, so
+ *   Gb_je = sum_i K_ij g_ie,
+ * with nu_je = sum_i |K_ij g_ie|.  `cols` as for oracle_gauss_grad_y.
+ */
+int oracle_gauss_grad_b(const float *x, const float *y, const float *g,
+                        int64_t M, int64_t N, int D, int E, double sigma,
+                        const int64_t *cols, int64_t ncols,
+                        double *out, double *nu) {
+    if (check_common(N, M, D, ncols, cols) || E < 1 || !(sigma > 0.0)) return -1;
+    const double inv_s2 = 1.0 / (sigma * sigma);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t c = 0; c < ncols; ++c) {
+        const int64_t j = cols ? cols[c] : c;
+        double *o = out + c * E, *n = nu ? nu + c * E : NULL;
+        for (int e = 0; e < E; ++e) { o[e] = 0.0; if (n) n[e] = 0.0; }
+        for (int64_t i = 0; i < M; ++i) {
+            const double k = exp(-sq_dist(x + i * D, y + j * D, D) * inv_s2);
+            for (int e = 0; e < E; ++e) {
+                const double t = k * (double)g[i * E + e];
+                o[e] += t;
+                if (n) n[e] += fabs(t);
             }
         }
     }

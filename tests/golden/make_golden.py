@@ -36,11 +36,15 @@ def main():
         a, n = oracle.gauss_sum(x, y, b, s)
         l = oracle.gauss_lse(x, y, b, s)
         G, nu = oracle.gauss_grad_x(x, y, b, g, s)
+        Gy, nuy = oracle.gauss_grad_y(x, y, b, g, s)
+        Gb, nub = oracle.gauss_grad_b(x, y, g, s)
         kd, ki = oracle.kmin(x, y, K)
         out[name] = dict(M=M, N=N, D=D, E=E, K=K, sigma=s, seed=seed,
                          x=x.tolist(), y=y.tolist(), b=b.tolist(), g=g.tolist(),
                          sum=a.tolist(), sum_norm=n.tolist(), lse=l.tolist(),
                          grad_x=G.tolist(), grad_norm=nu.tolist(),
+                         grad_y=Gy.tolist(), grad_y_norm=nuy.tolist(),
+                         grad_b=Gb.tolist(), grad_b_norm=nub.tolist(),
                          kmin_d=kd.tolist(), kmin_idx=ki.tolist())
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "small_cases.json")
     with open(path, "w") as f:

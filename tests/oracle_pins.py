@@ -292,6 +292,98 @@ def pin_grad_identity(lib=None):
     rel_close(G, expect, 0, 1e-12 * (1 + nu.max()))
 
 
+# --------------------------------------------------------------------------- grad_y, grad_b
+def pin_grad_yb_autograd(lib=None):
+    """grad_y and grad_b equal torch float64 autograd of sum(g * a) in y and in b; a
+    scrambled subset of the points gives the same values for those points."""
+    rng = np.random.default_rng(51)
+    for (M, N, D, E) in SHAPES:
+        sigma = np.float32(0.9 * math.sqrt(D))
+        x = rng.standard_normal((M, D)).astype(np.float32)
+        y = rng.standard_normal((N, D)).astype(np.float32)
+        b = rng.standard_normal((N, E)).astype(np.float32)
+        g = rng.standard_normal((M, E)).astype(np.float32)
+        Gy, nuy = oracle.gauss_grad_y(x, y, b, g, sigma, lib=lib)
+        Gb, nub = oracle.gauss_grad_b(x, y, g, sigma, lib=lib)
+        xt = torch.tensor(x, dtype=torch.float64)
+        yt = torch.tensor(y, dtype=torch.float64, requires_grad=True)
+        bt = torch.tensor(b, dtype=torch.float64, requires_grad=True)
+        d2 = ((xt[:, None, :] - yt[None, :, :]) ** 2).sum(-1)
+        a = torch.exp(-d2 / float(sigma) ** 2) @ bt
+        ref_y, ref_b = torch.autograd.grad((a * torch.tensor(g, dtype=torch.float64)).sum(), [yt, bt])
+        rel_close(Gy, ref_y.numpy(), 0, 1e-12 * (1 + nuy.max()))
+        rel_close(Gb, ref_b.numpy(), 0, 1e-12 * (1 + nub.max()))
+        assert np.all(np.abs(Gy) <= nuy * (1 + 1e-12)) and np.all(np.abs(Gb) <= nub * (1 + 1e-12))
+        cols = rng.permutation(N)[: max(1, N // 2)]
+        assert np.array_equal(oracle.gauss_grad_y(x, y, b, g, sigma, cols=cols, lib=lib)[0], Gy[cols])
+        assert np.array_equal(oracle.gauss_grad_b(x, y, g, sigma, cols=cols, lib=lib)[0], Gb[cols])
+
+
+def pin_grad_y_finite_differences(lib=None):
+    """Central differences of L(y) = sum_ie g_ie a_ie(y), all in double, match grad_y."""
+    rng = np.random.default_rng(52)
+    M, N, D, E = 30, 4, 3, 2
+    x = rng.standard_normal((M, D)).astype(np.float32)
+    y = dyadic(rng, (N, D), lo=-1, hi=1, step=1 / 16)
+    b = rng.standard_normal((N, E)).astype(np.float32)
+    g = rng.standard_normal((M, E)).astype(np.float32)
+    sigma = 1.25
+    Gy, nu = oracle.gauss_grad_y(x, y, b, g, sigma, lib=lib)
+    h = np.float32(2.0 ** -10)            # y +- h stays exact in fp32
+    for j in range(N):
+        for d in range(D):
+            yp, ym = y.copy(), y.copy()
+            yp[j, d] += h
+            ym[j, d] -= h
+            ap, _ = oracle.gauss_sum(x, yp, b, sigma, lib=lib)
+            am, _ = oracle.gauss_sum(x, ym, b, sigma, lib=lib)
+            fd = ((ap - am) * g.astype(np.float64)).sum() / (2 * float(h))
+            assert abs(fd - Gy[j, d]) <= 1e-5 * nu[j, d] + 1e-12, (j, d, fd, Gy[j, d], nu[j, d])
+
+
+def pin_grad_b_linear(lib=None):
+    """L = sum g * a is linear in b: a central difference with step 1 is exact up to rounding."""
+    rng = np.random.default_rng(53)
+    M, N, D, E = 20, 6, 3, 3
+    x = rng.standard_normal((M, D)).astype(np.float32)
+    y = rng.standard_normal((N, D)).astype(np.float32)
+    b = dyadic(rng, (N, E), step=1 / 16)
+    g = rng.standard_normal((M, E)).astype(np.float32)
+    sigma = 1.1
+    Gb, nu = oracle.gauss_grad_b(x, y, g, sigma, lib=lib)
+    for j in range(N):
+        for e in range(E):
+            bp, bm = b.copy(), b.copy()
+            bp[j, e] += 1
+            bm[j, e] -= 1
+            ap, _ = oracle.gauss_sum(x, y, bp, sigma, lib=lib)
+            am, _ = oracle.gauss_sum(x, y, bm, sigma, lib=lib)
+            fd = ((ap - am) * g.astype(np.float64)).sum() / 2
+            assert abs(fd - Gb[j, e]) <= 1e-12 * (1 + nu[j, e]), (j, e, fd, Gb[j, e])
+
+
+def pin_grad_pairing_and_balance(lib=None):
+    """<Gb, b> = <g, a> (a is linear in b), and sum_i Gx_i + sum_j Gy_j = 0 (the kernel
+    depends on x - y only, so moving every point together leaves L unchanged)."""
+    rng = np.random.default_rng(54)
+    for (M, N, D, E) in [(13, 21, 3, 1), (8, 30, 5, 2), (25, 7, 2, 3)]:
+        sigma = 1.3
+        x = rng.standard_normal((M, D)).astype(np.float32)
+        y = rng.standard_normal((N, D)).astype(np.float32)
+        b = rng.standard_normal((N, E)).astype(np.float32)
+        g = rng.standard_normal((M, E)).astype(np.float32)
+        a, n = oracle.gauss_sum(x, y, b, sigma, lib=lib)
+        Gb, nub = oracle.gauss_grad_b(x, y, g, sigma, lib=lib)
+        lhs = (Gb * b.astype(np.float64)).sum()
+        rhs = (g.astype(np.float64) * a).sum()
+        scale = (nub * np.abs(b)).sum() + (np.abs(g) * n).sum()
+        assert abs(lhs - rhs) <= 1e-12 * scale, (lhs, rhs)
+        Gx, nux = oracle.gauss_grad_x(x, y, b, g, sigma, lib=lib)
+        Gy, nuy = oracle.gauss_grad_y(x, y, b, g, sigma, lib=lib)
+        tot = Gx.sum(0) + Gy.sum(0)
+        assert np.all(np.abs(tot) <= 1e-12 * (nux.sum(0) + nuy.sum(0))), tot
+
+
 # --------------------------------------------------------------------------- kmin
 def pin_kmin_argsort(lib=None):
     """K-min equals a stable argsort of the materialised distances (ties -> smaller j)."""

@@ -27,6 +27,10 @@ def test_oracle_matches_golden(name):
     np.testing.assert_allclose(oracle.gauss_lse(x, y, b, c["sigma"]), c["lse"], rtol=1e-14)
     G, nu = oracle.gauss_grad_x(x, y, b, g, c["sigma"])
     np.testing.assert_allclose(G, c["grad_x"], rtol=1e-13, atol=1e-14 * max(1.0, np.max(nu)))
+    Gy, nuy = oracle.gauss_grad_y(x, y, b, g, c["sigma"])
+    np.testing.assert_allclose(Gy, c["grad_y"], rtol=1e-13, atol=1e-14 * max(1.0, np.max(nuy)))
+    Gb, nub = oracle.gauss_grad_b(x, y, g, c["sigma"])
+    np.testing.assert_allclose(Gb, c["grad_b"], rtol=1e-13, atol=1e-14 * max(1.0, np.max(nub)))
     kd, ki = oracle.kmin(x, y, c["K"])
     assert ki.tolist() == c["kmin_idx"]
     np.testing.assert_allclose(kd, c["kmin_d"], rtol=1e-15)

@@ -38,6 +38,19 @@ MUTANTS = {
                      "gb += (double)g[e] * (double)b[j * E + e];"),
     "grad_transposed_gb": ("gb += (double)g[i * E + e] * (double)b[j * E + e];",
                            "gb += (double)g[i * E + (E - 1 - e)] * (double)b[j * E + e];"),
+    "grad_y_sign": ("const double t = 2.0 * inv_s2 * k * gb", "const double t = -2.0 * inv_s2 * k * gb"),
+    "grad_y_factor": ("const double t = 2.0 * inv_s2 * k * gb", "const double t = 1.0 * inv_s2 * k * gb"),
+    "grad_y_b_column": ("gb += (double)g[i * E + e] * (double)b[j * E + e];\n            for (int d = 0; d < D; ++d) {\n"
+                        "                const double t = 2.0",
+                        "gb += (double)g[i * E + e] * (double)b[j * E];\n            for (int d = 0; d < D; ++d) {\n"
+                        "                const double t = 2.0"),
+    "grad_y_ignores_cols": ("const int64_t j = cols ? cols[c] : c;\n        double *o = out + c * D,",
+                            "const int64_t j = c;\n        double *o = out + c * D,"),
+    "grad_b_g_column": ("const double t = k * (double)g[i * E + e];", "const double t = k * (double)g[i * E];"),
+    "grad_b_kernel_sign": ("const double k = exp(-sq_dist(x + i * D, y + j * D, D) * inv_s2);\n            for (int e = 0; e < E; ++e) {\n"
+                           "                const double t = k * (double)g",
+                           "const double k = exp(sq_dist(x + i * D, y + j * D, D) * inv_s2 - 1.0);\n            for (int e = 0; e < E; ++e) {\n"
+                           "                const double t = k * (double)g"),
     "kmin_tie_break": ("(dj == bd[pos - 1] && j < bj[pos - 1])", "(dj == bd[pos - 1] && j > bj[pos - 1])"),
     "kmin_keep_last": ("if (count == K && !(dj < bd[K - 1]", "if (count == K && !(dj <= bd[K - 1]"),
 }
