@@ -45,6 +45,8 @@ BENCHES = {
     "sum": ("sum", "sum_lse_1M"),
     "lse": ("lse", "sum_lse_1M"),
     "grad": ("grad_x", "sum_grad_10k"),
+    "grad_y": ("grad_y", "sum_lse_1M"),
+    "grad_b": ("grad_b", "sum_lse_1M"),
     "sum10k": ("sum", "sum_grad_10k"),
     "sum1k": ("sum", "sum_1k"),
     "solver": ("sum", "solver_matvec_100k_x_10M"),
@@ -57,7 +59,8 @@ STREAM_MAX_ROWS = 64              # the library's few-rows layout (j per lane) f
 
 
 def flops_per_pair(op, D, E):
-    return {"sum": 3 * D + 1 + 2 * E, "lse": 3 * D + 5, "grad_x": 5 * D + 2 * E + 1, "kmin": 3 * D}[op]
+    return {"sum": 3 * D + 1 + 2 * E, "lse": 3 * D + 5, "grad_x": 5 * D + 2 * E + 1, "grad_y": 5 * D + 2 * E + 1,
+            "grad_b": 3 * D + 1 + 2 * E, "kmin": 3 * D}[op]
 
 
 def uses_mfma(op, D):
@@ -79,7 +82,9 @@ def roofline_of(op, M, D, E):
         return "hbm", None, "gauss_stream_kernel"
     if uses_mfma(op, D):
         return "mfma", 2 * D, ("gauss_mfma_sum_kernel" if op == "sum" else "kmin_mfma_kernel")
-    name = "kmin_valu_kernel" if op == "kmin" else f"gauss_valu_kernel<{op}>"
+    # the transposed gradients run the row kernels with y as the rows
+    kop = {"grad_y": "grad_x", "grad_b": "sum"}.get(op, op)
+    name = "kmin_valu_kernel" if op == "kmin" else f"gauss_valu_kernel<{kop}>"
     return "alu", flops_per_pair(op, D, E), name
 
 
@@ -127,6 +132,10 @@ def run_op(gm, op, X, Y, B, G, sigma, K, out):
         return gm.keops_gauss_lse(X, Y, B, sigma, out=out)
     if op == "grad_x":
         return gm.keops_gauss_grad_x(X, Y, B, G, sigma, out=out)
+    if op == "grad_y":
+        return gm.keops_gauss_grad_y(X, Y, B, G, sigma, out=out)
+    if op == "grad_b":
+        return gm.keops_gauss_grad_b(X, Y, G, sigma, out=out)
     return gm.keops_kmin(X, Y, K, out_d=out[0], out_idx=out[1])
 
 
@@ -144,23 +153,30 @@ def cpu_baseline(op, w, x, y, b, g, target_s, gpu_out):
             res = oracle.gauss_lse(x, y, b, w.sigma, rows=rows)
         elif op == "grad_x":
             res = oracle.gauss_grad_x(x, y, b, g, w.sigma, rows=rows)
+        elif op == "grad_y":
+            res = oracle.gauss_grad_y(x, y, b, g, w.sigma, cols=rows)
+        elif op == "grad_b":
+            res = oracle.gauss_grad_b(x, y, g, w.sigma, cols=rows)
         else:
             res = oracle.kmin(x, y, w.K, rows=rows)
         return time.perf_counter() - t0, res
 
-    probe = workloads.sample_rows(w.M, min(w.M, 64), seed=2)
+    # outputs per row i, or per point j for the transposed gradients
+    n_out, n_red = (w.N, w.M) if op in ("grad_y", "grad_b") else (w.M, w.N)
+    probe = workloads.sample_rows(n_out, min(n_out, 64), seed=2)
     t_probe, _ = call(probe)
     per_row = max(t_probe / len(probe), 1e-9)
-    n = int(min(w.M, max(64, target_s / per_row)))
-    rows = workloads.sample_rows(w.M, n, seed=1)
+    n = int(min(n_out, max(64, target_s / per_row)))
+    rows = workloads.sample_rows(n_out, n, seed=1)
     t, res = call(rows)
-    pairs = len(rows) * w.N
+    pairs = len(rows) * n_red
     base = {"value": pairs / t / 1e9, "unit": "G pair-evals/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"{len(rows)} seeded rows x all {w.N} j (float64 C/OpenMP oracle), {t:.1f} s"}
+            "sample": (f"{len(rows)} seeded points j x all {w.M} i" if op in ("grad_y", "grad_b") else
+                       f"{len(rows)} seeded rows x all {w.N} j") + f" (float64 C/OpenMP oracle), {t:.1f} s"}
     # the same rows double as a spot check of the GPU result
     check = None
-    if op in ("sum", "grad_x"):
+    if op in ("sum", "grad_x", "grad_y", "grad_b"):
         ref, nrm = res
         gpu = gpu_out[rows].reshape(ref.shape).astype(np.float64)
         check = {"rows": len(rows), "max_err_over_norm": float(np.max(np.abs(gpu - ref) / np.maximum(nrm, 1e-300)))}
@@ -216,11 +232,13 @@ def main():
     B = torch.from_numpy(b).to(dev) if b is not None else None
     g = None
     G = None
-    if op == "grad_x":
+    if op in ("grad_x", "grad_y", "grad_b"):
         g = np.random.default_rng(3).standard_normal((w.M, w.E)).astype(np.float32)
         G = torch.from_numpy(g).to(dev)
     if op == "kmin":
         out = (torch.empty((w.M, w.K), device=dev), torch.empty((w.M, w.K), device=dev, dtype=torch.int64))
+    elif op in ("grad_y", "grad_b"):
+        out = torch.empty((w.N, w.D if op == "grad_y" else w.E), device=dev)
     else:
         out = torch.empty((w.M, w.D if op == "grad_x" else w.E), device=dev)
 
@@ -247,7 +265,7 @@ def main():
     value = pairs / (ms_step * 1e-3) / 1e9
     bound, fpp, kname = roofline_of(op, w.M, w.D, w.E)
     kern_avg_ms = kern_ms / max(launches, 1)
-    src_key = "stream" if bound == "hbm" else op
+    src_key = "stream" if bound == "hbm" else {"grad_y": "grad_x", "grad_b": "sum"}.get(op, op)
     traffic = recorded_traffic(args.workload, src_key)
     if bound == "hbm":
         achieved = stream_bytes(w) / (kern_avg_ms * 1e-3) / 1e9

@@ -1,6 +1,6 @@
 """MI355X (gfx950) engine for KeOps-style Gaussian map-reductions.
 
-Four reductions over the symbolic matrix K_ij = exp(-|x_i - y_j|^2 / sigma^2),
+Reductions over the symbolic matrix K_ij = exp(-|x_i - y_j|^2 / sigma^2),
 never stored, run as hand-written gfx950 HIP kernels behind the C ABI of
 ``include/keops_mi355x.h`` (library ``libkeops_mi355x.so``, built by
 ``geometric_map_reduce_amd.build``):
@@ -8,10 +8,13 @@ never stored, run as hand-written gfx950 HIP kernels behind the C ABI of
 * ``keops_gauss_sum``    -- a_i = sum_j K_ij b_j
 * ``keops_gauss_lse``    -- log sum_j exp(-|x_i - y_j|^2/sigma^2 + b_j)
 * ``keops_gauss_grad_x`` -- gradient of the sum with respect to x
+* ``keops_gauss_grad_y``, ``keops_gauss_grad_b`` -- gradients with respect to y
+  and b (reductions over i, one output per point y_j)
 * ``keops_kmin``         -- K nearest neighbours with indices
 
 PyTorch supplies device memory and streams only.
 """
-from .binding import (KEOPS_OPT_FORM, KEOPS_OPT_PROFILE, KEOPS_OPT_ROWS, KEOPS_OPT_SPLIT_J, KEOPS_OPT_WG_TARGET,  # noqa: F401
-                      KeopsError, keops_gauss_grad_x, keops_gauss_lse, keops_gauss_sum, keops_kmin,
-                      keops_profile_read, keops_set_option, keops_version, lib, status_string)
+from .binding import (KEOPS_OPT_FORM, KEOPS_OPT_PROFILE, KEOPS_OPT_ROWS, KEOPS_OPT_SPLIT_J,  # noqa: F401
+                      KEOPS_OPT_WG_TARGET, KeopsError, keops_gauss_grad_b, keops_gauss_grad_x,
+                      keops_gauss_grad_y, keops_gauss_lse, keops_gauss_sum, keops_kmin, keops_profile_read,
+                      keops_set_option, keops_version, lib, status_string)

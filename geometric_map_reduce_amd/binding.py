@@ -57,12 +57,15 @@ def lib() -> ctypes.CDLL:
             L.keops_gauss_sum.argtypes = [P, P, P, i64, i64, i32, i32, f32, P, P]
             L.keops_gauss_lse.argtypes = [P, P, P, i64, i64, i32, i32, f32, P, P]
             L.keops_gauss_grad_x.argtypes = [P, P, P, P, i64, i64, i32, i32, f32, P, P]
+            L.keops_gauss_grad_y.argtypes = [P, P, P, P, i64, i64, i32, i32, f32, P, P]
+            L.keops_gauss_grad_b.argtypes = [P, P, P, i64, i64, i32, i32, f32, P, P]
             L.keops_kmin.argtypes = [P, P, i64, i64, i32, i32, P, P, P]
             L.keops_set_option.argtypes = [ctypes.c_int, i64]
             L.keops_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
             L.keops_status_string.argtypes = [ctypes.c_int]
             L.keops_status_string.restype = ctypes.c_char_p
-            for f in ("keops_gauss_sum", "keops_gauss_lse", "keops_gauss_grad_x", "keops_kmin",
+            for f in ("keops_gauss_sum", "keops_gauss_lse", "keops_gauss_grad_x", "keops_gauss_grad_y",
+                      "keops_gauss_grad_b", "keops_kmin",
                       "keops_set_option", "keops_version", "keops_profile_read"):
                 getattr(L, f).restype = ctypes.c_int
             _lib = L
@@ -144,6 +147,41 @@ def keops_gauss_lse(x, y, b, sigma, out=None, stream=None):
 def keops_gauss_grad_x(x, y, b, g, sigma, out=None, stream=None):
     """out[i, d] = sum_j (-2/sigma^2) K_ij <g_i, b_j> (x_id - y_jd), the VJP of the sum with cotangent g."""
     return _gauss("keops_gauss_grad_x", x, y, b, sigma, out, stream, g=g)
+
+
+def keops_gauss_grad_y(x, y, b, g, sigma, out=None, stream=None):
+    """out[j, d] = sum_i (2/sigma^2) K_ij <g_i, b_j> (x_id - y_jd): dL/dy for the cotangent g = dL/da."""
+    x = _mat(x, "x")
+    dev = x.device
+    y, b, g = _mat(y, "y", dev), _mat(b, "b", dev), _mat(g, "g", dev)
+    M, D = x.shape
+    N, E = b.shape
+    if y.shape != (N, D) or g.shape != (M, E):
+        raise ValueError(f"need y [N, D] = [{N}, {D}] and g [M, E] = [{M}, {E}]")
+    out = _out(out, (N, D), dev)
+    with torch.cuda.device(dev):
+        rc = lib().keops_gauss_grad_y(_ptr(x), _ptr(y), _ptr(b), _ptr(g), M, N, D, E, float(sigma), _ptr(out),
+                                      _stream(stream, dev))
+    _check("keops_gauss_grad_y", rc)
+    return out
+
+
+def keops_gauss_grad_b(x, y, g, sigma, out=None, stream=None):
+    """out[j, e] = sum_i K_ij g[i, e]: dL/db for the cotangent g = dL/da."""
+    x = _mat(x, "x")
+    dev = x.device
+    y, g = _mat(y, "y", dev), _mat(g, "g", dev)
+    M, D = x.shape
+    N = y.shape[0]
+    E = g.shape[1]
+    if y.shape != (N, D) or g.shape[0] != M:
+        raise ValueError(f"need y [N, {D}] and g [M, E] with M = {M}")
+    out = _out(out, (N, E), dev)
+    with torch.cuda.device(dev):
+        rc = lib().keops_gauss_grad_b(_ptr(x), _ptr(y), _ptr(g), M, N, D, E, float(sigma), _ptr(out),
+                                      _stream(stream, dev))
+    _check("keops_gauss_grad_b", rc)
+    return out
 
 
 def keops_kmin(x, y, K, out_d=None, out_idx=None, stream=None):

@@ -329,6 +329,20 @@ int keops_gauss_grad_x(const float *x, const float *y, const float *b, const flo
   return gauss_entry(OP_GRAD, x, y, b, g, M, N, D, E, sigma, out, stream);
 }
 
+// The transposed reductions run the row-side kernels with the roles exchanged:
+// the points y become the rows, x the columns; for grad_y the payload is g and
+// the cotangent b, and the sign of (x - y) flips with the roles, so
+//   sum_i (-2/s^2) K <b_j, g_i> (y_j - x_i) = sum_i (2/s^2) K <g_i, b_j> (x_i - y_j).
+int keops_gauss_grad_y(const float *x, const float *y, const float *b, const float *g, int64_t M, int64_t N,
+                       int32_t D, int32_t E, float sigma, float *out, void *stream) {
+  return gauss_entry(OP_GRAD, y, x, g, b, N, M, D, E, sigma, out, stream);
+}
+
+int keops_gauss_grad_b(const float *x, const float *y, const float *g, int64_t M, int64_t N, int32_t D,
+                       int32_t E, float sigma, float *out, void *stream) {
+  return gauss_entry(OP_SUM, y, x, g, nullptr, N, M, D, E, sigma, out, stream);
+}
+
 int keops_kmin(const float *x, const float *y, int64_t M, int64_t N, int32_t D, int32_t K, float *out_d,
                int64_t *out_idx, void *stream) {
   if (M < 0 || N < 0 || D < 1 || K < 1) return KEOPS_ERR_INVALID_ARG;

@@ -92,6 +92,25 @@ int keops_gauss_grad_x(const float *x, const float *y, const float *b, const flo
                        float *out, void *stream);
 
 /*
+ * Gradients of L = sum_ie g_ie a_ie with respect to the other two inputs of
+ * the kernel sum ([KO-GPU] §2 "Performance and differentiation": every input
+ * of a reduction is differentiable).  Both are reductions over the rows i,
+ * one output per point y_j (the transposed map-reduce):
+ *   keops_gauss_grad_y:  out[j, d] = sum_i (2/sigma^2) K_ij <g_i, b_j> (x[i,d] - y[j,d])   out: [N, D]
+ *   keops_gauss_grad_b:  out[j, e] = sum_i K_ij g[i, e]                                    out: [N, E]
+ * with K_ij = exp(-|x_i - y_j|^2/sigma^2), x: [M, D], y: [N, D], b: [N, E],
+ * g: [M, E] (dL/da).  Sizes: N = 0 is a no-op; M = 0 writes zeros.  The rest
+ * of the conventions (pointers, ownership, stream, errors) are those above;
+ * out must not overlap any input.
+ */
+int keops_gauss_grad_y(const float *x, const float *y, const float *b, const float *g,
+                       int64_t M, int64_t N, int32_t D, int32_t E, float sigma,
+                       float *out, void *stream);
+int keops_gauss_grad_b(const float *x, const float *y, const float *g,
+                       int64_t M, int64_t N, int32_t D, int32_t E, float sigma,
+                       float *out, void *stream);
+
+/*
  * K-min reduction with indices ([KO-GPU] §2 argmin / argKmin; [README] ArgMin,
  * K-min reductions): for each row i, the K smallest squared distances
  * |x_i - y_j|^2, ascending, and their indices j; equal distances are ordered

@@ -25,9 +25,10 @@ def L():
     return binding.lib()
 
 
-def test_header_declares_the_four_reductions():
+def test_header_declares_the_reductions():
     names = declared_functions()
-    for n in ("keops_gauss_sum", "keops_gauss_lse", "keops_gauss_grad_x", "keops_kmin"):
+    for n in ("keops_gauss_sum", "keops_gauss_lse", "keops_gauss_grad_x", "keops_gauss_grad_y",
+              "keops_gauss_grad_b", "keops_kmin"):
         assert n in names
 
 
@@ -74,6 +75,19 @@ def test_gauss_sum_validation(L, args, rc):
 def test_grad_needs_g(L):
     assert L.keops_gauss_grad_x(FAKE, FAKE2, FAKE2, None, 5, 7, 3, 1, 1.0, ctypes.c_void_p(0x900000), None) == -1
     assert L.keops_gauss_grad_x(None, None, None, None, 0, 0, 3, 1, 1.0, None, None) == 0
+
+
+def test_transposed_gradients_validation(L):
+    out = ctypes.c_void_p(0x900000)
+    # grad_y needs b (the cotangent side of the exchanged roles) and g when M > 0
+    assert L.keops_gauss_grad_y(FAKE, FAKE2, None, FAKE, 5, 7, 3, 1, 1.0, out, None) == -1
+    assert L.keops_gauss_grad_y(FAKE, FAKE2, FAKE2, None, 5, 7, 3, 1, 1.0, out, None) == -1
+    assert L.keops_gauss_grad_b(FAKE, FAKE2, None, 5, 7, 3, 1, 1.0, out, None) == -1
+    assert L.keops_gauss_grad_b(FAKE, FAKE2, FAKE, 5, 7, 3, 1, -1.0, out, None) == -1
+    assert L.keops_gauss_grad_b(FAKE, FAKE2, FAKE, 5, 7, 99, 1, 1.0, out, None) == -2
+    # N = 0: nothing to write
+    assert L.keops_gauss_grad_y(None, None, None, None, 0, 0, 3, 1, 1.0, None, None) == 0
+    assert L.keops_gauss_grad_b(None, None, None, 0, 0, 3, 1, 1.0, None, None) == 0
 
 
 @pytest.mark.parametrize("args,rc", [

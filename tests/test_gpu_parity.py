@@ -140,6 +140,40 @@ def test_far_from_origin_and_spread():
         _check_all(x, y, b, g, sigma, _run_all(x, y, b, g, sigma))
 
 
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "M%d_N%d_D%d_E%d_s%g" % c)
+def test_small_transposed_grads(case):
+    """grad_y and grad_b (reductions over i, one output per point y_j) on every small shape."""
+    M, N, D, E, sigma = case
+    say(f"transposed grads M={M} N={N} D={D} E={E} sigma={sigma}")
+    x, y, b, g = rand_case(2000 + M + N + D, M, N, D, E)
+    sigma = float(np.float32(sigma))
+    X, Y, B, G = dev(x), dev(y), dev(b), dev(g)
+    gy = gm.keops_gauss_grad_y(X, Y, B, G, sigma)
+    gb = gm.keops_gauss_grad_b(X, Y, G, sigma)
+    torch.cuda.synchronize()
+    Gy_ref, nuy = oracle.gauss_grad_y(x, y, b, g, sigma)
+    check_grad(host(gy), Gy_ref, nuy)
+    Gb_ref, nub = oracle.gauss_grad_b(x, y, g, sigma)
+    check_sum(host(gb), Gb_ref, nub, what="grad_b")
+
+
+def test_transposed_grads_degenerate_and_balance():
+    say("transposed grads: M = 0, N = 0, translation balance")
+    x, y, b, g = rand_case(77, 0, 50, 3, 2)
+    gy = gm.keops_gauss_grad_y(dev(np.zeros((0, 3), np.float32)), dev(y), dev(b), dev(np.zeros((0, 2), np.float32)), 1.0)
+    gb = gm.keops_gauss_grad_b(dev(np.zeros((0, 3), np.float32)), dev(y), dev(np.zeros((0, 2), np.float32)), 1.0)
+    torch.cuda.synchronize()
+    assert not host(gy).any() and not host(gb).any() and gy.shape == (50, 3) and gb.shape == (50, 2)
+    x, y, b, g = rand_case(78, 300, 500, 3, 1)
+    X, Y, B, G = dev(x), dev(y), dev(b), dev(g)
+    gx = host(gm.keops_gauss_grad_x(X, Y, B, G, 0.8)).astype(np.float64)
+    gy = host(gm.keops_gauss_grad_y(X, Y, B, G, 0.8)).astype(np.float64)
+    _, nux = oracle.gauss_grad_x(x, y, b, g, 0.8)
+    _, nuy = oracle.gauss_grad_y(x, y, b, g, 0.8)
+    # moving every point together leaves L unchanged: the two gradients balance
+    assert np.all(np.abs(gx.sum(0) + gy.sum(0)) <= 1e-4 * (nux.sum(0) + nuy.sum(0)))
+
+
 KMIN_SMALL = [(1, 1, 1, 1), (5, 40, 3, 10), (300, 1000, 3, 10), (257, 513, 2, 16), (100, 3000, 4, 32),
               (70, 600, 8, 7), (64, 300, 16, 5), (40, 500, 32, 10), (30, 200, 50, 3), (25, 300, 64, 10),
               (10, 128, 100, 2), (200, 900, 5, 1), (129, 129, 3, 12)]
@@ -295,6 +329,22 @@ def test_workload_stream_16_x_100M():
     a_ref, n_ref = oracle.gauss_sum(x, y, b, w.sigma)
     err = check_sum(host(a), a_ref, n_ref)
     say(f"  max err / norm {err:.3g}")
+
+
+def test_workload_transposed_grads_1M():
+    """grad_y and grad_b at M = N = 1e6 (D = 3, sigma = 0.1), sampled points against the oracle."""
+    w = workloads.WORKLOADS["sum_lse_1M"]
+    say("workload sum_lse_1M: grad_y, grad_b")
+    x, y, b = workloads.make_inputs(w)
+    g = np.random.default_rng(3).standard_normal((w.M, w.E)).astype(np.float32)
+    X, Y, B, G = dev(x), dev(y), dev(b), dev(g)
+    gy = host(gm.keops_gauss_grad_y(X, Y, B, G, w.sigma))
+    gb = host(gm.keops_gauss_grad_b(X, Y, G, w.sigma))
+    cols = _sample(w.N, 192)
+    Gy_ref, nuy = oracle.gauss_grad_y(x, y, b, g, w.sigma, cols=cols)
+    Gb_ref, nub = oracle.gauss_grad_b(x, y, g, w.sigma, cols=cols)
+    say(f"  grad_y max err/nu {check_grad(gy[cols], Gy_ref, nuy):.3g}; "
+        f"grad_b {check_sum(gb[cols], Gb_ref, nub, what='grad_b'):.3g}")
 
 
 @pytest.mark.parametrize("name", ["kmin10_1M_d3", "kmin10_1M_d64"])
