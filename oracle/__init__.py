@@ -64,6 +64,7 @@ def open_library(path: str):
     lib.oracle_gauss_grad_b.argtypes = [P, P, P, i64, i64, i32, i32, f64, P, i64, P, P]
     lib.oracle_kmin.argtypes = [P, P, i64, i64, i32, i32, P, i64, P, P]
     lib.oracle_sq_dist_pairs.argtypes = [P, P, i32, P, P, i64, P]
+    lib.oracle_gauss_matrix.argtypes = [P, P, i64, i64, i32, f64, P]
     for f in ("oracle_gauss_sum", "oracle_gauss_lse", "oracle_gauss_grad_x", "oracle_gauss_grad_y",
               "oracle_gauss_grad_b", "oracle_kmin", "oracle_sq_dist_pairs", "oracle_num_threads"):
         getattr(lib, f).restype = ctypes.c_int
@@ -217,3 +218,40 @@ def sq_dist_pairs(x, y, ii, jj, lib=None):
     _check((lib or _load()).oracle_sq_dist_pairs(_ptr(x), _ptr(y), x.shape[1], _ptr(ii), _ptr(jj),
                                         ii.shape[0], _ptr(out)), "sq_dist_pairs")
     return out
+
+
+def gauss_matrix(x, y, sigma, lib=None):
+    """K[i, j] = exp(-|x_i - y_j|^2 / sigma^2) materialised in float64 (small inputs only)."""
+    x, y = _f32(x, 2), _f32(y, 2)
+    M, D = x.shape
+    N = y.shape[0]
+    assert y.shape == (N, D)
+    out = np.empty((M, N), np.float64)
+    _check((lib or _load()).oracle_gauss_matrix(_ptr(x), _ptr(y), M, N, D, float(sigma), _ptr(out)),
+           "gauss_matrix")
+    return out
+
+
+def gauss_solve(x, b, sigma, lam, lib=None):
+    """The exact solution a* of (K + lam I) a = b, K = exp(-|x_i - x_j|^2/sigma^2), by a dense
+    float64 solve (what the conjugate gradient solver approximates; [README] feature list:
+    conjugate gradient solver for spline interpolation or kriging).  Small N only."""
+    b = np.asarray(b, np.float64)
+    if b.ndim == 1:
+        b = b.reshape(-1, 1)
+    K = gauss_matrix(x, x, sigma, lib=lib)
+    A = K + float(lam) * np.eye(K.shape[0])
+    return np.linalg.solve(A, b)
+
+
+def gauss_system_residual(x, b, a, sigma, lam, rows=None, lib=None):
+    """r = b - (K + lam I) a in float64 for the selected rows (all by default), with the
+    products K a taken by the sum oracle over all points: for checking an approximate
+    solution a (float32, e.g. from the GPU solver) at any size."""
+    x, b, a = _f32(x, 2), np.asarray(b, np.float64), _f32(a, 2)
+    if b.ndim == 1:
+        b = b.reshape(-1, 1)
+    Ka, _ = gauss_sum(x[rows] if rows is not None else x, x, a, sigma, lib=lib)
+    sel = rows if rows is not None else slice(None)
+    return b[sel] - Ka - float(lam) * a[sel].astype(np.float64)
+

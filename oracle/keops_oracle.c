@@ -280,3 +280,19 @@ int oracle_sq_dist_pairs(const float *x, const float *y, int D,
     for (int64_t p = 0; p < npairs; ++p) out[p] = sq_dist(x + ii[p] * D, y + jj[p] * D, D);
     return 0;
 }
+
+/*
+ * The Gaussian kernel matrix itself, K[i*N + j] = exp(-|x_i - y_j|^2/sigma^2)
+ * in double, for the dense linear solve that stands for the conjugate
+ * gradient solver ([README] feature list: a conjugate gradient solver for
+ * spline interpolation or kriging) on small inputs.
+ */
+int oracle_gauss_matrix(const float *x, const float *y, int64_t M, int64_t N, int D, double sigma,
+                        double *out) {
+    if (M < 0 || N < 0 || D < 1 || !(sigma > 0.0)) return -1;
+    const double inv_s2 = 1.0 / (sigma * sigma);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < N; ++j) out[i * N + j] = exp(-sq_dist(x + i * D, y + j * D, D) * inv_s2);
+    return 0;
+}

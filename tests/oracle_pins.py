@@ -384,6 +384,56 @@ def pin_grad_pairing_and_balance(lib=None):
         assert np.all(np.abs(tot) <= 1e-12 * (nux.sum(0) + nuy.sum(0))), tot
 
 
+# --------------------------------------------------------------------------- kernel matrix, dense solve
+def pin_matrix_brute_and_sum(lib=None):
+    """The materialised kernel matrix equals numpy's, and K @ b equals the sum oracle."""
+    rng = np.random.default_rng(61)
+    for (M, N, D, E) in SHAPES[:6]:
+        sigma = 0.8 * math.sqrt(D)
+        x = rng.standard_normal((M, D)).astype(np.float32)
+        y = rng.standard_normal((N, D)).astype(np.float32)
+        b = rng.standard_normal((N, E)).astype(np.float32)
+        K = oracle.gauss_matrix(x, y, sigma, lib=lib)
+        rel_close(K, brute_K(x, y, sigma), 1e-14)
+        a, n = oracle.gauss_sum(x, y, b, sigma, lib=lib)
+        rel_close(K @ b.astype(np.float64), a, 0, 1e-12 * (1 + n.max()))
+
+
+def pin_solve_closed_forms(lib=None):
+    """(K + lam I) a = b: K = I for far-apart points gives b / (1 + lam); two points at
+    squared distance d give the 2 x 2 inverse with k = exp(-d / sigma^2)."""
+    rng = np.random.default_rng(62)
+    x = (np.arange(12, dtype=np.float32)[:, None] * np.float32(100.0)).repeat(2, 1)
+    b = rng.standard_normal((12, 2)).astype(np.float32)
+    a = oracle.gauss_solve(x, b, 1.0, 0.25, lib=lib)
+    rel_close(a, b.astype(np.float64) / 1.25, 1e-14)
+    x2 = np.array([[0.0, 0.0], [0.75, 0.5]], np.float32)
+    b2 = np.array([[1.0], [-2.0]], np.float32)
+    sigma, lam = 0.9, 0.3
+    k = math.exp(-(0.75 ** 2 + 0.5 ** 2) / sigma ** 2)
+    det = (1 + lam) ** 2 - k ** 2
+    expect = np.array([[((1 + lam) * 1.0 - k * -2.0) / det], [((1 + lam) * -2.0 - k * 1.0) / det]])
+    rel_close(oracle.gauss_solve(x2, b2, sigma, lam, lib=lib), expect, 1e-13)
+
+
+def pin_solve_residual(lib=None):
+    """The dense solution leaves a residual at rounding level when the system is applied
+    through the sum oracle (an independent route to K a)."""
+    rng = np.random.default_rng(63)
+    for (N, D, E, sigma, lam) in [(60, 3, 1, 0.5, 0.1), (40, 5, 2, 1.5, 1.0), (25, 2, 3, 0.3, 0.01)]:
+        x = rng.standard_normal((N, D)).astype(np.float32)
+        b = rng.standard_normal((N, E)).astype(np.float32)
+        a = oracle.gauss_solve(x, b, sigma, lam, lib=lib)
+        K = oracle.gauss_matrix(x, x, sigma, lib=lib)
+        assert np.allclose(K, K.T, rtol=0, atol=0) and np.linalg.eigvalsh(K).min() > -1e-12
+        Ka = np.stack([oracle.gauss_sum(x, x, a[:, e:e + 1].astype(np.float32), sigma, lib=lib)[0][:, 0]
+                       for e in range(E)], 1)
+        # a rounded to fp32 for the sum oracle: the residual is that rounding times (K + lam I)
+        r = b - Ka - lam * a.astype(np.float32).astype(np.float64)
+        bound = 2.0 ** -23 * (np.abs(K).sum(1, keepdims=True) + lam) * np.abs(a).max(0, keepdims=True)
+        assert np.all(np.abs(r) <= bound + 1e-12), np.abs(r).max()
+
+
 # --------------------------------------------------------------------------- kmin
 def pin_kmin_argsort(lib=None):
     """K-min equals a stable argsort of the materialised distances (ties -> smaller j)."""

@@ -51,6 +51,11 @@ MUTANTS = {
                            "                const double t = k * (double)g",
                            "const double k = exp(sq_dist(x + i * D, y + j * D, D) * inv_s2 - 1.0);\n            for (int e = 0; e < E; ++e) {\n"
                            "                const double t = k * (double)g"),
+    "matrix_sigma_not_squared": ("const double inv_s2 = 1.0 / (sigma * sigma);\n#pragma omp parallel for schedule(dynamic, 1)\n"
+                                 "    for (int64_t i = 0; i < M; ++i)",
+                                 "const double inv_s2 = 1.0 / (2.0 * sigma * sigma);\n#pragma omp parallel for schedule(dynamic, 1)\n"
+                                 "    for (int64_t i = 0; i < M; ++i)"),
+    "matrix_row_stride": ("out[i * N + j] = exp(", "out[j * M + i] = exp("),
     "kmin_tie_break": ("(dj == bd[pos - 1] && j < bj[pos - 1])", "(dj == bd[pos - 1] && j > bj[pos - 1])"),
     "kmin_keep_last": ("if (count == K && !(dj < bd[K - 1]", "if (count == K && !(dj <= bd[K - 1]"),
 }
