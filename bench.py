@@ -53,13 +53,15 @@ BENCHES = {
     "kmin3": ("kmin", "kmin10_1M_d3"),
     "kmin64": ("kmin", "kmin10_1M_d64"),
     "stream": ("sum", "stream_16_x_100M"),
+    "cg": ("cg", "krige_100k"),
 }
+CG_RTOL = 1e-4
 PEAK_HBM_GBS = 8000.0             # MI355X HBM3E peak
 STREAM_MAX_ROWS = 64              # the library's few-rows layout (j per lane) for the sum
 
 
 def flops_per_pair(op, D, E):
-    return {"sum": 3 * D + 1 + 2 * E, "lse": 3 * D + 5, "grad_x": 5 * D + 2 * E + 1, "grad_y": 5 * D + 2 * E + 1,
+    return {"sum": 3 * D + 1 + 2 * E, "cg": 3 * D + 1 + 2 * E, "lse": 3 * D + 5, "grad_x": 5 * D + 2 * E + 1, "grad_y": 5 * D + 2 * E + 1,
             "grad_b": 3 * D + 1 + 2 * E, "kmin": 3 * D}[op]
 
 
@@ -83,7 +85,7 @@ def roofline_of(op, M, D, E):
     if uses_mfma(op, D):
         return "mfma", 2 * D, ("gauss_mfma_sum_kernel" if op == "sum" else "kmin_mfma_kernel")
     # the transposed gradients run the row kernels with y as the rows
-    kop = {"grad_y": "grad_x", "grad_b": "sum"}.get(op, op)
+    kop = {"grad_y": "grad_x", "grad_b": "sum", "cg": "sum"}.get(op, op)
     name = "kmin_valu_kernel" if op == "kmin" else f"gauss_valu_kernel<{kop}>"
     return "alu", flops_per_pair(op, D, E), name
 
@@ -125,7 +127,9 @@ def recorded_traffic(bench_name, op):
     return rec.get("hbm_bytes_per_launch")
 
 
-def run_op(gm, op, X, Y, B, G, sigma, K, out):
+def run_op(gm, op, X, Y, B, G, sigma, K, out, lam=0.0):
+    if op == "cg":
+        return gm.keops_gauss_cg(X, B, sigma, lam, rtol=CG_RTOL, max_iter=1000, out=out)
     if op == "sum":
         return gm.keops_gauss_sum(X, Y, B, sigma, out=out)
     if op == "lse":
@@ -149,6 +153,8 @@ def cpu_baseline(op, w, x, y, b, g, target_s, gpu_out):
         t0 = time.perf_counter()
         if op == "sum":
             res = oracle.gauss_sum(x, y, b, w.sigma, rows=rows)
+        elif op == "cg":        # the solver's work is its products K p: the sum oracle on x
+            res = oracle.gauss_sum(x, x, b, w.sigma, rows=rows)
         elif op == "lse":
             res = oracle.gauss_lse(x, y, b, w.sigma, rows=rows)
         elif op == "grad_x":
@@ -176,7 +182,9 @@ def cpu_baseline(op, w, x, y, b, g, target_s, gpu_out):
                        f"{len(rows)} seeded rows x all {w.N} j") + f" (float64 C/OpenMP oracle), {t:.1f} s"}
     # the same rows double as a spot check of the GPU result
     check = None
-    if op in ("sum", "grad_x", "grad_y", "grad_b"):
+    if op == "cg":
+        check = None
+    elif op in ("sum", "grad_x", "grad_y", "grad_b"):
         ref, nrm = res
         gpu = gpu_out[rows].reshape(ref.shape).astype(np.float64)
         check = {"rows": len(rows), "max_err_over_norm": float(np.max(np.abs(gpu - ref) / np.maximum(nrm, 1e-300)))}
@@ -237,13 +245,15 @@ def main():
         G = torch.from_numpy(g).to(dev)
     if op == "kmin":
         out = (torch.empty((w.M, w.K), device=dev), torch.empty((w.M, w.K), device=dev, dtype=torch.int64))
+    elif op == "cg":
+        out = torch.empty((w.N, w.E), device=dev)
     elif op in ("grad_y", "grad_b"):
         out = torch.empty((w.N, w.D if op == "grad_y" else w.E), device=dev)
     else:
         out = torch.empty((w.M, w.D if op == "grad_x" else w.E), device=dev)
 
     for _ in range(args.warmup):
-        run_op(gm, op, X, Y, B, G, w.sigma, w.K, out)
+        run_op(gm, op, X, Y, B, G, w.sigma, w.K, out, w.lam)
     torch.cuda.synchronize()
 
     gm.keops_set_option(gm.KEOPS_OPT_PROFILE, 1)
@@ -252,8 +262,9 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record()
+    solves = []
     for _ in range(args.steps):
-        run_op(gm, op, X, Y, B, G, w.sigma, w.K, out)
+        solves.append(run_op(gm, op, X, Y, B, G, w.sigma, w.K, out, w.lam))
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -262,6 +273,14 @@ def main():
     ms_step = ev0.elapsed_time(ev1) / args.steps
 
     pairs = w.M * w.N
+    cg_info = None
+    if op == "cg":
+        # one step = one whole solve; its pair-evaluations are those of its products K p
+        # (iterations + 1 for the final residual), every one N x N
+        iters = solves[-1][1]
+        cg_info = {"iterations": iters, "rel_residual": float(solves[-1][2].max()), "rtol": CG_RTOL,
+                   "products_per_solve": iters + 1}
+        pairs = (iters + 1) * w.N * w.N
     value = pairs / (ms_step * 1e-3) / 1e9
     bound, fpp, kname = roofline_of(op, w.M, w.D, w.E)
     kern_avg_ms = kern_ms / max(launches, 1)
@@ -273,7 +292,8 @@ def main():
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic}
         kinfo = {"bytes_per_launch": stream_bytes(w)}
     else:
-        achieved = fpp * pairs / (kern_avg_ms * 1e-3) / 1e12
+        per_launch = w.N * w.N if op == "cg" else pairs
+        achieved = fpp * per_launch / (kern_avg_ms * 1e-3) / 1e12
         roof = {"bound": bound, "achieved": round(achieved, 3), "peak": PEAK_FP32_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_TFLOPS, 4), "traffic": traffic}
         kinfo = {"flops_per_pair": fpp}
@@ -296,6 +316,8 @@ def main():
         "kernel": dict({"name": kname, "avg_ms": round(kern_avg_ms, 4), "launches": launches}, **kinfo),
         "wall_s_timed": round(wall, 3),
     }
+    if cg_info is not None:
+        res["solver"] = cg_info
     if not args.no_cpu_baseline:
         gpu_out = (out[0] if op == "kmin" else out).cpu().numpy()
         base, check = cpu_baseline(op, w, x, y, b, g, args.cpu_seconds, gpu_out)

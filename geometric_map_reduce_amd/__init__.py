@@ -10,11 +10,12 @@ never stored, run as hand-written gfx950 HIP kernels behind the C ABI of
 * ``keops_gauss_grad_x`` -- gradient of the sum with respect to x
 * ``keops_gauss_grad_y``, ``keops_gauss_grad_b`` -- gradients with respect to y
   and b (reductions over i, one output per point y_j)
+* ``keops_gauss_cg``     -- conjugate-gradient solve of (K + lambda I) a = b
 * ``keops_kmin``         -- K nearest neighbours with indices
 
 PyTorch supplies device memory and streams only.
 """
 from .binding import (KEOPS_OPT_FORM, KEOPS_OPT_PROFILE, KEOPS_OPT_ROWS, KEOPS_OPT_SPLIT_J,  # noqa: F401
-                      KEOPS_OPT_WG_TARGET, KeopsError, keops_gauss_grad_b, keops_gauss_grad_x,
+                      KEOPS_OPT_WG_TARGET, KeopsError, keops_gauss_cg, keops_gauss_grad_b, keops_gauss_grad_x,
                       keops_gauss_grad_y, keops_gauss_lse, keops_gauss_sum, keops_kmin, keops_profile_read,
                       keops_set_option, keops_version, lib, status_string)

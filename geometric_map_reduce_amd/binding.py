@@ -59,13 +59,15 @@ def lib() -> ctypes.CDLL:
             L.keops_gauss_grad_x.argtypes = [P, P, P, P, i64, i64, i32, i32, f32, P, P]
             L.keops_gauss_grad_y.argtypes = [P, P, P, P, i64, i64, i32, i32, f32, P, P]
             L.keops_gauss_grad_b.argtypes = [P, P, P, i64, i64, i32, i32, f32, P, P]
+            L.keops_gauss_cg.argtypes = [P, P, i64, i32, i32, f32, f32, f32, i32, P,
+                                         ctypes.POINTER(i32), ctypes.POINTER(f32), P]
             L.keops_kmin.argtypes = [P, P, i64, i64, i32, i32, P, P, P]
             L.keops_set_option.argtypes = [ctypes.c_int, i64]
             L.keops_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
             L.keops_status_string.argtypes = [ctypes.c_int]
             L.keops_status_string.restype = ctypes.c_char_p
             for f in ("keops_gauss_sum", "keops_gauss_lse", "keops_gauss_grad_x", "keops_gauss_grad_y",
-                      "keops_gauss_grad_b", "keops_kmin",
+                      "keops_gauss_grad_b", "keops_gauss_cg", "keops_kmin",
                       "keops_set_option", "keops_version", "keops_profile_read"):
                 getattr(L, f).restype = ctypes.c_int
             _lib = L
@@ -182,6 +184,29 @@ def keops_gauss_grad_b(x, y, g, sigma, out=None, stream=None):
                                       _stream(stream, dev))
     _check("keops_gauss_grad_b", rc)
     return out
+
+
+def keops_gauss_cg(x, b, sigma, lam, rtol=1e-5, max_iter=1000, out=None, stream=None):
+    """Solve (K + lam I) a = b, K_ij = exp(-|x_i - x_j|^2 / sigma^2), by conjugate gradients.
+
+    Returns (a [N, E], iterations, relative true residual per column as a numpy array).
+    Synchronises the stream (the residual norms are read on the host every iteration)."""
+    import numpy as np
+    x = _mat(x, "x")
+    dev = x.device
+    b = _mat(b, "b", dev)
+    N, D = x.shape
+    E = b.shape[1]
+    if b.shape[0] != N:
+        raise ValueError(f"b must have N = {N} rows")
+    out = _out(out, (N, E), dev)
+    it = ctypes.c_int32(0)
+    res = (ctypes.c_float * max(E, 1))()
+    with torch.cuda.device(dev):
+        rc = lib().keops_gauss_cg(_ptr(x), _ptr(b), N, D, E, float(sigma), float(lam), float(rtol), int(max_iter),
+                                  _ptr(out), ctypes.byref(it), res, _stream(stream, dev))
+    _check("keops_gauss_cg", rc)
+    return out, int(it.value), np.array(res[:E], np.float32)
 
 
 def keops_kmin(x, y, K, out_d=None, out_idx=None, stream=None):

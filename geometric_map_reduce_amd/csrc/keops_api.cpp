@@ -343,6 +343,96 @@ int keops_gauss_grad_b(const float *x, const float *y, const float *g, int64_t M
   return gauss_entry(OP_SUM, y, x, g, nullptr, N, M, D, E, sigma, out, stream);
 }
 
+int keops_gauss_cg(const float *x, const float *b, int64_t N, int32_t D, int32_t E, float sigma, float lambda,
+                   float rtol, int32_t max_iter, float *out, int32_t *iters, float *rel_residual, void *stream) {
+  // ---- validation (host only)
+  if (N < 0 || D < 1 || E < 1 || max_iter < 0) return KEOPS_ERR_INVALID_ARG;
+  if (!std::isfinite(sigma) || !(sigma > 0.0f) || !std::isfinite(lambda) || lambda < 0.0f) return KEOPS_ERR_INVALID_ARG;
+  if (!std::isfinite(rtol) || rtol < 0.0f) return KEOPS_ERR_INVALID_ARG;
+  if (N > 0 && (!x || !b || !out)) return KEOPS_ERR_INVALID_ARG;
+  for (const void *p : {(const void *)x, (const void *)b, (const void *)out})
+    if (p && !aligned4(p)) return KEOPS_ERR_INVALID_ARG;
+  if (N > 0 && (overlaps(out, N * E * 4, x, N * D * 4) || overlaps(out, N * E * 4, b, N * E * 4)))
+    return KEOPS_ERR_INVALID_ARG;
+  if (E > 4) return KEOPS_ERR_UNSUPPORTED;
+  {
+    VariantInfo vi{};
+    GaussDispatch fn = nullptr;
+    if (gauss_find(OP_SUM, D, E, 1, &vi, &fn)) return KEOPS_ERR_UNSUPPORTED;
+  }
+  if (iters) *iters = 0;
+  if (rel_residual)
+    for (int e = 0; e < E; ++e) rel_residual[e] = 0.0f;
+  if (N == 0) return KEOPS_OK;
+
+  // ---- device work: r, p, q [N][E] fp32; partials [kCgBlocks][E] and scalars
+  // bb, rr (two slots), pq, rt [E] in double
+  hipStream_t st = (hipStream_t)stream;
+  (void)hipGetLastError();
+  const size_t vec = ((size_t)N * E * sizeof(float) + 255) / 256 * 256;
+  const size_t part_bytes = (size_t)kCgBlocks * E * sizeof(double);
+  const size_t scal_bytes = 5 * 4 * sizeof(double);
+  char *ws = nullptr;
+  if (hipMallocAsync((void **)&ws, 3 * vec + part_bytes + scal_bytes, st) != hipSuccess || !ws) {
+    (void)hipGetLastError();
+    return KEOPS_ERR_ALLOC;
+  }
+  float *r = (float *)ws, *p = (float *)(ws + vec), *q = (float *)(ws + 2 * vec);
+  double *part = (double *)(ws + 3 * vec);
+  double *sc = (double *)(ws + 3 * vec + part_bytes);
+  double *bb = sc, *rr[2] = {sc + 4, sc + 8}, *pq = sc + 12, *rt = sc + 16;
+  double h_bb[4] = {0, 0, 0, 0}, h_rr[4] = {0, 0, 0, 0};
+  int rc = KEOPS_OK;
+  auto fetch = [&](double *host, const double *dev) -> int {
+    if (hipMemcpyAsync(host, dev, E * sizeof(double), hipMemcpyDeviceToHost, st) != hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess)
+      return KEOPS_ERR_HIP;
+    return KEOPS_OK;
+  };
+  auto converged = [&](const double *v) {
+    for (int e = 0; e < E; ++e)
+      if (!(v[e] <= (double)rtol * (double)rtol * h_bb[e])) return false;
+    return true;
+  };
+
+  launch_cg_init(b, N, E, out, r, p, part, bb, st);
+  rc = fetch(h_bb, bb);
+  int it = 0;
+  int cur = 0;
+  if (rc == KEOPS_OK && hipMemcpyAsync(rr[0], bb, E * sizeof(double), hipMemcpyDeviceToDevice, st) != hipSuccess)
+    rc = KEOPS_ERR_HIP;
+  bool done = converged(h_bb);                       // b = 0 (or rtol >= 1): a = 0
+  while (rc == KEOPS_OK && !done && it < max_iter) {
+    rc = gauss_entry(OP_SUM, x, x, p, nullptr, N, N, D, E, sigma, q, stream);     // q = K p
+    if (rc != KEOPS_OK) break;
+    launch_cg_apply(p, q, lambda, N, E, part, pq, st);                            // q += lam p; <p, q>
+    launch_cg_step(out, r, p, q, rr[cur], pq, N, E, part, rr[cur ^ 1], st);       // a, r; <r, r>
+    ++it;
+    rc = fetch(h_rr, rr[cur ^ 1]);
+    if (rc != KEOPS_OK) break;
+    done = converged(h_rr);
+    if (!done) launch_cg_direction(p, r, rr[cur ^ 1], rr[cur], N, E, st);          // p = r + beta p
+    cur ^= 1;
+  }
+  // ---- the true residual |b - (K + lam I) a| / |b| of the returned solution
+  if (rc == KEOPS_OK && rel_residual) {
+    rc = gauss_entry(OP_SUM, x, x, out, nullptr, N, N, D, E, sigma, q, stream);
+    if (rc == KEOPS_OK) {
+      launch_cg_apply(out, q, lambda, N, E, part, pq, st);
+      launch_cg_residual(b, q, N, E, part, rt, st);
+      double h_rt[4] = {0, 0, 0, 0};
+      rc = fetch(h_rt, rt);
+      for (int e = 0; e < E && rc == KEOPS_OK; ++e)
+        rel_residual[e] = h_bb[e] > 0.0 ? (float)std::sqrt(h_rt[e] / h_bb[e]) : 0.0f;
+    }
+  }
+  if (iters) *iters = it;
+  (void)hipFreeAsync(ws, st);
+  if (rc == KEOPS_OK) rc = check_launch();
+  if (rc == KEOPS_OK && hipStreamSynchronize(st) != hipSuccess) rc = KEOPS_ERR_HIP;
+  return rc;
+}
+
 int keops_kmin(const float *x, const float *y, int64_t M, int64_t N, int32_t D, int32_t K, float *out_d,
                int64_t *out_idx, void *stream) {
   if (M < 0 || N < 0 || D < 1 || K < 1) return KEOPS_ERR_INVALID_ARG;

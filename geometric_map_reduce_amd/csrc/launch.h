@@ -47,4 +47,19 @@ int launch_kmin_combine(const float *pd, const int32_t *pi, int nsplit, int64_t 
 void launch_fill(float *out, int64_t count, float v, hipStream_t st);
 void launch_stream_combine(const float *part, int nparts, int64_t count, float *out, hipStream_t st);
 
+// Conjugate-gradient vector kernels (E <= 4 columns).  Each launcher that
+// reduces writes kCgBlocks x E double partials to `part` and their sums to
+// `out[E]` (double).
+constexpr int kCgBlocks = 512;
+void launch_cg_init(const float *b, int64_t N, int E, float *a, float *r, float *p, double *part, double *out,
+                    hipStream_t st);
+void launch_cg_apply(const float *p, float *q, float lam, int64_t N, int E, double *part, double *out,
+                     hipStream_t st);
+void launch_cg_step(float *a, float *r, const float *p, const float *q, const double *rr, const double *pq,
+                    int64_t N, int E, double *part, double *out, hipStream_t st);
+void launch_cg_direction(float *p, const float *r, const double *rr_new, const double *rr_old, int64_t N, int E,
+                         hipStream_t st);
+void launch_cg_residual(const float *b, const float *q, int64_t N, int E, double *part, double *out,
+                        hipStream_t st);
+
 }  // namespace kmi

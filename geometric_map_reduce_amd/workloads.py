@@ -23,11 +23,14 @@ solver_matvec_100k_x_10M   1e5       1e7       50   E=1     1.0    x, y ~ N(0, I
 kmin10_1M_d3               1e6       1e6       3    K=10    --     16-component mixture
 kmin10_1M_d64              1e6       1e6       64   K=10    --     16-component mixture
 stream_16_x_100M           16        1e8       3    E=1     0.1    x, y ~ U[0,1)^3, b ~ N(0,1)
+krige_100k                 1e5       1e5       3    E=1     0.1    x ~ U[0,1)^3, b ~ N(0,1); lambda = 1
 =========================  ========  ========  ===  ======  =====  =========================
 
 stream_16_x_100M is the few-rows, many-j case (the Falkon issue's M << N taken
 to its end): 16 rows against 1e8 points, where streaming y and b from HBM
-once, not arithmetic, bounds the time.
+once, not arithmetic, bounds the time.  krige_100k is the conjugate-gradient
+solve of (K + lambda I) a = b on the points x (the README's kriging / spline
+use of the solver); its y draw is made, to keep the recipe's order, and unused.
 
 Mixture recipe: centres ~ U[-5, 5)^D (16 of them, drawn first), then for x:
 labels ~ U{0..15}, x = centres[label] + 0.5 * N(0, I); then the same for y.
@@ -53,6 +56,7 @@ class Workload:
     sigma: float = 1.0
     dist: str = "normal"      # normal | uniform | normal_scaled | mixture16
     ops: tuple = ("sum",)
+    lam: float = 0.0          # ridge of the linear solve (cg only)
 
     def describe(self) -> dict:
         d = {"workload": self.name, "M": self.M, "N": self.N, "D": self.D}
@@ -61,6 +65,8 @@ class Workload:
         else:
             d["E"] = self.E
             d["sigma"] = self.sigma
+        if self.lam:
+            d["lambda"] = self.lam
         d["inputs"] = self.dist
         return d
 
@@ -80,6 +86,7 @@ WORKLOADS = {
                  ops=("kmin",)),
         Workload("stream_16_x_100M", 16, 100_000_000, 3, E=1, sigma=0.1, dist="uniform",
                  ops=("sum",)),
+        Workload("krige_100k", 100_000, 100_000, 3, E=1, sigma=0.1, dist="uniform", ops=("cg",), lam=1.0),
     ]
 }
 

@@ -111,6 +111,25 @@ int keops_gauss_grad_b(const float *x, const float *y, const float *g,
                        float *out, void *stream);
 
 /*
+ * Conjugate-gradient solve of (K + lambda I) a = b with the Gaussian kernel
+ * matrix of one point set, K_ij = exp(-|x_i - x_j|^2/sigma^2) ([README] feature
+ * list: a conjugate gradient solver for spline interpolation, kriging or
+ * Gaussian process regression).  Each of the E <= 4 columns of b is solved
+ * independently, starting from a = 0, until |r_e| <= rtol |b_e| for every
+ * column (r the recursively updated residual) or after max_iter iterations.
+ * Every product K p is one keops_gauss_sum.
+ *   x: [N, D]; b, out (= a): [N, E]; sigma > 0; lambda >= 0; rtol >= 0.
+ *   iters (host, may be NULL): iterations run.
+ *   rel_residual (host [E], may be NULL): the true |b - (K + lambda I) a| / |b|
+ *     of the returned a, from one more product (0 for a zero column of b).
+ * Unlike the reductions above this call synchronises `stream`: it reads the
+ * residual norms on the host after every iteration.  Returns KEOPS_OK also when
+ * max_iter is reached first (see iters and rel_residual); N = 0 is a no-op.
+ */
+int keops_gauss_cg(const float *x, const float *b, int64_t N, int32_t D, int32_t E, float sigma, float lambda,
+                   float rtol, int32_t max_iter, float *out, int32_t *iters, float *rel_residual, void *stream);
+
+/*
  * K-min reduction with indices ([KO-GPU] §2 argmin / argKmin; [README] ArgMin,
  * K-min reductions): for each row i, the K smallest squared distances
  * |x_i - y_j|^2, ascending, and their indices j; equal distances are ordered

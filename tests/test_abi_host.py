@@ -28,7 +28,7 @@ def L():
 def test_header_declares_the_reductions():
     names = declared_functions()
     for n in ("keops_gauss_sum", "keops_gauss_lse", "keops_gauss_grad_x", "keops_gauss_grad_y",
-              "keops_gauss_grad_b", "keops_kmin"):
+              "keops_gauss_grad_b", "keops_gauss_cg", "keops_kmin"):
         assert n in names
 
 
@@ -116,3 +116,20 @@ def test_options(L):
     for opt in (1, 2, 3, 5):
         assert L.keops_set_option(opt, 0) == 0
     assert L.keops_version() >= 100
+
+
+def test_cg_validation(L):
+    out = ctypes.c_void_p(0x900000)
+    it = ctypes.c_int32(7)
+    res = (ctypes.c_float * 4)()
+    for args in [(FAKE, FAKE2, 10, 3, 1, 0.0, 1.0, 1e-5, 10),      # sigma = 0
+                 (FAKE, FAKE2, 10, 3, 1, 1.0, -1.0, 1e-5, 10),     # lambda < 0
+                 (FAKE, FAKE2, 10, 3, 1, 1.0, 1.0, -1e-5, 10),     # rtol < 0
+                 (FAKE, FAKE2, 10, 3, 1, 1.0, 1.0, 1e-5, -1),      # max_iter < 0
+                 (None, FAKE2, 10, 3, 1, 1.0, 1.0, 1e-5, 10)]:     # missing x
+        assert L.keops_gauss_cg(*args, out, ctypes.byref(it), res, None) == -1
+    assert L.keops_gauss_cg(FAKE, FAKE2, 10, 3, 5, 1.0, 1.0, 1e-5, 10, out, None, None, None) == -2   # E > 4
+    assert L.keops_gauss_cg(FAKE, FAKE2, 10, 99, 1, 1.0, 1.0, 1e-5, 10, out, None, None, None) == -2  # D
+    assert L.keops_gauss_cg(None, None, 0, 3, 2, 1.0, 0.0, 1e-5, 10, None, ctypes.byref(it), res, None) == 0
+    assert it.value == 0 and res[0] == 0.0 and res[1] == 0.0
+

@@ -174,6 +174,72 @@ def test_transposed_grads_degenerate_and_balance():
     assert np.all(np.abs(gx.sum(0) + gy.sum(0)) <= 1e-4 * (nux.sum(0) + nuy.sum(0)))
 
 
+def _check_cg(x, b, sigma, lam, a, iters, rel, rtol, max_iter):
+    """A conjugate-gradient solution against the dense float64 solve a*: the true residual
+    (double, through the sum oracle) is within the stopping rule's reach, the reported
+    residual agrees with it, and |a - a*| <= |r| / lam (K is positive semi-definite, so the
+    smallest eigenvalue of K + lam I is at least lam)."""
+    a = np.asarray(a, np.float64)
+    a_star = oracle.gauss_solve(x, b, sigma, lam)
+    r = oracle.gauss_system_residual(x, b, a.astype(np.float32), sigma, lam)
+    nb = np.linalg.norm(b.astype(np.float64), axis=0)
+    nr = np.linalg.norm(r, axis=0)
+    rel_true = np.where(nb > 0, nr / np.maximum(nb, 1e-300), 0.0)
+    assert iters <= max_iter
+    assert np.all(np.abs(rel - rel_true) <= 1e-5 + 1e-2 * rel_true), (rel, rel_true)
+    if iters < max_iter:
+        assert np.all(rel_true <= 2 * rtol + 1e-5), (rel_true, rtol)
+    err = np.linalg.norm(a - a_star, axis=0)
+    assert np.all(err <= nr / lam * (1 + 1e-3) + 1e-6 * np.linalg.norm(a_star, axis=0)), (err, nr / lam)
+    return rel_true
+
+
+# (N, D, E, sigma, lambda, rtol)
+CG_CASES = [(1, 3, 1, 1.0, 0.5, 1e-6), (50, 2, 1, 0.5, 0.1, 1e-6), (777, 3, 3, 0.3, 1.0, 1e-5),
+            (3000, 3, 1, 0.1, 1.0, 1e-5), (2500, 5, 2, 1.0, 10.0, 1e-5), (1500, 64, 1, 8.0, 0.5, 1e-5)]
+
+
+@pytest.mark.parametrize("case", CG_CASES, ids=lambda c: "N%d_D%d_E%d_s%g_l%g" % c[:5])
+def test_cg_against_dense_solve(case):
+    N, D, E, sigma, lam, rtol = case
+    say(f"cg N={N} D={D} E={E} sigma={sigma} lambda={lam}")
+    rng = np.random.default_rng(900 + N + D)
+    x = rng.random((N, D)).astype(np.float32)
+    b = rng.standard_normal((N, E)).astype(np.float32)
+    sigma = float(np.float32(sigma))
+    a, iters, rel = gm.keops_gauss_cg(dev(x), dev(b), sigma, lam, rtol=rtol, max_iter=2000)
+    a2, iters2, rel2 = gm.keops_gauss_cg(dev(x), dev(b), sigma, lam, rtol=rtol, max_iter=2000)
+    a, a2 = host(a), host(a2)
+    assert iters == iters2 and np.array_equal(a, a2) and np.array_equal(rel, rel2)   # reproducible
+    rel_true = _check_cg(x, b, sigma, lam, a, iters, rel, rtol, 2000)
+    say(f"  iterations {iters}, relative residual {rel_true.max():.3g}")
+
+
+def test_cg_edge_cases():
+    say("cg edge cases: b = 0, max_iter = 0, one point, early stop")
+    rng = np.random.default_rng(5)
+    x = rng.random((200, 3)).astype(np.float32)
+    b = np.zeros((200, 2), np.float32)
+    a, iters, rel = gm.keops_gauss_cg(dev(x), dev(b), 0.2, 1.0)
+    assert iters == 0 and not host(a).any() and not rel.any()
+    b = rng.standard_normal((200, 2)).astype(np.float32)
+    b[:, 1] = 0.0                                          # one zero column among others
+    a, iters, rel = gm.keops_gauss_cg(dev(x), dev(b), 0.2, 1.0, rtol=1e-6)
+    assert not host(a)[:, 1].any() and rel[1] == 0.0
+    _check_cg(x, b, 0.2, 1.0, host(a), iters, rel, 1e-6, 1000)
+    a, iters, rel = gm.keops_gauss_cg(dev(x), dev(b), 0.2, 1.0, max_iter=0)
+    assert iters == 0 and not host(a).any()
+    np.testing.assert_allclose(rel, [1.0, 0.0], rtol=1e-6)
+    a, iters, rel = gm.keops_gauss_cg(dev(x), dev(b), 0.2, 1.0, max_iter=3)   # stops early: still bounded
+    assert iters == 3
+    _check_cg(x, b, 0.2, 1.0, host(a), iters, rel, 1e-6, 3)
+    x1 = np.array([[0.3, -0.2, 0.5]], np.float32)
+    b1 = np.array([[2.0, -1.0]], np.float32)
+    a, iters, rel = gm.keops_gauss_cg(dev(x1), dev(b1), 1.0, 0.25)
+    np.testing.assert_allclose(host(a), b1 / 1.25, rtol=1e-6)
+    assert iters == 1
+
+
 KMIN_SMALL = [(1, 1, 1, 1), (5, 40, 3, 10), (300, 1000, 3, 10), (257, 513, 2, 16), (100, 3000, 4, 32),
               (70, 600, 8, 7), (64, 300, 16, 5), (40, 500, 32, 10), (30, 200, 50, 3), (25, 300, 64, 10),
               (10, 128, 100, 2), (200, 900, 5, 1), (129, 129, 3, 12)]
@@ -345,6 +411,23 @@ def test_workload_transposed_grads_1M():
     Gb_ref, nub = oracle.gauss_grad_b(x, y, g, w.sigma, cols=cols)
     say(f"  grad_y max err/nu {check_grad(gy[cols], Gy_ref, nuy):.3g}; "
         f"grad_b {check_sum(gb[cols], Gb_ref, nub, what='grad_b'):.3g}")
+
+
+def test_workload_krige_100k():
+    """CG at N = 1e5: the oracle recomputes sampled rows of the true residual in double; their
+    scaled root-mean-square matches the reported norm, which meets the stopping rule."""
+    w = workloads.WORKLOADS["krige_100k"]
+    say(f"workload {w.name}")
+    x, _, b = workloads.make_inputs(w)
+    rtol = 1e-4
+    a, iters, rel = gm.keops_gauss_cg(dev(x), dev(b), w.sigma, w.lam, rtol=rtol, max_iter=1000)
+    a = host(a)
+    rows = _sample(w.N, 512)
+    r = oracle.gauss_system_residual(x, b, a, w.sigma, w.lam, rows=rows)
+    est = np.sqrt((r ** 2).mean() * w.N) / np.linalg.norm(b.astype(np.float64))
+    say(f"  iterations {iters}, reported {rel[0]:.3g}, sampled estimate {est:.3g}")
+    assert iters < 1000 and rel[0] <= 2 * rtol
+    assert 0.5 * rel[0] - 1e-6 <= est <= 2.0 * rel[0] + 1e-6
 
 
 @pytest.mark.parametrize("name", ["kmin10_1M_d3", "kmin10_1M_d64"])
