@@ -114,6 +114,12 @@ constexpr int64_t kGaussWgsPerCu = 24;
 constexpr int64_t kMfmaSumWgsPerCu = 16;
 constexpr int64_t kKminWgsPerCu = 8;
 constexpr int64_t kKminMfmaWgsPerCu = 4;
+// Rows from which the sum and LSE take the wide variant (several rows per lane):
+// at 50k rows and above it was faster than one row per lane by 3-20 %, at 20k
+// and below slower (too few row blocks to fill the GPU).  grad_x keeps one row
+// per lane until the wide variant fills every CU: it was the faster one up to
+// 200k rows.
+constexpr int64_t kWideMinRows = 40000;
 
 struct Plan {
   int wide;
@@ -131,7 +137,7 @@ struct Plan {
 // size is not a multiple of the resident capacity leaves CUs idle, and at a
 // handful of work-groups per CU that tail costs several per cent.
 Plan make_plan(int64_t M, int64_t N, int cus, int64_t rows_wide, int64_t rows_narrow, int tile_j,
-               int64_t wgs_per_cu) {
+               int64_t wgs_per_cu, int64_t wide_min_rows) {
   const int64_t target = g_opt_wg_target.load();
   if (target > 0) wgs_per_cu = target;
   if (rows_wide < 1) rows_wide = 1;
@@ -140,7 +146,7 @@ Plan make_plan(int64_t M, int64_t N, int cus, int64_t rows_wide, int64_t rows_na
   const int64_t want_wgs = (int64_t)cus * (wgs_per_cu > 0 ? wgs_per_cu : 1);
   Plan p{};
   const int64_t opt_rows = g_opt_rows.load();
-  p.wide = opt_rows == 1 ? 0 : (opt_rows == 2 ? 1 : (M >= rows_wide * cus));
+  p.wide = opt_rows == 1 ? 0 : (opt_rows == 2 ? 1 : (M >= wide_min_rows));
   p.rows_wg = p.wide ? rows_wide : rows_narrow;
   p.tile_j = tile_j;
   p.nblk = (M + p.rows_wg - 1) / p.rows_wg;
@@ -257,9 +263,9 @@ int gauss_entry(int op, const float *x, const float *y, const float *b, const fl
   // The MFMA kernel and its direct-form companion both use 256-row work-groups
   // (the narrow VALU variant) and j-splits on the larger of the two tiles.
   const Plan p = use_mfma ? make_plan(M, N, cus, mfma_info.rows_per_wg, mfma_info.rows_per_wg,
-                                      std::max(mfma_info.tile_j, narrow_info.tile_j), kMfmaSumWgsPerCu)
+                                      std::max(mfma_info.tile_j, narrow_info.tile_j), kMfmaSumWgsPerCu, 0)
                           : make_plan(M, N, cus, wide_info.rows_per_wg, narrow_info.rows_per_wg, wide_info.tile_j,
-                                      kGaussWgsPerCu);
+                                      kGaussWgsPerCu, op == OP_GRAD ? wide_info.rows_per_wg * cus : kWideMinRows);
 
   const double s2 = (double)sigma * (double)sigma;
   const double scale = std::sqrt(1.4426950408889634 / s2);
@@ -465,7 +471,7 @@ int keops_kmin(const float *x, const float *y, int64_t M, int64_t N, int32_t D, 
   int cus = 0;
   if (int rc = device_setup(&cus)) return rc;
   const Plan p = make_plan(M, N, cus, info.rows_per_wg, info.rows_per_wg, info.tile_j,
-                           fn == kmin_dispatch_mfma ? kKminMfmaWgsPerCu : kKminWgsPerCu);
+                           fn == kmin_dispatch_mfma ? kKminMfmaWgsPerCu : kKminWgsPerCu, 0);
   KminArgs a{};
   a.x = x; a.y = y; a.M = M; a.N = N;
   a.j_per_split = p.jps;

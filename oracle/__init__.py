@@ -65,6 +65,8 @@ def open_library(path: str):
     lib.oracle_kmin.argtypes = [P, P, i64, i64, i32, i32, P, i64, P, P]
     lib.oracle_sq_dist_pairs.argtypes = [P, P, i32, P, P, i64, P]
     lib.oracle_gauss_matrix.argtypes = [P, P, i64, i64, i32, f64, P]
+    lib.oracle_gauss_sum_ranges.argtypes = [P, P, P, i64, i64, i32, i32, f64, P, i64, P, P, i64, P, P]
+    lib.oracle_gauss_lse_ranges.argtypes = [P, P, P, i64, i64, i32, i32, f64, P, i64, P, P, i64, P]
     for f in ("oracle_gauss_sum", "oracle_gauss_lse", "oracle_gauss_grad_x", "oracle_gauss_grad_y",
               "oracle_gauss_grad_b", "oracle_kmin", "oracle_sq_dist_pairs", "oracle_num_threads"):
         getattr(lib, f).restype = ctypes.c_int
@@ -254,4 +256,43 @@ def gauss_system_residual(x, b, a, sigma, lam, rows=None, lib=None):
     Ka, _ = gauss_sum(x[rows] if rows is not None else x, x, a, sigma, lib=lib)
     sel = rows if rows is not None else slice(None)
     return b[sel] - Ka - float(lam) * a[sel].astype(np.float64)
+
+
+def _ranges(ranges_i, slices_i, redranges_j):
+    ri = np.ascontiguousarray(ranges_i, dtype=np.int64).reshape(-1, 2)
+    si = np.ascontiguousarray(slices_i, dtype=np.int64).ravel()
+    rj = np.ascontiguousarray(redranges_j, dtype=np.int64).reshape(-1, 2)
+    assert si.shape[0] == ri.shape[0]
+    return ri, si, rj
+
+
+def gauss_sum_ranges(x, y, b, sigma, ranges_i, slices_i, redranges_j, lib=None):
+    """Block-sparse Gaussian sum over the kept pairs given by (ranges_i, slices_i, redranges_j)
+    (row range c meets the j ranges slices_i[c-1] .. slices_i[c]-1).  Returns (a, norm) for all
+    M rows, float64; rows in no row range get 0."""
+    x, y, b = _f32(x, 2), _f32(y, 2), _f32(b, 2)
+    M, D = x.shape
+    N, E = b.shape
+    assert y.shape == (N, D)
+    ri, si, rj = _ranges(ranges_i, slices_i, redranges_j)
+    out = np.empty((M, E), np.float64)
+    norm = np.empty((M, E), np.float64)
+    _check((lib or _load()).oracle_gauss_sum_ranges(_ptr(x), _ptr(y), _ptr(b), M, N, D, E, float(sigma),
+                                           _ptr(ri), ri.shape[0], _ptr(si), _ptr(rj), rj.shape[0],
+                                           _ptr(out), _ptr(norm)), "gauss_sum_ranges")
+    return out, norm
+
+
+def gauss_lse_ranges(x, y, b, sigma, ranges_i, slices_i, redranges_j, lib=None):
+    """Block-sparse LogSumExp over the kept pairs (rows with none get -inf), float64 [M, E]."""
+    x, y, b = _f32(x, 2), _f32(y, 2), _f32(b, 2)
+    M, D = x.shape
+    N, E = b.shape
+    assert y.shape == (N, D)
+    ri, si, rj = _ranges(ranges_i, slices_i, redranges_j)
+    out = np.empty((M, E), np.float64)
+    _check((lib or _load()).oracle_gauss_lse_ranges(_ptr(x), _ptr(y), _ptr(b), M, N, D, E, float(sigma),
+                                           _ptr(ri), ri.shape[0], _ptr(si), _ptr(rj), rj.shape[0],
+                                           _ptr(out)), "gauss_lse_ranges")
+    return out
 

@@ -296,3 +296,97 @@ int oracle_gauss_matrix(const float *x, const float *y, int64_t M, int64_t N, in
         for (int64_t j = 0; j < N; ++j) out[i * N + j] = exp(-sq_dist(x + i * D, y + j * D, D) * inv_s2);
     return 0;
 }
+
+/*
+ * Block-sparse reductions ([KO-GPU] §3 "Applications": cluster-wise
+ * block-sparsity for large kernel linear systems; §4: the block-sparse
+ * truncation rule; [README] feature list: an interface for block-sparse
+ * strategies).  The kept pairs are given as ranges: row range c covers rows
+ * [ranges_i[2c], ranges_i[2c+1]) and meets the j ranges
+ * [redranges_j[2k], redranges_j[2k+1]) for k from slices_i[c-1] (0 when c = 0)
+ * up to slices_i[c] - 1.  The reductions are the definitions above restricted
+ * to the kept pairs, j visited range by range in the listed order; a j listed
+ * in two ranges of one row range counts twice.  Rows in no row range get the
+ * empty reduction (0 for the sum, -inf for LogSumExp).  Row ranges must not
+ * overlap (-1 otherwise), and every range must lie inside [0, M) or [0, N).
+ */
+static int check_ranges(int64_t M, int64_t N, const int64_t *ranges_i, int64_t nri, const int64_t *slices_i,
+                        const int64_t *redranges_j, int64_t nrj) {
+    if (M < 0 || N < 0 || nri < 0 || nrj < 0) return -1;
+    if (nri > 0 && (!ranges_i || !slices_i)) return -1;
+    if (nrj > 0 && !redranges_j) return -1;
+    int64_t prev = 0;
+    for (int64_t c = 0; c < nri; ++c) {
+        const int64_t lo = ranges_i[2 * c], hi = ranges_i[2 * c + 1];
+        if (lo < 0 || lo > hi || hi > M) return -1;
+        if (slices_i[c] < prev || slices_i[c] > nrj) return -1;
+        prev = slices_i[c];
+        for (int64_t d = 0; d < c; ++d)   /* row ranges pairwise disjoint */
+            if (lo < ranges_i[2 * d + 1] && ranges_i[2 * d] < hi) return -1;
+    }
+    for (int64_t k = 0; k < nrj; ++k) {
+        const int64_t lo = redranges_j[2 * k], hi = redranges_j[2 * k + 1];
+        if (lo < 0 || lo > hi || hi > N) return -1;
+    }
+    return 0;
+}
+
+int oracle_gauss_sum_ranges(const float *x, const float *y, const float *b,
+                            int64_t M, int64_t N, int D, int E, double sigma,
+                            const int64_t *ranges_i, int64_t nri, const int64_t *slices_i,
+                            const int64_t *redranges_j, int64_t nrj,
+                            double *out, double *norm) {
+    if (D < 1 || E < 1 || !(sigma > 0.0) || check_ranges(M, N, ranges_i, nri, slices_i, redranges_j, nrj))
+        return -1;
+    const double inv_s2 = 1.0 / (sigma * sigma);
+    for (int64_t q = 0; q < M * E; ++q) { out[q] = 0.0; if (norm) norm[q] = 0.0; }
+    for (int64_t c = 0; c < nri; ++c) {
+        const int64_t k0 = c == 0 ? 0 : slices_i[c - 1], k1 = slices_i[c];
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t i = ranges_i[2 * c]; i < ranges_i[2 * c + 1]; ++i) {
+            double *o = out + i * E, *nm = norm ? norm + i * E : NULL;
+            for (int64_t k = k0; k < k1; ++k)
+                for (int64_t j = redranges_j[2 * k]; j < redranges_j[2 * k + 1]; ++j) {
+                    const double kv = exp(-sq_dist(x + i * D, y + j * D, D) * inv_s2);
+                    for (int e = 0; e < E; ++e) {
+                        const double t = kv * (double)b[j * E + e];
+                        o[e] += t;
+                        if (nm) nm[e] += fabs(t);
+                    }
+                }
+        }
+    }
+    return 0;
+}
+
+int oracle_gauss_lse_ranges(const float *x, const float *y, const float *b,
+                            int64_t M, int64_t N, int D, int E, double sigma,
+                            const int64_t *ranges_i, int64_t nri, const int64_t *slices_i,
+                            const int64_t *redranges_j, int64_t nrj, double *out) {
+    if (D < 1 || E < 1 || !(sigma > 0.0) || check_ranges(M, N, ranges_i, nri, slices_i, redranges_j, nrj))
+        return -1;
+    const double inv_s2 = 1.0 / (sigma * sigma);
+    for (int64_t q = 0; q < M * E; ++q) out[q] = -INFINITY;
+    for (int64_t c = 0; c < nri; ++c) {
+        const int64_t k0 = c == 0 ? 0 : slices_i[c - 1], k1 = slices_i[c];
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t i = ranges_i[2 * c]; i < ranges_i[2 * c + 1]; ++i) {
+            for (int e = 0; e < E; ++e) {
+                double m = -INFINITY;
+                for (int64_t k = k0; k < k1; ++k)
+                    for (int64_t j = redranges_j[2 * k]; j < redranges_j[2 * k + 1]; ++j) {
+                        const double v = -sq_dist(x + i * D, y + j * D, D) * inv_s2 + (double)b[j * E + e];
+                        if (v > m) m = v;
+                    }
+                if (!(m > -INFINITY)) continue;
+                double s = 0.0;
+                for (int64_t k = k0; k < k1; ++k)
+                    for (int64_t j = redranges_j[2 * k]; j < redranges_j[2 * k + 1]; ++j)
+                        s += exp(-sq_dist(x + i * D, y + j * D, D) * inv_s2 + (double)b[j * E + e] - m);
+                out[i * E + e] = m + log(s);
+            }
+        }
+    }
+    return 0;
+}
+

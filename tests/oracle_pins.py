@@ -434,6 +434,73 @@ def pin_solve_residual(lib=None):
         assert np.all(np.abs(r) <= bound + 1e-12), np.abs(r).max()
 
 
+# --------------------------------------------------------------------------- block-sparse ranges
+def random_ranges(rng, M, N, n_row_ranges, max_j_ranges, cover=False):
+    """Disjoint row ranges (a partition of [0, M) when ``cover``, else with gaps), each meeting
+    0..max_j_ranges random j ranges; returns (ranges_i, slices_i, redranges_j) and the mask."""
+    cuts = np.sort(rng.choice(np.arange(1, M), size=min(n_row_ranges - 1, M - 1), replace=False)).tolist() \
+        if M > 1 else []
+    bounds = [0, *cuts, M]
+    ranges_i, slices_i, redr = [], [], []
+    mask = np.zeros((M, N), np.int64)
+    for lo, hi in zip(bounds[:-1], bounds[1:]):
+        if not cover and rng.random() < 0.25:
+            continue                                         # a gap: rows in no range
+        for _ in range(int(rng.integers(0, max_j_ranges + 1))):
+            a, c = sorted(rng.integers(0, N + 1, size=2).tolist())
+            redr.append([a, c])
+            mask[lo:hi, a:c] += 1
+        ranges_i.append([lo, hi])
+        slices_i.append(len(redr))
+    return (np.array(ranges_i, np.int64).reshape(-1, 2), np.array(slices_i, np.int64),
+            np.array(redr, np.int64).reshape(-1, 2), mask)
+
+
+def pin_ranges_brute_mask(lib=None):
+    """The block-sparse sum and LSE equal the dense formulas with a materialised pair mask
+    (a pair listed twice counts twice); rows in no range get 0 and -inf."""
+    rng = np.random.default_rng(71)
+    for (M, N, D, E) in [(30, 40, 3, 1), (17, 50, 2, 2), (25, 9, 5, 3), (1, 1, 1, 1)]:
+        sigma = 1.2
+        x = rng.standard_normal((M, D)).astype(np.float32)
+        y = rng.standard_normal((N, D)).astype(np.float32)
+        b = rng.standard_normal((N, E)).astype(np.float32)
+        ri, si, rj, mask = random_ranges(rng, M, N, 5, 3)
+        a, n = oracle.gauss_sum_ranges(x, y, b, sigma, ri, si, rj, lib=lib)
+        W = mask * brute_K(x, y, sigma)
+        rel_close(a, W @ b.astype(np.float64), 0, 1e-12 * (1 + n.max()))
+        rel_close(n, W @ np.abs(b.astype(np.float64)), 1e-12)
+        l = oracle.gauss_lse_ranges(x, y, b, sigma, ri, si, rj, lib=lib)
+        V = -brute_sqdist(x, y)[:, :, None] / sigma ** 2 + b.astype(np.float64)[None, :, :]
+        ref = scipy.special.logsumexp(V, axis=1, b=np.broadcast_to(mask[:, :, None], V.shape))
+        ref = np.where(mask.sum(1)[:, None] > 0, ref, -np.inf)
+        fin = np.isfinite(ref)
+        assert np.array_equal(fin, np.isfinite(l))
+        rel_close(l[fin], ref[fin], 0, 1e-12 * (1 + np.abs(ref[fin]).max()) if fin.any() else 0)
+
+
+def pin_ranges_dense_and_split(lib=None):
+    """One row range meeting [0, N) is exactly the dense reduction; cutting a j range in two, or
+    a row range in two with the same j list, changes nothing (same order, same terms)."""
+    rng = np.random.default_rng(72)
+    M, N, D, E = 23, 37, 3, 2
+    x = rng.standard_normal((M, D)).astype(np.float32)
+    y = rng.standard_normal((N, D)).astype(np.float32)
+    b = rng.standard_normal((N, E)).astype(np.float32)
+    a0, n0 = oracle.gauss_sum(x, y, b, 0.9, lib=lib)
+    a1, n1 = oracle.gauss_sum_ranges(x, y, b, 0.9, [[0, M]], [1], [[0, N]], lib=lib)
+    assert np.array_equal(a0, a1) and np.array_equal(n0, n1)
+    assert np.array_equal(oracle.gauss_lse(x, y, b, 0.9, lib=lib),
+                          oracle.gauss_lse_ranges(x, y, b, 0.9, [[0, M]], [1], [[0, N]], lib=lib))
+    a2, _ = oracle.gauss_sum_ranges(x, y, b, 0.9, [[0, 9], [9, M]], [2, 4], [[0, 15], [15, N], [0, 15], [15, N]],
+                                    lib=lib)
+    assert np.array_equal(a0, a2)
+    # an empty j list and a range list that skips rows
+    a3, _ = oracle.gauss_sum_ranges(x, y, b, 0.9, [[2, 5], [7, 8]], [0, 1], [[4, 6]], lib=lib)
+    assert not a3[[0, 1, 5, 6] + list(range(8, M))].any() and not a3[2:5].any() and a3[7].all()
+    assert np.isneginf(oracle.gauss_lse_ranges(x, y, b, 0.9, [[2, 5]], [0], np.zeros((0, 2)), lib=lib)).all()
+
+
 # --------------------------------------------------------------------------- kmin
 def pin_kmin_argsort(lib=None):
     """K-min equals a stable argsort of the materialised distances (ties -> smaller j)."""

@@ -56,6 +56,13 @@ MUTANTS = {
                                  "const double inv_s2 = 1.0 / (2.0 * sigma * sigma);\n#pragma omp parallel for schedule(dynamic, 1)\n"
                                  "    for (int64_t i = 0; i < M; ++i)"),
     "matrix_row_stride": ("out[i * N + j] = exp(", "out[j * M + i] = exp("),
+    "ranges_slice_start": ("const int64_t k0 = c == 0 ? 0 : slices_i[c - 1], k1 = slices_i[c];\n#pragma omp parallel for schedule(dynamic, 1)\n"
+                           "        for (int64_t i = ranges_i[2 * c]; i < ranges_i[2 * c + 1]; ++i) {\n            double *o",
+                           "const int64_t k0 = c == 0 ? 0 : slices_i[c - 1] + 1, k1 = slices_i[c];\n#pragma omp parallel for schedule(dynamic, 1)\n"
+                           "        for (int64_t i = ranges_i[2 * c]; i < ranges_i[2 * c + 1]; ++i) {\n            double *o"),
+    "ranges_j_end": ("for (int64_t j = redranges_j[2 * k]; j < redranges_j[2 * k + 1]; ++j) {\n                    const double kv",
+                     "for (int64_t j = redranges_j[2 * k]; j + 1 < redranges_j[2 * k + 1]; ++j) {\n                    const double kv"),
+    "ranges_lse_drop_max": ("out[i * E + e] = m + log(s);", "out[i * E + e] = log(s);"),
     "kmin_tie_break": ("(dj == bd[pos - 1] && j < bj[pos - 1])", "(dj == bd[pos - 1] && j > bj[pos - 1])"),
     "kmin_keep_last": ("if (count == K && !(dj < bd[K - 1]", "if (count == K && !(dj <= bd[K - 1]"),
 }
