@@ -54,14 +54,16 @@ BENCHES = {
     "kmin64": ("kmin", "kmin10_1M_d64"),
     "stream": ("sum", "stream_16_x_100M"),
     "cg": ("cg", "krige_100k"),
+    "sum_bs": ("sum_ranges", "sum_lse_1M"),
 }
+BS_VOXEL, BS_EPS = 0.1, 1e-5       # block-sparse bench: voxel side and truncation threshold
 CG_RTOL = 1e-4
 PEAK_HBM_GBS = 8000.0             # MI355X HBM3E peak
 STREAM_MAX_ROWS = 64              # the library's few-rows layout (j per lane) for the sum
 
 
 def flops_per_pair(op, D, E):
-    return {"sum": 3 * D + 1 + 2 * E, "cg": 3 * D + 1 + 2 * E, "lse": 3 * D + 5, "grad_x": 5 * D + 2 * E + 1, "grad_y": 5 * D + 2 * E + 1,
+    return {"sum": 3 * D + 1 + 2 * E, "cg": 3 * D + 1 + 2 * E, "sum_ranges": 3 * D + 1 + 2 * E, "lse": 3 * D + 5, "grad_x": 5 * D + 2 * E + 1, "grad_y": 5 * D + 2 * E + 1,
             "grad_b": 3 * D + 1 + 2 * E, "kmin": 3 * D}[op]
 
 
@@ -85,7 +87,7 @@ def roofline_of(op, M, D, E):
     if uses_mfma(op, D):
         return "mfma", 2 * D, ("gauss_mfma_sum_kernel" if op == "sum" else "kmin_mfma_kernel")
     # the transposed gradients run the row kernels with y as the rows
-    kop = {"grad_y": "grad_x", "grad_b": "sum", "cg": "sum"}.get(op, op)
+    kop = {"grad_y": "grad_x", "grad_b": "sum", "cg": "sum", "sum_ranges": "sum"}.get(op, op)
     name = "kmin_valu_kernel" if op == "kmin" else f"gauss_valu_kernel<{kop}>"
     return "alu", flops_per_pair(op, D, E), name
 
@@ -127,7 +129,9 @@ def recorded_traffic(bench_name, op):
     return rec.get("hbm_bytes_per_launch")
 
 
-def run_op(gm, op, X, Y, B, G, sigma, K, out, lam=0.0):
+def run_op(gm, op, X, Y, B, G, sigma, K, out, lam=0.0, ranges=None):
+    if op == "sum_ranges":
+        return gm.keops_gauss_sum_ranges(X, Y, B, sigma, *ranges, out=out)
     if op == "cg":
         return gm.keops_gauss_cg(X, B, sigma, lam, rtol=CG_RTOL, max_iter=1000, out=out)
     if op == "sum":
@@ -143,7 +147,25 @@ def run_op(gm, op, X, Y, B, G, sigma, K, out, lam=0.0):
     return gm.keops_kmin(X, Y, K, out_d=out[0], out_idx=out[1])
 
 
-def cpu_baseline(op, w, x, y, b, g, target_s, gpu_out):
+def block_sparse_setup(x, y, b, sigma):
+    """Sort x, y (and b) by voxel clusters and build the truncation ranges (host preparation,
+    outside the timed region).  Returns the permuted inputs, the ranges and the kept pairs."""
+    import numpy as np
+
+    from geometric_map_reduce_amd import blocksparse as bs
+    lx, ly = bs.grid_cluster(x, BS_VOXEL), bs.grid_cluster(y, BS_VOXEL)
+    px, py = bs.sort_by_cluster(lx), bs.sort_by_cluster(ly)
+    rx, cx, radx = bs.cluster_ranges_centroids(x[px], lx[px])
+    ry, cy, rady = bs.cluster_ranges_centroids(y[py], ly[py])
+    mask = bs.truncation_mask(cx, radx, cy, rady, bs.cutoff_for(sigma, BS_EPS))
+    ri, si, rj = bs.ranges_from_mask(mask, rx, ry)
+    starts = np.r_[0, si[:-1]]
+    tj = np.array([(rj[s:e, 1] - rj[s:e, 0]).sum() for s, e in zip(starts, si)], np.int64)
+    kept = int(((ri[:, 1] - ri[:, 0]) * tj).sum())
+    return x[px], y[py], b[py], (ri, si, rj), kept
+
+
+def cpu_baseline(op, w, x, y, b, g, target_s, gpu_out, ranges=None):
     import numpy as np
 
     import oracle
@@ -151,6 +173,17 @@ def cpu_baseline(op, w, x, y, b, g, target_s, gpu_out):
 
     def call(rows):
         t0 = time.perf_counter()
+        if op == "sum_ranges":      # the oracle sum of each sampled row over its kept j ranges
+            ri, si, rj = ranges
+            owner = np.zeros(w.M, np.int64)
+            for c, (lo, hi) in enumerate(ri):
+                owner[lo:hi] = c
+            res = (np.zeros((len(rows), w.E)), np.zeros((len(rows), w.E)))
+            for c in np.unique(owner[rows]):
+                sel = np.flatnonzero(owner[rows] == c)
+                J = np.concatenate([np.arange(a, e) for a, e in rj[(si[c - 1] if c else 0):si[c]]])
+                res[0][sel], res[1][sel] = oracle.gauss_sum(x, y[J], b[J], w.sigma, rows=rows[sel])
+            return time.perf_counter() - t0, res
         if op == "sum":
             res = oracle.gauss_sum(x, y, b, w.sigma, rows=rows)
         elif op == "cg":        # the solver's work is its products K p: the sum oracle on x
@@ -176,15 +209,23 @@ def cpu_baseline(op, w, x, y, b, g, target_s, gpu_out):
     rows = workloads.sample_rows(n_out, n, seed=1)
     t, res = call(rows)
     pairs = len(rows) * n_red
+    if op == "sum_ranges":
+        ri, si, rj = ranges
+        per_c = np.array([(rj[s:e, 1] - rj[s:e, 0]).sum() for s, e in zip(np.r_[0, si[:-1]], si)])
+        owner = np.zeros(w.M, np.int64)
+        for c, (lo, hi) in enumerate(ri):
+            owner[lo:hi] = c
+        pairs = int(per_c[owner[rows]].sum())
     base = {"value": pairs / t / 1e9, "unit": "G pair-evals/s", "cores": oracle.num_threads(),
             "kind": "oracle",
             "sample": (f"{len(rows)} seeded points j x all {w.M} i" if op in ("grad_y", "grad_b") else
+                       f"{len(rows)} seeded rows x their kept j ({pairs} pairs)" if op == "sum_ranges" else
                        f"{len(rows)} seeded rows x all {w.N} j") + f" (float64 C/OpenMP oracle), {t:.1f} s"}
     # the same rows double as a spot check of the GPU result
     check = None
     if op == "cg":
         check = None
-    elif op in ("sum", "grad_x", "grad_y", "grad_b"):
+    elif op in ("sum", "grad_x", "grad_y", "grad_b", "sum_ranges"):
         ref, nrm = res
         gpu = gpu_out[rows].reshape(ref.shape).astype(np.float64)
         check = {"rows": len(rows), "max_err_over_norm": float(np.max(np.abs(gpu - ref) / np.maximum(nrm, 1e-300)))}
@@ -235,6 +276,9 @@ def main():
     op, wname = BENCHES[args.workload]
     w = workloads.WORKLOADS[wname]
     x, y, b = workloads.make_inputs(w)
+    ranges, kept = None, None
+    if op == "sum_ranges":
+        x, y, b, ranges, kept = block_sparse_setup(x, y, b, w.sigma)
     dev = torch.device("cuda:0")
     X, Y = torch.from_numpy(x).to(dev), torch.from_numpy(y).to(dev)
     B = torch.from_numpy(b).to(dev) if b is not None else None
@@ -253,7 +297,7 @@ def main():
         out = torch.empty((w.M, w.D if op == "grad_x" else w.E), device=dev)
 
     for _ in range(args.warmup):
-        run_op(gm, op, X, Y, B, G, w.sigma, w.K, out, w.lam)
+        run_op(gm, op, X, Y, B, G, w.sigma, w.K, out, w.lam, ranges)
     torch.cuda.synchronize()
 
     gm.keops_set_option(gm.KEOPS_OPT_PROFILE, 1)
@@ -264,7 +308,7 @@ def main():
     ev0.record()
     solves = []
     for _ in range(args.steps):
-        solves.append(run_op(gm, op, X, Y, B, G, w.sigma, w.K, out, w.lam))
+        solves.append(run_op(gm, op, X, Y, B, G, w.sigma, w.K, out, w.lam, ranges))
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -281,6 +325,12 @@ def main():
         cg_info = {"iterations": iters, "rel_residual": float(solves[-1][2].max()), "rtol": CG_RTOL,
                    "products_per_solve": iters + 1}
         pairs = (iters + 1) * w.N * w.N
+    bs_info = None
+    if op == "sum_ranges":
+        # kept pairs only; the dense-equivalent rate is reported beside it
+        bs_info = {"voxel": BS_VOXEL, "eps": BS_EPS, "kept_pairs": kept, "kept_fraction": round(kept / pairs, 4),
+                   "dense_equivalent_G_pair_evals_per_s": round(pairs / (ms_step * 1e-3) / 1e9, 1)}
+        pairs = kept
     value = pairs / (ms_step * 1e-3) / 1e9
     bound, fpp, kname = roofline_of(op, w.M, w.D, w.E)
     kern_avg_ms = kern_ms / max(launches, 1)
@@ -318,9 +368,11 @@ def main():
     }
     if cg_info is not None:
         res["solver"] = cg_info
+    if bs_info is not None:
+        res["block_sparse"] = bs_info
     if not args.no_cpu_baseline:
         gpu_out = (out[0] if op == "kmin" else out).cpu().numpy()
-        base, check = cpu_baseline(op, w, x, y, b, g, args.cpu_seconds, gpu_out)
+        base, check = cpu_baseline(op, w, x, y, b, g, args.cpu_seconds, gpu_out, ranges)
         res["cpu_baseline"] = base
         if check is not None:
             res["check"] = check

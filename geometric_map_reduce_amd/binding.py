@@ -61,13 +61,17 @@ def lib() -> ctypes.CDLL:
             L.keops_gauss_grad_b.argtypes = [P, P, P, i64, i64, i32, i32, f32, P, P]
             L.keops_gauss_cg.argtypes = [P, P, i64, i32, i32, f32, f32, f32, i32, P,
                                          ctypes.POINTER(i32), ctypes.POINTER(f32), P]
+            L.keops_gauss_sum_ranges.argtypes = [P, P, P, i64, i64, i32, i32, f32, P, i64, P, P, i64, P, P]
+            L.keops_gauss_lse_ranges.argtypes = [P, P, P, i64, i64, i32, i32, f32, P, i64, P, P, i64, P, P]
+            L.keops_gauss_grad_x_ranges.argtypes = [P, P, P, P, i64, i64, i32, i32, f32, P, i64, P, P, i64, P, P]
             L.keops_kmin.argtypes = [P, P, i64, i64, i32, i32, P, P, P]
             L.keops_set_option.argtypes = [ctypes.c_int, i64]
             L.keops_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
             L.keops_status_string.argtypes = [ctypes.c_int]
             L.keops_status_string.restype = ctypes.c_char_p
             for f in ("keops_gauss_sum", "keops_gauss_lse", "keops_gauss_grad_x", "keops_gauss_grad_y",
-                      "keops_gauss_grad_b", "keops_gauss_cg", "keops_kmin",
+                      "keops_gauss_grad_b", "keops_gauss_cg", "keops_gauss_sum_ranges", "keops_gauss_lse_ranges",
+                      "keops_gauss_grad_x_ranges", "keops_kmin",
                       "keops_set_option", "keops_version", "keops_profile_read"):
                 getattr(L, f).restype = ctypes.c_int
             _lib = L
@@ -207,6 +211,61 @@ def keops_gauss_cg(x, b, sigma, lam, rtol=1e-5, max_iter=1000, out=None, stream=
                                   _ptr(out), ctypes.byref(it), res, _stream(stream, dev))
     _check("keops_gauss_cg", rc)
     return out, int(it.value), np.array(res[:E], np.float32)
+
+
+def _host_ranges(ranges_i, slices_i, redranges_j):
+    """The three range arrays as contiguous host int64 arrays (numpy or CPU tensors accepted)."""
+    import numpy as np
+
+    def arr(a, shape):
+        if isinstance(a, torch.Tensor):
+            a = a.detach().cpu().numpy()
+        return np.ascontiguousarray(np.asarray(a, dtype=np.int64).reshape(shape))
+    ri, si, rj = arr(ranges_i, (-1, 2)), arr(slices_i, (-1,)), arr(redranges_j, (-1, 2))
+    if si.shape[0] != ri.shape[0]:
+        raise ValueError("slices_i needs one entry per row range")
+    return ri, si, rj
+
+
+def _gauss_ranges(fn_name, x, y, b, sigma, ranges, out, stream, g=None):
+    x = _mat(x, "x")
+    dev = x.device
+    y, b = _mat(y, "y", dev), _mat(b, "b", dev)
+    M, D = x.shape
+    N, E = b.shape
+    if y.shape != (N, D):
+        raise ValueError(f"y must be [N, D] = [{N}, {D}], got {tuple(y.shape)}")
+    ri, si, rj = _host_ranges(*ranges)
+    args = [_ptr(x), _ptr(y), _ptr(b)]
+    if g is not None:
+        g = _mat(g, "g", dev)
+        if g.shape != (M, E):
+            raise ValueError(f"g must be [M, E] = [{M}, {E}]")
+        args.append(_ptr(g))
+    out = _out(out, (M, D if g is not None else E), dev)
+    hp = lambda a: a.ctypes.data_as(ctypes.c_void_p) if a.size else None  # noqa: E731
+    with torch.cuda.device(dev):
+        rc = getattr(lib(), fn_name)(*args, M, N, D, E, float(sigma), hp(ri), ri.shape[0], hp(si), hp(rj),
+                                     rj.shape[0], _ptr(out), _stream(stream, dev))
+    _check(fn_name, rc)
+    return out
+
+
+def keops_gauss_sum_ranges(x, y, b, sigma, ranges_i, slices_i, redranges_j, out=None, stream=None):
+    """Block-sparse keops_gauss_sum: row range c of ``ranges_i`` meets the j ranges
+    ``redranges_j[slices_i[c-1]:slices_i[c]]``; the ranges are host arrays."""
+    return _gauss_ranges("keops_gauss_sum_ranges", x, y, b, sigma, (ranges_i, slices_i, redranges_j), out, stream)
+
+
+def keops_gauss_lse_ranges(x, y, b, sigma, ranges_i, slices_i, redranges_j, out=None, stream=None):
+    """Block-sparse keops_gauss_lse (rows with no kept pair get -inf)."""
+    return _gauss_ranges("keops_gauss_lse_ranges", x, y, b, sigma, (ranges_i, slices_i, redranges_j), out, stream)
+
+
+def keops_gauss_grad_x_ranges(x, y, b, g, sigma, ranges_i, slices_i, redranges_j, out=None, stream=None):
+    """Block-sparse keops_gauss_grad_x."""
+    return _gauss_ranges("keops_gauss_grad_x_ranges", x, y, b, sigma, (ranges_i, slices_i, redranges_j), out,
+                         stream, g=g)
 
 
 def keops_kmin(x, y, K, out_d=None, out_idx=None, stream=None):

@@ -1,4 +1,4 @@
-// combine.hip -- pass 2 of the split-j reductions and the empty-N fills.
+// combine.hip -- pass 2 of the split-j reductions and the fills of empty results.
 //
 // With S splits of the j range, pass 1 leaves S partial results per row:
 //   sum / grad_x : partial sums,               combined as  sum_s p_s
@@ -76,6 +76,12 @@ __global__ __launch_bounds__(kThreads) void fill_kernel(float *__restrict__ out,
   if (t < count) out[t] = v;
 }
 
+// out[2t] = v0, out[2t + 1] = v1: the neutral (max, sum) pair of LogSumExp partials
+__global__ __launch_bounds__(kThreads) void fill2_kernel(float *__restrict__ out, int64_t pairs, float v0, float v1) {
+  const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (t < pairs) { out[2 * t] = v0; out[2 * t + 1] = v1; }
+}
+
 static inline unsigned blocks_for(int64_t n) { return (unsigned)((n + kThreads - 1) / kThreads); }
 
 void launch_sum_combine(const float *ws, int nsplit, int64_t count, float *out, hipStream_t st) {
@@ -100,6 +106,10 @@ int launch_kmin_combine(const float *pd, const int32_t *pi, int nsplit, int64_t 
 
 void launch_fill(float *out, int64_t count, float v, hipStream_t st) {
   if (count > 0) hipLaunchKernelGGL(fill_kernel, dim3(blocks_for(count)), dim3(kThreads), 0, st, out, count, v);
+}
+
+void launch_fill2(float *out, int64_t pairs, float v0, float v1, hipStream_t st) {
+  if (pairs > 0) hipLaunchKernelGGL(fill2_kernel, dim3(blocks_for(pairs)), dim3(kThreads), 0, st, out, pairs, v0, v1);
 }
 
 }  // namespace kmi

@@ -21,6 +21,18 @@ constexpr float kDirectOffset = 64.0f;
 enum Op : int { OP_SUM = 0, OP_LSE = 1, OP_GRAD = 2 };
 enum Form : int { FORM_AUTO = 0, FORM_DIRECT = 1 };
 
+// One work-group's share of a block-sparse launch: rows [row_lo, row_hi)
+// (inside one row range, at most the kernel's rows per work-group) against
+// the j ranges k0..k1 of that row range, the first starting at j0 and the
+// last ending before j1; its partial sums go to split slot `slot`.
+struct BsItem {
+  int64_t row_lo, row_hi;
+  int64_t k0, j0;
+  int64_t k1, j1;
+  int32_t slot;
+  int32_t pad;
+};
+
 // Arguments of the sum / LSE / grad_x pass-1 kernels.
 struct GaussArgs {
   const float *x, *y, *b, *g;
@@ -35,6 +47,10 @@ struct GaussArgs {
   // Per row-block form decisions of the MFMA kernel (1 = done there); when set,
   // the VALU kernel skips those blocks.  Null otherwise.
   int *wg_flags;
+  // Block-sparse launches: work item blockIdx.x and the [nrj][2] j ranges.
+  // Null for dense launches (rows from blockIdx.x, j from blockIdx.y).
+  const BsItem *items;
+  const int64_t *redr;
 };
 
 // Arguments of the few-rows sum kernel (j per lane, rows in LDS).

@@ -101,19 +101,19 @@ __device__ __forceinline__ void pair_exponent(const float (&xs)[R][D], const flo
   }
 }
 
-// The j loop of one work-group for a fixed form (FAST = expanded distance).
+// The j loop of one work-group over [jb, je) for a fixed form (FAST = expanded
+// distance).  Starts and ends with every wave past the LDS buffers, so calls
+// can follow each other (one per j range in block-sparse launches).
 template <int OP, int D, int E, int R, bool FAST>
 __device__ __forceinline__ void gauss_jloop(const GaussArgs &a,
                                             float4 (*sRec)[GaussShape<OP, D, E>::TJ * GaussShape<OP, D, E>::NV],
                                             float (*sPay)[GaussShape<OP, D, E>::PAY * GaussShape<OP, D, E>::TJ],
                                             const float (&xs)[R][D], const float (&gr)[R][E], const float (&cen)[D],
-                                            float G, float (&acc)[R][GaussShape<OP, D, E>::NACC]) {
+                                            float G, float (&acc)[R][GaussShape<OP, D, E>::NACC],
+                                            int64_t jb, int64_t je) {
   using S = GaussShape<OP, D, E>;
   constexpr int NV = S::NV, PAY = S::PAY, TJ = S::TJ, NP = S::NPART;
   const int tid = threadIdx.x;
-  const int64_t N = a.N;
-  const int64_t jb = (int64_t)blockIdx.y * a.j_per_split;
-  const int64_t je = (jb + a.j_per_split < N) ? jb + a.j_per_split : N;
   const float s2 = a.scale * a.scale;
   // exponent offset of the direct form (see the file comment); LSE tracks its own max
   const float off = (FAST || OP == OP_LSE) ? 0.0f : kDirectOffset;
@@ -310,7 +310,9 @@ __global__ __launch_bounds__(kThreads) void gauss_valu_kernel(GaussArgs a) {
 
   const int tid = threadIdx.x;
   const int wid = tid / kWave, lane = tid & (kWave - 1);
-  const int64_t row0 = (int64_t)blockIdx.x * (kThreads * R);
+  const BsItem *item = a.items ? a.items + blockIdx.x : nullptr;
+  const int64_t row0 = item ? item->row_lo : (int64_t)blockIdx.x * (kThreads * R);
+  const int64_t row_end = item ? item->row_hi : a.M;
   const int64_t M = a.M;
 
   // ---- rows (raw), bounding-box centre of the work-group
@@ -319,7 +321,7 @@ __global__ __launch_bounds__(kThreads) void gauss_valu_kernel(GaussArgs a) {
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int64_t i = row0 + (int64_t)r * kThreads + tid;
-    valid[r] = i < M;
+    valid[r] = i < row_end;
 #pragma unroll
     for (int k = 0; k < D; ++k) xs[r][k] = valid[r] ? a.x[i * D + k] : 0.0f;
   }
@@ -399,9 +401,22 @@ __global__ __launch_bounds__(kThreads) void gauss_valu_kernel(GaussArgs a) {
       for (int e = 0; e < E; ++e) acc[r][2 * e] = -3.0e38f;   // running max (finite: keeps u - m defined)
   }
 
-  // ---- the j loop, specialised on the form (uniform across the work-group)
-  if (fast) gauss_jloop<OP, D, E, R, true>(a, sRec, sPay, xs, gr, cen, G, acc);
-  else gauss_jloop<OP, D, E, R, false>(a, sRec, sPay, xs, gr, cen, G, acc);
+  // ---- the j loop, specialised on the form (uniform across the work-group):
+  // one j split of a dense launch, or the item's j ranges in order
+  if (!item) {
+    const int64_t jb = (int64_t)blockIdx.y * a.j_per_split;
+    const int64_t je = (jb + a.j_per_split < a.N) ? jb + a.j_per_split : a.N;
+    if (fast) gauss_jloop<OP, D, E, R, true>(a, sRec, sPay, xs, gr, cen, G, acc, jb, je);
+    else gauss_jloop<OP, D, E, R, false>(a, sRec, sPay, xs, gr, cen, G, acc, jb, je);
+  } else {
+    for (int64_t k = item->k0; k <= item->k1; ++k) {
+      const int64_t jb = k == item->k0 ? item->j0 : a.redr[2 * k];
+      const int64_t je = k == item->k1 ? item->j1 : a.redr[2 * k + 1];
+      if (jb >= je) continue;
+      if (fast) gauss_jloop<OP, D, E, R, true>(a, sRec, sPay, xs, gr, cen, G, acc, jb, je);
+      else gauss_jloop<OP, D, E, R, false>(a, sRec, sPay, xs, gr, cen, G, acc, jb, je);
+    }
+  }
 
   // ---- finalise and store
   const bool partial = a.nsplit > 1;
@@ -428,7 +443,8 @@ __global__ __launch_bounds__(kThreads) void gauss_valu_kernel(GaussArgs a) {
       for (int k = 0; k < D; ++k) res[k] = (f * acc[r][k]) * f2;
     }
     if (partial) {
-      float *dst = a.out + ((int64_t)blockIdx.y * M + i) * W;
+      const int64_t slot = item ? item->slot : blockIdx.y;
+      float *dst = a.out + (slot * M + i) * W;
 #pragma unroll
       for (int w = 0; w < W; ++w) dst[w] = res[w];
     } else if (OP == OP_LSE) {

@@ -313,6 +313,173 @@ int gauss_entry(int op, const float *x, const float *y, const float *b, const fl
   return check_launch();
 }
 
+// ---- block-sparse launches
+// Most split slots per row in a block-sparse launch.
+constexpr int64_t kMaxRangeSlots = 16;
+
+// Checks the host range arrays: row ranges inside [0, M) and pairwise disjoint,
+// slice ends non-decreasing up to nrj, j ranges inside [0, N).
+bool ranges_valid(int64_t M, int64_t N, const int64_t *ri, int64_t nri, const int64_t *si, const int64_t *rj,
+                  int64_t nrj) {
+  if (nri < 0 || nrj < 0 || (nri > 0 && (!ri || !si)) || (nrj > 0 && !rj)) return false;
+  std::vector<std::pair<int64_t, int64_t>> rows;
+  rows.reserve((size_t)nri);
+  int64_t prev = 0;
+  for (int64_t c = 0; c < nri; ++c) {
+    const int64_t lo = ri[2 * c], hi = ri[2 * c + 1];
+    if (lo < 0 || lo > hi || hi > M) return false;
+    if (si[c] < prev || si[c] > nrj) return false;
+    prev = si[c];
+    if (lo < hi) rows.emplace_back(lo, hi);
+  }
+  std::sort(rows.begin(), rows.end());
+  for (size_t c = 1; c < rows.size(); ++c)
+    if (rows[c].first < rows[c - 1].second) return false;
+  for (int64_t k = 0; k < nrj; ++k)
+    if (rj[2 * k] < 0 || rj[2 * k] > rj[2 * k + 1] || rj[2 * k + 1] > N) return false;
+  return true;
+}
+
+int gauss_ranges_entry(int op, const float *x, const float *y, const float *b, const float *g, int64_t M,
+                       int64_t N, int32_t D, int32_t E, float sigma, const int64_t *ranges_i, int64_t nri,
+                       const int64_t *slices_i, const int64_t *redranges_j, int64_t nrj, float *out, void *stream) {
+  // ---- validation (host only): the same rules as the dense calls, plus the ranges
+  if (M < 0 || N < 0 || D < 1 || E < 1) return KEOPS_ERR_INVALID_ARG;
+  if (!std::isfinite(sigma) || !(sigma > 0.0f)) return KEOPS_ERR_INVALID_ARG;
+  if (M > 0 && (!x || !out)) return KEOPS_ERR_INVALID_ARG;
+  if (N > 0 && (!y || !b)) return KEOPS_ERR_INVALID_ARG;
+  if (op == OP_GRAD && M > 0 && !g) return KEOPS_ERR_INVALID_ARG;
+  for (const void *p : {(const void *)x, (const void *)y, (const void *)b, (const void *)g, (const void *)out})
+    if (p && !aligned4(p)) return KEOPS_ERR_INVALID_ARG;
+  const int W = op == OP_GRAD ? D : E;
+  if (M > 0) {
+    const int64_t ob = M * W * 4;
+    if (overlaps(out, ob, x, M * D * 4) || overlaps(out, ob, y, N * D * 4) || overlaps(out, ob, b, N * E * 4) ||
+        (op == OP_GRAD && overlaps(out, ob, g, M * E * 4)))
+      return KEOPS_ERR_INVALID_ARG;
+  }
+  if (!ranges_valid(M, N, ranges_i, nri, slices_i, redranges_j, nrj)) return KEOPS_ERR_INVALID_ARG;
+  VariantInfo wide_info{}, narrow_info{};
+  GaussDispatch fn = nullptr;
+  if (gauss_find(op, D, E, 1, &wide_info, &fn) || gauss_find(op, D, E, 0, &narrow_info, &fn))
+    return KEOPS_ERR_UNSUPPORTED;
+  if (M == 0) return KEOPS_OK;
+
+  // ---- plan on the host: rows per work-group from the mean row-range size,
+  // j portions (split slots) from the kept pairs per row range
+  int64_t covered = 0, nonempty = 0;
+  double pairs = 0.0;
+  std::vector<int64_t> tj((size_t)nri, 0);
+  for (int64_t c = 0; c < nri; ++c) {
+    const int64_t len = ranges_i[2 * c + 1] - ranges_i[2 * c];
+    for (int64_t k = c == 0 ? 0 : slices_i[c - 1]; k < slices_i[c]; ++k) tj[c] += redranges_j[2 * k + 1] - redranges_j[2 * k];
+    if (len > 0 && tj[c] > 0) { covered += len; ++nonempty; pairs += (double)len * (double)tj[c]; }
+  }
+  hipStream_t st = (hipStream_t)stream;
+  (void)hipGetLastError();
+  const float empty = op == OP_LSE ? -INFINITY : 0.0f;
+  if (nonempty == 0) {
+    launch_fill(out, M * W, empty, st);
+    return check_launch();
+  }
+  int cus = 0;
+  if (int rc = device_setup(&cus)) return rc;
+  const bool wide = g_opt_rows.load() == 2 || (g_opt_rows.load() == 0 && covered / nonempty >= 2 * wide_info.rows_per_wg);
+  const int64_t rw = wide ? wide_info.rows_per_wg : narrow_info.rows_per_wg;
+  const int tile = wide_info.tile_j;
+  const int64_t target = g_opt_wg_target.load() > 0 ? g_opt_wg_target.load() : kGaussWgsPerCu;
+  // j per item: the kept pairs spread over ~target work-groups per CU, at least four tiles
+  const double jt = std::max(4.0 * tile, pairs / ((double)target * cus * (double)rw));
+  const int64_t forced = g_opt_split.load();
+  std::vector<BsItem> items;
+  int64_t smax = 1;
+  for (int64_t c = 0; c < nri; ++c) {
+    const int64_t lo = ranges_i[2 * c], hi = ranges_i[2 * c + 1];
+    if (lo >= hi || tj[c] == 0) continue;
+    const int64_t k0 = c == 0 ? 0 : slices_i[c - 1], k1 = slices_i[c];
+    int64_t sc = forced > 0 ? forced : (int64_t)std::ceil((double)tj[c] / jt);
+    sc = std::max<int64_t>(1, std::min(sc, std::min(kMaxRangeSlots, tj[c])));
+    smax = std::max(smax, sc);
+    // the flat position f of the row range's j list as (range k, j)
+    auto locate = [&](int64_t f, bool end, int64_t *kk, int64_t *jj) {
+      int64_t acc = 0;
+      for (int64_t k = k0; k < k1; ++k) {
+        const int64_t len = redranges_j[2 * k + 1] - redranges_j[2 * k];
+        if (f < acc + len || (end && f == acc + len && len > 0)) { *kk = k; *jj = redranges_j[2 * k] + (f - acc); return; }
+        acc += len;
+      }
+      *kk = k1 - 1;
+      *jj = redranges_j[2 * (k1 - 1) + 1];
+    };
+    for (int64_t s = 0; s < sc; ++s) {
+      const int64_t f0 = tj[c] * s / sc, f1 = tj[c] * (s + 1) / sc;
+      if (f0 >= f1) continue;
+      BsItem it{};
+      locate(f0, false, &it.k0, &it.j0);
+      locate(f1, true, &it.k1, &it.j1);
+      it.slot = (int32_t)s;
+      for (int64_t r = lo; r < hi; r += rw) {
+        it.row_lo = r;
+        it.row_hi = std::min(r + rw, hi);
+        items.push_back(it);
+      }
+    }
+  }
+  if (items.size() > 0x7fffffffu) return KEOPS_ERR_UNSUPPORTED;
+
+  // ---- workspace: items, j ranges, then (several slots) the partials
+  const int PW = op == OP_SUM ? E : (op == OP_LSE ? 2 * E : D);
+  const size_t ib = (items.size() * sizeof(BsItem) + 255) / 256 * 256;
+  const size_t rb = ((size_t)nrj * 2 * sizeof(int64_t) + 255) / 256 * 256;
+  const size_t pb = smax > 1 ? (size_t)smax * M * PW * sizeof(float) : 0;
+  char *ws = nullptr;
+  if (hipMallocAsync((void **)&ws, ib + rb + pb, st) != hipSuccess || !ws) {
+    (void)hipGetLastError();
+    return KEOPS_ERR_ALLOC;
+  }
+  std::vector<char> host(ib + rb);
+  std::memcpy(host.data(), items.data(), items.size() * sizeof(BsItem));
+  if (nrj > 0) std::memcpy(host.data() + ib, redranges_j, (size_t)nrj * 2 * sizeof(int64_t));
+  // the host copy must outlive the transfer: wait for it
+  if (hipMemcpyAsync(ws, host.data(), ib + rb, hipMemcpyHostToDevice, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess) {
+    (void)hipFreeAsync(ws, st);
+    return KEOPS_ERR_HIP;
+  }
+  float *part = smax > 1 ? (float *)(ws + ib + rb) : nullptr;
+  // rows outside every kept range (and slots a row range does not use) hold the empty reduction
+  if (smax > 1) {
+    if (op == OP_LSE) launch_fill2(part, smax * M * E, -3.0e38f, 0.0f, st);
+    else launch_fill(part, smax * M * PW, 0.0f, st);
+  } else {
+    launch_fill(out, M * W, empty, st);
+  }
+
+  const double s2 = (double)sigma * (double)sigma;
+  const double scale = std::sqrt(1.4426950408889634 / s2);
+  GaussArgs a{};
+  a.x = x; a.y = y; a.b = b; a.g = g;
+  a.M = M; a.N = N;
+  a.scale = (float)scale;
+  a.grad_coef = (float)(-2.0 / s2 / scale);
+  a.grad_coef_direct = (float)(-2.0 / s2);
+  a.j_per_split = 0;
+  a.nsplit = (int)smax;
+  a.form = g_opt_form.load() == 1 ? FORM_DIRECT : FORM_AUTO;
+  a.items = (const BsItem *)ws;
+  a.redr = (const int64_t *)(ws + ib);
+  a.out = smax > 1 ? part : out;
+  const int prof = prof_begin(st);
+  fn(D, E, wide ? 1 : 0, nullptr, dim3((unsigned)items.size(), 1), &a, st);
+  prof_end(prof, st);
+  if (smax > 1) {
+    if (op == OP_LSE) launch_lse_combine(part, (int)smax, M, E, out, st);
+    else launch_sum_combine(part, (int)smax, M * PW, out, st);
+  }
+  (void)hipFreeAsync(ws, st);
+  return check_launch();
+}
+
 }  // namespace
 }  // namespace kmi
 
@@ -437,6 +604,28 @@ int keops_gauss_cg(const float *x, const float *b, int64_t N, int32_t D, int32_t
   if (rc == KEOPS_OK) rc = check_launch();
   if (rc == KEOPS_OK && hipStreamSynchronize(st) != hipSuccess) rc = KEOPS_ERR_HIP;
   return rc;
+}
+
+int keops_gauss_sum_ranges(const float *x, const float *y, const float *b, int64_t M, int64_t N, int32_t D,
+                           int32_t E, float sigma, const int64_t *ranges_i, int64_t nri, const int64_t *slices_i,
+                           const int64_t *redranges_j, int64_t nrj, float *out, void *stream) {
+  return gauss_ranges_entry(OP_SUM, x, y, b, nullptr, M, N, D, E, sigma, ranges_i, nri, slices_i, redranges_j, nrj,
+                            out, stream);
+}
+
+int keops_gauss_lse_ranges(const float *x, const float *y, const float *b, int64_t M, int64_t N, int32_t D,
+                           int32_t E, float sigma, const int64_t *ranges_i, int64_t nri, const int64_t *slices_i,
+                           const int64_t *redranges_j, int64_t nrj, float *out, void *stream) {
+  return gauss_ranges_entry(OP_LSE, x, y, b, nullptr, M, N, D, E, sigma, ranges_i, nri, slices_i, redranges_j, nrj,
+                            out, stream);
+}
+
+int keops_gauss_grad_x_ranges(const float *x, const float *y, const float *b, const float *g, int64_t M, int64_t N,
+                              int32_t D, int32_t E, float sigma, const int64_t *ranges_i, int64_t nri,
+                              const int64_t *slices_i, const int64_t *redranges_j, int64_t nrj, float *out,
+                              void *stream) {
+  return gauss_ranges_entry(OP_GRAD, x, y, b, g, M, N, D, E, sigma, ranges_i, nri, slices_i, redranges_j, nrj, out,
+                            stream);
 }
 
 int keops_kmin(const float *x, const float *y, int64_t M, int64_t N, int32_t D, int32_t K, float *out_d,

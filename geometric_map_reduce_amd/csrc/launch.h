@@ -45,6 +45,7 @@ void launch_lse_combine(const float *ws, int nsplit, int64_t M, int E, float *ou
 int launch_kmin_combine(const float *pd, const int32_t *pi, int nsplit, int64_t M, int K, float *out_d,
                         int64_t *out_i, hipStream_t st);
 void launch_fill(float *out, int64_t count, float v, hipStream_t st);
+void launch_fill2(float *out, int64_t pairs, float v0, float v1, hipStream_t st);
 void launch_stream_combine(const float *part, int nparts, int64_t count, float *out, hipStream_t st);
 
 // Conjugate-gradient vector kernels (E <= 4 columns).  Each launcher that

@@ -111,6 +111,42 @@ int keops_gauss_grad_b(const float *x, const float *y, const float *g,
                        float *out, void *stream);
 
 /*
+ * Block-sparse reductions ([KO-GPU] §3 "Applications": cluster-wise
+ * block-sparsity for large kernel linear systems, §4: the block-sparse
+ * truncation rule; [README] feature list: an interface for block-sparse
+ * strategies).  Only the kept pairs (i, j) enter the reduction; they are given
+ * as ranges over rows and points, typically of points sorted by cluster:
+ *   ranges_i    [nri][2]  row range c = [ranges_i[c][0], ranges_i[c][1]); row
+ *                         ranges must not overlap;
+ *   slices_i    [nri]     end (exclusive) in redranges_j of row range c's j
+ *                         ranges, non-decreasing; they start at slices_i[c-1]
+ *                         (0 for c = 0);
+ *   redranges_j [nrj][2]  j range k = [redranges_j[k][0], redranges_j[k][1])
+ *                         inside [0, N).
+ * Row i in row range c reduces over the j of its ranges, in the listed order
+ * (a j listed twice counts twice); rows in no row range get the empty
+ * reduction (0, or -inf for LogSumExp).  The three arrays are HOST arrays of
+ * int64 (the library validates them and plans the launch on the host, then
+ * copies what the kernels need); x, y, b, g, out are device arrays as above.
+ * These calls synchronise `stream` once, after that copy.  Any invalid range
+ * (out of bounds, overlapping row ranges, decreasing slices) returns
+ * KEOPS_ERR_INVALID_ARG before any device work.
+ *   keops_gauss_sum_ranges:    out [M, E] as keops_gauss_sum over the kept pairs
+ *   keops_gauss_lse_ranges:    out [M, E] as keops_gauss_lse over the kept pairs
+ *   keops_gauss_grad_x_ranges: out [M, D] as keops_gauss_grad_x over the kept pairs
+ */
+int keops_gauss_sum_ranges(const float *x, const float *y, const float *b, int64_t M, int64_t N, int32_t D,
+                           int32_t E, float sigma, const int64_t *ranges_i, int64_t nri, const int64_t *slices_i,
+                           const int64_t *redranges_j, int64_t nrj, float *out, void *stream);
+int keops_gauss_lse_ranges(const float *x, const float *y, const float *b, int64_t M, int64_t N, int32_t D,
+                           int32_t E, float sigma, const int64_t *ranges_i, int64_t nri, const int64_t *slices_i,
+                           const int64_t *redranges_j, int64_t nrj, float *out, void *stream);
+int keops_gauss_grad_x_ranges(const float *x, const float *y, const float *b, const float *g, int64_t M, int64_t N,
+                              int32_t D, int32_t E, float sigma, const int64_t *ranges_i, int64_t nri,
+                              const int64_t *slices_i, const int64_t *redranges_j, int64_t nrj, float *out,
+                              void *stream);
+
+/*
  * Conjugate-gradient solve of (K + lambda I) a = b with the Gaussian kernel
  * matrix of one point set, K_ij = exp(-|x_i - x_j|^2/sigma^2) ([README] feature
  * list: a conjugate gradient solver for spline interpolation, kriging or

@@ -47,7 +47,8 @@ def check_sum(a_gpu, a_ref, n_ref, rtol=SUM_RTOL, what="sum"):
 def check_lse(l_gpu, l_ref, atol=LSE_ATOL, rtol=LSE_RTOL):
     l_gpu = np.asarray(l_gpu, np.float64).reshape(l_ref.shape)
     both_inf = np.isneginf(l_gpu) & np.isneginf(l_ref)
-    err = np.where(both_inf, 0.0, np.abs(l_gpu - l_ref))
+    with np.errstate(invalid="ignore"):
+        err = np.where(both_inf, 0.0, np.abs(l_gpu - l_ref))
     bad = ~(err <= atol + rtol * np.where(both_inf, 0.0, np.abs(l_ref)))
     assert not bad.any(), f"lse: {bad.sum()} outside tol; max err {np.nanmax(err):.3g}"
     return float(err.max()) if err.size else 0.0

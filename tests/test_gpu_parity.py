@@ -240,6 +240,112 @@ def test_cg_edge_cases():
     assert iters == 1
 
 
+def _composed_reference(x, y, b, g, sigma, ri, si, rj, rows, op):
+    """Oracle values of the block-sparse reduction at ``rows``: for each row range, the dense
+    oracle over the concatenation of its j ranges (the definition restricted to kept pairs)."""
+    M = x.shape[0]
+    W = x.shape[1] if op == "grad" else b.shape[1]
+    ref = np.zeros((len(rows), W))
+    nu = np.zeros((len(rows), W))
+    if op == "lse":
+        ref[:] = -np.inf
+    owner = np.full(M, -1)
+    for c, (lo, hi) in enumerate(ri):
+        owner[lo:hi] = c
+    for c in range(len(ri)):
+        sel = np.flatnonzero(owner[rows] == c)
+        if not sel.size:
+            continue
+        J = np.concatenate([np.arange(a, e) for a, e in rj[(si[c - 1] if c else 0):si[c]]] + [np.zeros(0, np.int64)])
+        if not J.size:
+            continue
+        r = rows[sel]
+        if op == "sum":
+            ref[sel], nu[sel] = oracle.gauss_sum(x, y[J], b[J], sigma, rows=r)
+        elif op == "lse":
+            ref[sel] = oracle.gauss_lse(x, y[J], b[J], sigma, rows=r)
+        else:
+            ref[sel], nu[sel] = oracle.gauss_grad_x(x, y[J], b[J], g, sigma, rows=r)
+    return ref, nu
+
+
+@pytest.mark.parametrize("form", [0, 1], ids=["auto", "direct"])
+@pytest.mark.parametrize("split", [0, 1, 3])
+@pytest.mark.parametrize("rows", [1, 2], ids=["narrow", "wide"])
+def test_ranges_random(form, split, rows):
+    """Random row ranges (with gaps) meeting random, possibly repeated, j ranges."""
+    from oracle_pins import random_ranges
+    say(f"ranges form={form} split={split} rows={rows}")
+    for (M, N, D, E, sigma, nr) in [(700, 900, 3, 1, 0.6, 9), (3000, 2500, 3, 2, 0.4, 6), (257, 4100, 5, 1, 1.1, 4),
+                                    (1, 1, 1, 1, 1.0, 1), (5000, 300, 2, 3, 0.8, 3)]:
+        rng = np.random.default_rng(M + N + 17 * split)
+        x, y, b, g = rand_case(M + N, M, N, D, E)
+        ri, si, rj, _ = random_ranges(rng, M, N, nr, 4)
+        X, Y, B, G = dev(x), dev(y), dev(b), dev(g)
+        gm.keops_set_option(gm.KEOPS_OPT_FORM, form)
+        gm.keops_set_option(gm.KEOPS_OPT_SPLIT_J, split)
+        gm.keops_set_option(gm.KEOPS_OPT_ROWS, rows)
+        a = host(gm.keops_gauss_sum_ranges(X, Y, B, sigma, ri, si, rj))
+        l = host(gm.keops_gauss_lse_ranges(X, Y, B, sigma, ri, si, rj))
+        gx = host(gm.keops_gauss_grad_x_ranges(X, Y, B, G, sigma, ri, si, rj))
+        a_ref, n_ref = oracle.gauss_sum_ranges(x, y, b, sigma, ri, si, rj)
+        check_sum(a, a_ref, n_ref, what="sum_ranges")
+        check_lse(l, oracle.gauss_lse_ranges(x, y, b, sigma, ri, si, rj))
+        G_ref, nu = _composed_reference(x, y, b, g, sigma, ri, si, rj, np.arange(M), "grad")
+        check_grad(gx, G_ref, nu)
+
+
+def test_ranges_cover_all_equals_dense():
+    say("ranges covering every pair")
+    x, y, b, g = rand_case(5, 2100, 1900, 3, 2)
+    X, Y, B = dev(x), dev(y), dev(b)
+    ri = np.array([[0, 700], [700, 2100]])
+    si = np.array([2, 3])
+    rj = np.array([[0, 1000], [1000, 1900], [0, 1900]])
+    a = host(gm.keops_gauss_sum_ranges(X, Y, B, 0.5, ri, si, rj))
+    a_ref, n_ref = oracle.gauss_sum(x, y, b, 0.5)
+    check_sum(a, a_ref, n_ref)
+    l = host(gm.keops_gauss_lse_ranges(X, Y, B, 0.5, ri, si, rj))
+    check_lse(l, oracle.gauss_lse(x, y, b, 0.5))
+    # no kept pair at all: 0 and -inf everywhere
+    a0 = host(gm.keops_gauss_sum_ranges(X, Y, B, 0.5, ri, [0, 0], np.zeros((0, 2))))
+    l0 = host(gm.keops_gauss_lse_ranges(X, Y, B, 0.5, ri, [0, 0], np.zeros((0, 2))))
+    assert not a0.any() and np.isneginf(l0).all()
+
+
+def _grid_ranges(x, y, voxel, sigma, eps):
+    from geometric_map_reduce_amd import blocksparse as bs
+    lx, ly = bs.grid_cluster(x, voxel), bs.grid_cluster(y, voxel)
+    px, py = bs.sort_by_cluster(lx), bs.sort_by_cluster(ly)
+    rx, cx, radx = bs.cluster_ranges_centroids(x[px], lx[px])
+    ry, cy, rady = bs.cluster_ranges_centroids(y[py], ly[py])
+    mask = bs.truncation_mask(cx, radx, cy, rady, bs.cutoff_for(sigma, eps))
+    return px, py, bs.ranges_from_mask(mask, rx, ry), mask
+
+
+def test_ranges_grid_truncation_1M():
+    """M = N = 1e6 (D = 3, sigma = 0.1, U[0,1)^3) sorted into voxels of 0.1 with the eps = 1e-5
+    truncation mask: sampled rows against the oracle over their kept pairs, and the truncation
+    error against the dense oracle within eps * sum_j |b_j|."""
+    w = workloads.WORKLOADS["sum_lse_1M"]
+    say("block-sparse sum_lse_1M, voxel 0.1, eps 1e-5")
+    x, y, b = workloads.make_inputs(w)
+    px, py, (ri, si, rj), mask = _grid_ranges(x, y, 0.1, w.sigma, 1e-5)
+    xs, ys, bs_ = x[px], y[py], b[py]
+    X, Y, B = dev(xs), dev(ys), dev(bs_)
+    a = host(gm.keops_gauss_sum_ranges(X, Y, B, w.sigma, ri, si, rj))
+    l = host(gm.keops_gauss_lse_ranges(X, Y, B, w.sigma, ri, si, rj))
+    rows = _sample(w.M, 256)
+    a_ref, n_ref = _composed_reference(xs, ys, bs_, None, w.sigma, ri, si, rj, rows, "sum")
+    check_sum(a[rows], a_ref, n_ref, what="sum_ranges")
+    l_ref, _ = _composed_reference(xs, ys, bs_, None, w.sigma, ri, si, rj, rows, "lse")
+    check_lse(l[rows], l_ref)
+    full, _ = oracle.gauss_sum(xs, ys, bs_, w.sigma, rows=rows)
+    bound = 1e-5 * np.abs(b.astype(np.float64)).sum() + 1e-4 * n_ref
+    assert np.all(np.abs(a[rows] - full) <= bound)
+    say(f"  kept cluster pairs {mask.mean():.3f}; worst truncation error {np.abs(a[rows] - full).max():.3g}")
+
+
 KMIN_SMALL = [(1, 1, 1, 1), (5, 40, 3, 10), (300, 1000, 3, 10), (257, 513, 2, 16), (100, 3000, 4, 32),
               (70, 600, 8, 7), (64, 300, 16, 5), (40, 500, 32, 10), (30, 200, 50, 3), (25, 300, 64, 10),
               (10, 128, 100, 2), (200, 900, 5, 1), (129, 129, 3, 12)]
