@@ -65,6 +65,7 @@ def open_library(path: str):
     lib.oracle_kmin.argtypes = [P, P, i64, i64, i32, i32, P, i64, P, P]
     lib.oracle_sq_dist_pairs.argtypes = [P, P, i32, P, P, i64, P]
     lib.oracle_gauss_matrix.argtypes = [P, P, i64, i64, i32, f64, P]
+    lib.oracle_gauss_max.argtypes = [P, P, P, i64, i64, i32, i32, f64, i32, P, i64, P, P]
     lib.oracle_gauss_sum_ranges.argtypes = [P, P, P, i64, i64, i32, i32, f64, P, i64, P, P, i64, P, P]
     lib.oracle_gauss_lse_ranges.argtypes = [P, P, P, i64, i64, i32, i32, f64, P, i64, P, P, i64, P]
     for f in ("oracle_gauss_sum", "oracle_gauss_lse", "oracle_gauss_grad_x", "oracle_gauss_grad_y",
@@ -295,4 +296,20 @@ def gauss_lse_ranges(x, y, b, sigma, ranges_i, slices_i, redranges_j, lib=None):
                                            _ptr(ri), ri.shape[0], _ptr(si), _ptr(rj), rj.shape[0],
                                            _ptr(out)), "gauss_lse_ranges")
     return out
+
+
+def gauss_max(x, y, b, sigma, sign=1, rows=None, lib=None):
+    """max_j sign * K_ij b_je and the smallest j reaching it, per row and column: sign = +1 is
+    Max / ArgMax of K b, sign = -1 is -(Min) / ArgMin.  Returns (values float64, indices int64);
+    N = 0 gives -inf and -1."""
+    x, y, b = _f32(x, 2), _f32(y, 2), _f32(b, 2)
+    M, D = x.shape
+    N, E = b.shape
+    assert y.shape == (N, D)
+    r, n = _rows(rows, M)
+    out = np.empty((n, E), np.float64)
+    idx = np.empty((n, E), np.int64)
+    _check((lib or _load()).oracle_gauss_max(_ptr(x), _ptr(y), _ptr(b), M, N, D, E, float(sigma), int(sign),
+                                    _ptr(r), n, _ptr(out), _ptr(idx)), "gauss_max")
+    return out, idx
 

@@ -390,3 +390,31 @@ int oracle_gauss_lse_ranges(const float *x, const float *y, const float *b,
     return 0;
 }
 
+/*
+ * Max / ArgMax reduction of the kernel product ([KO-GPU] §2 reductions list
+ * "sum, max, argmin, and log-sum-exp"; [README] feature list "Sum, LogSumExp,
+ * Min, Max but also ArgMin, ArgMax").  For row i and column e:
+ *   out_ie = max_j  sgn * K_ij b_je,  idx_ie = the smallest j reaching it,
+ * so sgn = +1 is Max / ArgMax of K b and sgn = -1 gives -(Min / ArgMin of
+ * K b).  N = 0 gives -inf and index -1.  The comparison is in double.
+ */
+int oracle_gauss_max(const float *x, const float *y, const float *b,
+                     int64_t M, int64_t N, int D, int E, double sigma, int sgn,
+                     const int64_t *rows, int64_t nrows, double *out, int64_t *idx) {
+    if (check_common(M, N, D, nrows, rows) || E < 1 || !(sigma > 0.0) || (sgn != 1 && sgn != -1)) return -1;
+    const double inv_s2 = 1.0 / (sigma * sigma);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t i = rows ? rows[r] : r;
+        for (int e = 0; e < E; ++e) { out[r * E + e] = -INFINITY; idx[r * E + e] = -1; }
+        for (int64_t j = 0; j < N; ++j) {
+            const double k = exp(-sq_dist(x + i * D, y + j * D, D) * inv_s2);
+            for (int e = 0; e < E; ++e) {
+                const double v = (double)sgn * k * (double)b[j * E + e];
+                if (v > out[r * E + e]) { out[r * E + e] = v; idx[r * E + e] = j; }
+            }
+        }
+    }
+    return 0;
+}
+

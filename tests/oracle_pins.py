@@ -501,6 +501,30 @@ def pin_ranges_dense_and_split(lib=None):
     assert np.isneginf(oracle.gauss_lse_ranges(x, y, b, 0.9, [[2, 5]], [0], np.zeros((0, 2)), lib=lib)).all()
 
 
+# --------------------------------------------------------------------------- max / argmax
+def pin_max_brute(lib=None):
+    """Max/ArgMax and Min/ArgMin of K b equal numpy's on the materialised product (first index
+    on ties, forced with duplicated points and payloads); N = 0 gives -inf and -1."""
+    rng = np.random.default_rng(81)
+    for (M, N, D, E) in SHAPES:
+        sigma = 0.9 * math.sqrt(D)
+        x = rng.standard_normal((M, D)).astype(np.float32)
+        y = rng.standard_normal((N, D)).astype(np.float32)
+        b = rng.standard_normal((N, E)).astype(np.float32)
+        if N >= 4:
+            y[N - 1], b[N - 1] = y[0], b[0]          # exact ties: the smaller index wins
+        P = brute_K(x, y, sigma)[:, :, None] * b.astype(np.float64)[None, :, :]
+        v, i = oracle.gauss_max(x, y, b, sigma, 1, lib=lib)
+        assert np.array_equal(i, P.argmax(1))
+        rel_close(v, P.max(1), 1e-13)
+        v, i = oracle.gauss_max(x, y, b, sigma, -1, lib=lib)
+        assert np.array_equal(i, P.argmin(1))
+        rel_close(-v, P.min(1), 1e-13)
+    v, i = oracle.gauss_max(np.zeros((3, 2), np.float32), np.zeros((0, 2), np.float32), np.zeros((0, 1), np.float32),
+                            1.0, lib=lib)
+    assert np.isneginf(v).all() and (i == -1).all()
+
+
 # --------------------------------------------------------------------------- kmin
 def pin_kmin_argsort(lib=None):
     """K-min equals a stable argsort of the materialised distances (ties -> smaller j)."""

@@ -63,6 +63,8 @@ MUTANTS = {
     "ranges_j_end": ("for (int64_t j = redranges_j[2 * k]; j < redranges_j[2 * k + 1]; ++j) {\n                    const double kv",
                      "for (int64_t j = redranges_j[2 * k]; j + 1 < redranges_j[2 * k + 1]; ++j) {\n                    const double kv"),
     "ranges_lse_drop_max": ("out[i * E + e] = m + log(s);", "out[i * E + e] = log(s);"),
+    "max_ties_last": ("if (v > out[r * E + e]) { out[r * E + e] = v;", "if (v >= out[r * E + e]) { out[r * E + e] = v;"),
+    "max_no_sign": ("const double v = (double)sgn * k * (double)b[j * E + e];", "const double v = k * (double)b[j * E + e];"),
     "kmin_tie_break": ("(dj == bd[pos - 1] && j < bj[pos - 1])", "(dj == bd[pos - 1] && j > bj[pos - 1])"),
     "kmin_keep_last": ("if (count == K && !(dj < bd[K - 1]", "if (count == K && !(dj <= bd[K - 1]"),
 }
