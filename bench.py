@@ -55,6 +55,7 @@ BENCHES = {
     "stream": ("sum", "stream_16_x_100M"),
     "cg": ("cg", "krige_100k"),
     "sum_bs": ("sum_ranges", "sum_lse_1M"),
+    "max": ("max", "sum_lse_1M"),
 }
 BS_VOXEL, BS_EPS = 0.1, 1e-5       # block-sparse bench: voxel side and truncation threshold
 CG_RTOL = 1e-4
@@ -63,7 +64,8 @@ STREAM_MAX_ROWS = 64              # the library's few-rows layout (j per lane) f
 
 
 def flops_per_pair(op, D, E):
-    return {"sum": 3 * D + 1 + 2 * E, "cg": 3 * D + 1 + 2 * E, "sum_ranges": 3 * D + 1 + 2 * E, "lse": 3 * D + 5, "grad_x": 5 * D + 2 * E + 1, "grad_y": 5 * D + 2 * E + 1,
+    return {"sum": 3 * D + 1 + 2 * E, "cg": 3 * D + 1 + 2 * E, "sum_ranges": 3 * D + 1 + 2 * E,
+            "max": 3 * D + 1 + 2 * E, "lse": 3 * D + 5, "grad_x": 5 * D + 2 * E + 1, "grad_y": 5 * D + 2 * E + 1,
             "grad_b": 3 * D + 1 + 2 * E, "kmin": 3 * D}[op]
 
 
@@ -136,6 +138,8 @@ def run_op(gm, op, X, Y, B, G, sigma, K, out, lam=0.0, ranges=None):
         return gm.keops_gauss_cg(X, B, sigma, lam, rtol=CG_RTOL, max_iter=1000, out=out)
     if op == "sum":
         return gm.keops_gauss_sum(X, Y, B, sigma, out=out)
+    if op == "max":
+        return gm.keops_gauss_max(X, Y, B, sigma, out=out[0], out_idx=out[1])
     if op == "lse":
         return gm.keops_gauss_lse(X, Y, B, sigma, out=out)
     if op == "grad_x":
@@ -186,6 +190,8 @@ def cpu_baseline(op, w, x, y, b, g, target_s, gpu_out, ranges=None):
             return time.perf_counter() - t0, res
         if op == "sum":
             res = oracle.gauss_sum(x, y, b, w.sigma, rows=rows)
+        elif op == "max":
+            res = oracle.gauss_max(x, y, b, w.sigma, 1, rows=rows)
         elif op == "cg":        # the solver's work is its products K p: the sum oracle on x
             res = oracle.gauss_sum(x, x, b, w.sigma, rows=rows)
         elif op == "lse":
@@ -225,6 +231,10 @@ def cpu_baseline(op, w, x, y, b, g, target_s, gpu_out, ranges=None):
     check = None
     if op == "cg":
         check = None
+    elif op == "max":
+        ref, _ = res
+        gpu = gpu_out[rows].reshape(ref.shape).astype(np.float64)
+        check = {"rows": len(rows), "max_rel_err": float(np.max(np.abs(gpu - ref) / np.maximum(np.abs(ref), 1e-300)))}
     elif op in ("sum", "grad_x", "grad_y", "grad_b", "sum_ranges"):
         ref, nrm = res
         gpu = gpu_out[rows].reshape(ref.shape).astype(np.float64)
@@ -291,6 +301,8 @@ def main():
         out = (torch.empty((w.M, w.K), device=dev), torch.empty((w.M, w.K), device=dev, dtype=torch.int64))
     elif op == "cg":
         out = torch.empty((w.N, w.E), device=dev)
+    elif op == "max":
+        out = (torch.empty((w.M, w.E), device=dev), torch.empty((w.M, w.E), device=dev, dtype=torch.int64))
     elif op in ("grad_y", "grad_b"):
         out = torch.empty((w.N, w.D if op == "grad_y" else w.E), device=dev)
     else:
@@ -371,7 +383,7 @@ def main():
     if bs_info is not None:
         res["block_sparse"] = bs_info
     if not args.no_cpu_baseline:
-        gpu_out = (out[0] if op == "kmin" else out).cpu().numpy()
+        gpu_out = (out[0] if op in ("kmin", "max") else out).cpu().numpy()
         base, check = cpu_baseline(op, w, x, y, b, g, args.cpu_seconds, gpu_out, ranges)
         res["cpu_baseline"] = base
         if check is not None:

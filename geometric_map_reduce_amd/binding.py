@@ -64,6 +64,8 @@ def lib() -> ctypes.CDLL:
             L.keops_gauss_sum_ranges.argtypes = [P, P, P, i64, i64, i32, i32, f32, P, i64, P, P, i64, P, P]
             L.keops_gauss_lse_ranges.argtypes = [P, P, P, i64, i64, i32, i32, f32, P, i64, P, P, i64, P, P]
             L.keops_gauss_grad_x_ranges.argtypes = [P, P, P, P, i64, i64, i32, i32, f32, P, i64, P, P, i64, P, P]
+            L.keops_gauss_max.argtypes = [P, P, P, i64, i64, i32, i32, f32, P, P, P]
+            L.keops_gauss_min.argtypes = [P, P, P, i64, i64, i32, i32, f32, P, P, P]
             L.keops_kmin.argtypes = [P, P, i64, i64, i32, i32, P, P, P]
             L.keops_set_option.argtypes = [ctypes.c_int, i64]
             L.keops_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
@@ -71,7 +73,7 @@ def lib() -> ctypes.CDLL:
             L.keops_status_string.restype = ctypes.c_char_p
             for f in ("keops_gauss_sum", "keops_gauss_lse", "keops_gauss_grad_x", "keops_gauss_grad_y",
                       "keops_gauss_grad_b", "keops_gauss_cg", "keops_gauss_sum_ranges", "keops_gauss_lse_ranges",
-                      "keops_gauss_grad_x_ranges", "keops_kmin",
+                      "keops_gauss_grad_x_ranges", "keops_gauss_max", "keops_gauss_min", "keops_kmin",
                       "keops_set_option", "keops_version", "keops_profile_read"):
                 getattr(L, f).restype = ctypes.c_int
             _lib = L
@@ -266,6 +268,33 @@ def keops_gauss_grad_x_ranges(x, y, b, g, sigma, ranges_i, slices_i, redranges_j
     """Block-sparse keops_gauss_grad_x."""
     return _gauss_ranges("keops_gauss_grad_x_ranges", x, y, b, sigma, (ranges_i, slices_i, redranges_j), out,
                          stream, g=g)
+
+
+def _gauss_extremum(fn_name, x, y, b, sigma, out, out_idx, stream):
+    x = _mat(x, "x")
+    dev = x.device
+    y, b = _mat(y, "y", dev), _mat(b, "b", dev)
+    M, D = x.shape
+    N, E = b.shape
+    if y.shape != (N, D):
+        raise ValueError(f"y must be [N, D] = [{N}, {D}], got {tuple(y.shape)}")
+    out = _out(out, (M, E), dev)
+    out_idx = _out(out_idx, (M, E), dev, dtype=torch.int64, name="out_idx")
+    with torch.cuda.device(dev):
+        rc = getattr(lib(), fn_name)(_ptr(x), _ptr(y), _ptr(b), M, N, D, E, float(sigma), _ptr(out), _ptr(out_idx),
+                                     _stream(stream, dev))
+    _check(fn_name, rc)
+    return out, out_idx
+
+
+def keops_gauss_max(x, y, b, sigma, out=None, out_idx=None, stream=None):
+    """(max_j K_ij b[j, e], its j) per row and column (ties: smaller j)."""
+    return _gauss_extremum("keops_gauss_max", x, y, b, sigma, out, out_idx, stream)
+
+
+def keops_gauss_min(x, y, b, sigma, out=None, out_idx=None, stream=None):
+    """(min_j K_ij b[j, e], its j) per row and column (ties: smaller j)."""
+    return _gauss_extremum("keops_gauss_min", x, y, b, sigma, out, out_idx, stream)
 
 
 def keops_kmin(x, y, K, out_d=None, out_idx=None, stream=None):

@@ -4,7 +4,8 @@
 //   sum / grad_x : partial sums,               combined as  sum_s p_s
 //   LogSumExp    : (m_s, s_s) in log2 units,   combined as  m = max_s m_s,
 //                  s = sum_s s_s 2^(m_s - m),  out = ln2 (m + log2 s)
-//   K-min        : sorted (d^2, j) lists,      merged by (d^2, j) order.
+//   K-min        : sorted (d^2, j) lists,      merged by (d^2, j) order;
+//   Max/ArgMax   : (value, j) pairs,           the largest value, then the smaller j.
 // Splits are visited in order, so results do not depend on scheduling.
 #include "common.h"
 #include "launch.h"
@@ -76,6 +77,33 @@ __global__ __launch_bounds__(kThreads) void fill_kernel(float *__restrict__ out,
   if (t < count) out[t] = v;
 }
 
+// Max/ArgMax: for row i, column e, the split with the largest signed value
+// (NaN never wins), the smaller index among equal values; splits in order.
+__global__ __launch_bounds__(kThreads) void max_combine_kernel(const float *__restrict__ ws, int nsplit, int64_t M,
+                                                               int E, float sign, float *__restrict__ out,
+                                                               int64_t *__restrict__ out_idx) {
+  const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (t >= M * E) return;
+  const int64_t i = t / E;
+  const int e = (int)(t - i * E);
+  const int64_t stride = M * 2 * E;
+  const float *p = ws + i * 2 * E + 2 * e;
+  float best = -INFINITY;
+  int bi = -1;
+  for (int k = 0; k < nsplit; ++k) {
+    const float v = p[k * stride];
+    const int j = __float_as_int(p[k * stride + 1]);
+    if (j >= 0 && (v > best || (v == best && (bi < 0 || j < bi)))) { best = v; bi = j; }
+  }
+  out[t] = sign * best;
+  out_idx[t] = (int64_t)bi;
+}
+
+__global__ __launch_bounds__(kThreads) void fill_i64_kernel(int64_t *__restrict__ out, int64_t count, int64_t v) {
+  const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (t < count) out[t] = v;
+}
+
 // out[2t] = v0, out[2t + 1] = v1: the neutral (max, sum) pair of LogSumExp partials
 __global__ __launch_bounds__(kThreads) void fill2_kernel(float *__restrict__ out, int64_t pairs, float v0, float v1) {
   const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
@@ -106,6 +134,17 @@ int launch_kmin_combine(const float *pd, const int32_t *pi, int nsplit, int64_t 
 
 void launch_fill(float *out, int64_t count, float v, hipStream_t st) {
   if (count > 0) hipLaunchKernelGGL(fill_kernel, dim3(blocks_for(count)), dim3(kThreads), 0, st, out, count, v);
+}
+
+void launch_max_combine(const float *ws, int nsplit, int64_t M, int E, float sign, float *out, int64_t *out_idx,
+                        hipStream_t st) {
+  if (M * E > 0)
+    hipLaunchKernelGGL(max_combine_kernel, dim3(blocks_for(M * E)), dim3(kThreads), 0, st, ws, nsplit, M, E, sign,
+                       out, out_idx);
+}
+
+void launch_fill_i64(int64_t *out, int64_t count, int64_t v, hipStream_t st) {
+  if (count > 0) hipLaunchKernelGGL(fill_i64_kernel, dim3(blocks_for(count)), dim3(kThreads), 0, st, out, count, v);
 }
 
 void launch_fill2(float *out, int64_t pairs, float v0, float v1, hipStream_t st) {

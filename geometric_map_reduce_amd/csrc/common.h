@@ -18,7 +18,7 @@ constexpr float kFastR2 = 128.0f;
 // Exponent offset (log2 units) of the direct form's sums and gradients.
 constexpr float kDirectOffset = 64.0f;
 
-enum Op : int { OP_SUM = 0, OP_LSE = 1, OP_GRAD = 2 };
+enum Op : int { OP_SUM = 0, OP_LSE = 1, OP_GRAD = 2, OP_MAX = 3 };
 enum Form : int { FORM_AUTO = 0, FORM_DIRECT = 1 };
 
 // One work-group's share of a block-sparse launch: rows [row_lo, row_hi)
@@ -41,6 +41,8 @@ struct GaussArgs {
   float grad_coef;      // -(2 / sigma^2) / scale  (expanded form: scaled coordinates)
   float grad_coef_direct;  // -(2 / sigma^2)        (direct form: raw coordinates)
   float *out;           // final output when nsplit == 1, else partials [nsplit][M][W]
+  int64_t *out_idx;     // OP_MAX: [M][E] indices when nsplit == 1
+  float max_sign;       // OP_MAX: +1 (Max / ArgMax of K b) or -1 (Min / ArgMin)
   int64_t j_per_split;  // multiple of kTileJ
   int nsplit;
   int form;             // Form

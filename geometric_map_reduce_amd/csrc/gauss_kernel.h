@@ -1,6 +1,6 @@
-// gauss_kernel.h -- pass-1 kernel of the Gaussian sum, LogSumExp and grad_x
-// reductions on gfx950 VALU (the D < 32 hot path; also the reference VALU
-// path at large D).
+// gauss_kernel.h -- pass-1 kernel of the Gaussian sum, LogSumExp, grad_x and
+// Max/ArgMax reductions on gfx950 VALU (the D < 32 hot path; also the
+// reference VALU path at large D).
 //
 // Operation (KeOps pages: "Kernel Operations on the GPU, with Autodiff,
 // without Memory Overflows" §1 "Target operation" and §2; KeOps README
@@ -45,7 +45,7 @@ template <int OP, int D, int E>
 struct GaussShape {
   static constexpr int NV = (D + 1 + 3) / 4;                              // float4 per j record
   static constexpr int PAY = E;                                           // payload floats per j (b)
-  // per-row accumulators: sum E; LSE (max, sum) per column; grad D
+  // per-row accumulators: sum E; LSE (max, sum) per column; grad D; max E (with indices)
   static constexpr int NACC = (OP == OP_GRAD) ? D : (OP == OP_LSE ? 2 * E : E);
   // per-tile partial sums: sum E; LSE E; grad D
   static constexpr int NPART = (OP == OP_GRAD) ? D : E;
@@ -110,7 +110,7 @@ __device__ __forceinline__ void gauss_jloop(const GaussArgs &a,
                                             float (*sPay)[GaussShape<OP, D, E>::PAY * GaussShape<OP, D, E>::TJ],
                                             const float (&xs)[R][D], const float (&gr)[R][E], const float (&cen)[D],
                                             float G, float (&acc)[R][GaussShape<OP, D, E>::NACC],
-                                            int64_t jb, int64_t je) {
+                                            int (&ix)[R][E], int64_t jb, int64_t je) {
   using S = GaussShape<OP, D, E>;
   constexpr int NV = S::NV, PAY = S::PAY, TJ = S::TJ, NP = S::NPART;
   const int tid = threadIdx.x;
@@ -160,6 +160,10 @@ __device__ __forceinline__ void gauss_jloop(const GaussArgs &a,
     } else if (OP == OP_LSE) {
 #pragma unroll
       for (int e = 0; e < E; ++e) sPay[buf][e * TJ + tid] = ok ? kLog2e * rb[e] : -INFINITY;
+    } else if (OP == OP_MAX) {
+      // signed payload; padded j carry -inf, so K * b is -inf or NaN and never wins
+#pragma unroll
+      for (int e = 0; e < E; ++e) sPay[buf][e * TJ + tid] = ok ? a.max_sign * rb[e] : -INFINITY;
     } else {
 #pragma unroll
       for (int e = 0; e < E; ++e) sPay[buf][e * TJ + tid] = ok ? rb[e] : 0.0f;
@@ -257,6 +261,16 @@ __device__ __forceinline__ void gauss_jloop(const GaussArgs &a,
             if (OP == OP_SUM) {
 #pragma unroll
               for (int e = 0; e < E; ++e) part[r][e] = fmaf(ex[r], lane4(pq[e], u), part[r][e]);
+            } else if (OP == OP_MAX) {
+              // strict >: j increases along the lane's loop, so ties keep the smaller j
+              const int j = (int)(jt + jj + u);
+#pragma unroll
+              for (int e = 0; e < E; ++e) {
+                const float v = ex[r] * lane4(pq[e], u);
+                const bool up = v > acc[r][e];
+                acc[r][e] = up ? v : acc[r][e];
+                ix[r][e] = up ? j : ix[r][e];
+              }
             } else {
               // grad: A_k += K <g_i, b_j> (x_k - y_k), the difference taken per pair
               // (never as x * sum - sum * y, which cancels for near neighbours)
@@ -286,6 +300,8 @@ __device__ __forceinline__ void gauss_jloop(const GaussArgs &a,
       if (OP == OP_LSE) {
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[r][2 * e + 1] += part[r][e];
+      } else if (OP == OP_MAX) {
+        // the maximum is kept in acc directly
       } else {
 #pragma unroll
         for (int q = 0; q < NP; ++q) acc[r][q] += part[r][q];
@@ -400,27 +416,35 @@ __global__ __launch_bounds__(kThreads) void gauss_valu_kernel(GaussArgs a) {
 #pragma unroll
       for (int e = 0; e < E; ++e) acc[r][2 * e] = -3.0e38f;   // running max (finite: keeps u - m defined)
   }
+  int ix[R][E];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      ix[r][e] = -1;
+      if (OP == OP_MAX) acc[r][e] = -INFINITY;
+    }
 
   // ---- the j loop, specialised on the form (uniform across the work-group):
   // one j split of a dense launch, or the item's j ranges in order
   if (!item) {
     const int64_t jb = (int64_t)blockIdx.y * a.j_per_split;
     const int64_t je = (jb + a.j_per_split < a.N) ? jb + a.j_per_split : a.N;
-    if (fast) gauss_jloop<OP, D, E, R, true>(a, sRec, sPay, xs, gr, cen, G, acc, jb, je);
-    else gauss_jloop<OP, D, E, R, false>(a, sRec, sPay, xs, gr, cen, G, acc, jb, je);
+    if (fast) gauss_jloop<OP, D, E, R, true>(a, sRec, sPay, xs, gr, cen, G, acc, ix, jb, je);
+    else gauss_jloop<OP, D, E, R, false>(a, sRec, sPay, xs, gr, cen, G, acc, ix, jb, je);
   } else {
     for (int64_t k = item->k0; k <= item->k1; ++k) {
       const int64_t jb = k == item->k0 ? item->j0 : a.redr[2 * k];
       const int64_t je = k == item->k1 ? item->j1 : a.redr[2 * k + 1];
       if (jb >= je) continue;
-      if (fast) gauss_jloop<OP, D, E, R, true>(a, sRec, sPay, xs, gr, cen, G, acc, jb, je);
-      else gauss_jloop<OP, D, E, R, false>(a, sRec, sPay, xs, gr, cen, G, acc, jb, je);
+      if (fast) gauss_jloop<OP, D, E, R, true>(a, sRec, sPay, xs, gr, cen, G, acc, ix, jb, je);
+      else gauss_jloop<OP, D, E, R, false>(a, sRec, sPay, xs, gr, cen, G, acc, ix, jb, je);
     }
   }
 
   // ---- finalise and store
   const bool partial = a.nsplit > 1;
-  constexpr int W = (OP == OP_SUM) ? E : (OP == OP_LSE ? (2 * E) : D);
+  constexpr int W = (OP == OP_SUM) ? E : ((OP == OP_LSE || OP == OP_MAX) ? (2 * E) : D);
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     if (!valid[r]) continue;
@@ -430,6 +454,11 @@ __global__ __launch_bounds__(kThreads) void gauss_valu_kernel(GaussArgs a) {
       const float f = fast ? exp2f(G - nx[r]) : exp2f(-kDirectOffset);
 #pragma unroll
       for (int e = 0; e < E; ++e) res[e] = acc[r][e] * f;
+    } else if (OP == OP_MAX) {
+      // (signed value, index) pairs; the row factor is positive, so the argmax is that of acc
+      const float f = fast ? exp2f(G - nx[r]) : exp2f(-kDirectOffset);
+#pragma unroll
+      for (int e = 0; e < E; ++e) { res[2 * e] = acc[r][e] * f; res[2 * e + 1] = __int_as_float(ix[r][e]); }
     } else if (OP == OP_LSE) {
       const float off = fast ? nx[r] : 0.0f;
 #pragma unroll
@@ -450,6 +479,12 @@ __global__ __launch_bounds__(kThreads) void gauss_valu_kernel(GaussArgs a) {
     } else if (OP == OP_LSE) {
 #pragma unroll
       for (int e = 0; e < E; ++e) a.out[i * E + e] = kLn2 * (res[2 * e] + log2f(res[2 * e + 1]));
+    } else if (OP == OP_MAX) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        a.out[i * E + e] = a.max_sign * res[2 * e];
+        a.out_idx[i * E + e] = (int64_t)__float_as_int(res[2 * e + 1]);
+      }
     } else {
 #pragma unroll
       for (int w = 0; w < W; ++w) a.out[i * W + w] = res[w];

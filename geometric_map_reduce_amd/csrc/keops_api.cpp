@@ -87,10 +87,11 @@ bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
 using GaussDispatch = int (*)(int, int, int, VariantInfo *, dim3, const GaussArgs *, hipStream_t);
 using KminDispatch = int (*)(int, int, VariantInfo *, dim3, const KminArgs *, hipStream_t);
 
-const GaussDispatch kGaussUnits[3][2] = {
+const GaussDispatch kGaussUnits[4][2] = {
     {gauss_dispatch_sum_small, gauss_dispatch_sum_large},
     {gauss_dispatch_lse_small, gauss_dispatch_lse_large},
     {gauss_dispatch_grad_small, gauss_dispatch_grad_large},
+    {gauss_dispatch_max_small, gauss_dispatch_max_large},
 };
 const KminDispatch kKminUnits[3] = {kmin_dispatch_d1_4, kmin_dispatch_d5_8, kmin_dispatch_large};
 
@@ -216,13 +217,15 @@ int gauss_stream_entry(const float *x, const float *y, const float *b, int64_t M
 }
 
 int gauss_entry(int op, const float *x, const float *y, const float *b, const float *g, int64_t M, int64_t N,
-                int32_t D, int32_t E, float sigma, float *out, void *stream) {
+                int32_t D, int32_t E, float sigma, float *out, void *stream, int64_t *out_idx = nullptr,
+                float max_sign = 1.0f) {
   // ---- validation (host only)
   if (M < 0 || N < 0 || D < 1 || E < 1) return KEOPS_ERR_INVALID_ARG;
   if (!std::isfinite(sigma) || !(sigma > 0.0f)) return KEOPS_ERR_INVALID_ARG;
   if (M > 0 && (!x || !out)) return KEOPS_ERR_INVALID_ARG;
   if (N > 0 && (!y || !b)) return KEOPS_ERR_INVALID_ARG;
   if (op == OP_GRAD && M > 0 && !g) return KEOPS_ERR_INVALID_ARG;
+  if (op == OP_MAX && M > 0 && (!out_idx || ((uintptr_t)out_idx & 7u))) return KEOPS_ERR_INVALID_ARG;
   for (const void *p : {(const void *)x, (const void *)y, (const void *)b, (const void *)g, (const void *)out})
     if (p && !aligned4(p)) return KEOPS_ERR_INVALID_ARG;
   const int W = op == OP_GRAD ? D : E;
@@ -231,7 +234,14 @@ int gauss_entry(int op, const float *x, const float *y, const float *b, const fl
     if (overlaps(out, ob, x, M * D * 4) || overlaps(out, ob, y, N * D * 4) || overlaps(out, ob, b, N * E * 4) ||
         (op == OP_GRAD && overlaps(out, ob, g, M * E * 4)))
       return KEOPS_ERR_INVALID_ARG;
+    if (op == OP_MAX) {
+      const int64_t ib = M * E * 8;
+      if (overlaps(out_idx, ib, x, M * D * 4) || overlaps(out_idx, ib, y, N * D * 4) ||
+          overlaps(out_idx, ib, b, N * E * 4) || overlaps(out_idx, ib, out, ob))
+        return KEOPS_ERR_INVALID_ARG;
+    }
   }
+  if (op == OP_MAX && N > 0x7fffffffLL) return KEOPS_ERR_UNSUPPORTED;   // indices are int32 inside
   VariantInfo wide_info{}, narrow_info{}, mfma_info{};
   GaussDispatch fn = nullptr;
   if (gauss_find(op, D, E, 1, &wide_info, &fn) || gauss_find(op, D, E, 0, &narrow_info, &fn))
@@ -246,7 +256,8 @@ int gauss_entry(int op, const float *x, const float *y, const float *b, const fl
   hipStream_t st = (hipStream_t)stream;
   (void)hipGetLastError();
   if (N == 0) {
-    launch_fill(out, M * W, op == OP_LSE ? -INFINITY : 0.0f, st);
+    launch_fill(out, M * W, op == OP_LSE ? -INFINITY : (op == OP_MAX ? -max_sign * INFINITY : 0.0f), st);
+    if (op == OP_MAX) launch_fill_i64(out_idx, M * E, -1, st);
     return check_launch();
   }
   int cus = 0;
@@ -279,10 +290,12 @@ int gauss_entry(int op, const float *x, const float *y, const float *b, const fl
   a.nsplit = p.nsplit;
   a.form = form == 1 ? FORM_DIRECT : FORM_AUTO;
   a.wg_flags = nullptr;
+  a.out_idx = out_idx;
+  a.max_sign = max_sign;
 
   // workspace: split-j partials, then (MFMA path) one form flag per row block
   float *ws = nullptr;
-  const int PW = op == OP_SUM ? E : (op == OP_LSE ? 2 * E : D);
+  const int PW = op == OP_SUM ? E : ((op == OP_LSE || op == OP_MAX) ? 2 * E : D);
   const size_t part_bytes = p.nsplit > 1 ? ((size_t)p.nsplit * M * PW * sizeof(float) + 255) / 256 * 256 : 0;
   const size_t flag_bytes = use_mfma ? (size_t)p.nblk * sizeof(int) : 0;
   if (part_bytes + flag_bytes > 0) {
@@ -307,6 +320,7 @@ int gauss_entry(int op, const float *x, const float *y, const float *b, const fl
   }
   if (p.nsplit > 1) {
     if (op == OP_LSE) launch_lse_combine(ws, p.nsplit, M, E, out, st);
+    else if (op == OP_MAX) launch_max_combine(ws, p.nsplit, M, E, max_sign, out, out_idx, st);
     else launch_sum_combine(ws, p.nsplit, M * PW, out, st);
   }
   if (ws) (void)hipFreeAsync(ws, st);
@@ -626,6 +640,16 @@ int keops_gauss_grad_x_ranges(const float *x, const float *y, const float *b, co
                               void *stream) {
   return gauss_ranges_entry(OP_GRAD, x, y, b, g, M, N, D, E, sigma, ranges_i, nri, slices_i, redranges_j, nrj, out,
                             stream);
+}
+
+int keops_gauss_max(const float *x, const float *y, const float *b, int64_t M, int64_t N, int32_t D, int32_t E,
+                    float sigma, float *out, int64_t *out_idx, void *stream) {
+  return gauss_entry(OP_MAX, x, y, b, nullptr, M, N, D, E, sigma, out, stream, out_idx, 1.0f);
+}
+
+int keops_gauss_min(const float *x, const float *y, const float *b, int64_t M, int64_t N, int32_t D, int32_t E,
+                    float sigma, float *out, int64_t *out_idx, void *stream) {
+  return gauss_entry(OP_MAX, x, y, b, nullptr, M, N, D, E, sigma, out, stream, out_idx, -1.0f);
 }
 
 int keops_kmin(const float *x, const float *y, int64_t M, int64_t N, int32_t D, int32_t K, float *out_d,

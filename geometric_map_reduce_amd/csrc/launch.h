@@ -21,6 +21,8 @@ KMI_DECLARE_GAUSS(gauss_dispatch_lse_small)
 KMI_DECLARE_GAUSS(gauss_dispatch_lse_large)
 KMI_DECLARE_GAUSS(gauss_dispatch_grad_small)
 KMI_DECLARE_GAUSS(gauss_dispatch_grad_large)
+KMI_DECLARE_GAUSS(gauss_dispatch_max_small)
+KMI_DECLARE_GAUSS(gauss_dispatch_max_large)
 KMI_DECLARE_GAUSS(gauss_dispatch_sum_mfma)
 #undef KMI_DECLARE_GAUSS
 
@@ -46,6 +48,11 @@ int launch_kmin_combine(const float *pd, const int32_t *pi, int nsplit, int64_t 
                         int64_t *out_i, hipStream_t st);
 void launch_fill(float *out, int64_t count, float v, hipStream_t st);
 void launch_fill2(float *out, int64_t pairs, float v0, float v1, hipStream_t st);
+void launch_fill_i64(int64_t *out, int64_t count, int64_t v, hipStream_t st);
+// Max/ArgMax pass 2: partials [nsplit][M][E] of (signed value, index bits); the
+// largest value wins, the smaller index on ties; out = sign * value.
+void launch_max_combine(const float *ws, int nsplit, int64_t M, int E, float sign, float *out, int64_t *out_idx,
+                        hipStream_t st);
 void launch_stream_combine(const float *part, int nparts, int64_t count, float *out, hipStream_t st);
 
 // Conjugate-gradient vector kernels (E <= 4 columns).  Each launcher that

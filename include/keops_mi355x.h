@@ -81,6 +81,24 @@ int keops_gauss_lse(const float *x, const float *y, const float *b,
                     float *out, void *stream);
 
 /*
+ * Max / ArgMax and Min / ArgMin reductions of the kernel product ([KO-GPU] §2
+ * reductions list; [README] feature list "Sum, LogSumExp, Min, Max but also
+ * ArgMin, ArgMax"):
+ *   keops_gauss_max: out[i, e] = max_j K_ij b[j, e],  out_idx[i, e] = its j
+ *   keops_gauss_min: out[i, e] = min_j K_ij b[j, e],  out_idx[i, e] = its j
+ * with K_ij = exp(-|x_i - y_j|^2/sigma^2); among equal values the smaller j is
+ * returned.  out: [M, E] fp32; out_idx: [M, E] int64, 8-byte aligned.  The
+ * values are compared in fp32 as computed (K to about 1e-6 relative), so two
+ * j whose products differ by less than that may be returned either way.
+ * N = 0 gives -inf (max) or +inf (min) and index -1; NaN products never win.
+ * Requires N < 2^31.
+ */
+int keops_gauss_max(const float *x, const float *y, const float *b, int64_t M, int64_t N, int32_t D, int32_t E,
+                    float sigma, float *out, int64_t *out_idx, void *stream);
+int keops_gauss_min(const float *x, const float *y, const float *b, int64_t M, int64_t N, int32_t D, int32_t E,
+                    float sigma, float *out, int64_t *out_idx, void *stream);
+
+/*
  * Gradient of the kernel sum with respect to x ([KO-GPU] §2 "Performance and
  * differentiation"; [README] torch.autograd.grad((a_i ** 2).sum(), [x])), as
  * the vector-Jacobian product with the cotangent g = dL/da:

@@ -89,7 +89,10 @@ int oracle_gauss_sum(const float *x, const float *y, const float *b,
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t r = 0; r < nrows; ++r) {
         const int64_t i = rows ? rows[r] : r;
-        double *o = out + r * E, *nm = norm ? norm + r * E : NULL;
+        /* the row's accumulators live on the thread's stack: threads writing
+         * neighbouring rows of `out` would otherwise share its cache lines */
+        double o[E], nacc[E];
+        double *nm = norm ? nacc : NULL;
         for (int e = 0; e < E; ++e) { o[e] = 0.0; if (nm) nm[e] = 0.0; }
         for (int64_t j = 0; j < N; ++j) {
             const double k = exp(-sq_dist(x + i * D, y + j * D, D) * inv_s2);
@@ -99,6 +102,7 @@ int oracle_gauss_sum(const float *x, const float *y, const float *b,
                 if (nm) nm[e] += fabs(t);
             }
         }
+        for (int e = 0; e < E; ++e) { out[r * E + e] = o[e]; if (norm) norm[r * E + e] = nacc[e]; }
     }
     return 0;
 }
@@ -156,7 +160,8 @@ int oracle_gauss_grad_x(const float *x, const float *y, const float *b, const fl
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t r = 0; r < nrows; ++r) {
         const int64_t i = rows ? rows[r] : r;
-        double *o = out + r * D, *n = nu ? nu + r * D : NULL;
+        double o[D], nacc[D];               /* stack accumulators, as in the sum */
+        double *n = nu ? nacc : NULL;
         for (int d = 0; d < D; ++d) { o[d] = 0.0; if (n) n[d] = 0.0; }
         for (int64_t j = 0; j < N; ++j) {
             const double k = exp(-sq_dist(x + i * D, y + j * D, D) * inv_s2);
@@ -168,6 +173,7 @@ int oracle_gauss_grad_x(const float *x, const float *y, const float *b, const fl
                 if (n) n[d] += fabs(t);
             }
         }
+        for (int d = 0; d < D; ++d) { out[r * D + d] = o[d]; if (nu) nu[r * D + d] = nacc[d]; }
     }
     return 0;
 }
@@ -191,7 +197,8 @@ int oracle_gauss_grad_y(const float *x, const float *y, const float *b, const fl
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t c = 0; c < ncols; ++c) {
         const int64_t j = cols ? cols[c] : c;
-        double *o = out + c * D, *n = nu ? nu + c * D : NULL;
+        double o[D], nacc[D];               /* stack accumulators, as in the sum */
+        double *n = nu ? nacc : NULL;
         for (int d = 0; d < D; ++d) { o[d] = 0.0; if (n) n[d] = 0.0; }
         for (int64_t i = 0; i < M; ++i) {
             const double k = exp(-sq_dist(x + i * D, y + j * D, D) * inv_s2);
@@ -203,6 +210,7 @@ int oracle_gauss_grad_y(const float *x, const float *y, const float *b, const fl
                 if (n) n[d] += fabs(t);
             }
         }
+        for (int d = 0; d < D; ++d) { out[c * D + d] = o[d]; if (nu) nu[c * D + d] = nacc[d]; }
     }
     return 0;
 }
@@ -222,7 +230,8 @@ int oracle_gauss_grad_b(const float *x, const float *y, const float *g,
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t c = 0; c < ncols; ++c) {
         const int64_t j = cols ? cols[c] : c;
-        double *o = out + c * E, *n = nu ? nu + c * E : NULL;
+        double o[E], nacc[E];               /* stack accumulators, as in the sum */
+        double *n = nu ? nacc : NULL;
         for (int e = 0; e < E; ++e) { o[e] = 0.0; if (n) n[e] = 0.0; }
         for (int64_t i = 0; i < M; ++i) {
             const double k = exp(-sq_dist(x + i * D, y + j * D, D) * inv_s2);
@@ -232,6 +241,7 @@ int oracle_gauss_grad_b(const float *x, const float *y, const float *g,
                 if (n) n[e] += fabs(t);
             }
         }
+        for (int e = 0; e < E; ++e) { out[c * E + e] = o[e]; if (nu) nu[c * E + e] = nacc[e]; }
     }
     return 0;
 }
@@ -344,7 +354,9 @@ int oracle_gauss_sum_ranges(const float *x, const float *y, const float *b,
         const int64_t k0 = c == 0 ? 0 : slices_i[c - 1], k1 = slices_i[c];
 #pragma omp parallel for schedule(dynamic, 1)
         for (int64_t i = ranges_i[2 * c]; i < ranges_i[2 * c + 1]; ++i) {
-            double *o = out + i * E, *nm = norm ? norm + i * E : NULL;
+            double o[E], nacc[E];           /* stack accumulators, as in the sum */
+            double *nm = norm ? nacc : NULL;
+            for (int e = 0; e < E; ++e) { o[e] = 0.0; nacc[e] = 0.0; }
             for (int64_t k = k0; k < k1; ++k)
                 for (int64_t j = redranges_j[2 * k]; j < redranges_j[2 * k + 1]; ++j) {
                     const double kv = exp(-sq_dist(x + i * D, y + j * D, D) * inv_s2);
@@ -354,6 +366,7 @@ int oracle_gauss_sum_ranges(const float *x, const float *y, const float *b,
                         if (nm) nm[e] += fabs(t);
                     }
                 }
+            for (int e = 0; e < E; ++e) { out[i * E + e] = o[e]; if (norm) norm[i * E + e] = nacc[e]; }
         }
     }
     return 0;

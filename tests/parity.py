@@ -7,6 +7,8 @@ Acceptance (fp32 GPU results against the float64 oracle):
                                       plus 8 fp32 ulps of the output itself, which an
                                       fp32 result of magnitude |l*| cannot beat)
   grad   |G - G*| <= 1e-4 * nu       nu = sum_j |(2/sigma^2) K <g,b> (x - y)|
+  max    |max - max*| <= 2e-5 |max*| + 1e-37; an index other than the oracle's is
+         accepted when its exact product is within that tolerance of the maximum
   kmin   indices distinct and in range; each pick equals the oracle's or its
          distance is within 1e-5 relative of the oracle's k-th distance (near
          ties); returned distances non-decreasing and within
@@ -56,6 +58,32 @@ def check_lse(l_gpu, l_ref, atol=LSE_ATOL, rtol=LSE_RTOL):
 
 def check_grad(G_gpu, G_ref, nu_ref, rtol=GRAD_RTOL):
     return check_sum(G_gpu, G_ref, nu_ref, rtol, what="grad_x")
+
+
+MAX_RTOL = 2e-5
+
+
+def check_max(x, y, b, sigma, sign, rows, v_gpu, i_gpu, v_ref, i_ref, rtol=MAX_RTOL):
+    """Max/ArgMax (sign = +1) or Min/ArgMin (sign = -1) of K b against the oracle's signed maximum
+    v_ref = max_j sign K_ij b_je with index i_ref: the value within rtol (plus a floor below the
+    smallest normal fp32), and each index either the oracle's or one whose exact product is
+    within the same tolerance of the maximum (near ties)."""
+    s = sign * np.asarray(v_gpu, np.float64).reshape(v_ref.shape)
+    i_gpu = np.asarray(i_gpu).reshape(i_ref.shape)
+    tol = rtol * np.abs(v_ref) + 1e-37
+    both_inf = np.isneginf(s) & np.isneginf(v_ref)
+    with np.errstate(invalid="ignore"):
+        err = np.where(both_inf, 0.0, np.abs(s - v_ref))
+    assert np.all(err <= tol), f"max: worst {np.nanmax(err / tol):.3g} x tol"
+    N = y.shape[0]
+    diff = np.argwhere(i_gpu != i_ref)
+    for r, e in diff:
+        j = int(i_gpu[r, e])
+        assert 0 <= j < N, (r, e, j)
+        d2 = oracle.sq_dist_pairs(x, y, np.array([rows[r]]), np.array([j]))[0]
+        exact = sign * np.exp(-d2 / float(sigma) ** 2) * float(b[j, e])
+        assert abs(exact - v_ref[r, e]) <= tol[r, e], (r, e, j, exact, v_ref[r, e])
+    return len(diff)
 
 
 def check_kmin(x, y, rows, d_gpu, i_gpu, d_ref, i_ref):

@@ -28,7 +28,7 @@ def L():
 def test_header_declares_the_reductions():
     names = declared_functions()
     for n in ("keops_gauss_sum", "keops_gauss_lse", "keops_gauss_grad_x", "keops_gauss_grad_y",
-              "keops_gauss_grad_b", "keops_gauss_cg", "keops_kmin"):
+              "keops_gauss_grad_b", "keops_gauss_cg", "keops_gauss_max", "keops_gauss_min", "keops_kmin"):
         assert n in names
 
 
@@ -132,4 +132,14 @@ def test_cg_validation(L):
     assert L.keops_gauss_cg(FAKE, FAKE2, 10, 99, 1, 1.0, 1.0, 1e-5, 10, out, None, None, None) == -2  # D
     assert L.keops_gauss_cg(None, None, 0, 3, 2, 1.0, 0.0, 1e-5, 10, None, ctypes.byref(it), res, None) == 0
     assert it.value == 0 and res[0] == 0.0 and res[1] == 0.0
+
+
+def test_max_validation(L):
+    out = ctypes.c_void_p(0x900000)
+    idx = ctypes.c_void_p(0xA00000)
+    assert L.keops_gauss_max(FAKE, FAKE2, FAKE2, 5, 7, 3, 1, 1.0, out, None, None) == -1          # no indices
+    assert L.keops_gauss_max(FAKE, FAKE2, FAKE2, 5, 7, 3, 1, 1.0, out, ctypes.c_void_p(0xA00004), None) == -1
+    assert L.keops_gauss_min(FAKE, FAKE2, FAKE2, 5, 7, 3, 1, 0.0, out, idx, None) == -1            # sigma
+    assert L.keops_gauss_min(FAKE, FAKE2, FAKE2, 5, 7, 99, 1, 1.0, out, idx, None) == -2           # D
+    assert L.keops_gauss_max(None, None, None, 0, 0, 3, 1, 1.0, None, None, None) == 0
 

@@ -17,7 +17,7 @@ import pytest
 import torch
 
 import oracle
-from parity import check_grad, check_kmin, check_lse, check_sum, dev, host
+from parity import check_grad, check_kmin, check_lse, check_max, check_sum, dev, host
 
 pytestmark = pytest.mark.gpu
 
@@ -344,6 +344,64 @@ def test_ranges_grid_truncation_1M():
     bound = 1e-5 * np.abs(b.astype(np.float64)).sum() + 1e-4 * n_ref
     assert np.all(np.abs(a[rows] - full) <= bound)
     say(f"  kept cluster pairs {mask.mean():.3f}; worst truncation error {np.abs(a[rows] - full).max():.3g}")
+
+
+def _run_max(x, y, b, sigma, rows=None):
+    X, Y, B = dev(x), dev(y), dev(b)
+    out = []
+    for sign, fn in ((1, gm.keops_gauss_max), (-1, gm.keops_gauss_min)):
+        v, i = fn(X, Y, B, sigma)
+        torch.cuda.synchronize()
+        v, i = host(v), host(i)
+        r = np.arange(x.shape[0]) if rows is None else rows
+        v_ref, i_ref = oracle.gauss_max(x, y, b, sigma, sign, rows=None if rows is None else rows)
+        out.append(check_max(x, y, b, sigma, sign, r, v[r], i[r], v_ref, i_ref))
+    return out
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "M%d_N%d_D%d_E%d_s%g" % c)
+def test_small_max_min(case):
+    M, N, D, E, sigma = case
+    say(f"max/min M={M} N={N} D={D} E={E} sigma={sigma}")
+    x, y, b, _ = rand_case(4000 + M + N + D, M, N, D, E)
+    if N >= 4:
+        y[N - 1], b[N - 1] = y[1], b[1]          # an exact tie: the smaller index
+    _run_max(x, y, b, float(np.float32(sigma)))
+
+
+@pytest.mark.parametrize("form", [0, 1], ids=["auto", "direct"])
+@pytest.mark.parametrize("split", [0, 1, 5])
+@pytest.mark.parametrize("rows", [1, 2], ids=["narrow", "wide"])
+def test_max_forms_splits_layouts(form, split, rows):
+    say(f"max forced form={form} split={split} rows={rows}")
+    for (M, N, D, E, sigma) in [(2100, 1900, 3, 1, 0.4), (600, 2500, 5, 2, 1.1)]:
+        gm.keops_set_option(gm.KEOPS_OPT_FORM, form)
+        gm.keops_set_option(gm.KEOPS_OPT_SPLIT_J, split)
+        gm.keops_set_option(gm.KEOPS_OPT_ROWS, rows)
+        x, y, b, _ = rand_case(11 + D, M, N, D, E)
+        _run_max(x, y, b, sigma)
+
+
+def test_max_empty_and_far():
+    say("max/min: N = 0, far data, all-negative payload")
+    x = np.zeros((5, 3), np.float32)
+    v, i = gm.keops_gauss_max(dev(x), dev(np.zeros((0, 3), np.float32)), dev(np.zeros((0, 2), np.float32)), 1.0)
+    w, k = gm.keops_gauss_min(dev(x), dev(np.zeros((0, 3), np.float32)), dev(np.zeros((0, 2), np.float32)), 1.0)
+    v, i, w, k = host(v), host(i), host(w), host(k)
+    assert np.isneginf(v).all() and np.isposinf(w).all() and (i == -1).all() and (k == -1).all()
+    rng = np.random.default_rng(9)
+    x = (rng.standard_normal((700, 3)) * 5 + 300).astype(np.float32)
+    y = (rng.standard_normal((900, 3)) * 5 + 300).astype(np.float32)
+    b = -np.abs(rng.standard_normal((900, 1))).astype(np.float32)
+    _run_max(x, y, b, 0.7)
+
+
+def test_workload_max_1M():
+    w = workloads.WORKLOADS["sum_lse_1M"]
+    say("workload sum_lse_1M: max/min")
+    x, y, b = workloads.make_inputs(w)
+    n = _run_max(x, y, b, w.sigma, rows=_sample(w.M, 256))
+    say(f"  indices differing from the oracle's (near ties): {n}")
 
 
 KMIN_SMALL = [(1, 1, 1, 1), (5, 40, 3, 10), (300, 1000, 3, 10), (257, 513, 2, 16), (100, 3000, 4, 32),

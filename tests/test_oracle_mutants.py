@@ -21,13 +21,13 @@ MUTANTS = {
                     "            for (int e = 0; e < E; ++e) {"),
     "sigma_not_squared": ("const double inv_s2 = 1.0 / (sigma * sigma);\n#pragma omp parallel for schedule(dynamic, 1)\n"
                           "    for (int64_t r = 0; r < nrows; ++r) {\n        const int64_t i = rows ? rows[r] : r;\n"
-                          "        double *o = out + r * E,",
+                          "        /* the row's accumulators",
                           "const double inv_s2 = 1.0 / (2.0 * sigma * sigma);\n#pragma omp parallel for schedule(dynamic, 1)\n"
                           "    for (int64_t r = 0; r < nrows; ++r) {\n        const int64_t i = rows ? rows[r] : r;\n"
-                          "        double *o = out + r * E,"),
+                          "        /* the row's accumulators"),
     "sum_b_column": ("const double t = k * (double)b[j * E + e];", "const double t = k * (double)b[j * E];"),
-    "sum_row_index": ("const int64_t i = rows ? rows[r] : r;\n        double *o = out + r * E,",
-                      "const int64_t i = r;\n        double *o = out + r * E,"),
+    "sum_row_index": ("const int64_t i = rows ? rows[r] : r;\n        /* the row's accumulators",
+                      "const int64_t i = r;\n        /* the row's accumulators"),
     "lse_drop_max": ("out[r * E + e] = m + log(s);", "out[r * E + e] = log(s);"),
     "lse_b_sign": ("* inv_s2 + (double)b[j * E + e];\n                    s += exp(v - m);",
                    "* inv_s2 - (double)b[j * E + e];\n                    s += exp(v - m);"),
@@ -44,8 +44,8 @@ MUTANTS = {
                         "                const double t = 2.0",
                         "gb += (double)g[i * E + e] * (double)b[j * E];\n            for (int d = 0; d < D; ++d) {\n"
                         "                const double t = 2.0"),
-    "grad_y_ignores_cols": ("const int64_t j = cols ? cols[c] : c;\n        double *o = out + c * D,",
-                            "const int64_t j = c;\n        double *o = out + c * D,"),
+    "grad_y_ignores_cols": ("const int64_t j = cols ? cols[c] : c;\n        double o[D],",
+                            "const int64_t j = c;\n        double o[D],"),
     "grad_b_g_column": ("const double t = k * (double)g[i * E + e];", "const double t = k * (double)g[i * E];"),
     "grad_b_kernel_sign": ("const double k = exp(-sq_dist(x + i * D, y + j * D, D) * inv_s2);\n            for (int e = 0; e < E; ++e) {\n"
                            "                const double t = k * (double)g",
@@ -57,9 +57,9 @@ MUTANTS = {
                                  "    for (int64_t i = 0; i < M; ++i)"),
     "matrix_row_stride": ("out[i * N + j] = exp(", "out[j * M + i] = exp("),
     "ranges_slice_start": ("const int64_t k0 = c == 0 ? 0 : slices_i[c - 1], k1 = slices_i[c];\n#pragma omp parallel for schedule(dynamic, 1)\n"
-                           "        for (int64_t i = ranges_i[2 * c]; i < ranges_i[2 * c + 1]; ++i) {\n            double *o",
+                           "        for (int64_t i = ranges_i[2 * c]; i < ranges_i[2 * c + 1]; ++i) {\n            double o[E]",
                            "const int64_t k0 = c == 0 ? 0 : slices_i[c - 1] + 1, k1 = slices_i[c];\n#pragma omp parallel for schedule(dynamic, 1)\n"
-                           "        for (int64_t i = ranges_i[2 * c]; i < ranges_i[2 * c + 1]; ++i) {\n            double *o"),
+                           "        for (int64_t i = ranges_i[2 * c]; i < ranges_i[2 * c + 1]; ++i) {\n            double o[E]"),
     "ranges_j_end": ("for (int64_t j = redranges_j[2 * k]; j < redranges_j[2 * k + 1]; ++j) {\n                    const double kv",
                      "for (int64_t j = redranges_j[2 * k]; j + 1 < redranges_j[2 * k + 1]; ++j) {\n                    const double kv"),
     "ranges_lse_drop_max": ("out[i * E + e] = m + log(s);", "out[i * E + e] = log(s);"),
