@@ -65,6 +65,7 @@ def open_library(path: str):
     lib.oracle_kmin.argtypes = [P, P, i64, i64, i32, i32, P, i64, P, P]
     lib.oracle_sq_dist_pairs.argtypes = [P, P, i32, P, P, i64, P]
     lib.oracle_gauss_matrix.argtypes = [P, P, i64, i64, i32, f64, P]
+    lib.oracle_laplace_sum.argtypes = [P, P, P, i64, i64, i32, i32, f64, P, i64, P, P]
     lib.oracle_gauss_max.argtypes = [P, P, P, i64, i64, i32, i32, f64, i32, P, i64, P, P]
     lib.oracle_gauss_sum_ranges.argtypes = [P, P, P, i64, i64, i32, i32, f64, P, i64, P, P, i64, P, P]
     lib.oracle_gauss_lse_ranges.argtypes = [P, P, P, i64, i64, i32, i32, f64, P, i64, P, P, i64, P]
@@ -312,4 +313,18 @@ def gauss_max(x, y, b, sigma, sign=1, rows=None, lib=None):
     _check((lib or _load()).oracle_gauss_max(_ptr(x), _ptr(y), _ptr(b), M, N, D, E, float(sigma), int(sign),
                                     _ptr(r), n, _ptr(out), _ptr(idx)), "gauss_max")
     return out, idx
+
+
+def laplace_sum(x, y, b, sigma, rows=None, lib=None):
+    """a[r, e] = sum_j exp(-|x_i - y_j| / sigma) b[j, e] for i = rows[r]; returns (a, norm) in float64."""
+    x, y, b = _f32(x, 2), _f32(y, 2), _f32(b, 2)
+    M, D = x.shape
+    N, E = b.shape
+    assert y.shape == (N, D)
+    r, n = _rows(rows, M)
+    out = np.empty((n, E), np.float64)
+    norm = np.empty((n, E), np.float64)
+    _check((lib or _load()).oracle_laplace_sum(_ptr(x), _ptr(y), _ptr(b), M, N, D, E, float(sigma), _ptr(r), n,
+                                      _ptr(out), _ptr(norm)), "laplace_sum")
+    return out, norm
 

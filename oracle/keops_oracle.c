@@ -431,3 +431,31 @@ int oracle_gauss_max(const float *x, const float *y, const float *b,
     return 0;
 }
 
+/*
+ * Laplacian kernel sum ([README] feature list: a wide range of formulas; the
+ * pages name Gaussian and other kernels for kernel methods):
+ *   a_ie = sum_j exp(-|x_i - y_j| / sigma) b_je,  |.| the Euclidean norm,
+ * with norm_ie = sum_j |exp(-|x_i - y_j|/sigma) b_je|.
+ */
+int oracle_laplace_sum(const float *x, const float *y, const float *b,
+                       int64_t M, int64_t N, int D, int E, double sigma,
+                       const int64_t *rows, int64_t nrows, double *out, double *norm) {
+    if (check_common(M, N, D, nrows, rows) || E < 1 || !(sigma > 0.0)) return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t i = rows ? rows[r] : r;
+        double o[E], nacc[E];               /* stack accumulators, as in the sum */
+        for (int e = 0; e < E; ++e) { o[e] = 0.0; nacc[e] = 0.0; }
+        for (int64_t j = 0; j < N; ++j) {
+            const double k = exp(-sqrt(sq_dist(x + i * D, y + j * D, D)) / sigma);
+            for (int e = 0; e < E; ++e) {
+                const double t = k * (double)b[j * E + e];
+                o[e] += t;
+                nacc[e] += fabs(t);
+            }
+        }
+        for (int e = 0; e < E; ++e) { out[r * E + e] = o[e]; if (norm) norm[r * E + e] = nacc[e]; }
+    }
+    return 0;
+}
+

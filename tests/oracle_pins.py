@@ -525,6 +525,33 @@ def pin_max_brute(lib=None):
     assert np.isneginf(v).all() and (i == -1).all()
 
 
+# --------------------------------------------------------------------------- Laplacian kernel
+def pin_laplace_brute_and_limits(lib=None):
+    """exp(-|x - y| / sigma) sums equal numpy's materialised product; x = y gives b; a very large
+    sigma gives sum_j b_j; D = 1 on a sorted line is a geometric-series closed form."""
+    rng = np.random.default_rng(91)
+    for (M, N, D, E) in SHAPES:
+        sigma = 0.7 * math.sqrt(D)
+        x = rng.standard_normal((M, D)).astype(np.float32)
+        y = rng.standard_normal((N, D)).astype(np.float32)
+        b = rng.standard_normal((N, E)).astype(np.float32)
+        a, n = oracle.laplace_sum(x, y, b, sigma, lib=lib)
+        Kl = np.exp(-np.sqrt(brute_sqdist(x, y)) / sigma)
+        rel_close(a, Kl @ b.astype(np.float64), 0, 1e-12 * (1 + n.max()))
+    p = np.array([[0.25, -1.5]], np.float32)
+    bb = np.array([[2.0, -3.0]], np.float32)
+    rel_close(oracle.laplace_sum(p, p, bb, 0.3, lib=lib)[0], bb, 0)
+    y = rng.standard_normal((40, 3)).astype(np.float32)
+    b = rng.standard_normal((40, 1)).astype(np.float32)
+    rel_close(oracle.laplace_sum(y[:5], y, b, 1e9, lib=lib)[0], np.full((5, 1), b.astype(np.float64).sum()), 1e-7)
+    # points 0, h, 2h, ... on a line, b = 1: a_0 = sum_k q^k with q = exp(-h / sigma)
+    h, sigma, n = 0.25, 0.8, 30
+    line = (np.arange(n, dtype=np.float32) * np.float32(h))[:, None]
+    q = math.exp(-h / sigma)
+    a0 = oracle.laplace_sum(line[:1], line, np.ones((n, 1), np.float32), sigma, lib=lib)[0][0, 0]
+    assert abs(a0 - (1 - q ** n) / (1 - q)) <= 1e-13 * a0
+
+
 # --------------------------------------------------------------------------- kmin
 def pin_kmin_argsort(lib=None):
     """K-min equals a stable argsort of the materialised distances (ties -> smaller j)."""

@@ -65,6 +65,10 @@ MUTANTS = {
     "ranges_lse_drop_max": ("out[i * E + e] = m + log(s);", "out[i * E + e] = log(s);"),
     "max_ties_last": ("if (v > out[r * E + e]) { out[r * E + e] = v;", "if (v >= out[r * E + e]) { out[r * E + e] = v;"),
     "max_no_sign": ("const double v = (double)sgn * k * (double)b[j * E + e];", "const double v = k * (double)b[j * E + e];"),
+    "laplace_no_sqrt": ("const double k = exp(-sqrt(sq_dist(x + i * D, y + j * D, D)) / sigma);",
+                        "const double k = exp(-sq_dist(x + i * D, y + j * D, D) / sigma);"),
+    "laplace_sigma_squared": ("const double k = exp(-sqrt(sq_dist(x + i * D, y + j * D, D)) / sigma);",
+                              "const double k = exp(-sqrt(sq_dist(x + i * D, y + j * D, D)) / (sigma * sigma));"),
     "kmin_tie_break": ("(dj == bd[pos - 1] && j < bj[pos - 1])", "(dj == bd[pos - 1] && j > bj[pos - 1])"),
     "kmin_keep_last": ("if (count == K && !(dj < bd[K - 1]", "if (count == K && !(dj <= bd[K - 1]"),
 }
