@@ -56,6 +56,7 @@ BENCHES = {
     "cg": ("cg", "krige_100k"),
     "sum_bs": ("sum_ranges", "sum_lse_1M"),
     "max": ("max", "sum_lse_1M"),
+    "laplace": ("laplace", "sum_lse_1M"),
 }
 BS_VOXEL, BS_EPS = 0.1, 1e-5       # block-sparse bench: voxel side and truncation threshold
 CG_RTOL = 1e-4
@@ -65,7 +66,7 @@ STREAM_MAX_ROWS = 64              # the library's few-rows layout (j per lane) f
 
 def flops_per_pair(op, D, E):
     return {"sum": 3 * D + 1 + 2 * E, "cg": 3 * D + 1 + 2 * E, "sum_ranges": 3 * D + 1 + 2 * E,
-            "max": 3 * D + 1 + 2 * E, "lse": 3 * D + 5, "grad_x": 5 * D + 2 * E + 1, "grad_y": 5 * D + 2 * E + 1,
+            "max": 3 * D + 1 + 2 * E, "laplace": 3 * D + 2 + 2 * E, "lse": 3 * D + 5, "grad_x": 5 * D + 2 * E + 1, "grad_y": 5 * D + 2 * E + 1,
             "grad_b": 3 * D + 1 + 2 * E, "kmin": 3 * D}[op]
 
 
@@ -90,6 +91,8 @@ def roofline_of(op, M, D, E):
         return "mfma", 2 * D, ("gauss_mfma_sum_kernel" if op == "sum" else "kmin_mfma_kernel")
     # the transposed gradients run the row kernels with y as the rows
     kop = {"grad_y": "grad_x", "grad_b": "sum", "cg": "sum", "sum_ranges": "sum"}.get(op, op)
+    if op == "laplace":
+        return "alu", flops_per_pair(op, D, E), "laplace_sum (gauss_valu_kernel<OP_LAPLACE>)"
     name = "kmin_valu_kernel" if op == "kmin" else f"gauss_valu_kernel<{kop}>"
     return "alu", flops_per_pair(op, D, E), name
 
@@ -140,6 +143,8 @@ def run_op(gm, op, X, Y, B, G, sigma, K, out, lam=0.0, ranges=None):
         return gm.keops_gauss_sum(X, Y, B, sigma, out=out)
     if op == "max":
         return gm.keops_gauss_max(X, Y, B, sigma, out=out[0], out_idx=out[1])
+    if op == "laplace":
+        return gm.keops_laplace_sum(X, Y, B, sigma, out=out)
     if op == "lse":
         return gm.keops_gauss_lse(X, Y, B, sigma, out=out)
     if op == "grad_x":
@@ -192,6 +197,8 @@ def cpu_baseline(op, w, x, y, b, g, target_s, gpu_out, ranges=None):
             res = oracle.gauss_sum(x, y, b, w.sigma, rows=rows)
         elif op == "max":
             res = oracle.gauss_max(x, y, b, w.sigma, 1, rows=rows)
+        elif op == "laplace":
+            res = oracle.laplace_sum(x, y, b, w.sigma, rows=rows)
         elif op == "cg":        # the solver's work is its products K p: the sum oracle on x
             res = oracle.gauss_sum(x, x, b, w.sigma, rows=rows)
         elif op == "lse":
@@ -235,7 +242,7 @@ def cpu_baseline(op, w, x, y, b, g, target_s, gpu_out, ranges=None):
         ref, _ = res
         gpu = gpu_out[rows].reshape(ref.shape).astype(np.float64)
         check = {"rows": len(rows), "max_rel_err": float(np.max(np.abs(gpu - ref) / np.maximum(np.abs(ref), 1e-300)))}
-    elif op in ("sum", "grad_x", "grad_y", "grad_b", "sum_ranges"):
+    elif op in ("sum", "grad_x", "grad_y", "grad_b", "sum_ranges", "laplace"):
         ref, nrm = res
         gpu = gpu_out[rows].reshape(ref.shape).astype(np.float64)
         check = {"rows": len(rows), "max_err_over_norm": float(np.max(np.abs(gpu - ref) / np.maximum(nrm, 1e-300)))}

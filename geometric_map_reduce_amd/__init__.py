@@ -14,6 +14,7 @@ never stored, run as hand-written gfx950 HIP kernels behind the C ABI of
   given as row and j ranges
 * ``keops_gauss_cg``     -- conjugate-gradient solve of (K + lambda I) a = b
 * ``keops_gauss_max``, ``keops_gauss_min`` -- Max/ArgMax and Min/ArgMin of K b
+* ``keops_laplace_sum``  -- the Laplacian kernel sum, exp(-|x - y| / sigma)
 * ``keops_kmin``         -- K nearest neighbours with indices
 
 PyTorch supplies device memory and streams only.
@@ -21,6 +22,6 @@ PyTorch supplies device memory and streams only.
 from .binding import (KEOPS_OPT_FORM, KEOPS_OPT_PROFILE, KEOPS_OPT_ROWS, KEOPS_OPT_SPLIT_J,  # noqa: F401
                       KEOPS_OPT_WG_TARGET, KeopsError, keops_gauss_cg, keops_gauss_grad_b, keops_gauss_grad_x,
                       keops_gauss_grad_x_ranges, keops_gauss_grad_y, keops_gauss_lse, keops_gauss_lse_ranges,
-                      keops_gauss_max, keops_gauss_min,
+                      keops_gauss_max, keops_gauss_min, keops_laplace_sum,
                       keops_gauss_sum, keops_gauss_sum_ranges, keops_kmin, keops_profile_read,
                       keops_set_option, keops_version, lib, status_string)

@@ -64,6 +64,7 @@ def lib() -> ctypes.CDLL:
             L.keops_gauss_sum_ranges.argtypes = [P, P, P, i64, i64, i32, i32, f32, P, i64, P, P, i64, P, P]
             L.keops_gauss_lse_ranges.argtypes = [P, P, P, i64, i64, i32, i32, f32, P, i64, P, P, i64, P, P]
             L.keops_gauss_grad_x_ranges.argtypes = [P, P, P, P, i64, i64, i32, i32, f32, P, i64, P, P, i64, P, P]
+            L.keops_laplace_sum.argtypes = [P, P, P, i64, i64, i32, i32, f32, P, P]
             L.keops_gauss_max.argtypes = [P, P, P, i64, i64, i32, i32, f32, P, P, P]
             L.keops_gauss_min.argtypes = [P, P, P, i64, i64, i32, i32, f32, P, P, P]
             L.keops_kmin.argtypes = [P, P, i64, i64, i32, i32, P, P, P]
@@ -73,7 +74,8 @@ def lib() -> ctypes.CDLL:
             L.keops_status_string.restype = ctypes.c_char_p
             for f in ("keops_gauss_sum", "keops_gauss_lse", "keops_gauss_grad_x", "keops_gauss_grad_y",
                       "keops_gauss_grad_b", "keops_gauss_cg", "keops_gauss_sum_ranges", "keops_gauss_lse_ranges",
-                      "keops_gauss_grad_x_ranges", "keops_gauss_max", "keops_gauss_min", "keops_kmin",
+                      "keops_gauss_grad_x_ranges", "keops_gauss_max", "keops_gauss_min", "keops_laplace_sum",
+                      "keops_kmin",
                       "keops_set_option", "keops_version", "keops_profile_read"):
                 getattr(L, f).restype = ctypes.c_int
             _lib = L
@@ -150,6 +152,11 @@ def keops_gauss_sum(x, y, b, sigma, out=None, stream=None):
 def keops_gauss_lse(x, y, b, sigma, out=None, stream=None):
     """out[i, e] = log sum_j exp(-|x_i - y_j|^2 / sigma^2 + b[j, e])."""
     return _gauss("keops_gauss_lse", x, y, b, sigma, out, stream)
+
+
+def keops_laplace_sum(x, y, b, sigma, out=None, stream=None):
+    """out[i, e] = sum_j exp(-|x_i - y_j| / sigma) b[j, e]   (the Laplacian kernel)."""
+    return _gauss("keops_laplace_sum", x, y, b, sigma, out, stream)
 
 
 def keops_gauss_grad_x(x, y, b, g, sigma, out=None, stream=None):

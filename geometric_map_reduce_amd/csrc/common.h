@@ -18,7 +18,7 @@ constexpr float kFastR2 = 128.0f;
 // Exponent offset (log2 units) of the direct form's sums and gradients.
 constexpr float kDirectOffset = 64.0f;
 
-enum Op : int { OP_SUM = 0, OP_LSE = 1, OP_GRAD = 2, OP_MAX = 3 };
+enum Op : int { OP_SUM = 0, OP_LSE = 1, OP_GRAD = 2, OP_MAX = 3, OP_LAPLACE = 4 };
 enum Form : int { FORM_AUTO = 0, FORM_DIRECT = 1 };
 
 // One work-group's share of a block-sparse launch: rows [row_lo, row_hi)
@@ -37,7 +37,8 @@ struct BsItem {
 struct GaussArgs {
   const float *x, *y, *b, *g;
   int64_t M, N;
-  float scale;          // sqrt(log2 e) / sigma: exp(-d^2/sigma^2) = exp2(-|scale*(x-y)|^2)
+  float scale;          // sqrt(log2 e) / sigma: exp(-d^2/sigma^2) = exp2(-|scale*(x-y)|^2);
+                        // OP_LAPLACE: sqrt(log2 e / sigma), so scale^2 |x - y| is the log2 exponent
   float grad_coef;      // -(2 / sigma^2) / scale  (expanded form: scaled coordinates)
   float grad_coef_direct;  // -(2 / sigma^2)        (direct form: raw coordinates)
   float *out;           // final output when nsplit == 1, else partials [nsplit][M][W]

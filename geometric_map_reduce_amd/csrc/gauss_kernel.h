@@ -1,6 +1,6 @@
 // gauss_kernel.h -- pass-1 kernel of the Gaussian sum, LogSumExp, grad_x and
-// Max/ArgMax reductions on gfx950 VALU (the D < 32 hot path; also the
-// reference VALU path at large D).
+// Max/ArgMax reductions, and of the Laplacian kernel sum, on gfx950 VALU (the
+// D < 32 hot path; also the reference VALU path at large D).
 //
 // Operation (KeOps pages: "Kernel Operations on the GPU, with Autodiff,
 // without Memory Overflows" §1 "Target operation" and §2; KeOps README
@@ -75,7 +75,8 @@ __device__ __forceinline__ float lane4(const float4 &v, int u) {
 //   EXPANDED: q_r = <x'_r, 2y'> + c_j      (xs = x', record = (2y', c_j))
 //   DIRECT  : q_r = off - s^2 |x_r - y|^2  (xs = raw x, record = raw y); the
 //             differences are kept in d for the grad_x accumulation.
-template <bool FAST, int R, int D, int NV4>
+//   LAPLACE : q_r = off - s2 |x_r - y|      (direct form only; s2 = log2 e / sigma)
+template <bool FAST, int R, int D, int NV4, bool LAPLACE = false>
 __device__ __forceinline__ void pair_exponent(const float (&xs)[R][D], const float (&yv)[NV4], float s2, float off,
                                               float (&q)[R], float (&d)[FAST ? 1 : R][D]) {
   if (FAST) {
@@ -96,6 +97,10 @@ __device__ __forceinline__ void pair_exponent(const float (&xs)[R][D], const flo
     for (int k = 0; k < D; ++k)
 #pragma unroll
       for (int r = 0; r < R; ++r) q[r] = fmaf(d[FAST ? 0 : r][k], d[FAST ? 0 : r][k], q[r]);
+    if (LAPLACE) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) q[r] = __builtin_amdgcn_sqrtf(q[r]);   // v_sqrt_f32, about 1 ulp
+    }
 #pragma unroll
     for (int r = 0; r < R; ++r) q[r] = fmaf(-s2, q[r], off);
   }
@@ -253,12 +258,12 @@ __device__ __forceinline__ void gauss_jloop(const GaussArgs &a,
           float yv[4 * NV];
           load_rec<NV>(rec, jj + u, yv);
           float ex[R], dd[FAST ? 1 : R][D];
-          pair_exponent<FAST>(xs, yv, s2, off, ex, dd);
+          pair_exponent<FAST, R, D, 4 * NV, OP == OP_LAPLACE>(xs, yv, s2, off, ex, dd);
 #pragma unroll
           for (int r = 0; r < R; ++r) ex[r] = fast_exp2(ex[r]);
 #pragma unroll
           for (int r = 0; r < R; ++r) {
-            if (OP == OP_SUM) {
+            if (OP == OP_SUM || OP == OP_LAPLACE) {
 #pragma unroll
               for (int e = 0; e < E; ++e) part[r][e] = fmaf(ex[r], lane4(pq[e], u), part[r][e]);
             } else if (OP == OP_MAX) {
@@ -385,7 +390,9 @@ __global__ __launch_bounds__(kThreads) void gauss_valu_kernel(GaussArgs a) {
     if (valid[r]) r2 = fmaxf(r2, n);
   }
   r2 = block_max(r2, sRed + 2 * D * (kThreads / kWave));
-  const bool fast = a.form == FORM_AUTO && r2 <= kFastR2;
+  // the Laplacian kernel needs |x - y| itself, which the expanded form cannot give
+  // accurately for close pairs: always the direct form
+  const bool fast = OP != OP_LAPLACE && a.form == FORM_AUTO && r2 <= kFastR2;
   // Offset folded into every j constant so that exp2 stays within range: the
   // largest exponent is r2 - G and the smallest row factor exponent is -G.
   const float G = (OP == OP_LSE || !fast) ? 0.0f : 0.5f * r2;
@@ -444,13 +451,13 @@ __global__ __launch_bounds__(kThreads) void gauss_valu_kernel(GaussArgs a) {
 
   // ---- finalise and store
   const bool partial = a.nsplit > 1;
-  constexpr int W = (OP == OP_SUM) ? E : ((OP == OP_LSE || OP == OP_MAX) ? (2 * E) : D);
+  constexpr int W = (OP == OP_SUM || OP == OP_LAPLACE) ? E : ((OP == OP_LSE || OP == OP_MAX) ? (2 * E) : D);
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     if (!valid[r]) continue;
     const int64_t i = row0 + (int64_t)r * kThreads + tid;
     float res[W];
-    if (OP == OP_SUM) {
+    if (OP == OP_SUM || OP == OP_LAPLACE) {
       const float f = fast ? exp2f(G - nx[r]) : exp2f(-kDirectOffset);
 #pragma unroll
       for (int e = 0; e < E; ++e) res[e] = acc[r][e] * f;

@@ -87,11 +87,12 @@ bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
 using GaussDispatch = int (*)(int, int, int, VariantInfo *, dim3, const GaussArgs *, hipStream_t);
 using KminDispatch = int (*)(int, int, VariantInfo *, dim3, const KminArgs *, hipStream_t);
 
-const GaussDispatch kGaussUnits[4][2] = {
+const GaussDispatch kGaussUnits[5][2] = {
     {gauss_dispatch_sum_small, gauss_dispatch_sum_large},
     {gauss_dispatch_lse_small, gauss_dispatch_lse_large},
     {gauss_dispatch_grad_small, gauss_dispatch_grad_large},
     {gauss_dispatch_max_small, gauss_dispatch_max_large},
+    {laplace_dispatch_sum_small, laplace_dispatch_sum_large},
 };
 const KminDispatch kKminUnits[3] = {kmin_dispatch_d1_4, kmin_dispatch_d5_8, kmin_dispatch_large};
 
@@ -279,7 +280,9 @@ int gauss_entry(int op, const float *x, const float *y, const float *b, const fl
                                       kGaussWgsPerCu, op == OP_GRAD ? wide_info.rows_per_wg * cus : kWideMinRows);
 
   const double s2 = (double)sigma * (double)sigma;
-  const double scale = std::sqrt(1.4426950408889634 / s2);
+  // Laplacian: scale^2 = log2(e) / sigma multiplies |x - y|
+  const double scale = op == OP_LAPLACE ? std::sqrt(1.4426950408889634 / (double)sigma)
+                                        : std::sqrt(1.4426950408889634 / s2);
   GaussArgs a{};
   a.x = x; a.y = y; a.b = b; a.g = g;
   a.M = M; a.N = N;
@@ -295,7 +298,7 @@ int gauss_entry(int op, const float *x, const float *y, const float *b, const fl
 
   // workspace: split-j partials, then (MFMA path) one form flag per row block
   float *ws = nullptr;
-  const int PW = op == OP_SUM ? E : ((op == OP_LSE || op == OP_MAX) ? 2 * E : D);
+  const int PW = (op == OP_SUM || op == OP_LAPLACE) ? E : ((op == OP_LSE || op == OP_MAX) ? 2 * E : D);
   const size_t part_bytes = p.nsplit > 1 ? ((size_t)p.nsplit * M * PW * sizeof(float) + 255) / 256 * 256 : 0;
   const size_t flag_bytes = use_mfma ? (size_t)p.nblk * sizeof(int) : 0;
   if (part_bytes + flag_bytes > 0) {
@@ -650,6 +653,11 @@ int keops_gauss_max(const float *x, const float *y, const float *b, int64_t M, i
 int keops_gauss_min(const float *x, const float *y, const float *b, int64_t M, int64_t N, int32_t D, int32_t E,
                     float sigma, float *out, int64_t *out_idx, void *stream) {
   return gauss_entry(OP_MAX, x, y, b, nullptr, M, N, D, E, sigma, out, stream, out_idx, -1.0f);
+}
+
+int keops_laplace_sum(const float *x, const float *y, const float *b, int64_t M, int64_t N, int32_t D, int32_t E,
+                      float sigma, float *out, void *stream) {
+  return gauss_entry(OP_LAPLACE, x, y, b, nullptr, M, N, D, E, sigma, out, stream);
 }
 
 int keops_kmin(const float *x, const float *y, int64_t M, int64_t N, int32_t D, int32_t K, float *out_d,

@@ -23,6 +23,8 @@ KMI_DECLARE_GAUSS(gauss_dispatch_grad_small)
 KMI_DECLARE_GAUSS(gauss_dispatch_grad_large)
 KMI_DECLARE_GAUSS(gauss_dispatch_max_small)
 KMI_DECLARE_GAUSS(gauss_dispatch_max_large)
+KMI_DECLARE_GAUSS(laplace_dispatch_sum_small)
+KMI_DECLARE_GAUSS(laplace_dispatch_sum_large)
 KMI_DECLARE_GAUSS(gauss_dispatch_sum_mfma)
 #undef KMI_DECLARE_GAUSS
 

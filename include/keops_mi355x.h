@@ -99,6 +99,17 @@ int keops_gauss_min(const float *x, const float *y, const float *b, int64_t M, i
                     float sigma, float *out, int64_t *out_idx, void *stream);
 
 /*
+ * Laplacian kernel sum ([README] feature list: a wide range of formulas,
+ * beyond the Gaussian kernel):
+ *   out[i, e] = sum_j exp(-|x_i - y_j| / sigma) b[j, e],  |.| the Euclidean norm.
+ * Shapes, conventions and errors as keops_gauss_sum.  Computed from raw
+ * differences (never the expanded distance, whose rounding near x = y would
+ * reach the square root).
+ */
+int keops_laplace_sum(const float *x, const float *y, const float *b, int64_t M, int64_t N, int32_t D, int32_t E,
+                      float sigma, float *out, void *stream);
+
+/*
  * Gradient of the kernel sum with respect to x ([KO-GPU] §2 "Performance and
  * differentiation"; [README] torch.autograd.grad((a_i ** 2).sum(), [x])), as
  * the vector-Jacobian product with the cotangent g = dL/da:

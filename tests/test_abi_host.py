@@ -28,7 +28,8 @@ def L():
 def test_header_declares_the_reductions():
     names = declared_functions()
     for n in ("keops_gauss_sum", "keops_gauss_lse", "keops_gauss_grad_x", "keops_gauss_grad_y",
-              "keops_gauss_grad_b", "keops_gauss_cg", "keops_gauss_max", "keops_gauss_min", "keops_kmin"):
+              "keops_gauss_grad_b", "keops_gauss_cg", "keops_gauss_max", "keops_gauss_min", "keops_laplace_sum",
+              "keops_kmin"):
         assert n in names
 
 

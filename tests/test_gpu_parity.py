@@ -404,6 +404,44 @@ def test_workload_max_1M():
     say(f"  indices differing from the oracle's (near ties): {n}")
 
 
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "M%d_N%d_D%d_E%d_s%g" % c)
+def test_small_laplace(case):
+    M, N, D, E, sigma = case
+    say(f"laplace M={M} N={N} D={D} E={E} sigma={sigma}")
+    x, y, b, _ = rand_case(5000 + M + N + D, M, N, D, E)
+    sigma = float(np.float32(sigma))
+    a = host(gm.keops_laplace_sum(dev(x), dev(y), dev(b), sigma))
+    a_ref, n_ref = oracle.laplace_sum(x, y, b, sigma)
+    check_sum(a, a_ref, n_ref, what="laplace")
+
+
+@pytest.mark.parametrize("split", [0, 1, 4])
+@pytest.mark.parametrize("rows", [1, 2], ids=["narrow", "wide"])
+def test_laplace_splits_layouts_far(split, rows):
+    say(f"laplace split={split} rows={rows}")
+    gm.keops_set_option(gm.KEOPS_OPT_SPLIT_J, split)
+    gm.keops_set_option(gm.KEOPS_OPT_ROWS, rows)
+    rng = np.random.default_rng(31 + split)
+    for shift, scale, sigma in [(0.0, 1.0, 0.3), (500.0, 3.0, 0.8), (0.0, 20.0, 2.0)]:
+        x = (rng.standard_normal((1500, 3)) * scale + shift).astype(np.float32)
+        y = np.concatenate([x[::2] + np.float32(1e-3) * rng.standard_normal((750, 3)).astype(np.float32),
+                            (rng.standard_normal((900, 3)) * scale + shift).astype(np.float32)])
+        b = rng.standard_normal((y.shape[0], 2)).astype(np.float32)
+        a = host(gm.keops_laplace_sum(dev(x), dev(y), dev(b), sigma))
+        a_ref, n_ref = oracle.laplace_sum(x, y, b, sigma)
+        check_sum(a, a_ref, n_ref, what="laplace")
+
+
+def test_workload_laplace_1M():
+    w = workloads.WORKLOADS["sum_lse_1M"]
+    say("workload sum_lse_1M: Laplacian sum")
+    x, y, b = workloads.make_inputs(w)
+    a = host(gm.keops_laplace_sum(dev(x), dev(y), dev(b), w.sigma))
+    rows = _sample(w.M, 256)
+    a_ref, n_ref = oracle.laplace_sum(x, y, b, w.sigma, rows=rows)
+    say(f"  max err / norm {check_sum(a[rows], a_ref, n_ref, what='laplace'):.3g}")
+
+
 KMIN_SMALL = [(1, 1, 1, 1), (5, 40, 3, 10), (300, 1000, 3, 10), (257, 513, 2, 16), (100, 3000, 4, 32),
               (70, 600, 8, 7), (64, 300, 16, 5), (40, 500, 32, 10), (30, 200, 50, 3), (25, 300, 64, 10),
               (10, 128, 100, 2), (200, 900, 5, 1), (129, 129, 3, 12)]
