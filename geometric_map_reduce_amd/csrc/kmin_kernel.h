@@ -29,8 +29,12 @@ struct KminShape {
   static constexpr int TJ = (2 * 256 * BYTES_PER_J <= 49152) ? 256
                           : (2 * 128 * BYTES_PER_J <= 49152) ? 128
                           : (2 * 64 * BYTES_PER_J <= 49152) ? 64 : 32;
-  // rows per lane: keep roughly 100 VGPRs of per-row state
-  static constexpr int R0 = 100 / (2 * K + 2 * D + 4);
+  // rows per lane: the most (up to 4) that keep the kernel within 128 VGPRs, i.e.
+  // four waves per SIMD.  The register model 30 + R (2K + 3D + 8) follows the
+  // compiled counts (e.g. D = 3, K = 10: 66 / 102 / 132 VGPRs for R = 1 / 2 / 3);
+  // at that shape R = 2 (4 waves) ran 8 % faster than R = 3 (3 waves) and 11 %
+  // faster than R = 1 (7 waves).
+  static constexpr int R0 = (124 - 30) / (2 * K + 3 * D + 8);
   static constexpr int R = R0 < 1 ? 1 : (R0 > 4 ? 4 : R0);
 };
 
