@@ -32,6 +32,7 @@ KEOPS_OPT_FORM = 2
 KEOPS_OPT_ROWS = 3
 KEOPS_OPT_PROFILE = 4
 KEOPS_OPT_WG_TARGET = 5
+KEOPS_OPT_MFMA = 6
 
 _lock = threading.Lock()
 _lib = None

@@ -26,6 +26,9 @@ CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
     # no packed fp32 (v_pk_*_f32) code generation anywhere
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs: no accumulation-register copies before the
+    # VALU reads them, and a smaller register footprint (more waves per SIMD)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-result", "-Wno-unused-value",
     "-I", INCLUDE, "-I", CSRC,
 ]

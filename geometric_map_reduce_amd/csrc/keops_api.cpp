@@ -18,7 +18,8 @@
 namespace kmi {
 namespace {
 
-std::atomic<int64_t> g_opt_split{0}, g_opt_form{0}, g_opt_rows{0}, g_opt_profile{0}, g_opt_wg_target{0};
+std::atomic<int64_t> g_opt_split{0}, g_opt_form{0}, g_opt_rows{0}, g_opt_profile{0}, g_opt_wg_target{0},
+    g_opt_mfma{0};
 
 // ---- pass-1 timing (KEOPS_OPT_PROFILE)
 struct EventPair { hipEvent_t start, stop; };
@@ -247,9 +248,9 @@ int gauss_entry(int op, const float *x, const float *y, const float *b, const fl
   GaussDispatch fn = nullptr;
   if (gauss_find(op, D, E, 1, &wide_info, &fn) || gauss_find(op, D, E, 0, &narrow_info, &fn))
     return KEOPS_ERR_UNSUPPORTED;
-  // fp32-MFMA cross term where the contraction is large enough (D >= 32)
+  // fp32-MFMA cross term where the contraction is large enough (D >= 32), unless switched off
   const int64_t form = g_opt_form.load();
-  const bool use_mfma = op == OP_SUM && D >= 32 && form == 0 &&
+  const bool use_mfma = op == OP_SUM && D >= 32 && form == 0 && g_opt_mfma.load() == 0 &&
                         gauss_dispatch_sum_mfma(D, E, 0, &mfma_info, dim3(), nullptr, nullptr) == 0;
   if (M == 0) return KEOPS_OK;
 
@@ -681,7 +682,8 @@ int keops_kmin(const float *x, const float *y, int64_t M, int64_t N, int32_t D, 
   if (kmin_find(D, K, &info, &fn)) return KEOPS_ERR_UNSUPPORTED;
   // fp32-MFMA prefilter at D >= 32 (the result is the same direct-form K-min)
   VariantInfo mfma_info{};
-  if (D >= 32 && g_opt_form.load() == 0 && kmin_dispatch_mfma(D, K, &mfma_info, dim3(), nullptr, nullptr) == 0) {
+  if (D >= 32 && g_opt_form.load() == 0 && g_opt_mfma.load() == 0 &&
+      kmin_dispatch_mfma(D, K, &mfma_info, dim3(), nullptr, nullptr) == 0) {
     fn = kmin_dispatch_mfma;
     info = mfma_info;
   }
@@ -752,6 +754,10 @@ int keops_set_option(int option, int64_t value) {
     case KEOPS_OPT_WG_TARGET:
       if (value < 0 || value > 4096) return KEOPS_ERR_INVALID_ARG;
       g_opt_wg_target.store(value);
+      return KEOPS_OK;
+    case KEOPS_OPT_MFMA:
+      if (value < 0 || value > 1) return KEOPS_ERR_INVALID_ARG;
+      g_opt_mfma.store(value);
       return KEOPS_OK;
     default:
       return KEOPS_ERR_INVALID_ARG;

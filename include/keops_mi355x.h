@@ -221,6 +221,9 @@ const char *keops_status_string(int status);
  *                          automatically for M <= 64 at D <= 8)
  *   KEOPS_OPT_WG_TARGET -- work-groups per CU the automatic j-split aims for
  *                          (1..4096; ignored when KEOPS_OPT_SPLIT_J is set)
+ *   KEOPS_OPT_MFMA      -- 1 = the Gaussian sum and K-min never use the fp32
+ *                          matrix cores (the VALU expanded form runs at every
+ *                          D; automatically they are used for D >= 32)
  * Returns KEOPS_OK, or KEOPS_ERR_INVALID_ARG for an unknown option or value.
  */
 #define KEOPS_OPT_SPLIT_J 1
@@ -228,6 +231,7 @@ const char *keops_status_string(int status);
 #define KEOPS_OPT_ROWS 3
 #define KEOPS_OPT_PROFILE 4   /* 1 = record HIP events around each pass-1 launch */
 #define KEOPS_OPT_WG_TARGET 5
+#define KEOPS_OPT_MFMA 6
 int keops_set_option(int option, int64_t value);
 
 /*

@@ -35,10 +35,10 @@ def say(msg):
 def _options():
     if not torch.cuda.is_available():
         pytest.skip("needs a GPU")
-    for o in (gm.KEOPS_OPT_SPLIT_J, gm.KEOPS_OPT_FORM, gm.KEOPS_OPT_ROWS, gm.KEOPS_OPT_WG_TARGET):
+    for o in (gm.KEOPS_OPT_SPLIT_J, gm.KEOPS_OPT_FORM, gm.KEOPS_OPT_ROWS, gm.KEOPS_OPT_WG_TARGET, gm.KEOPS_OPT_MFMA):
         gm.keops_set_option(o, 0)
     yield
-    for o in (gm.KEOPS_OPT_SPLIT_J, gm.KEOPS_OPT_FORM, gm.KEOPS_OPT_ROWS, gm.KEOPS_OPT_WG_TARGET):
+    for o in (gm.KEOPS_OPT_SPLIT_J, gm.KEOPS_OPT_FORM, gm.KEOPS_OPT_ROWS, gm.KEOPS_OPT_WG_TARGET, gm.KEOPS_OPT_MFMA):
         gm.keops_set_option(o, 0)
 
 
@@ -649,20 +649,26 @@ def test_workload_kmin(name):
 @pytest.mark.parametrize("D", [32, 50, 64, 100])
 @pytest.mark.parametrize("E", [1, 3])
 def test_mfma_vs_valu(D, E):
-    """fp32-MFMA cross term (automatic at D >= 32) and the VALU direct form (forced)
-    both match the oracle; the deviation between the two paths is reported."""
+    """fp32-MFMA cross term (automatic at D >= 32), the VALU expanded form (matrix cores
+    switched off) and the VALU direct form (forced) all match the oracle; the deviation
+    between the MFMA and VALU paths is reported."""
     M, N, sigma = 700, 2300, 0.9 * np.sqrt(D / 3.0)
     say(f"mfma vs valu D={D} E={E}")
     x, y, b, _ = rand_case(50 + D + E, M, N, D, E, scale=1.0)
     X, Y, B = dev(x), dev(y), dev(b)
     a_ref, n_ref = oracle.gauss_sum(x, y, b, float(np.float32(sigma)))
     a_mfma = host(gm.keops_gauss_sum(X, Y, B, sigma))
+    gm.keops_set_option(gm.KEOPS_OPT_MFMA, 1)
+    a_vexp = host(gm.keops_gauss_sum(X, Y, B, sigma))
+    gm.keops_set_option(gm.KEOPS_OPT_MFMA, 0)
     gm.keops_set_option(gm.KEOPS_OPT_FORM, 1)
     a_valu = host(gm.keops_gauss_sum(X, Y, B, sigma))
     e1 = check_sum(a_mfma, a_ref, n_ref, what="sum (mfma)")
-    e2 = check_sum(a_valu, a_ref, n_ref, what="sum (valu)")
+    e2 = check_sum(a_valu, a_ref, n_ref, what="sum (valu direct)")
+    e3 = check_sum(a_vexp, a_ref, n_ref, what="sum (valu expanded)")
     dev_paths = float(np.max(np.abs(a_mfma - a_valu) / np.maximum(n_ref, 1e-300)))
-    say(json.dumps({"D": D, "E": E, "mfma_err": e1, "valu_err": e2, "mfma_vs_valu": dev_paths}))
+    say(json.dumps({"D": D, "E": E, "mfma_err": e1, "valu_err": e2, "valu_expanded_err": e3,
+                    "mfma_vs_valu": dev_paths}))
 
 
 @pytest.mark.parametrize("split", [0, 1, 4])
@@ -695,9 +701,13 @@ def test_kmin_mfma_equals_valu(D, K):
     y[2999] = y[5]                                   # an exact tie
     X, Y = dev(x), dev(y)
     d1, i1 = gm.keops_kmin(X, Y, K)
+    gm.keops_set_option(gm.KEOPS_OPT_MFMA, 1)        # matrix cores off: the VALU kernel
+    d3, i3 = gm.keops_kmin(X, Y, K)
+    gm.keops_set_option(gm.KEOPS_OPT_MFMA, 0)
     gm.keops_set_option(gm.KEOPS_OPT_FORM, 1)        # forces the VALU kernel
     d2, i2 = gm.keops_kmin(X, Y, K)
-    d1, i1, d2, i2 = host(d1), host(i1), host(d2), host(i2)
+    d1, i1, d2, i2, d3, i3 = host(d1), host(i1), host(d2), host(i2), host(d3), host(i3)
+    assert np.array_equal(i3, i2) and np.array_equal(d3.view(np.int32), d2.view(np.int32))
     d_ref, i_ref = oracle.kmin(x, y, K)
     check_kmin(x, y, np.arange(600), d2, i2, d_ref, i_ref)   # VALU path
     check_kmin(x, y, np.arange(600), d1, i1, d_ref, i_ref)   # MFMA path
