@@ -112,10 +112,12 @@ int kmin_find(int D, int K, VariantInfo *info, KminDispatch *fn) {
 // Default work-groups per CU for each kernel family, from sweeps at the
 // 1M x 1M (D = 3), 100k x 10M (D = 50) and 1M x 1M K-min shapes: the VALU sum,
 // LSE and grad gain 7-8 % going from 4 to 24, the MFMA sum 7 % from 4 to 16;
-// K-min's partial lists are larger, and more splits cost about what they balance.
+// K-min's partial lists are larger, and every split starts its lists empty (the
+// early candidates nearly all insert): at 1M x 1M, D = 3, one split (4 per CU)
+// ran 112 ms against 115 ms with two (8 per CU) and 114 ms with 16 per CU.
 constexpr int64_t kGaussWgsPerCu = 24;
 constexpr int64_t kMfmaSumWgsPerCu = 16;
-constexpr int64_t kKminWgsPerCu = 8;
+constexpr int64_t kKminWgsPerCu = 4;
 constexpr int64_t kKminMfmaWgsPerCu = 4;
 // Rows from which the sum and LSE take the wide variant (several rows per lane):
 // at 50k rows and above it was faster than one row per lane by 3-20 %, at 20k

@@ -207,16 +207,27 @@ __global__ __launch_bounds__(kThreads) void kmin_valu_kernel(KminArgs a) {
     const int cnt = (int)(((je - jt < TJ ? je - jt : TJ) + 3) & ~3);
     const float4 *rec = sRec[buf];
     const float4 *raw = sRaw[buf];
-    for (int jj = 0; jj < cnt; jj += 4) {
-      // prefilter 4 j x R rows; one wave-level branch for the whole group
+    // Records of a group of 4 j live in registers: two buffers, each read from
+    // LDS one group ahead of its use (wrapping inside the tile past its end, where
+    // the values are never used).
+    auto read_group = [&](float4 (&g)[4][NV], int jj) {
+      const int jw = jj & (TJ - 1);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < NV; ++v) g[u][v] = rec[(jw + u) * NV + v];
+    };
+    // Filter 4 j x R rows; one wave-level branch for the whole group (each
+    // compare's lane mask is ORed in scalar registers: one VALU compare per pair).
+    auto filter_group = [&](const float4 (&g)[4][NV], int jj) {
       float t[4][R];
-      float lowest = INFINITY;
+      uint64_t hit = 0;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         float yv[4 * NV];
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
-          const float4 q = rec[(jj + u) * NV + v];
+          const float4 q = g[u][v];
           yv[4 * v] = q.x; yv[4 * v + 1] = q.y; yv[4 * v + 2] = q.z; yv[4 * v + 3] = q.w;
         }
 #pragma unroll
@@ -226,14 +237,18 @@ __global__ __launch_bounds__(kThreads) void kmin_valu_kernel(KminArgs a) {
 #pragma unroll
           for (int r = 0; r < R; ++r) t[u][r] = fmaf(xm[r][k], yv[k], t[u][r]);
 #pragma unroll
-        for (int r = 0; r < R; ++r) lowest = fminf(lowest, t[u][r] - thr[r]);
+        for (int r = 0; r < R; ++r) hit |= __builtin_amdgcn_ballot_w64(t[u][r] < thr[r]);
       }
-      if (lowest < 0.0f) {
+      if (hit) {   // wave-uniform
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
 #pragma unroll
           for (int r = 0; r < R; ++r) {
-            if (t[u][r] < thr[r]) {
+            // compare again here (an opaque copy of t): keeping the loop's compare
+            // results alive across the branch costs more VALU work than redoing it
+            float tt = t[u][r];
+            asm volatile("" : "+v"(tt));
+            if (tt < thr[r]) {
               float yr[4 * NR];
 #pragma unroll
               for (int v = 0; v < NR; ++v) {
@@ -252,6 +267,16 @@ __global__ __launch_bounds__(kThreads) void kmin_valu_kernel(KminArgs a) {
             }
           }
         }
+      }
+    };
+    float4 ga[4][NV], gb[4][NV];
+    read_group(ga, 0);
+    for (int jj = 0; jj < cnt; jj += 8) {
+      read_group(gb, jj + 4);
+      filter_group(ga, jj);
+      if (jj + 4 < cnt) {   // wave-uniform
+        read_group(ga, jj + 8);
+        filter_group(gb, jj + 4);
       }
     }
     if (has_next) stage(buf ^ 1, ok_next);
