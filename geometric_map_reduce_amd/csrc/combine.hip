@@ -22,7 +22,7 @@ __global__ __launch_bounds__(kThreads) void sum_combine_kernel(const float *__re
 }
 
 __global__ __launch_bounds__(kThreads) void lse_combine_kernel(const float *__restrict__ ws, int nsplit,
-                                                               int64_t M, int E, float *__restrict__ out) {
+                                                               int64_t M, int E, float thr, float *__restrict__ out) {
   const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (t >= M * E) return;
   const int64_t i = t / E;
@@ -33,7 +33,25 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(const float *__re
   for (int k = 0; k < nsplit; ++k) m = fmaxf(m, p[k * stride]);
   float s = 0.0f;
   for (int k = 0; k < nsplit; ++k) s += p[k * stride + 1] * exp2f(p[k * stride] - m);
-  out[t] = kLn2 * (m + log2f(s));
+  // a sum below thr (fixed-shift partials: possibly lost to underflow) or NaN is
+  // left as NaN for the fix-up launch
+  out[t] = s >= thr ? kLn2 * (m + log2f(s)) : __int_as_float(0x7fc00000);
+}
+
+// part[blockIdx.x] = max of b over a grid-strided share (NaN ignored; -inf if empty)
+__global__ __launch_bounds__(kThreads) void bmax_kernel(const float *__restrict__ b, int64_t n,
+                                                        float *__restrict__ part) {
+  __shared__ float red[kThreads];
+  float m = -INFINITY;
+  for (int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x; t < n; t += (int64_t)gridDim.x * kThreads)
+    m = fmaxf(m, b[t]);
+  red[threadIdx.x] = m;
+  __syncthreads();
+  for (int w = kThreads / 2; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + w]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) part[blockIdx.x] = red[0];
 }
 
 template <int K>
@@ -116,8 +134,13 @@ void launch_sum_combine(const float *ws, int nsplit, int64_t count, float *out, 
   if (count > 0) hipLaunchKernelGGL(sum_combine_kernel, dim3(blocks_for(count)), dim3(kThreads), 0, st, ws, nsplit, count, out);
 }
 
-void launch_lse_combine(const float *ws, int nsplit, int64_t M, int E, float *out, hipStream_t st) {
-  if (M * E > 0) hipLaunchKernelGGL(lse_combine_kernel, dim3(blocks_for(M * E)), dim3(kThreads), 0, st, ws, nsplit, M, E, out);
+void launch_lse_combine(const float *ws, int nsplit, int64_t M, int E, float thr, float *out, hipStream_t st) {
+  if (M * E > 0)
+    hipLaunchKernelGGL(lse_combine_kernel, dim3(blocks_for(M * E)), dim3(kThreads), 0, st, ws, nsplit, M, E, thr, out);
+}
+
+void launch_bmax(const float *b, int64_t n, float *part, hipStream_t st) {
+  hipLaunchKernelGGL(bmax_kernel, dim3(kBmaxParts), dim3(kThreads), 0, st, b, n, part);
 }
 
 int launch_kmin_combine(const float *pd, const int32_t *pi, int nsplit, int64_t M, int K, float *out_d,

@@ -54,7 +54,20 @@ struct GaussArgs {
   // Null for dense launches (rows from blockIdx.x, j from blockIdx.y).
   const BsItem *items;
   const int64_t *redr;
+  // LogSumExp with a fixed per-row shift (dense launches): kBmaxParts partial
+  // maxima of b (null: always the running-maximum form), ceil(log2 N), and the
+  // smallest row sum (shifted scale) trusted against underflow; below it, or NaN,
+  // the row is written as NaN for the fix-up launch.
+  const float *lse_bmax;
+  float lse_log2n;
+  float lse_thr;
+  // LogSumExp fix-up launch: a work-group returns at once unless one of its rows
+  // holds NaN; otherwise it recomputes its rows with the running maximum.
+  int lse_fixup;
 };
+
+// Partial maxima of b for the fixed-shift LogSumExp (one per pre-pass work-group).
+constexpr int kBmaxParts = 64;
 
 // Arguments of the few-rows sum kernel (j per lane, rows in LDS).
 struct StreamArgs {

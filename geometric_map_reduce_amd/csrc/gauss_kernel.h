@@ -109,7 +109,10 @@ __device__ __forceinline__ void pair_exponent(const float (&xs)[R][D], const flo
 // The j loop of one work-group over [jb, je) for a fixed form (FAST = expanded
 // distance).  Starts and ends with every wave past the LDS buffers, so calls
 // can follow each other (one per j range in block-sparse launches).
-template <int OP, int D, int E, int R, bool FAST>
+// FIXED (LogSumExp, expanded form only): the exponent is taken relative to a
+// shift fixed per row in advance instead of a running maximum, so a pair costs
+// what it costs in the sum (exponent, exp2, add); see the kernel below.
+template <int OP, int D, int E, int R, bool FAST, bool FIXED = false>
 __device__ __forceinline__ void gauss_jloop(const GaussArgs &a,
                                             float4 (*sRec)[GaussShape<OP, D, E>::TJ * GaussShape<OP, D, E>::NV],
                                             float (*sPay)[GaussShape<OP, D, E>::PAY * GaussShape<OP, D, E>::TJ],
@@ -200,7 +203,22 @@ __device__ __forceinline__ void gauss_jloop(const GaussArgs &a,
 #pragma unroll
       for (int p = 0; p < PAY; ++p) pq[p] = *reinterpret_cast<const float4 *>(pay + p * TJ + jj);
 
-      if (OP == OP_LSE) {
+      if (OP == OP_LSE && FIXED) {
+        // exponents are at most G + max_j b_j log2 e (< 128 with the sum below
+        // 2^128): exp2 and accumulate, no maximum to track
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          float yv[4 * NV];
+          load_rec<NV>(rec, jj + u, yv);
+          float q[R], dd[1][D];
+          pair_exponent<true>(xs, yv, s2, off, q, dd);
+#pragma unroll
+          for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+              part[r][e] += fast_exp2(E == 1 ? q[r] : q[r] + lane4(pq[e], u));
+        }
+      } else if (OP == OP_LSE) {
         // online LogSumExp in log2 units: four exponents per row, raise the
         // running max when one exceeds it (rescaling the sums), accumulate.
         float uu[4][R][E];
@@ -328,6 +346,18 @@ __global__ __launch_bounds__(kThreads) void gauss_valu_kernel(GaussArgs a) {
 
   // row blocks already computed by the MFMA kernel (uniform across the work-group)
   if (a.wg_flags && a.wg_flags[blockIdx.x]) return;
+  // LogSumExp fix-up: only work-groups with a row the fixed-shift pass left as NaN
+  if (OP == OP_LSE && a.lse_fixup) {
+    bool bad = false;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t i = (int64_t)blockIdx.x * (kThreads * R) + (int64_t)r * kThreads + threadIdx.x;
+      if (i < a.M)
+#pragma unroll
+        for (int e = 0; e < E; ++e) bad |= a.out[i * E + e] != a.out[i * E + e];
+    }
+    if (!__syncthreads_or(bad)) return;
+  }
 
   const int tid = threadIdx.x;
   const int wid = tid / kWave, lane = tid & (kWave - 1);
@@ -395,7 +425,16 @@ __global__ __launch_bounds__(kThreads) void gauss_valu_kernel(GaussArgs a) {
   const bool fast = OP != OP_LAPLACE && a.form == FORM_AUTO && r2 <= kFastR2;
   // Offset folded into every j constant so that exp2 stays within range: the
   // largest exponent is r2 - G and the smallest row factor exponent is -G.
-  const float G = (OP == OP_LSE || !fast) ? 0.0f : 0.5f * r2;
+  // LogSumExp takes the fixed shift G - |x'|^2 + (max b) log2 e per row when the
+  // exponents, at most G + (max b) log2 e, keep the row sum of N terms below
+  // 2^120; else (and on the fix-up launch) it tracks a running maximum
+  bool lse_fixed = false;
+  if (OP == OP_LSE && fast && a.lse_bmax && !item && !a.lse_fixup) {
+    float bm = -INFINITY;
+    for (int t = 0; t < kBmaxParts; ++t) bm = fmaxf(bm, a.lse_bmax[t]);   // uniform loads
+    lse_fixed = 0.5f * r2 + bm * kLog2e + a.lse_log2n <= 120.0f;
+  }
+  const float G = ((OP == OP_LSE && !lse_fixed) || !fast) ? 0.0f : 0.5f * r2;
   if (fast) {
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -437,7 +476,8 @@ __global__ __launch_bounds__(kThreads) void gauss_valu_kernel(GaussArgs a) {
   if (!item) {
     const int64_t jb = (int64_t)blockIdx.y * a.j_per_split;
     const int64_t je = (jb + a.j_per_split < a.N) ? jb + a.j_per_split : a.N;
-    if (fast) gauss_jloop<OP, D, E, R, true>(a, sRec, sPay, xs, gr, cen, G, acc, ix, jb, je);
+    if (OP == OP_LSE && lse_fixed) gauss_jloop<OP, D, E, R, true, true>(a, sRec, sPay, xs, gr, cen, G, acc, ix, jb, je);
+    else if (fast) gauss_jloop<OP, D, E, R, true>(a, sRec, sPay, xs, gr, cen, G, acc, ix, jb, je);
     else gauss_jloop<OP, D, E, R, false>(a, sRec, sPay, xs, gr, cen, G, acc, ix, jb, je);
   } else {
     for (int64_t k = item->k0; k <= item->k1; ++k) {
@@ -467,9 +507,14 @@ __global__ __launch_bounds__(kThreads) void gauss_valu_kernel(GaussArgs a) {
 #pragma unroll
       for (int e = 0; e < E; ++e) { res[2 * e] = acc[r][e] * f; res[2 * e + 1] = __int_as_float(ix[r][e]); }
     } else if (OP == OP_LSE) {
+      // (max, sum) in log2 units; the fixed form's shift is G - |x'|^2 (the
+      // (max b) log2 e of the bound never enters the exponents)
       const float off = fast ? nx[r] : 0.0f;
 #pragma unroll
-      for (int e = 0; e < E; ++e) { res[2 * e] = acc[r][2 * e] - off; res[2 * e + 1] = acc[r][2 * e + 1]; }
+      for (int e = 0; e < E; ++e) {
+        res[2 * e] = lse_fixed ? G - nx[r] : acc[r][2 * e] - off;
+        res[2 * e + 1] = acc[r][2 * e + 1];
+      }
     } else {
       // expanded: G_k = -(2/sigma^2) (1/s) exp2(G - |x'|^2) sum_j K' <g, b> (x'_k - y'_k)
       // direct:   G_k = -(2/sigma^2) sum_j K <g, b> (x_k - y_k)
@@ -484,8 +529,11 @@ __global__ __launch_bounds__(kThreads) void gauss_valu_kernel(GaussArgs a) {
 #pragma unroll
       for (int w = 0; w < W; ++w) dst[w] = res[w];
     } else if (OP == OP_LSE) {
+      // a fixed-shift sum below the underflow threshold (or NaN) is left as NaN
 #pragma unroll
-      for (int e = 0; e < E; ++e) a.out[i * E + e] = kLn2 * (res[2 * e] + log2f(res[2 * e + 1]));
+      for (int e = 0; e < E; ++e)
+        a.out[i * E + e] = (lse_fixed && !(res[2 * e + 1] >= a.lse_thr)) ? __int_as_float(0x7fc00000)
+                                                                        : kLn2 * (res[2 * e] + log2f(res[2 * e + 1]));
     } else if (OP == OP_MAX) {
 #pragma unroll
       for (int e = 0; e < E; ++e) {

@@ -299,19 +299,33 @@ int gauss_entry(int op, const float *x, const float *y, const float *b, const fl
   a.out_idx = out_idx;
   a.max_sign = max_sign;
 
-  // workspace: split-j partials, then (MFMA path) one form flag per row block
+  // workspace: split-j partials, then (MFMA path) one form flag per row block,
+  // then (LSE) the partial maxima of b
   float *ws = nullptr;
   const int PW = (op == OP_SUM || op == OP_LAPLACE) ? E : ((op == OP_LSE || op == OP_MAX) ? 2 * E : D);
   const size_t part_bytes = p.nsplit > 1 ? ((size_t)p.nsplit * M * PW * sizeof(float) + 255) / 256 * 256 : 0;
-  const size_t flag_bytes = use_mfma ? (size_t)p.nblk * sizeof(int) : 0;
-  if (part_bytes + flag_bytes > 0) {
-    if (hipMallocAsync((void **)&ws, part_bytes + flag_bytes, st) != hipSuccess || !ws) {
+  const size_t flag_bytes = use_mfma ? ((size_t)p.nblk * sizeof(int) + 255) / 256 * 256 : 0;
+  const size_t bmax_bytes = op == OP_LSE ? kBmaxParts * sizeof(float) : 0;
+  if (part_bytes + flag_bytes + bmax_bytes > 0) {
+    if (hipMallocAsync((void **)&ws, part_bytes + flag_bytes + bmax_bytes, st) != hipSuccess || !ws) {
       (void)hipGetLastError();
       return KEOPS_ERR_ALLOC;
     }
   }
   a.out = p.nsplit > 1 ? ws : out;
   const dim3 grid((unsigned)p.nblk, (unsigned)p.nsplit);
+  // LogSumExp: fixed per-row shift where the range allows (bound from max b), with
+  // rows whose shifted sum falls below lse_thr recomputed by the fix-up launch;
+  // each lost term is below 2^-126, so what the threshold trusts is within
+  // N 2^-126 / thr = 2^-16 relative of the sum
+  const int log2n = (int)std::ceil(std::log2((double)N));
+  if (op == OP_LSE) {
+    float *bm = (float *)((char *)ws + part_bytes + flag_bytes);
+    launch_bmax(b, N * E, bm, st);
+    a.lse_bmax = bm;
+    a.lse_log2n = (float)log2n;
+    a.lse_thr = std::ldexp(1.0f, log2n + 16 - 126);
+  }
   const int prof = prof_begin(st);
   if (use_mfma) {
     a.wg_flags = (int *)((char *)ws + part_bytes);
@@ -325,9 +339,20 @@ int gauss_entry(int op, const float *x, const float *y, const float *b, const fl
     prof_end(prof, st);
   }
   if (p.nsplit > 1) {
-    if (op == OP_LSE) launch_lse_combine(ws, p.nsplit, M, E, out, st);
+    if (op == OP_LSE) launch_lse_combine(ws, p.nsplit, M, E, a.lse_thr, out, st);
     else if (op == OP_MAX) launch_max_combine(ws, p.nsplit, M, E, max_sign, out, out_idx, st);
     else launch_sum_combine(ws, p.nsplit, M * PW, out, st);
+  }
+  if (op == OP_LSE) {
+    // rows left as NaN: their 256-row blocks again, one row per lane, whole j range,
+    // with the running maximum (every other work-group returns at once)
+    GaussArgs f = a;
+    f.out = out;
+    f.nsplit = 1;
+    f.j_per_split = N;
+    f.lse_bmax = nullptr;
+    f.lse_fixup = 1;
+    fn(D, E, 0, nullptr, dim3((unsigned)((M + narrow_info.rows_per_wg - 1) / narrow_info.rows_per_wg), 1), &f, st);
   }
   if (ws) (void)hipFreeAsync(ws, st);
   return check_launch();
@@ -493,7 +518,7 @@ int gauss_ranges_entry(int op, const float *x, const float *y, const float *b, c
   fn(D, E, wide ? 1 : 0, nullptr, dim3((unsigned)items.size(), 1), &a, st);
   prof_end(prof, st);
   if (smax > 1) {
-    if (op == OP_LSE) launch_lse_combine(part, (int)smax, M, E, out, st);
+    if (op == OP_LSE) launch_lse_combine(part, (int)smax, M, E, 0.0f, out, st);
     else launch_sum_combine(part, (int)smax, M * PW, out, st);
   }
   (void)hipFreeAsync(ws, st);

@@ -45,7 +45,10 @@ KMI_DECLARE_KMIN(kmin_dispatch_mfma)
 #undef KMI_DECLARE_KMIN
 
 void launch_sum_combine(const float *ws, int nsplit, int64_t count, float *out, hipStream_t st);
-void launch_lse_combine(const float *ws, int nsplit, int64_t M, int E, float *out, hipStream_t st);
+// thr: merged sums below it (or NaN) are written as NaN (0 keeps every finite value)
+void launch_lse_combine(const float *ws, int nsplit, int64_t M, int E, float thr, float *out, hipStream_t st);
+// kBmaxParts partial maxima of b[0..n) into part
+void launch_bmax(const float *b, int64_t n, float *part, hipStream_t st);
 int launch_kmin_combine(const float *pd, const int32_t *pi, int nsplit, int64_t M, int K, float *out_d,
                         int64_t *out_i, hipStream_t st);
 void launch_fill(float *out, int64_t count, float v, hipStream_t st);

@@ -475,6 +475,44 @@ def test_kmin_self_and_permutation():
     assert all(sorted(r) == list(range(16)) for r in i.tolist())
 
 
+@pytest.mark.parametrize("E", [1, 2])
+@pytest.mark.parametrize("rows", [1, 2], ids=["narrow", "wide"])
+@pytest.mark.parametrize("split", [0, 1, 3])
+def test_lse_fixed_shift_and_fixup(split, rows, E):
+    """LogSumExp rows spread over 18 sigma, still inside one work-group's expanded-form
+    range, with every y at one end: rows near the y take the fixed per-row shift; for the
+    far ones every term underflows there, so they are flagged and recomputed by the fix-up
+    launch with a running maximum."""
+    say(f"lse fixed shift / fix-up split={split} rows={rows} E={E}")
+    rng = np.random.default_rng(91 + E)
+    M, N, sigma = 1500, 2000, 1.0
+    x = np.zeros((M, 3), np.float32)
+    x[:, 0] = rng.uniform(-9.0, 9.0, M)
+    x[:, 1:] = 0.1 * rng.standard_normal((M, 2))
+    y = np.zeros((N, 3), np.float32)
+    y[:, 0] = -9.0 + 0.5 * rng.random(N)
+    y[:, 1:] = 0.3 * rng.standard_normal((N, 2))
+    b = rng.standard_normal((N, E)).astype(np.float32)
+    gm.keops_set_option(gm.KEOPS_OPT_SPLIT_J, split)
+    gm.keops_set_option(gm.KEOPS_OPT_ROWS, rows)
+    l = host(gm.keops_gauss_lse(dev(x), dev(y), dev(b), sigma))
+    l_ref = oracle.gauss_lse(x, y, b, sigma)
+    assert l_ref.min() < -250.0 and l_ref.max() > -5.0      # both regimes present
+    check_lse(l, l_ref)
+
+
+def test_lse_large_payload():
+    """b up to about 90: the bound G + (max b) log2 e rules the fixed shift out and the
+    running maximum is used throughout."""
+    say("lse large payload")
+    x, y, b, _ = rand_case(5, 700, 900, 3, 2)
+    b = (b * np.float32(30.0)).astype(np.float32)
+    assert b.max() * np.log2(np.e) > 120
+    for split in (0, 3):
+        gm.keops_set_option(gm.KEOPS_OPT_SPLIT_J, split)
+        check_lse(host(gm.keops_gauss_lse(dev(x), dev(y), dev(b), 0.8)), oracle.gauss_lse(x, y, b, 0.8))
+
+
 def test_empty_and_degenerate():
     say("empty / degenerate sizes")
     x = dev(np.ones((5, 3), np.float32))
