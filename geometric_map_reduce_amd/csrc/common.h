@@ -54,20 +54,30 @@ struct GaussArgs {
   // Null for dense launches (rows from blockIdx.x, j from blockIdx.y).
   const BsItem *items;
   const int64_t *redr;
-  // LogSumExp with a fixed per-row shift (dense launches): kBmaxParts partial
-  // maxima of b (null: always the running-maximum form), ceil(log2 N), and the
-  // smallest row sum (shifted scale) trusted against underflow; below it, or NaN,
-  // the row is written as NaN for the fix-up launch.
-  const float *lse_bmax;
-  float lse_log2n;
+  // Underflow guard of the expanded form (dense launches): the maximum of b
+  // (LogSumExp) or of |b| (sum, grad_x, Max), one float, null when off; ceil(log2 N).
+  // LogSumExp: a fixed per-row shift where the maximum allows; lse_thr is the
+  // smallest shifted row sum trusted against underflow.  Sum and grad_x: a row
+  // whose shifted accumulator falls below N max|b| 2^-109 (grad_x: times
+  // 32 sum_e |g_e|) may have lost terms to the floor of exp2.  Such rows are
+  // written as NaN and recomputed by the fix-up launch.
+  const float *bmax;
+  float log2n;
   float lse_thr;
-  // LogSumExp fix-up launch: a work-group returns at once unless one of its rows
-  // holds NaN; otherwise it recomputes its rows with the running maximum.
-  int lse_fixup;
+  // Split launches of the sum and grad_x with the guard: the partials are left
+  // unscaled, and split 0 writes each row's factor and threshold (threshold -1:
+  // a direct-form row, whose factor is followed by 2^-64 and which is never
+  // flagged).  Null otherwise.
+  float *row_f;
+  float *row_t;
+  // Fix-up launch: a work-group returns at once unless one of its rows holds
+  // NaN; otherwise it recomputes its rows (direct form for the sum and grad_x,
+  // the running maximum for LogSumExp).
+  int fixup;
 };
 
-// Partial maxima of b for the fixed-shift LogSumExp (one per pre-pass work-group).
-constexpr int kBmaxParts = 64;
+// Most work-groups of the max-of-b pre-pass (its scratch holds one float each).
+constexpr int kBmaxParts = 1024;
 
 // Arguments of the few-rows sum kernel (j per lane, rows in LDS).
 struct StreamArgs {
@@ -77,6 +87,11 @@ struct StreamArgs {
   int64_t j_per_wg;     // multiple of the kernel's step (kThreads * j per lane)
   float *part;          // [gridDim.x][M][E] partial sums
   int form;             // Form
+  // Underflow guard: each row's factor exp2(G - |x'|^2) applied to its partials
+  // (expanded form), or -1 (direct form), written by the work-groups of j chunk 0;
+  // and the maximum of |b| over each j chunk (written by row group 0).  Null when off.
+  float *row_fac;
+  float *chunk_bmax;
 };
 
 // Arguments of the K-min pass-1 kernel.

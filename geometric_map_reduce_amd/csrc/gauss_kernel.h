@@ -346,15 +346,16 @@ __global__ __launch_bounds__(kThreads) void gauss_valu_kernel(GaussArgs a) {
 
   // row blocks already computed by the MFMA kernel (uniform across the work-group)
   if (a.wg_flags && a.wg_flags[blockIdx.x]) return;
-  // LogSumExp fix-up: only work-groups with a row the fixed-shift pass left as NaN
-  if (OP == OP_LSE && a.lse_fixup) {
+  // fix-up launch: only work-groups with a row the first pass left as NaN
+  if ((OP == OP_LSE || OP == OP_SUM || OP == OP_GRAD || OP == OP_MAX) && a.fixup) {
+    constexpr int WO = OP == OP_GRAD ? D : E;
     bool bad = false;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int64_t i = (int64_t)blockIdx.x * (kThreads * R) + (int64_t)r * kThreads + threadIdx.x;
       if (i < a.M)
 #pragma unroll
-        for (int e = 0; e < E; ++e) bad |= a.out[i * E + e] != a.out[i * E + e];
+        for (int w = 0; w < WO; ++w) bad |= a.out[i * WO + w] != a.out[i * WO + w];
     }
     if (!__syncthreads_or(bad)) return;
   }
@@ -429,11 +430,15 @@ __global__ __launch_bounds__(kThreads) void gauss_valu_kernel(GaussArgs a) {
   // exponents, at most G + (max b) log2 e, keep the row sum of N terms below
   // 2^120; else (and on the fix-up launch) it tracks a running maximum
   bool lse_fixed = false;
-  if (OP == OP_LSE && fast && a.lse_bmax && !item && !a.lse_fixup) {
-    float bm = -INFINITY;
-    for (int t = 0; t < kBmaxParts; ++t) bm = fmaxf(bm, a.lse_bmax[t]);   // uniform loads
-    lse_fixed = 0.5f * r2 + bm * kLog2e + a.lse_log2n <= 120.0f;
-  }
+  float bm = 0.0f;   // max b (LogSumExp) or max |b| (sum, grad_x) when the guard is on
+  const bool guard = fast && a.bmax && !item && !a.fixup;
+  if (guard) bm = a.bmax[0];   // uniform load
+  if (OP == OP_LSE && guard) lse_fixed = 0.5f * r2 + bm * kLog2e + a.log2n <= 120.0f;
+  // sum, grad_x: below this a shifted accumulator may have lost terms to the floor
+  // (each flushed term is under 2^-126 max|b|, times |g| |x' - y'| < 32 |g| for grad_x);
+  // Max: a maximum below 2^-109 max|b| may be a flushed term's place
+  const float thr_base = !(guard && (OP == OP_SUM || OP == OP_GRAD || OP == OP_MAX)) ? 0.0f
+                         : (OP == OP_MAX ? exp2f(-109.0f) * bm : exp2f(a.log2n - 109.0f) * bm);
   const float G = ((OP == OP_LSE && !lse_fixed) || !fast) ? 0.0f : 0.5f * r2;
   if (fast) {
 #pragma unroll
@@ -492,10 +497,71 @@ __global__ __launch_bounds__(kThreads) void gauss_valu_kernel(GaussArgs a) {
   // ---- finalise and store
   const bool partial = a.nsplit > 1;
   constexpr int W = (OP == OP_SUM || OP == OP_LAPLACE) ? E : ((OP == OP_LSE || OP == OP_MAX) ? (2 * E) : D);
+  // guarded sum / grad_x: split launches leave partials unscaled (pass 2 applies the
+  // row factor and the threshold to the whole row); one split tests here
+  const bool rowwise = (OP == OP_SUM || OP == OP_GRAD || OP == OP_MAX) && a.bmax && !item && !a.fixup;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     if (!valid[r]) continue;
     const int64_t i = row0 + (int64_t)r * kThreads + tid;
+    if (rowwise) {
+      // factor and threshold of the row; threshold -1 marks a direct-form row (factor
+      // then 2^-64, never flagged)
+      float f, t;
+      if (OP == OP_SUM || OP == OP_MAX) {
+        f = fast ? exp2f(G - nx[r]) : 1.0f;
+      } else {
+        f = (fast ? exp2f(G - nx[r]) * a.grad_coef : a.grad_coef_direct) * (E == 1 ? gr[r][0] : 1.0f);
+      }
+      if (fast) {
+        float gs = 32.0f;
+        if (OP == OP_GRAD && E > 1) {
+          gs = 0.0f;
+#pragma unroll
+          for (int e = 0; e < E; ++e) gs += fabsf(gr[r][e]);
+          gs *= 32.0f;
+        }
+        t = OP == OP_GRAD ? thr_base * gs : thr_base;
+      } else {
+        t = -1.0f;
+      }
+      if (OP == OP_MAX) {
+        // (unscaled value, index) partials, or the finished pair
+        if (partial) {
+          float *dst = a.out + ((int64_t)blockIdx.y * M + i) * W;
+#pragma unroll
+          for (int e = 0; e < E; ++e) { dst[2 * e] = acc[r][e]; dst[2 * e + 1] = __int_as_float(ix[r][e]); }
+          if (blockIdx.y == 0) { a.row_f[i] = f; a.row_t[i] = t; }
+        } else {
+          bool low = false;
+#pragma unroll
+          for (int e = 0; e < E; ++e) low |= !(fabsf(acc[r][e]) >= t);
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            const bool flag = t >= 0.0f && low;
+            const float v = t >= 0.0f ? acc[r][e] * f : (acc[r][e] * f) * exp2f(-kDirectOffset);
+            a.out[i * E + e] = flag ? __int_as_float(0x7fc00000) : a.max_sign * v;
+            a.out_idx[i * E + e] = flag ? -1 : (int64_t)ix[r][e];
+          }
+        }
+        continue;
+      }
+      if (partial) {
+        float *dst = a.out + ((int64_t)blockIdx.y * M + i) * W;
+#pragma unroll
+        for (int w = 0; w < W; ++w) dst[w] = acc[r][w];
+        if (blockIdx.y == 0) { a.row_f[i] = f; a.row_t[i] = t; }
+      } else {
+        bool low = false;
+#pragma unroll
+        for (int w = 0; w < W; ++w) low |= !(fabsf(acc[r][w]) >= t);
+#pragma unroll
+        for (int w = 0; w < W; ++w)
+          a.out[i * W + w] = (t >= 0.0f && low) ? __int_as_float(0x7fc00000)
+                                                : (t >= 0.0f ? acc[r][w] * f : (acc[r][w] * f) * exp2f(-kDirectOffset));
+      }
+      continue;
+    }
     float res[W];
     if (OP == OP_SUM || OP == OP_LAPLACE) {
       const float f = fast ? exp2f(G - nx[r]) : exp2f(-kDirectOffset);
@@ -549,6 +615,9 @@ __global__ __launch_bounds__(kThreads) void gauss_valu_kernel(GaussArgs a) {
 
 // Rows per lane of the "wide" variant (large M); the narrow variant holds 1.
 __host__ __device__ constexpr int gauss_rows_wide(int op, int D, int E) {
+#ifdef KMI_SUM_RW
+  if (op == OP_SUM && D <= 4) return KMI_SUM_RW;
+#endif
   return D <= 4 ? (op == OP_SUM ? 8 : 4) : (D <= 8 ? (E <= 2 ? 4 : 2) : (D <= 16 ? 2 : 1));
 }
 

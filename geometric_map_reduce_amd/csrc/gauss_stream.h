@@ -110,7 +110,7 @@ __device__ __forceinline__ void stream_step(float (&ty)[J][D], const float (&tb)
 // in bounds) with b = 0, so they add nothing.
 template <int D, int E, int MR, bool FAST>
 __device__ __forceinline__ void stream_jloop(const StreamArgs &a, const float *sRow, const float (&cen)[D],
-                                             float G, int64_t jb, int cnt, float (&acc)[MR][E]) {
+                                             float G, int64_t jb, int cnt, float (&acc)[MR][E], float &bmx) {
   constexpr int J = stream_j(D, E), STEP = kThreads * J;
   const int tid = threadIdx.x;
   const float s = a.scale;
@@ -130,14 +130,24 @@ __device__ __forceinline__ void stream_jloop(const StreamArgs &a, const float *s
       for (int e = 0; e < E; ++e) tb[k][e] = ok ? pb[e] : 0.0f;
     }
   };
+  // max |b| for the underflow guard, one per j (not per pair), taken when the
+  // payload is used so that the loads stay one step ahead
+  auto track = [&](const float (&tb)[J][E]) {
+#pragma unroll
+    for (int k = 0; k < J; ++k)
+#pragma unroll
+      for (int e = 0; e < E; ++e) bmx = fmaxf(bmx, fabsf(tb[k][e]));
+  };
   float y0[J][D], b0[J][E], y1[J][D], b1[J][E];
   load(y0, b0, 0);
   for (int off = 0; off < cnt; off += 2 * STEP) {
     load(y1, b1, off + STEP);
     stream_step<D, E, MR, J, FAST>(y0, b0, sRow, cen, s, G, acc);
+    track(b0);
     if (off + STEP < cnt) {            // wave-uniform
       load(y0, b0, off + 2 * STEP);
       stream_step<D, E, MR, J, FAST>(y1, b1, sRow, cen, s, G, acc);
+      track(b1);
     }
   }
 }
@@ -152,6 +162,7 @@ void gauss_stream_kernel(StreamArgs a) {
   __shared__ float sG;
   __shared__ int sFast;
   __shared__ float sRed[kThreads / kWave][MR * E];
+  __shared__ float sBm[kThreads / kWave];
 
   const int tid = threadIdx.x;
   const int64_t r0 = (int64_t)blockIdx.y * MR;
@@ -194,12 +205,16 @@ void gauss_stream_kernel(StreamArgs a) {
     }
     sG = G;
     sFast = fast ? 1 : 0;
+    if (a.row_fac && blockIdx.x == 0)
+      for (int i = 0; i < nr; ++i) a.row_fac[r0 + i] = fast ? sFac[i] : -1.0f;
   }
   __syncthreads();
 
+  // uniform across the work-group: held in scalar registers
   float cen[D];
 #pragma unroll
-  for (int d = 0; d < D; ++d) cen[d] = sCen[d];
+  for (int d = 0; d < D; ++d) cen[d] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sCen[d])));
+  const float Gs = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sG)));
   float acc[MR][E];
 #pragma unroll
   for (int i = 0; i < MR; ++i)
@@ -208,8 +223,9 @@ void gauss_stream_kernel(StreamArgs a) {
 
   const int64_t jb = (int64_t)blockIdx.x * a.j_per_wg;
   const int cnt = (int)((jb + a.j_per_wg < a.N) ? a.j_per_wg : a.N - jb);   // >= 1 by the grid
-  if (sFast) stream_jloop<D, E, MR, true>(a, sRow, cen, sG, jb, cnt, acc);
-  else stream_jloop<D, E, MR, false>(a, sRow, cen, sG, jb, cnt, acc);
+  float bmx = 0.0f;
+  if (sFast) stream_jloop<D, E, MR, true>(a, sRow, cen, Gs, jb, cnt, acc, bmx);
+  else stream_jloop<D, E, MR, false>(a, sRow, cen, Gs, jb, cnt, acc, bmx);
 
   // ---- reduce every (row, e) over the work-group: DPP rows, shuffles, then LDS
   const int wid = tid / kWave, lane = tid & (kWave - 1);
@@ -225,7 +241,17 @@ void gauss_stream_kernel(StreamArgs a) {
       }
     }
   }
+  if (a.chunk_bmax && blockIdx.y == 0) {
+    const float m = wave_max(bmx);
+    if (lane == 0) sBm[wid] = m;
+  }
   __syncthreads();
+  if (a.chunk_bmax && blockIdx.y == 0 && tid == 0) {
+    float m = sBm[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / kWave; ++w) m = fmaxf(m, sBm[w]);
+    a.chunk_bmax[blockIdx.x] = m;
+  }
   if (tid < nr * E) {
     const int i = tid / E, e = tid - i * E;
     float v = sRed[0][tid];

@@ -501,6 +501,73 @@ def test_lse_fixed_shift_and_fixup(split, rows, E):
     check_lse(l, l_ref)
 
 
+def _far_rows_case(seed, E):
+    """Rows spread over 18 sigma along x0, inside one work-group's expanded-form range,
+    with every y at the x0 = -9 end: the far rows' values fall to 1e-30 and below."""
+    rng = np.random.default_rng(seed)
+    M, N = 1500, 2000
+    x = np.zeros((M, 3), np.float32)
+    x[:, 0] = rng.uniform(-9.0, 9.0, M)
+    x[:, 1:] = 0.1 * rng.standard_normal((M, 2))
+    y = np.zeros((N, 3), np.float32)
+    y[:, 0] = -9.0 + 0.5 * rng.random(N)
+    y[:, 1:] = 0.3 * rng.standard_normal((N, 2))
+    b = rng.standard_normal((N, E)).astype(np.float32)
+    return x, y, b
+
+
+@pytest.mark.parametrize("E", [1, 2])
+@pytest.mark.parametrize("rows", [1, 2], ids=["narrow", "wide"])
+@pytest.mark.parametrize("split", [0, 1, 3])
+def test_sum_far_rows(split, rows, E):
+    """Sum rows 7-9 sigma from every y inside an expanded-form work-group: their terms lie
+    below that form's floor, so they must come out of the direct form, not as 0."""
+    say(f"sum far rows split={split} rows={rows} E={E}")
+    x, y, b = _far_rows_case(191 + E, E)
+    gm.keops_set_option(gm.KEOPS_OPT_SPLIT_J, split)
+    gm.keops_set_option(gm.KEOPS_OPT_ROWS, rows)
+    a = host(gm.keops_gauss_sum(dev(x), dev(y), dev(b), 1.0))
+    a_ref, n_ref = oracle.gauss_sum(x, y, b, 1.0)
+    assert ((n_ref > 1e-30) & (n_ref < 1e-20)).sum() > 20       # rows in the floor's range exist
+    check_sum(a, a_ref, n_ref)
+
+
+@pytest.mark.parametrize("E", [1, 2])
+@pytest.mark.parametrize("split", [0, 1, 3])
+def test_grad_far_rows(split, E):
+    """grad_x of rows 7-9 sigma from every y inside an expanded-form work-group."""
+    say(f"grad_x far rows split={split} E={E}")
+    x, y, b = _far_rows_case(291 + E, E)
+    g = np.random.default_rng(5).standard_normal((x.shape[0], E)).astype(np.float32)
+    gm.keops_set_option(gm.KEOPS_OPT_SPLIT_J, split)
+    G = host(gm.keops_gauss_grad_x(dev(x), dev(y), dev(b), dev(g), 1.0))
+    G_ref, nu = oracle.gauss_grad_x(x, y, b, g, 1.0)
+    check_grad(G, G_ref, nu)
+
+
+@pytest.mark.parametrize("split", [0, 1, 3])
+def test_max_far_rows(split):
+    """Max / ArgMax of rows 7-9 sigma from every y inside an expanded-form work-group."""
+    say(f"max far rows split={split}")
+    x, y, b = _far_rows_case(391, 1)
+    gm.keops_set_option(gm.KEOPS_OPT_SPLIT_J, split)
+    v, i = gm.keops_gauss_max(dev(x), dev(y), dev(b), 1.0)
+    v_ref, i_ref = oracle.gauss_max(x, y, b, 1.0, 1)
+    check_max(x, y, b, 1.0, 1, np.arange(x.shape[0]), host(v), host(i), v_ref, i_ref)
+
+
+@pytest.mark.parametrize("M", [3, 16, 40])
+def test_stream_far_rows(M):
+    """Few-rows layout: rows spread over 18 sigma with every y at one end."""
+    say(f"stream far rows M={M}")
+    x, y, b = _far_rows_case(491 + M, 1)
+    x = x[np.argsort(x[:, 0])][np.linspace(0, x.shape[0] - 1, M).astype(int)]
+    gm.keops_set_option(gm.KEOPS_OPT_ROWS, 3)
+    a = host(gm.keops_gauss_sum(dev(x), dev(y), dev(b), 1.0))
+    a_ref, n_ref = oracle.gauss_sum(x, y, b, 1.0)
+    check_sum(a, a_ref, n_ref)
+
+
 def test_lse_large_payload():
     """b up to about 90: the bound G + (max b) log2 e rules the fixed shift out and the
     running maximum is used throughout."""
