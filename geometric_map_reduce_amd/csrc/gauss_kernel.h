@@ -45,8 +45,9 @@ template <int OP, int D, int E>
 struct GaussShape {
   static constexpr int NV = (D + 1 + 3) / 4;                              // float4 per j record
   static constexpr int PAY = E;                                           // payload floats per j (b)
-  // per-row accumulators: sum E; LSE (max, sum) per column; grad D; max E (with indices)
-  static constexpr int NACC = (OP == OP_GRAD) ? D : (OP == OP_LSE ? 2 * E : E);
+  // per-row accumulators: sum E; LSE (max, sum) per column; grad D; max E (with indices;
+  // 2 for the sign-split tile: best positive and best negative class)
+  static constexpr int NACC = (OP == OP_GRAD) ? D : ((OP == OP_LSE || OP == OP_MAX) ? 2 * E : E);
   // per-tile partial sums: sum E; LSE E; grad D
   static constexpr int NPART = (OP == OP_GRAD) ? D : E;
   static constexpr int BYTES_PER_J = NV * 16 + PAY * 4;
@@ -54,6 +55,13 @@ struct GaussShape {
                           : (2 * 128 * BYTES_PER_J <= 49152) ? 128
                           : (2 * 64 * BYTES_PER_J <= 49152) ? 64
                           : (2 * 32 * BYTES_PER_J <= 49152) ? 32 : 16;
+  // Sign-split tile (sum and Max with one payload column, expanded form, D <= 8):
+  // the tile's j are stored with b > 0 first and the rest after (each class in j
+  // order, padded to whole groups of 4); log2 |b| is folded into the j constant, so
+  // the sum adds or subtracts exp2 of the exponent and Max compares exponents
+  // without any exp2.
+  static constexpr bool SPLIT = (OP == OP_SUM || OP == OP_MAX) && E == 1 && D <= 8 && TJ == 256;
+  static constexpr int TJR = SPLIT ? TJ + 8 : TJ;   // records per tile buffer
 };
 
 // Record of one j (NV float4 from LDS) into registers.
@@ -114,13 +122,15 @@ __device__ __forceinline__ void pair_exponent(const float (&xs)[R][D], const flo
 // what it costs in the sum (exponent, exp2, add); see the kernel below.
 template <int OP, int D, int E, int R, bool FAST, bool FIXED = false>
 __device__ __forceinline__ void gauss_jloop(const GaussArgs &a,
-                                            float4 (*sRec)[GaussShape<OP, D, E>::TJ * GaussShape<OP, D, E>::NV],
+                                            float4 (*sRec)[GaussShape<OP, D, E>::TJR * GaussShape<OP, D, E>::NV],
                                             float (*sPay)[GaussShape<OP, D, E>::PAY * GaussShape<OP, D, E>::TJ],
+                                            int (*sIdx)[GaussShape<OP, D, E>::TJR], int (*sSeg)[4],
                                             const float (&xs)[R][D], const float (&gr)[R][E], const float (&cen)[D],
                                             float G, float (&acc)[R][GaussShape<OP, D, E>::NACC],
-                                            int (&ix)[R][E], int64_t jb, int64_t je) {
+                                            int (&ix)[R][2 * E], int64_t jb, int64_t je) {
   using S = GaussShape<OP, D, E>;
   constexpr int NV = S::NV, PAY = S::PAY, TJ = S::TJ, NP = S::NPART;
+  constexpr bool SPLIT = S::SPLIT && FAST;
   const int tid = threadIdx.x;
   const float s2 = a.scale * a.scale;
   // exponent offset of the direct form (see the file comment); LSE tracks its own max
@@ -139,8 +149,67 @@ __device__ __forceinline__ void gauss_jloop(const GaussArgs &a,
   };
   // Transform the staged raw j rows into LDS records and payloads.  Padded j
   // (beyond je) get records whose contribution is exactly zero.
-  auto stage = [&](int buf, bool ok) {
+  // a record whose exponent slot holds c and every other value 0
+  auto put_pad = [&](int buf, int slot, float c) {
+    float pr[4 * NV];
+#pragma unroll
+    for (int q = 0; q < 4 * NV; ++q) pr[q] = 0.0f;
+    pr[D] = c;
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+      sRec[buf][slot * NV + v] = make_float4(pr[4 * v], pr[4 * v + 1], pr[4 * v + 2], pr[4 * v + 3]);
+  };
+  auto stage = [&](int buf, bool ok, int64_t jt_stage) {
     if (tid >= TJ) return;
+    if (SPLIT) {
+      // record (2y', c_j + log2 |b|) at the j's place in its wave's segment: b > 0
+      // first, then the rest (b <= 0, NaN, and padded j), in j order within each class
+      float rec[4 * NV];
+#pragma unroll
+      for (int q = 0; q < 4 * NV; ++q) rec[q] = 0.0f;
+      float ny = 0.0f;
+#pragma unroll
+      for (int k = 0; k < D; ++k) {
+        const float yp = a.scale * (ry[k] - cen[k]);
+        rec[k] = 2.0f * yp;
+        ny = fmaf(yp, yp, ny);
+      }
+      const float bv = OP == OP_MAX ? a.max_sign * rb[0] : rb[0];
+      const bool pos = ok && bv > 0.0f;
+      // padded j: 0 for the sum; never chosen by Max (its class looks for the least exponent)
+      rec[D] = ok ? (-ny - G) + __builtin_amdgcn_logf(fabsf(bv)) : (OP == OP_MAX ? INFINITY : -INFINITY);
+      // place = rank within the class over the whole tile: ballot counts per wave,
+      // the waves' counts through LDS (one barrier; every thread of the work-group
+      // stages, so all reach it)
+      const int lane = tid & (kWave - 1), w = tid / kWave;
+      const uint64_t mpos = __ballot(pos);
+      const int below = __popcll(mpos & ((1ull << lane) - 1ull));
+      if (lane == 0) sSeg[buf][w] = __popcll(mpos);
+      __syncthreads();
+      int P = 0, offp = 0;
+#pragma unroll
+      for (int v = 0; v < TJ / kWave; ++v) {
+        const int c = sSeg[buf][v];
+        P += c;
+        offp += v < w ? c : 0;
+      }
+      const int P4 = (P + 3) & ~3, Q = TJ - P, Q4 = (Q + 3) & ~3;
+      const int slot = pos ? offp + below : P4 + (w * kWave - offp) + (lane - below);
+#pragma unroll
+      for (int v = 0; v < NV; ++v)
+        sRec[buf][slot * NV + v] = make_float4(rec[4 * v], rec[4 * v + 1], rec[4 * v + 2], rec[4 * v + 3]);
+      if (OP == OP_MAX) sIdx[buf][slot] = ok ? (int)(jt_stage + tid) : -1;
+      // pads to whole groups of 4: never contribute (sum) and never win (Max)
+      if (tid < P4 - P) {
+        put_pad(buf, P + tid, -INFINITY);
+        if (OP == OP_MAX) sIdx[buf][P + tid] = -1;
+      }
+      if (tid < Q4 - Q) {
+        put_pad(buf, P4 + Q + tid, OP == OP_MAX ? INFINITY : -INFINITY);
+        if (OP == OP_MAX) sIdx[buf][P4 + Q + tid] = -1;
+      }
+      return;
+    }
     float rec[4 * NV];
 #pragma unroll
     for (int q = 0; q < 4 * NV; ++q) rec[q] = 0.0f;
@@ -180,7 +249,7 @@ __device__ __forceinline__ void gauss_jloop(const GaussArgs &a,
 
   if (jb < je) {
     const bool ok = load_raw(jb);
-    stage(0, ok);
+    stage(0, ok, jb);
   }
   __syncthreads();
   int buf = 0;
@@ -198,6 +267,61 @@ __device__ __forceinline__ void gauss_jloop(const GaussArgs &a,
 #pragma unroll
       for (int q = 0; q < NP; ++q) part[r][q] = 0.0f;
 
+    if (SPLIT) {
+      // the b > 0 class, then the rest; bounds are uniform
+      const int *idx = sIdx[buf];
+      int P = 0;
+#pragma unroll
+      for (int v = 0; v < TJ / kWave; ++v) P += sSeg[buf][v];
+      P = __builtin_amdgcn_readfirstlane(P);
+      const int p4 = (P + 3) & ~3, q4 = (TJ - P + 3) & ~3;
+      {
+        for (int jj = 0; jj < p4; jj += 4) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            float yv[4 * NV];
+            load_rec<NV>(rec, jj + u, yv);
+            float q[R], dd[1][D];
+            pair_exponent<true>(xs, yv, s2, off, q, dd);
+            if (OP == OP_SUM) {
+#pragma unroll
+              for (int r = 0; r < R; ++r) part[r][0] += fast_exp2(q[r]);
+            } else {
+              // largest exponent of a positive product; strict: ties keep the smaller j
+              const int j = idx[jj + u];
+#pragma unroll
+              for (int r = 0; r < R; ++r) {
+                const bool up = q[r] > acc[r][0];
+                acc[r][0] = up ? q[r] : acc[r][0];
+                ix[r][0] = up ? j : ix[r][0];
+              }
+            }
+          }
+        }
+        for (int jj = p4; jj < p4 + q4; jj += 4) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            float yv[4 * NV];
+            load_rec<NV>(rec, jj + u, yv);
+            float q[R], dd[1][D];
+            pair_exponent<true>(xs, yv, s2, off, q, dd);
+            if (OP == OP_SUM) {
+#pragma unroll
+              for (int r = 0; r < R; ++r) part[r][0] -= fast_exp2(q[r]);
+            } else {
+              // least exponent of a non-positive product (b = 0 gives -inf: the value 0)
+              const int j = idx[jj + u];
+#pragma unroll
+              for (int r = 0; r < R; ++r) {
+                const bool up = q[r] < acc[r][1];
+                acc[r][1] = up ? q[r] : acc[r][1];
+                ix[r][1] = up ? j : ix[r][1];
+              }
+            }
+          }
+        }
+      }
+    } else
     for (int jj = 0; jj < cnt; jj += 4) {
       float4 pq[PAY];
 #pragma unroll
@@ -330,7 +454,7 @@ __device__ __forceinline__ void gauss_jloop(const GaussArgs &a,
         for (int q = 0; q < NP; ++q) acc[r][q] += part[r][q];
       }
     }
-    if (has_next) stage(buf ^ 1, ok_next);
+    if (has_next) stage(buf ^ 1, ok_next, jt + TJ);
     __syncthreads();
     buf ^= 1;
   }
@@ -340,9 +464,11 @@ template <int OP, int D, int E, int R>
 __global__ __launch_bounds__(kThreads) void gauss_valu_kernel(GaussArgs a) {
   using S = GaussShape<OP, D, E>;
   constexpr int NV = S::NV, PAY = S::PAY, TJ = S::TJ;
-  __shared__ float4 sRec[2][TJ * NV];
+  __shared__ float4 sRec[2][S::TJR * NV];
   __shared__ __attribute__((aligned(16))) float sPay[2][PAY * TJ];
   __shared__ float sRed[2 * D * (kThreads / kWave) + 8];
+  __shared__ int sIdx[S::SPLIT && OP == OP_MAX ? 2 : 1][S::SPLIT && OP == OP_MAX ? S::TJR : 1];   // j of each record
+  __shared__ int sSeg[2][4];                                                                     // class sizes per wave
 
   // row blocks already computed by the MFMA kernel (uniform across the work-group)
   if (a.wg_flags && a.wg_flags[blockIdx.x]) return;
@@ -437,8 +563,11 @@ __global__ __launch_bounds__(kThreads) void gauss_valu_kernel(GaussArgs a) {
   // sum, grad_x: below this a shifted accumulator may have lost terms to the floor
   // (each flushed term is under 2^-126 max|b|, times |g| |x' - y'| < 32 |g| for grad_x);
   // Max: a maximum below 2^-109 max|b| may be a flushed term's place
+  // (the sign-split tile folds log2 |b| into the exponent, so there a flushed term is
+  // under 2^-126 itself: max(1, max|b|) covers both forms)
+  const float bmg = (OP == OP_SUM || OP == OP_MAX) ? fmaxf(bm, 1.0f) : bm;
   const float thr_base = !(guard && (OP == OP_SUM || OP == OP_GRAD || OP == OP_MAX)) ? 0.0f
-                         : (OP == OP_MAX ? exp2f(-109.0f) * bm : exp2f(a.log2n - 109.0f) * bm);
+                         : (OP == OP_MAX ? exp2f(-109.0f) * bmg : exp2f(a.log2n - 109.0f) * bmg);
   const float G = ((OP == OP_LSE && !lse_fixed) || !fast) ? 0.0f : 0.5f * r2;
   if (fast) {
 #pragma unroll
@@ -467,30 +596,48 @@ __global__ __launch_bounds__(kThreads) void gauss_valu_kernel(GaussArgs a) {
 #pragma unroll
       for (int e = 0; e < E; ++e) acc[r][2 * e] = -3.0e38f;   // running max (finite: keeps u - m defined)
   }
-  int ix[R][E];
+  int ix[R][2 * E];
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       ix[r][e] = -1;
-      if (OP == OP_MAX) acc[r][e] = -INFINITY;
+      ix[r][E + e] = -1;
+      if (OP == OP_MAX) {
+        acc[r][e] = -INFINITY;      // best value (sign-split tile: best exponent of a positive product)
+        acc[r][E + e] = INFINITY;   // sign-split tile: least exponent of a non-positive product
+      }
     }
+  // the sign-split tile's index array only exists for Max (a 1 x 1 stand-in otherwise)
+  int (*sIdxP)[S::TJR] = reinterpret_cast<int (*)[S::TJR]>(&sIdx[0][0]);
 
   // ---- the j loop, specialised on the form (uniform across the work-group):
   // one j split of a dense launch, or the item's j ranges in order
   if (!item) {
     const int64_t jb = (int64_t)blockIdx.y * a.j_per_split;
     const int64_t je = (jb + a.j_per_split < a.N) ? jb + a.j_per_split : a.N;
-    if (OP == OP_LSE && lse_fixed) gauss_jloop<OP, D, E, R, true, true>(a, sRec, sPay, xs, gr, cen, G, acc, ix, jb, je);
-    else if (fast) gauss_jloop<OP, D, E, R, true>(a, sRec, sPay, xs, gr, cen, G, acc, ix, jb, je);
-    else gauss_jloop<OP, D, E, R, false>(a, sRec, sPay, xs, gr, cen, G, acc, ix, jb, je);
+    if (OP == OP_LSE && lse_fixed) gauss_jloop<OP, D, E, R, true, true>(a, sRec, sPay, sIdxP, sSeg, xs, gr, cen, G, acc, ix, jb, je);
+    else if (fast) gauss_jloop<OP, D, E, R, true>(a, sRec, sPay, sIdxP, sSeg, xs, gr, cen, G, acc, ix, jb, je);
+    else gauss_jloop<OP, D, E, R, false>(a, sRec, sPay, sIdxP, sSeg, xs, gr, cen, G, acc, ix, jb, je);
   } else {
     for (int64_t k = item->k0; k <= item->k1; ++k) {
       const int64_t jb = k == item->k0 ? item->j0 : a.redr[2 * k];
       const int64_t je = k == item->k1 ? item->j1 : a.redr[2 * k + 1];
       if (jb >= je) continue;
-      if (fast) gauss_jloop<OP, D, E, R, true>(a, sRec, sPay, xs, gr, cen, G, acc, ix, jb, je);
-      else gauss_jloop<OP, D, E, R, false>(a, sRec, sPay, xs, gr, cen, G, acc, ix, jb, je);
+      if (fast) gauss_jloop<OP, D, E, R, true>(a, sRec, sPay, sIdxP, sSeg, xs, gr, cen, G, acc, ix, jb, je);
+      else gauss_jloop<OP, D, E, R, false>(a, sRec, sPay, sIdxP, sSeg, xs, gr, cen, G, acc, ix, jb, je);
+    }
+  }
+
+  // sign-split Max: back from exponents to the value in the shifted scale -- the best
+  // positive product if there is one, else the least negative (or zero) one
+  if (OP == OP_MAX && S::SPLIT && fast) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const bool haspos = acc[r][0] > -INFINITY;
+      const bool hasneg = acc[r][1] < INFINITY;
+      acc[r][0] = haspos ? fast_exp2(acc[r][0]) : (hasneg ? -fast_exp2(acc[r][1]) : -INFINITY);
+      ix[r][0] = haspos ? ix[r][0] : (hasneg ? ix[r][1] : -1);
     }
   }
 
@@ -615,10 +762,9 @@ __global__ __launch_bounds__(kThreads) void gauss_valu_kernel(GaussArgs a) {
 
 // Rows per lane of the "wide" variant (large M); the narrow variant holds 1.
 __host__ __device__ constexpr int gauss_rows_wide(int op, int D, int E) {
-#ifdef KMI_SUM_RW
-  if (op == OP_SUM && D <= 4) return KMI_SUM_RW;
-#endif
-  return D <= 4 ? (op == OP_SUM ? 8 : 4) : (D <= 8 ? (E <= 2 ? 4 : 2) : (D <= 16 ? 2 : 1));
+  // 4 rows at D <= 4 for every op: the sign-split sum holds them within 128 VGPRs
+  // (8 needed 151, three waves per SIMD); before it, 8 and 4 rows ran alike
+  return D <= 4 ? 4 : (D <= 8 ? (E <= 2 ? 4 : 2) : (D <= 16 ? 2 : 1));
 }
 
 template <int OP, int D, int E, int R>
