@@ -60,7 +60,7 @@ struct GaussShape {
   // order, padded to whole groups of 4); log2 |b| is folded into the j constant, so
   // the sum adds or subtracts exp2 of the exponent and Max compares exponents
   // without any exp2.
-  static constexpr bool SPLIT = (OP == OP_SUM || OP == OP_MAX) && E == 1 && D <= 8 && TJ == 256;
+  static constexpr bool SPLIT = (OP == OP_SUM || OP == OP_MAX || OP == OP_GRAD) && E == 1 && D <= 8 && TJ == 256;
   static constexpr int TJR = SPLIT ? TJ + 8 : TJ;   // records per tile buffer
 };
 
@@ -286,6 +286,14 @@ __device__ __forceinline__ void gauss_jloop(const GaussArgs &a,
             if (OP == OP_SUM) {
 #pragma unroll
               for (int r = 0; r < R; ++r) part[r][0] += fast_exp2(q[r]);
+            } else if (OP == OP_GRAD) {
+              // K b (x' - y'): the weight already holds |b|
+#pragma unroll
+              for (int r = 0; r < R; ++r) {
+                const float wgt = fast_exp2(q[r]);
+#pragma unroll
+                for (int k = 0; k < D; ++k) part[r][k] = fmaf(wgt, fmaf(yv[k], -0.5f, xs[r][k]), part[r][k]);
+              }
             } else {
               // largest exponent of a positive product; strict: ties keep the smaller j
               const int j = idx[jj + u];
@@ -308,6 +316,13 @@ __device__ __forceinline__ void gauss_jloop(const GaussArgs &a,
             if (OP == OP_SUM) {
 #pragma unroll
               for (int r = 0; r < R; ++r) part[r][0] -= fast_exp2(q[r]);
+            } else if (OP == OP_GRAD) {
+#pragma unroll
+              for (int r = 0; r < R; ++r) {
+                const float wgt = fast_exp2(q[r]);
+#pragma unroll
+                for (int k = 0; k < D; ++k) part[r][k] = fmaf(-wgt, fmaf(yv[k], -0.5f, xs[r][k]), part[r][k]);
+              }
             } else {
               // least exponent of a non-positive product (b = 0 gives -inf: the value 0)
               const int j = idx[jj + u];
@@ -565,7 +580,7 @@ __global__ __launch_bounds__(kThreads) void gauss_valu_kernel(GaussArgs a) {
   // Max: a maximum below 2^-109 max|b| may be a flushed term's place
   // (the sign-split tile folds log2 |b| into the exponent, so there a flushed term is
   // under 2^-126 itself: max(1, max|b|) covers both forms)
-  const float bmg = (OP == OP_SUM || OP == OP_MAX) ? fmaxf(bm, 1.0f) : bm;
+  const float bmg = (OP == OP_SUM || OP == OP_MAX || (OP == OP_GRAD && E == 1)) ? fmaxf(bm, 1.0f) : bm;
   const float thr_base = !(guard && (OP == OP_SUM || OP == OP_GRAD || OP == OP_MAX)) ? 0.0f
                          : (OP == OP_MAX ? exp2f(-109.0f) * bmg : exp2f(a.log2n - 109.0f) * bmg);
   const float G = ((OP == OP_LSE && !lse_fixed) || !fast) ? 0.0f : 0.5f * r2;
@@ -644,81 +659,31 @@ __global__ __launch_bounds__(kThreads) void gauss_valu_kernel(GaussArgs a) {
   // ---- finalise and store
   const bool partial = a.nsplit > 1;
   constexpr int W = (OP == OP_SUM || OP == OP_LAPLACE) ? E : ((OP == OP_LSE || OP == OP_MAX) ? (2 * E) : D);
-  // guarded sum / grad_x: split launches leave partials unscaled (pass 2 applies the
-  // row factor and the threshold to the whole row); one split tests here
+  // Guarded sum / grad_x / Max: split launches leave their partials unscaled, and split
+  // 0 writes each row's factor and threshold (pass 2 applies both to the whole row);
+  // one split tests here.  Threshold -1 marks a direct-form row (never flagged).
   const bool rowwise = (OP == OP_SUM || OP == OP_GRAD || OP == OP_MAX) && a.bmax && !item && !a.fixup;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     if (!valid[r]) continue;
     const int64_t i = row0 + (int64_t)r * kThreads + tid;
-    if (rowwise) {
-      // factor and threshold of the row; threshold -1 marks a direct-form row (factor
-      // then 2^-64, never flagged)
-      float f, t;
-      if (OP == OP_SUM || OP == OP_MAX) {
-        f = fast ? exp2f(G - nx[r]) : 1.0f;
-      } else {
-        f = (fast ? exp2f(G - nx[r]) * a.grad_coef : a.grad_coef_direct) * (E == 1 ? gr[r][0] : 1.0f);
-      }
-      if (fast) {
-        float gs = 32.0f;
-        if (OP == OP_GRAD && E > 1) {
-          gs = 0.0f;
-#pragma unroll
-          for (int e = 0; e < E; ++e) gs += fabsf(gr[r][e]);
-          gs *= 32.0f;
-        }
-        t = OP == OP_GRAD ? thr_base * gs : thr_base;
-      } else {
-        t = -1.0f;
-      }
-      if (OP == OP_MAX) {
-        // (unscaled value, index) partials, or the finished pair
-        if (partial) {
-          float *dst = a.out + ((int64_t)blockIdx.y * M + i) * W;
-#pragma unroll
-          for (int e = 0; e < E; ++e) { dst[2 * e] = acc[r][e]; dst[2 * e + 1] = __int_as_float(ix[r][e]); }
-          if (blockIdx.y == 0) { a.row_f[i] = f; a.row_t[i] = t; }
-        } else {
-          bool low = false;
-#pragma unroll
-          for (int e = 0; e < E; ++e) low |= !(fabsf(acc[r][e]) >= t);
-#pragma unroll
-          for (int e = 0; e < E; ++e) {
-            const bool flag = t >= 0.0f && low;
-            const float v = t >= 0.0f ? acc[r][e] * f : (acc[r][e] * f) * exp2f(-kDirectOffset);
-            a.out[i * E + e] = flag ? __int_as_float(0x7fc00000) : a.max_sign * v;
-            a.out_idx[i * E + e] = flag ? -1 : (int64_t)ix[r][e];
-          }
-        }
-        continue;
-      }
-      if (partial) {
-        float *dst = a.out + ((int64_t)blockIdx.y * M + i) * W;
-#pragma unroll
-        for (int w = 0; w < W; ++w) dst[w] = acc[r][w];
-        if (blockIdx.y == 0) { a.row_f[i] = f; a.row_t[i] = t; }
-      } else {
-        bool low = false;
-#pragma unroll
-        for (int w = 0; w < W; ++w) low |= !(fabsf(acc[r][w]) >= t);
-#pragma unroll
-        for (int w = 0; w < W; ++w)
-          a.out[i * W + w] = (t >= 0.0f && low) ? __int_as_float(0x7fc00000)
-                                                : (t >= 0.0f ? acc[r][w] * f : (acc[r][w] * f) * exp2f(-kDirectOffset));
-      }
-      continue;
+    // row factor f1, then f2 = 2^-64 for the direct form's offset
+    float f1 = 1.0f;
+    const float f2 = fast ? 1.0f : exp2f(-kDirectOffset);
+    if (OP == OP_SUM || OP == OP_LAPLACE || OP == OP_MAX) {
+      f1 = fast ? exp2f(G - nx[r]) : 1.0f;
+    } else if (OP == OP_GRAD) {
+      // expanded: G_k = -(2/sigma^2) (1/s) exp2(G - |x'|^2) sum_j K' <g, b> (x'_k - y'_k)
+      // direct:   G_k = -(2/sigma^2) sum_j K <g, b> (x_k - y_k)
+      f1 = (fast ? exp2f(G - nx[r]) * a.grad_coef : a.grad_coef_direct) * (E == 1 ? gr[r][0] : 1.0f);
     }
-    float res[W];
-    if (OP == OP_SUM || OP == OP_LAPLACE) {
-      const float f = fast ? exp2f(G - nx[r]) : exp2f(-kDirectOffset);
-#pragma unroll
-      for (int e = 0; e < E; ++e) res[e] = acc[r][e] * f;
-    } else if (OP == OP_MAX) {
+    // (LogSumExp and Max pairs are built here; the sum and grad_x scale each value
+    // as it is stored, so only the accumulators stay live)
+    float res[(OP == OP_LSE || OP == OP_MAX) ? W : 1];
+    if (OP == OP_MAX) {
       // (signed value, index) pairs; the row factor is positive, so the argmax is that of acc
-      const float f = fast ? exp2f(G - nx[r]) : exp2f(-kDirectOffset);
 #pragma unroll
-      for (int e = 0; e < E; ++e) { res[2 * e] = acc[r][e] * f; res[2 * e + 1] = __int_as_float(ix[r][e]); }
+      for (int e = 0; e < E; ++e) { res[2 * e] = (acc[r][e] * f1) * f2; res[2 * e + 1] = __int_as_float(ix[r][e]); }
     } else if (OP == OP_LSE) {
       // (max, sum) in log2 units; the fixed form's shift is G - |x'|^2 (the
       // (max b) log2 e of the bound never enters the exponents)
@@ -728,19 +693,37 @@ __global__ __launch_bounds__(kThreads) void gauss_valu_kernel(GaussArgs a) {
         res[2 * e] = lse_fixed ? G - nx[r] : acc[r][2 * e] - off;
         res[2 * e + 1] = acc[r][2 * e + 1];
       }
-    } else {
-      // expanded: G_k = -(2/sigma^2) (1/s) exp2(G - |x'|^2) sum_j K' <g, b> (x'_k - y'_k)
-      // direct:   G_k = -(2/sigma^2) sum_j K <g, b> (x_k - y_k)
-      const float f = (fast ? exp2f(G - nx[r]) * a.grad_coef : a.grad_coef_direct) * (E == 1 ? gr[r][0] : 1.0f);
-      const float f2 = fast ? 1.0f : exp2f(-kDirectOffset);
-#pragma unroll
-      for (int k = 0; k < D; ++k) res[k] = (f * acc[r][k]) * f2;
     }
+    // the guard's threshold for this row, and (one split) its verdict
+    float t = -1.0f;
+    if ((OP == OP_SUM || OP == OP_GRAD || OP == OP_MAX) && rowwise && fast) {
+      float gs = 32.0f;
+      if (OP == OP_GRAD && E > 1) {
+        gs = 0.0f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) gs += fabsf(gr[r][e]);
+        gs *= 32.0f;
+      }
+      t = OP == OP_GRAD ? thr_base * gs : thr_base;
+    }
+    // one split: each value below the threshold (or NaN) is stored as NaN; the fix-up
+    // launch recomputes every row of a block that holds one
+    const bool test = (OP == OP_SUM || OP == OP_GRAD || OP == OP_MAX) && rowwise && !partial && t >= 0.0f;
     if (partial) {
       const int64_t slot = item ? item->slot : blockIdx.y;
       float *dst = a.out + (slot * M + i) * W;
+      if ((OP == OP_SUM || OP == OP_GRAD || OP == OP_MAX) && rowwise) {
 #pragma unroll
-      for (int w = 0; w < W; ++w) dst[w] = res[w];
+        for (int w = 0; w < W; ++w)
+          dst[w] = OP == OP_MAX ? ((w & 1) ? res[OP == OP_MAX ? w : 0] : acc[r][w / 2]) : acc[r][w];   // unscaled
+        if (blockIdx.y == 0) { a.row_f[i] = f1; a.row_t[i] = t; }
+      } else if (OP == OP_LSE || OP == OP_MAX) {
+#pragma unroll
+        for (int w = 0; w < W; ++w) dst[w] = res[(OP == OP_LSE || OP == OP_MAX) ? w : 0];
+      } else {
+#pragma unroll
+        for (int w = 0; w < W; ++w) dst[w] = (acc[r][w] * f1) * f2;
+      }
     } else if (OP == OP_LSE) {
       // a fixed-shift sum below the underflow threshold (or NaN) is left as NaN
 #pragma unroll
@@ -750,12 +733,14 @@ __global__ __launch_bounds__(kThreads) void gauss_valu_kernel(GaussArgs a) {
     } else if (OP == OP_MAX) {
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        a.out[i * E + e] = a.max_sign * res[2 * e];
-        a.out_idx[i * E + e] = (int64_t)__float_as_int(res[2 * e + 1]);
+        const bool low = test && !(fabsf(acc[r][e]) >= t);
+        a.out[i * E + e] = low ? __int_as_float(0x7fc00000) : a.max_sign * res[2 * e];
+        a.out_idx[i * E + e] = low ? -1 : (int64_t)__float_as_int(res[2 * e + 1]);
       }
     } else {
 #pragma unroll
-      for (int w = 0; w < W; ++w) a.out[i * W + w] = res[w];
+      for (int w = 0; w < W; ++w)
+        a.out[i * W + w] = (test && !(fabsf(acc[r][w]) >= t)) ? __int_as_float(0x7fc00000) : (acc[r][w] * f1) * f2;
     }
   }
 }
@@ -764,7 +749,9 @@ __global__ __launch_bounds__(kThreads) void gauss_valu_kernel(GaussArgs a) {
 __host__ __device__ constexpr int gauss_rows_wide(int op, int D, int E) {
   // 4 rows at D <= 4 for every op: the sign-split sum holds them within 128 VGPRs
   // (8 needed 151, three waves per SIMD); before it, 8 and 4 rows ran alike
-  return D <= 4 ? 4 : (D <= 8 ? (E <= 2 ? 4 : 2) : (D <= 16 ? 2 : 1));
+  // grad_x at D = 16 keeps one row per lane: with two its E = 3, 4 variants reached
+  // 256 VGPRs and spilled
+  return D <= 4 ? 4 : (D <= 8 ? (E <= 2 ? 4 : 2) : (D <= 16 ? (op == OP_GRAD ? 1 : 2) : 1));
 }
 
 template <int OP, int D, int E, int R>
