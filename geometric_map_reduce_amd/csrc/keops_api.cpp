@@ -111,11 +111,15 @@ int kmin_find(int D, int K, VariantInfo *info, KminDispatch *fn) {
 
 // Default work-groups per CU for each kernel family, from sweeps at the
 // 1M x 1M (D = 3), 100k x 10M (D = 50) and 1M x 1M K-min shapes: the VALU sum,
-// LSE and grad gain 7-8 % going from 4 to 24, the MFMA sum 7 % from 4 to 16;
+// LSE and grad gain 7-8 % going from 4 to 24 and, with 4 rows per lane, another
+// 1.5-2 % at 64 (sum 136.6 -> 134.0 ms, LogSumExp 134.6 -> 132.2, Max 107.0 -> 104.5,
+// grad_y 232.9 -> 228.8; flat from 64 to 192); the MFMA sum gains 7 % from 4 to 16;
 // K-min's partial lists are larger, and every split starts its lists empty (the
 // early candidates nearly all insert): at 1M x 1M, D = 3, one split (4 per CU)
 // ran 112 ms against 115 ms with two (8 per CU) and 114 ms with 16 per CU.
-constexpr int64_t kGaussWgsPerCu = 24;
+constexpr int64_t kGaussWgsPerCu = 64;
+// Block-sparse launches spread the kept pairs over this many work-groups per CU.
+constexpr int64_t kRangesWgsPerCu = 24;
 constexpr int64_t kMfmaSumWgsPerCu = 16;
 constexpr int64_t kKminWgsPerCu = 4;
 constexpr int64_t kKminMfmaWgsPerCu = 4;
@@ -468,7 +472,7 @@ int gauss_ranges_entry(int op, const float *x, const float *y, const float *b, c
   const bool wide = g_opt_rows.load() == 2 || (g_opt_rows.load() == 0 && covered / nonempty >= 2 * wide_info.rows_per_wg);
   const int64_t rw = wide ? wide_info.rows_per_wg : narrow_info.rows_per_wg;
   const int tile = wide_info.tile_j;
-  const int64_t target = g_opt_wg_target.load() > 0 ? g_opt_wg_target.load() : kGaussWgsPerCu;
+  const int64_t target = g_opt_wg_target.load() > 0 ? g_opt_wg_target.load() : kRangesWgsPerCu;
   // j per item: the kept pairs spread over ~target work-groups per CU, at least four tiles
   const double jt = std::max(4.0 * tile, pairs / ((double)target * cus * (double)rw));
   const int64_t forced = g_opt_split.load();
