@@ -217,8 +217,10 @@ __global__ __launch_bounds__(kThreads) void kmin_valu_kernel(KminArgs a) {
 #pragma unroll
         for (int v = 0; v < NV; ++v) g[u][v] = rec[(jw + u) * NV + v];
     };
-    // Filter 4 j x R rows; one wave-level branch for the whole group (each
-    // compare's lane mask is ORed in scalar registers: one VALU compare per pair).
+    // Filter 4 j x R rows; one wave-level branch for the whole group.  Per row the
+    // least of the 4 prefilter values (v_min3 + v_min) is compared once, and the
+    // lane masks are ORed in scalar registers: the CU's one scalar unit, shared by
+    // its four SIMDs, sees one OR per row per group instead of one per pair.
     auto filter_group = [&](const float4 (&g)[4][NV], int jj) {
       float t[4][R];
       uint64_t hit = 0;
@@ -236,8 +238,12 @@ __global__ __launch_bounds__(kThreads) void kmin_valu_kernel(KminArgs a) {
         for (int k = 0; k < D; ++k)
 #pragma unroll
           for (int r = 0; r < R; ++r) t[u][r] = fmaf(xm[r][k], yv[k], t[u][r]);
+      }
 #pragma unroll
-        for (int r = 0; r < R; ++r) hit |= __builtin_amdgcn_ballot_w64(t[u][r] < thr[r]);
+      for (int r = 0; r < R; ++r) {
+        // NaN values drop out of fminf, as they fail the compare
+        const float lo = fminf(fminf(t[0][r], t[1][r]), fminf(t[2][r], t[3][r]));
+        hit |= __builtin_amdgcn_ballot_w64(lo < thr[r]);
       }
       if (hit) {   // wave-uniform
 #pragma unroll
