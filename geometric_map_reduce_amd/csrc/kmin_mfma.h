@@ -13,8 +13,9 @@
 // distance minus |x_c|^2 plus a bound on the rounding of both forms; only then
 // is the exact direct-form fp32 distance sum_k (x_k - y_k)^2 formed (raw
 // coordinates, from global memory) and inserted into the lane's sorted
-// register list.  The four lanes that share a row see disjoint j's; their
-// lists are merged with cross-lane exchanges at the end.  The result is that of a
+// register list.  The four lanes that share a row see disjoint j's and share
+// the least of their thresholds; their lists are merged with cross-lane
+// exchanges at the end.  The result is that of a
 // direct-form K-min in fp32, for any spread of the data.
 #pragma once
 
@@ -25,21 +26,28 @@ namespace kmi {
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-template <int D>
+// 16-row tiles per wave: three where the kernel still fits in 256 VGPRs (two
+// waves per SIMD; the LDS tiles allow no more than three work-groups per CU),
+// else two.  A third tile reuses each A operand once more and gives the
+// matrix core a third independent accumulation chain.
+constexpr int kmin_mfma_tiles(int D, int K) { return K <= (D <= 50 ? 13 : (D <= 64 ? 12 : 8)) ? 3 : 2; }
+
+template <int D, int K>
 struct KminMfmaShape {
   static constexpr int DP = (D + 1 + 3) / 4 * 4;
   static constexpr int KS = DP / 4;
   static constexpr int KSP = (KS + 3) / 4 * 4;
   static constexpr int JSTRIDE = 4 * KSP + 4;
   static constexpr int TJ = 64;                    // j rows per LDS tile
-  static constexpr int TI = 2;                     // 16-row tiles per wave
+  static constexpr int TI = kmin_mfma_tiles(D, K);
   static constexpr int ROWS_WG = 4 * 16 * TI;      // rows per work-group
 };
 
 template <int D, int K>
 __global__ __launch_bounds__(kThreads) void kmin_mfma_kernel(KminArgs a) {
-  using S = KminMfmaShape<D>;
+  using S = KminMfmaShape<D, K>;
   constexpr int KS = S::KS, KSP = S::KSP, JS = S::JSTRIDE, TJ = S::TJ, TI = S::TI;
+  static_assert(S::ROWS_WG <= kThreads, "one thread per row for the centre");
   __shared__ __attribute__((aligned(16))) float sMem[2 * TJ * JS];   // double-buffered y~ tiles
   __shared__ float sRed[2 * D * (kThreads / kWave) + 8];
   __shared__ float sCen[D];
@@ -185,13 +193,13 @@ __global__ __launch_bounds__(kThreads) void kmin_mfma_kernel(KminArgs a) {
       for (int s = 0; s < KS; ++s)
 #pragma unroll
         for (int t = 0; t < TI; ++t) u[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(ya[s], xb[t][s], u[t], 0, 0, 0);
-      // one wave-level branch for the 4 x TI candidates of every lane
+      // one wave-uniform branch for the 4 x TI candidates of every lane
       float lowest = INFINITY;
 #pragma unroll
       for (int t = 0; t < TI; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) lowest = fminf(lowest, u[t][r] - thr[t]);
-      if (lowest < 0.0f) {
+      if (__builtin_amdgcn_ballot_w64(lowest < 0.0f)) {
 #pragma unroll
         for (int t = 0; t < TI; ++t)
 #pragma unroll
@@ -210,6 +218,16 @@ __global__ __launch_bounds__(kThreads) void kmin_mfma_kernel(KminArgs a) {
               }
             }
           }
+        // The four lane groups of a row see disjoint j, and each group's
+        // threshold bounds its own K-th distance.  A candidate that fails the
+        // least of the four trails K candidates of that group, so it cannot
+        // be among the row's K smallest: the groups share the least threshold.
+        // (All lanes run this: the branch above is wave-uniform.)
+#pragma unroll
+        for (int t = 0; t < TI; ++t) {
+          thr[t] = fminf(thr[t], __shfl_xor(thr[t], 16));
+          thr[t] = fminf(thr[t], __shfl_xor(thr[t], 32));
+        }
       }
     }
     if (has_next) stage_tile(buf ^ 1, jt + TJ);

@@ -9,8 +9,8 @@ int kmin_dispatch_mfma(int D, int K, VariantInfo *info, dim3 grid, const KminArg
 #define KMI_KMM_CASE(DD, KK)                                          \
   if (D == DD && K == KK) {                                           \
     if (info) {                                                       \
-      info->rows_per_wg = KminMfmaShape<DD>::ROWS_WG;                 \
-      info->tile_j = KminMfmaShape<DD>::TJ;                           \
+      info->rows_per_wg = KminMfmaShape<DD, KK>::ROWS_WG;             \
+      info->tile_j = KminMfmaShape<DD, KK>::TJ;                       \
       return 0;                                                       \
     }                                                                 \
     launch_kmin_mfma_t<DD, KK>(grid, *args, st);                      \

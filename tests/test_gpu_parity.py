@@ -794,16 +794,25 @@ def test_mfma_mixed_blocks(split):
     check_sum(a, a_ref, n_ref)
 
 
-@pytest.mark.parametrize("D,K", [(32, 10), (50, 3), (64, 10), (64, 16), (100, 1), (100, 10), (64, 1), (64, 32)])
-def test_kmin_mfma_equals_valu(D, K):
+@pytest.mark.parametrize("D,K,data", [(32, 10, "mix"), (50, 3, "mix"), (64, 10, "mix"), (64, 16, "mix"), (100, 1, "mix"),
+                                       (100, 10, "mix"), (64, 1, "mix"), (64, 32, "mix"), (64, 10, "dups"),
+                                       (100, 16, "dups"), (32, 13, "dups")])
+def test_kmin_mfma_equals_valu(D, K, data):
     """The MFMA-prefiltered K-min and the VALU K-min both return the direct-form fp32
-    K-min: identical indices and bitwise-identical distances; both match the oracle."""
-    say(f"kmin mfma == valu D={D} K={K}")
+    K-min: identical indices and bitwise-identical distances; both match the oracle.
+    "dups": y holds 100 points, each 30 times at scattered j, so every row's K
+    smallest are exact ties, spread over the lane groups that share a threshold,
+    and only the smallest j among the copies may be returned."""
+    say(f"kmin mfma == valu D={D} K={K} data={data}")
     rng = np.random.default_rng(D * 100 + K)
     centres = rng.uniform(-5, 5, (16, D))
     x = (centres[rng.integers(0, 16, 600)] + 0.5 * rng.standard_normal((600, D))).astype(np.float32)
-    y = (centres[rng.integers(0, 16, 3000)] + 0.5 * rng.standard_normal((3000, D))).astype(np.float32)
-    y[2999] = y[5]                                   # an exact tie
+    if data == "dups":
+        base = (centres[rng.integers(0, 16, 100)] + 0.5 * rng.standard_normal((100, D))).astype(np.float32)
+        y = base[rng.permutation(np.repeat(np.arange(100), 30))]
+    else:
+        y = (centres[rng.integers(0, 16, 3000)] + 0.5 * rng.standard_normal((3000, D))).astype(np.float32)
+        y[2999] = y[5]                               # an exact tie
     X, Y = dev(x), dev(y)
     d1, i1 = gm.keops_kmin(X, Y, K)
     gm.keops_set_option(gm.KEOPS_OPT_MFMA, 1)        # matrix cores off: the VALU kernel
