@@ -114,6 +114,38 @@ __device__ __forceinline__ void pair_exponent(const float (&xs)[R][D], const flo
   }
 }
 
+// Expanded-form records [j0, j1) (a multiple of 4) visited in groups of 4,
+// with the next group's records read from LDS as soon as this group's
+// exponents are formed, into the same registers: the read's latency then
+// hides behind this group's exp2 and accumulation.  The last group re-reads
+// itself.  visit(q) receives the exponents q[R] of one record, in j order.
+// The visitor must read nothing from LDS: a wait for such a read would also
+// wait for the records in flight.
+template <int NV, int R, int D, typename Visit>
+__device__ __forceinline__ void pipelined_records(const float4 *rec, int j0, int j1, const float (&xs)[R][D],
+                                                  float s2, Visit &&visit) {
+  if (j0 >= j1) return;
+  float yv[4][4 * NV];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    load_rec<NV>(rec, j0 + u, yv[u]);
+    // opaque, so that the compiler cannot merge this read with the one in
+    // the loop into a single read at the top of each iteration
+#pragma unroll
+    for (int k = 0; k < 4 * NV; ++k) asm volatile("" : "+v"(yv[u][k]));
+  }
+  for (int jj = j0; jj < j1; jj += 4) {
+    float q[4][R], dd[1][D];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) pair_exponent<true>(xs, yv[u], s2, 0.0f, q[u], dd);
+    const int jn = jj + 4 < j1 ? jj + 4 : jj;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) load_rec<NV>(rec, jn + u, yv[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) visit(q[u]);
+  }
+}
+
 // The j loop of one work-group over [jb, je) for a fixed form (FAST = expanded
 // distance).  Starts and ends with every wave past the LDS buffers, so calls
 // can follow each other (one per j range in block-sparse launches).
@@ -275,7 +307,19 @@ __device__ __forceinline__ void gauss_jloop(const GaussArgs &a,
       for (int v = 0; v < TJ / kWave; ++v) P += sSeg[buf][v];
       P = __builtin_amdgcn_readfirstlane(P);
       const int p4 = (P + 3) & ~3, q4 = (TJ - P + 3) & ~3;
-      {
+      if (OP == OP_SUM) {
+        pipelined_records<NV>(rec, 0, p4, xs, s2, [&](const float (&q)[R]) {
+#pragma unroll
+          for (int r = 0; r < R; ++r) part[r][0] += fast_exp2(q[r]);
+        });
+        pipelined_records<NV>(rec, p4, p4 + q4, xs, s2, [&](const float (&q)[R]) {
+#pragma unroll
+          for (int r = 0; r < R; ++r) part[r][0] -= fast_exp2(q[r]);
+        });
+      } else {
+        // grad and Max: the records are still needed after the exp2 (grad), or
+        // the loop also reads the record's j from LDS (Max), so the records
+        // are read group by group
         for (int jj = 0; jj < p4; jj += 4) {
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
@@ -283,10 +327,7 @@ __device__ __forceinline__ void gauss_jloop(const GaussArgs &a,
             load_rec<NV>(rec, jj + u, yv);
             float q[R], dd[1][D];
             pair_exponent<true>(xs, yv, s2, off, q, dd);
-            if (OP == OP_SUM) {
-#pragma unroll
-              for (int r = 0; r < R; ++r) part[r][0] += fast_exp2(q[r]);
-            } else if (OP == OP_GRAD) {
+            if (OP == OP_GRAD) {
               // K b (x' - y'): the weight already holds |b|
 #pragma unroll
               for (int r = 0; r < R; ++r) {
@@ -313,10 +354,7 @@ __device__ __forceinline__ void gauss_jloop(const GaussArgs &a,
             load_rec<NV>(rec, jj + u, yv);
             float q[R], dd[1][D];
             pair_exponent<true>(xs, yv, s2, off, q, dd);
-            if (OP == OP_SUM) {
-#pragma unroll
-              for (int r = 0; r < R; ++r) part[r][0] -= fast_exp2(q[r]);
-            } else if (OP == OP_GRAD) {
+            if (OP == OP_GRAD) {
 #pragma unroll
               for (int r = 0; r < R; ++r) {
                 const float wgt = fast_exp2(q[r]);
@@ -336,6 +374,12 @@ __device__ __forceinline__ void gauss_jloop(const GaussArgs &a,
           }
         }
       }
+    } else if (OP == OP_LSE && FIXED && E == 1) {
+      // the payload is folded into the records' constant: exp2 and accumulate
+      pipelined_records<NV>(rec, 0, cnt, xs, s2, [&](const float (&q)[R]) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) part[r][0] += fast_exp2(q[r]);
+      });
     } else
     for (int jj = 0; jj < cnt; jj += 4) {
       float4 pq[PAY];
