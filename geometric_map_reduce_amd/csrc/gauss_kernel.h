@@ -380,6 +380,32 @@ __device__ __forceinline__ void gauss_jloop(const GaussArgs &a,
 #pragma unroll
         for (int r = 0; r < R; ++r) part[r][0] += fast_exp2(q[r]);
       });
+    } else if (OP == OP_LAPLACE && E == 1) {
+      // direct form with the records of the next group read ahead, as in
+      // pipelined_records.  This group's b is read first, at the top, so that
+      // waiting for it does not wait for the records in flight.
+      float yv[4][4 * NV];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        load_rec<NV>(rec, u, yv[u]);
+#pragma unroll
+        for (int k = 0; k < 4 * NV; ++k) asm volatile("" : "+v"(yv[u][k]));   // see pipelined_records
+      }
+      for (int jj = 0; jj < cnt; jj += 4) {
+        const float4 pb = *reinterpret_cast<const float4 *>(pay + jj);
+        __builtin_amdgcn_sched_barrier(0);   // the b read stays ahead of the exponents
+        float q[4][R], dd[R][D];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) pair_exponent<false, R, D, 4 * NV, true>(xs, yv[u], s2, off, q[u], dd);
+        const int jn = jj + 4 < cnt ? jj + 4 : jj;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) load_rec<NV>(rec, jn + u, yv[u]);
+        __builtin_amdgcn_sched_barrier(0);   // and the record reads ahead of the exp2s
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int r = 0; r < R; ++r) part[r][0] = fmaf(fast_exp2(q[u][r]), lane4(pb, u), part[r][0]);
+      }
     } else
     for (int jj = 0; jj < cnt; jj += 4) {
       float4 pq[PAY];
