@@ -532,6 +532,42 @@ def test_sum_far_rows(split, rows, E):
     check_sum(a, a_ref, n_ref)
 
 
+SIGN_PATTERNS = {"all_pos": 1, "all_neg": 2, "one_pos_per_tile": 3, "zeros_and_neg": 4}
+
+
+@pytest.mark.parametrize("pattern", list(SIGN_PATTERNS))
+@pytest.mark.parametrize("split", [0, 3])
+def test_sign_classes_and_read_ahead(pattern, split):
+    """Sum, LogSumExp and the Laplacian sum over payloads that leave one class of
+    the sign-split tile empty, or one group long, in the 256-j tiles, over a
+    ragged j range: the loops that read the next group's records ahead start,
+    end and re-read the last group at every class boundary."""
+    say(f"sign classes {pattern} split={split}")
+    rng = np.random.default_rng(40 + SIGN_PATTERNS[pattern] * 7 + split)
+    M, N = 700, 256 * 5 + 37
+    x = rng.uniform(0, 1, (M, 3)).astype(np.float32)
+    y = rng.uniform(0, 1, (N, 3)).astype(np.float32)
+    mag = rng.uniform(0.5, 2.0, (N, 1))
+    b = -mag
+    if pattern == "all_pos":
+        b = mag
+    elif pattern == "one_pos_per_tile":
+        b[::256] = mag[::256]
+    elif pattern == "zeros_and_neg":
+        b[rng.random(N) < 0.5] = 0.0
+    b = b.astype(np.float32)
+    sigma = 0.2
+    gm.keops_set_option(gm.KEOPS_OPT_SPLIT_J, split)
+    a = host(gm.keops_gauss_sum(dev(x), dev(y), dev(b), sigma))
+    a_ref, n_ref = oracle.gauss_sum(x, y, b, sigma)
+    check_sum(a, a_ref, n_ref)
+    lap = host(gm.keops_laplace_sum(dev(x), dev(y), dev(b), sigma))
+    lap_ref, lap_n = oracle.laplace_sum(x, y, b, sigma)
+    check_sum(lap, lap_ref, lap_n, what="laplace")
+    lse = host(gm.keops_gauss_lse(dev(x), dev(y), dev(b), sigma))
+    check_lse(lse, oracle.gauss_lse(x, y, b, sigma))
+
+
 @pytest.mark.parametrize("E", [1, 2])
 @pytest.mark.parametrize("split", [0, 1, 3])
 def test_grad_far_rows(split, E):
