@@ -817,13 +817,15 @@ __global__ __launch_bounds__(kThreads) void gauss_valu_kernel(GaussArgs a) {
 
 // Rows per lane of the "wide" variant (large M); the narrow variant holds 1.
 __host__ __device__ constexpr int gauss_rows_wide(int op, int D, int E) {
-  // 4 rows at D <= 4 for the other ops: the sign-split sum holds them within 128
-  // VGPRs (8 needed 151, three waves per SIMD); before it, 8 and 4 rows ran alike.
-  // grad_x at D <= 4 takes 2: 111 VGPRs (four waves) against 149 (three) with 4,
-  // 3.4 % faster at 1M x 1M, D = 3 (3 rows: 120 VGPRs, no faster than 4).
+  // At D <= 4 (1M x 1M, D = 3): the sum and grad_x take 2 rows per lane, the other
+  // ops 4.  Sum: 129.3 ms with 2, 132.0 with 4, 134 with 3; the extra waves per SIMD
+  // that fewer VGPRs allow hide more than the doubled LDS record reads cost.
+  // grad_x: 111 VGPRs (four waves) against 149 (three) with 4, 3.4 % faster (3 rows:
+  // 120 VGPRs, no faster than 4).  LSE ran alike with 2 and 4, Max 11 % slower with
+  // 2.  Before the sign-split tile the sum ran alike with 8 and 4.
   // grad_x at D = 16 keeps one row per lane: with two its E = 3, 4 variants reached
   // 256 VGPRs and spilled
-  return D <= 4 ? (op == OP_GRAD ? 2 : 4)
+  return D <= 4 ? ((op == OP_GRAD || op == OP_SUM) ? 2 : 4)
                 : (D <= 8 ? (E <= 2 ? 4 : 2) : (D <= 16 ? (op == OP_GRAD ? 1 : 2) : 1));
 }
 
