@@ -113,11 +113,14 @@ int kmin_find(int D, int K, VariantInfo *info, KminDispatch *fn) {
 // 1M x 1M (D = 3), 100k x 10M (D = 50) and 1M x 1M K-min shapes: the VALU sum,
 // LSE and grad gain 7-8 % going from 4 to 24 and, with 4 rows per lane, another
 // 1.5-2 % at 64 (sum 136.6 -> 134.0 ms, LogSumExp 134.6 -> 132.2, Max 107.0 -> 104.5,
-// grad_y 232.9 -> 228.8; flat from 64 to 192); the MFMA sum gains 7 % from 4 to 16;
+// grad_y 232.9 -> 228.8); with the sum and grad at 2 rows per lane, 128 gains about
+// 1 % more on each of them (sum 128.6 -> 127.4 ms, LogSumExp 126.8 -> 126.1, Max
+// 100.9 -> 100.0, grad_y 219.1 -> 217.1; 256 about 0.3 % beyond that, with twice
+// the partial sums); the MFMA sum gains 7 % from 4 to 16;
 // K-min's partial lists are larger, and every split starts its lists empty (the
 // early candidates nearly all insert): at 1M x 1M, D = 3, one split (4 per CU)
 // ran 112 ms against 115 ms with two (8 per CU) and 114 ms with 16 per CU.
-constexpr int64_t kGaussWgsPerCu = 64;
+constexpr int64_t kGaussWgsPerCu = 128;
 // Block-sparse launches spread the kept pairs over this many work-groups per CU.
 constexpr int64_t kRangesWgsPerCu = 24;
 constexpr int64_t kMfmaSumWgsPerCu = 16;
@@ -166,7 +169,8 @@ Plan make_plan(int64_t M, int64_t N, int cus, int64_t rows_wide, int64_t rows_na
     s = forced;
   } else if (p.nblk < want_wgs) {
     s = (want_wgs + p.nblk - 1) / p.nblk;
-    const int64_t max_s = ntiles / 2 > 1 ? ntiles / 2 : 1;
+    // at least 4 j tiles per split: with 2-3, the CG solve at 100k x 100k ran 2 % slower
+    const int64_t max_s = ntiles / 4 > 1 ? ntiles / 4 : 1;
     if (s > max_s) s = max_s;
   }
   if (s > ntiles) s = ntiles;
