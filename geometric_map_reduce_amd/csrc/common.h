@@ -13,7 +13,10 @@ constexpr int kTileJ = 256;             // j rows staged in LDS per tile (one pe
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2 = 0.69314718055994530942f;
 // Largest |x'_i|^2 (scaled, centred, log2 units) for which the expanded form
-// exp2(2<x',y'> - |y'|^2 - G) keeps both range and precision; see the design doc.
+// exp2(2<x',y'> - |y'|^2 - G) keeps both range and precision: at R^2 <= 128
+// the fp32 rounding of the expansion stays near 1e-5 relative in K_ij, and the
+// shifted exponent stays inside the fp32 range; beyond it a work-group takes
+// the direct form from raw differences.
 constexpr float kFastR2 = 128.0f;
 // Exponent offset (log2 units) of the direct form's sums and gradients.
 constexpr float kDirectOffset = 64.0f;
