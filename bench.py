@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "Gaussian kernel mat-vec G pair-evals/s @ M=N=1M,D=3; % fp32 VALU peak"
 PEAK_FP32_TFLOPS = 157.3          # MI355X fp32 vector peak, and fp32 MFMA (dense) peak
+PEAK_BF16_TFLOPS = 2500.0         # MI355X bf16 MFMA (dense) peak
 PAGES_PAIRS_PER_S_1M = 1e12 / 1.38  # the pages' KeOps timing at N = 1M (hardware not stated)
 
 # (op, workload name, algorithmic flops per pair)
@@ -82,13 +83,17 @@ def is_stream(op, M, D):
 
 def roofline_of(op, M, D, E):
     """(bound, algorithmic units per pair, kernel name) of the dominant pass-1 kernel.
-    MFMA path: the contraction <x~, y~> of 2D flops per pair against the fp32 matrix peak
-    (the per-pair exp and accumulate are VALU work on top).  Few-rows sum: HBM bytes,
-    priced per launch (y and b read once) rather than per pair."""
+    MFMA sum: the contraction <x~, y~> of 2D flops per pair against the fp32 matrix peak
+    (the per-pair exp and accumulate are VALU work on top).  MFMA K-min: the split-bf16
+    prefilter's three bf16 products over D coordinates, 6D flops per pair, against the
+    bf16 matrix peak.  Few-rows sum: HBM bytes, priced per launch (y and b read once)
+    rather than per pair."""
     if is_stream(op, M, D):
         return "hbm", None, "gauss_stream_kernel"
     if uses_mfma(op, D):
-        return "mfma", 2 * D, ("gauss_mfma_sum_kernel" if op == "sum" else "kmin_mfma_kernel")
+        if op == "sum":
+            return "mfma", 2 * D, "gauss_mfma_sum_kernel"
+        return "mfma_bf16", 6 * D, "kmin_mfma_split_kernel"
     # the transposed gradients run the row kernels with y as the rows
     kop = {"grad_y": "grad_x", "grad_b": "sum", "cg": "sum", "sum_ranges": "sum"}.get(op, op)
     if op == "laplace":
@@ -363,9 +368,13 @@ def main():
     else:
         per_launch = w.N * w.N if op == "cg" else pairs
         achieved = fpp * per_launch / (kern_avg_ms * 1e-3) / 1e12
-        roof = {"bound": bound, "achieved": round(achieved, 3), "peak": PEAK_FP32_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_TFLOPS, 4), "traffic": traffic}
+        peak = PEAK_BF16_TFLOPS if bound == "mfma_bf16" else PEAK_FP32_TFLOPS
+        roof = {"bound": "mfma" if bound == "mfma_bf16" else bound, "achieved": round(achieved, 3), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic}
         kinfo = {"flops_per_pair": fpp}
+        if bound == "mfma_bf16":
+            # the same prefilter as an fp32 contraction (2D flops per pair) for comparison
+            kinfo["fp32_equivalent_TFLOP_s"] = round(2 * w.D * per_launch / (kern_avg_ms * 1e-3) / 1e12, 3)
 
     res = {
         "metric": METRIC if args.workload == "sum" else f"{op} G pair-evals/s @ {w.name}",

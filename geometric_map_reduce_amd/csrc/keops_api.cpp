@@ -751,11 +751,14 @@ int keops_kmin(const float *x, const float *y, int64_t M, int64_t N, int32_t D, 
   VariantInfo info{};
   KminDispatch fn = nullptr;
   if (kmin_find(D, K, &info, &fn)) return KEOPS_ERR_UNSUPPORTED;
-  // fp32-MFMA prefilter at D >= 32 (the result is the same direct-form K-min)
+  // matrix-core prefilter at D >= 32 (the result is the same direct-form K-min):
+  // the split-bf16 form by default, the fp32 form when KEOPS_OPT_MFMA is 2
   VariantInfo mfma_info{};
-  if (D >= 32 && g_opt_form.load() == 0 && g_opt_mfma.load() == 0 &&
-      kmin_dispatch_mfma(D, K, &mfma_info, dim3(), nullptr, nullptr) == 0) {
-    fn = kmin_dispatch_mfma;
+  const int opt_mfma = g_opt_mfma.load();
+  const KminDispatch mfma_fn = opt_mfma == 2 ? kmin_dispatch_mfma : kmin_dispatch_mfma_split;
+  if (D >= 32 && g_opt_form.load() == 0 && opt_mfma != 1 &&
+      mfma_fn(D, K, &mfma_info, dim3(), nullptr, nullptr) == 0) {
+    fn = mfma_fn;
     info = mfma_info;
   }
   if (M == 0) return KEOPS_OK;
@@ -765,7 +768,7 @@ int keops_kmin(const float *x, const float *y, int64_t M, int64_t N, int32_t D, 
   int cus = 0;
   if (int rc = device_setup(&cus)) return rc;
   const Plan p = make_plan(M, N, cus, info.rows_per_wg, info.rows_per_wg, info.tile_j,
-                           fn == kmin_dispatch_mfma ? kKminMfmaWgsPerCu : kKminWgsPerCu, 0);
+                           (fn == kmin_dispatch_mfma || fn == kmin_dispatch_mfma_split) ? kKminMfmaWgsPerCu : kKminWgsPerCu, 0);
   KminArgs a{};
   a.x = x; a.y = y; a.M = M; a.N = N;
   a.j_per_split = p.jps;
@@ -827,7 +830,7 @@ int keops_set_option(int option, int64_t value) {
       g_opt_wg_target.store(value);
       return KEOPS_OK;
     case KEOPS_OPT_MFMA:
-      if (value < 0 || value > 1) return KEOPS_ERR_INVALID_ARG;
+      if (value < 0 || value > 2) return KEOPS_ERR_INVALID_ARG;
       g_opt_mfma.store(value);
       return KEOPS_OK;
     default:

@@ -1,0 +1,314 @@
+// kmin_mfma_split.h -- pass-1 kernel of the K-min reduction for D >= 32 whose
+// prefilter runs on gfx950's bf16 matrix cores (KeOps pages: "Kernel Operations
+// on the GPU, with Autodiff, without Memory Overflows" §2, argKmin; KeOps
+// README feature list, "K-min reductions").
+//
+// The prefilter value is the one of the fp32-MFMA kernel,
+//   u_ij = |y_c|^2 - 2<x_c, y_c> = |x_i - y_j|^2 - |x_c|^2      (c: work-group centre),
+// but the cross term is formed from a two-part bf16 split of each operand,
+// v = v_hi + v_lo (v_hi = bf16(v), v_lo = bf16(v - v_hi)):
+//   <y, -2x> ~ <y_hi, (-2x)_hi> + <y_hi, (-2x)_lo> + <y_lo, (-2x)_hi>
+// with three v_mfma_f32_16x16x32_bf16 per 32 coordinates (products exact in
+// fp32, fp32 accumulation), and |y_c|^2 entering as the instruction's C input.
+// The dropped product y_lo (-2x)_lo and the rounding of the lo parts are each
+// below 2^-18 |y_k| |2x_k|, so the whole split error is below 1.6 * 2^-18 of
+// (2|x_c| + sqrt(K-th distance))^2; the pass margin adds 2^-16 of that to the
+// accumulation bound of the fp32 form over 3 * 32 * ceil(D / 32) products.  A
+// candidate whose exact distance could be below the row's K-th therefore
+// always passes; passing candidates get the exact direct-form fp32 distance
+// from raw coordinates and the same register insertion, lane-group threshold
+// sharing and final merge as the fp32-MFMA kernel, so the result is that of
+// the direct-form K-min in fp32, bit for bit.
+//
+// Per 16 x 16 tile at D = 64 this is 6 bf16 MFMA (16 cycles each) against 17
+// fp32 ones (32 cycles each) for the fp32 form.
+#pragma once
+
+#include "common.h"
+#include "kmin_kernel.h"
+
+namespace kmi {
+
+typedef float floatx4s __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8s __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2s __attribute__((ext_vector_type(2)));
+typedef float float2s __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4s __attribute__((ext_vector_type(4)));
+
+// Split two floats into packed bf16 hi parts (round to nearest even, one
+// v_cvt_pk_bf16_f32) and packed bf16 parts of the exact remainders.
+__device__ __forceinline__ void split_bf16x2(float v0, float v1, unsigned &hi, unsigned &lo) {
+  hi = __builtin_bit_cast(unsigned, __builtin_convertvector((float2s){v0, v1}, bf16x2s));
+  const float h0 = __builtin_bit_cast(float, hi << 16);
+  const float h1 = __builtin_bit_cast(float, hi & 0xffff0000u);
+  lo = __builtin_bit_cast(unsigned, __builtin_convertvector((float2s){v0 - h0, v1 - h1}, bf16x2s));
+}
+
+// Pass margin coefficient of the split form (see the header comment): the fp32
+// form's bound taken over the 3 * DP products, plus 2^-16 for the split.
+__device__ __forceinline__ float kmin_split_margin_coef(int DP) { return kmin_margin_coef(3 * DP) + 1.52587890625e-5f; }
+
+// 16-row tiles per wave: three where the kernel stays within 256 VGPRs, else two.
+constexpr int kmin_split_tiles(int D, int K) { return K <= (D <= 32 ? 13 : (D <= 64 ? 12 : 4)) ? 3 : 2; }
+
+template <int D, int K>
+struct KminSplitShape {
+  static constexpr int DP = (D + 31) / 32 * 32;    // coordinates padded to whole MFMA steps
+  static constexpr int NS = DP / 32;               // MFMA steps per product
+  static constexpr int RS = DP + 4;                // u32 per LDS record: DP/2 hi, DP/2 lo, 4 pad
+  static constexpr int TJ = 64;                    // j rows per LDS tile
+  static constexpr int TI = kmin_split_tiles(D, K);
+  static constexpr int ROWS_WG = 4 * 16 * TI;      // rows per work-group
+};
+
+template <int D, int K>
+__global__ __launch_bounds__(kThreads) void kmin_mfma_split_kernel(KminArgs a) {
+  using S = KminSplitShape<D, K>;
+  constexpr int DP = S::DP, NS = S::NS, RS = S::RS, TJ = S::TJ, TI = S::TI;
+  static_assert(S::ROWS_WG <= kThreads, "one thread per row for the centre");
+  __shared__ __attribute__((aligned(16))) unsigned sRec[2 * TJ * RS];   // double-buffered split y tiles
+  __shared__ __attribute__((aligned(16))) float sNy[2 * TJ];            // |y_c|^2 per j (kPadU: padding)
+  __shared__ float sRed[2 * D * (kThreads / kWave) + 8];
+  __shared__ float sCen[D];
+
+  const int tid = threadIdx.x;
+  const int wid = tid / kWave, lane = tid & (kWave - 1);
+  const int lrow = lane & 15, lgrp = lane >> 4;
+  const int64_t M = a.M, N = a.N;
+  const int64_t wg_row0 = (int64_t)blockIdx.x * S::ROWS_WG;
+
+  // ---- work-group bounding-box centre
+  {
+    const int64_t i = wg_row0 + tid;
+    const bool ok = tid < S::ROWS_WG && i < M;
+    for (int d0 = 0; d0 < D; d0 += 4) {
+      float lo[4], hi[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int d = d0 + q;
+        const float v = (ok && d < D) ? a.x[i * D + d] : 0.0f;
+        lo[q] = wave_min((ok && d < D) ? v : INFINITY);
+        hi[q] = wave_max((ok && d < D) ? v : -INFINITY);
+      }
+      if (lane == 0) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (d0 + q < D) { sRed[(2 * (d0 + q)) * 4 + wid] = lo[q]; sRed[(2 * (d0 + q) + 1) * 4 + wid] = hi[q]; }
+      }
+    }
+    __syncthreads();
+    for (int d = tid; d < D; d += kThreads) {
+      float l = sRed[(2 * d) * 4], h = sRed[(2 * d + 1) * 4];
+#pragma unroll
+      for (int w = 1; w < kThreads / kWave; ++w) { l = fminf(l, sRed[(2 * d) * 4 + w]); h = fmaxf(h, sRed[(2 * d + 1) * 4 + w]); }
+      sCen[d] = 0.5f * l + 0.5f * h;
+    }
+    __syncthreads();
+  }
+
+  // ---- B operands: split -2 x_c of row t*16 + l%16, coordinates 32s + 8(l/16) + e
+  u32x4s xh[TI][NS], xl[TI][NS];
+  float nx[TI], ax[TI];
+  int64_t row[TI];
+#pragma unroll
+  for (int t = 0; t < TI; ++t) {
+    row[t] = wg_row0 + wid * (16 * TI) + t * 16 + lrow;
+    const bool ok = row[t] < M;
+    float n = 0.0f;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int k = 32 * s + 8 * lgrp + e;
+        const float c = (ok && k < D) ? a.x[row[t] * D + k] - sCen[k < D ? k : 0] : 0.0f;
+        n = fmaf(c, c, n);
+        v[e] = -2.0f * c;
+      }
+      unsigned h[4], l[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) split_bf16x2(v[2 * e], v[2 * e + 1], h[e], l[e]);
+      xh[t][s] = (u32x4s){h[0], h[1], h[2], h[3]};
+      xl[t][s] = (u32x4s){l[0], l[1], l[2], l[3]};
+    }
+    n += __shfl_xor(n, 16);
+    n += __shfl_xor(n, 32);
+    nx[t] = n;
+    ax[t] = sqrtf(n);
+  }
+  const float mcoef = kmin_split_margin_coef(DP);
+
+  // Prefilter thresholds stay below kPadU, the value padded j carry, so padding
+  // never passes; rows beyond M get -inf and never pass either.
+  constexpr float kPadU = 1.0e30f, kThrCap = 5.0e29f;
+  float bd[TI][K];
+  int bi[TI][K];
+  float thr[TI];
+#pragma unroll
+  for (int t = 0; t < TI; ++t) {
+    thr[t] = row[t] < M ? kThrCap : -INFINITY;
+#pragma unroll
+    for (int k = 0; k < K; ++k) { bd[t][k] = INFINITY; bi[t][k] = -1; }
+  }
+
+  const int64_t jb = (int64_t)blockIdx.y * a.j_per_split;
+  const int64_t je = (jb + a.j_per_split < N) ? jb + a.j_per_split : N;
+
+  // tile staging: thread (sj = tid/4, sg = tid%4) owns the 8-coordinate chunks
+  // c = 4q + sg (q < NS) of column sj, i.e. coordinates 32q + 8sg + e
+  static_assert(TJ * 4 == kThreads, "four staging threads per j");
+  const int sj = tid >> 2, sg = tid & 3;
+  float ry[NS][8];
+  auto load_tile = [&](int64_t jt) {
+    const int64_t j = jt + sj;
+    const bool ok = j < je;
+#pragma unroll
+    for (int q = 0; q < NS; ++q)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int k = 32 * q + 8 * sg + e;
+        ry[q][e] = (ok && k < D) ? a.y[j * D + k] : 0.0f;
+      }
+  };
+  auto stage_tile = [&](int buf, int64_t jt) {
+    const bool ok = jt + sj < je;
+    float ny = 0.0f;
+    unsigned *rec = sRec + (buf * TJ + sj) * RS;
+#pragma unroll
+    for (int q = 0; q < NS; ++q) {
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int k = 32 * q + 8 * sg + e;
+        v[e] = k < D ? ry[q][e] - sCen[k < D ? k : 0] : 0.0f;
+        ny = fmaf(v[e], v[e], ny);
+      }
+      unsigned h[4], l[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) split_bf16x2(v[2 * e], v[2 * e + 1], h[e], l[e]);
+      const int off = 16 * q + 4 * sg;
+      *reinterpret_cast<u32x4s *>(rec + off) = (u32x4s){h[0], h[1], h[2], h[3]};
+      *reinterpret_cast<u32x4s *>(rec + DP / 2 + off) = (u32x4s){l[0], l[1], l[2], l[3]};
+    }
+    ny += __shfl_xor(ny, 1);
+    ny += __shfl_xor(ny, 2);
+    if (sg == 0) sNy[buf * TJ + sj] = ok ? ny : kPadU;   // padded j: u ~ kPadU, never passes
+  };
+
+  if (jb < je) {
+    load_tile(jb);
+    stage_tile(0, jb);
+  }
+  __syncthreads();
+  int buf = 0;
+  for (int64_t jt = jb; jt < je; jt += TJ) {
+    const bool has_next = jt + TJ < je;
+    if (has_next) load_tile(jt + TJ);
+    const int cnt = (int)(je - jt < TJ ? je - jt : TJ);
+    const unsigned *yt = sRec + buf * TJ * RS;
+    for (int j16 = 0; j16 < cnt; j16 += 16) {
+      // A operands: split y_c of column j16 + l%16, the same coordinates as the B operands
+      u32x4s yh[NS], yl[NS];
+      const unsigned *src = yt + (j16 + lrow) * RS + 4 * lgrp;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        yh[s] = *reinterpret_cast<const u32x4s *>(src + 16 * s);
+        yl[s] = *reinterpret_cast<const u32x4s *>(src + DP / 2 + 16 * s);
+      }
+      // output lane l holds j = j16 + 4(l/16) + r of row l%16: C starts at |y_c|^2 of those j
+      const floatx4s c0 = *reinterpret_cast<const floatx4s *>(sNy + buf * TJ + j16 + 4 * lgrp);
+      floatx4s u[TI];
+#pragma unroll
+      for (int t = 0; t < TI; ++t) u[t] = c0;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+#pragma unroll
+        for (int t = 0; t < TI; ++t)
+          u[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8s, yl[s]),
+                                                         __builtin_bit_cast(bf16x8s, xh[t][s]), u[t], 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < TI; ++t)
+          u[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8s, yh[s]),
+                                                         __builtin_bit_cast(bf16x8s, xl[t][s]), u[t], 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < TI; ++t)
+          u[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8s, yh[s]),
+                                                         __builtin_bit_cast(bf16x8s, xh[t][s]), u[t], 0, 0, 0);
+      }
+      // one wave-uniform branch for the 4 x TI candidates of every lane
+      bool any = false;
+#pragma unroll
+      for (int t = 0; t < TI; ++t) any |= fminf(fminf(u[t][0], u[t][1]), fminf(u[t][2], u[t][3])) < thr[t];
+      if (__builtin_amdgcn_ballot_w64(any)) {
+#pragma unroll
+        for (int t = 0; t < TI; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int64_t j = jt + j16 + 4 * lgrp + r;
+            if (u[t][r] < thr[t] && j < je && row[t] < M) {
+              const float *xi = a.x + row[t] * D;
+              const float *yj = a.y + j * D;
+              float d2 = 0.0f;
+              for (int k = 0; k < D; ++k) { const float d = xi[k] - yj[k]; d2 = fmaf(d, d, d2); }
+              if (d2 < bd[t][K - 1]) {
+                kmin_insert<K>(bd[t], bi[t], d2, (int)j);
+                const float kth = bd[t][K - 1];
+                const float sm = 2.0f * ax[t] + sqrtf(kth);
+                thr[t] = fminf((kth - nx[t]) + mcoef * sm * sm, kThrCap);
+              }
+            }
+          }
+        // The four lane groups of a row see disjoint j; a candidate that fails
+        // the least of their thresholds trails K candidates of that group, so
+        // the groups share it.  (All lanes run this: the branch is wave-uniform.)
+#pragma unroll
+        for (int t = 0; t < TI; ++t) {
+          thr[t] = fminf(thr[t], __shfl_xor(thr[t], 16));
+          thr[t] = fminf(thr[t], __shfl_xor(thr[t], 32));
+        }
+      }
+    }
+    if (has_next) stage_tile(buf ^ 1, jt + TJ);
+    __syncthreads();
+    buf ^= 1;
+  }
+
+  // ---- merge the four lane groups' lists of each row (lanes l, l^16, l^32, l^48)
+  for (int step = 0; step < 2; ++step) {
+    const int off = step == 0 ? 16 : 32;
+#pragma unroll
+    for (int t = 0; t < TI; ++t) {
+      float pd[K];
+      int pi[K];
+#pragma unroll
+      for (int q = 0; q < K; ++q) { pd[q] = __shfl_xor(bd[t][q], off); pi[q] = __shfl_xor(bi[t][q], off); }
+#pragma unroll
+      for (int q = 0; q < K; ++q) kmin_insert_lex<K>(bd[t], bi[t], pd[q], pi[q]);
+    }
+  }
+  if (lgrp == 0) {
+    const bool partial = a.nsplit > 1;
+#pragma unroll
+    for (int t = 0; t < TI; ++t) {
+      if (row[t] >= M) continue;
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        if (partial) {
+          const int64_t base = ((int64_t)blockIdx.y * M + row[t]) * K;
+          a.out_d[base + k] = bd[t][k];
+          a.part_idx[base + k] = bi[t][k];
+        } else {
+          a.out_d[row[t] * K + k] = bd[t][k];
+          a.out_idx[row[t] * K + k] = (int64_t)bi[t][k];
+        }
+      }
+    }
+  }
+}
+
+template <int D, int K>
+void launch_kmin_mfma_split_t(dim3 grid, const KminArgs &a, hipStream_t st) {
+  hipLaunchKernelGGL((kmin_mfma_split_kernel<D, K>), grid, dim3(kThreads), 0, st, a);
+}
+
+}  // namespace kmi

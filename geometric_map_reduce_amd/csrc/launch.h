@@ -42,6 +42,7 @@ KMI_DECLARE_KMIN(kmin_dispatch_d1_4)
 KMI_DECLARE_KMIN(kmin_dispatch_d5_8)
 KMI_DECLARE_KMIN(kmin_dispatch_large)
 KMI_DECLARE_KMIN(kmin_dispatch_mfma)
+KMI_DECLARE_KMIN(kmin_dispatch_mfma_split)
 #undef KMI_DECLARE_KMIN
 
 void launch_sum_combine(const float *ws, int nsplit, int64_t count, float *out, hipStream_t st);

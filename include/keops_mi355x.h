@@ -221,9 +221,12 @@ const char *keops_status_string(int status);
  *                          automatically for M <= 64 at D <= 8)
  *   KEOPS_OPT_WG_TARGET -- work-groups per CU the automatic j-split aims for
  *                          (1..4096; ignored when KEOPS_OPT_SPLIT_J is set)
- *   KEOPS_OPT_MFMA      -- 1 = the Gaussian sum and K-min never use the fp32
+ *   KEOPS_OPT_MFMA      -- 1 = the Gaussian sum and K-min never use the
  *                          matrix cores (the VALU expanded form runs at every
- *                          D; automatically they are used for D >= 32)
+ *                          D; automatically they are used for D >= 32);
+ *                          2 = the K-min prefilter at D >= 32 takes the fp32
+ *                          MFMA form instead of the split-bf16 one (the same
+ *                          results; the sum is unaffected)
  * Returns KEOPS_OK, or KEOPS_ERR_INVALID_ARG for an unknown option or value.
  */
 #define KEOPS_OPT_SPLIT_J 1

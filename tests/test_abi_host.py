@@ -114,7 +114,8 @@ def test_options(L):
     assert L.keops_set_option(5, -1) == -1
     assert L.keops_set_option(5, 4097) == -1
     assert L.keops_set_option(5, 16) == 0
-    assert L.keops_set_option(6, 2) == -1
+    assert L.keops_set_option(6, 3) == -1
+    assert L.keops_set_option(6, 2) == 0
     assert L.keops_set_option(6, 1) == 0
     for opt in (1, 2, 3, 5, 6):
         assert L.keops_set_option(opt, 0) == 0

@@ -832,13 +832,16 @@ def test_mfma_mixed_blocks(split):
 
 @pytest.mark.parametrize("D,K,data", [(32, 10, "mix"), (50, 3, "mix"), (64, 10, "mix"), (64, 16, "mix"), (100, 1, "mix"),
                                        (100, 10, "mix"), (64, 1, "mix"), (64, 32, "mix"), (64, 10, "dups"),
-                                       (100, 16, "dups"), (32, 13, "dups")])
+                                       (100, 16, "dups"), (32, 13, "dups"), (64, 10, "far"), (50, 4, "far"),
+                                       (100, 3, "mix")])
 def test_kmin_mfma_equals_valu(D, K, data):
-    """The MFMA-prefiltered K-min and the VALU K-min both return the direct-form fp32
-    K-min: identical indices and bitwise-identical distances; both match the oracle.
+    """Both MFMA-prefiltered K-min forms (split bf16, the default, and fp32) and the
+    VALU K-min return the direct-form fp32 K-min: identical indices and
+    bitwise-identical distances; all match the oracle.
     "dups": y holds 100 points, each 30 times at scattered j, so every row's K
     smallest are exact ties, spread over the lane groups that share a threshold,
-    and only the smallest j among the copies may be returned."""
+    and only the smallest j among the copies may be returned.  "far": the
+    mixture moved 300 units off the origin in every coordinate."""
     say(f"kmin mfma == valu D={D} K={K} data={data}")
     rng = np.random.default_rng(D * 100 + K)
     centres = rng.uniform(-5, 5, (16, D))
@@ -849,15 +852,21 @@ def test_kmin_mfma_equals_valu(D, K, data):
     else:
         y = (centres[rng.integers(0, 16, 3000)] + 0.5 * rng.standard_normal((3000, D))).astype(np.float32)
         y[2999] = y[5]                               # an exact tie
+    if data == "far":
+        x, y = x + np.float32(300.0), y + np.float32(300.0)
     X, Y = dev(x), dev(y)
     d1, i1 = gm.keops_kmin(X, Y, K)
+    gm.keops_set_option(gm.KEOPS_OPT_MFMA, 2)        # fp32-MFMA prefilter
+    d4, i4 = gm.keops_kmin(X, Y, K)
     gm.keops_set_option(gm.KEOPS_OPT_MFMA, 1)        # matrix cores off: the VALU kernel
     d3, i3 = gm.keops_kmin(X, Y, K)
     gm.keops_set_option(gm.KEOPS_OPT_MFMA, 0)
     gm.keops_set_option(gm.KEOPS_OPT_FORM, 1)        # forces the VALU kernel
     d2, i2 = gm.keops_kmin(X, Y, K)
     d1, i1, d2, i2, d3, i3 = host(d1), host(i1), host(d2), host(i2), host(d3), host(i3)
+    d4, i4 = host(d4), host(i4)
     assert np.array_equal(i3, i2) and np.array_equal(d3.view(np.int32), d2.view(np.int32))
+    assert np.array_equal(i4, i2) and np.array_equal(d4.view(np.int32), d2.view(np.int32))
     d_ref, i_ref = oracle.kmin(x, y, K)
     check_kmin(x, y, np.arange(600), d2, i2, d_ref, i_ref)   # VALU path
     check_kmin(x, y, np.arange(600), d1, i1, d_ref, i_ref)   # MFMA path
