@@ -48,27 +48,56 @@ __device__ __forceinline__ void split_bf16x2(float v0, float v1, unsigned &hi, u
 // form's bound taken over the 3 * DP products, plus 2^-16 for the split.
 __device__ __forceinline__ float kmin_split_margin_coef(int DP) { return kmin_margin_coef(3 * DP) + 1.52587890625e-5f; }
 
+// Exact direct-form squared distance sum_k (x_k - y_k)^2 in fp32, in coordinate
+// order (the same arithmetic as every other K-min kernel); 16-byte loads when D
+// is a multiple of 4 and both arrays are 16-byte aligned.
+template <int D>
+__device__ __forceinline__ float exact_sq_dist(const float *xi, const float *yj, bool v4) {
+  float d2 = 0.0f;
+  if constexpr (D % 4 == 0) {
+    if (v4) {
+#pragma unroll
+      for (int k = 0; k < D; k += 4) {
+        const float4 p = *reinterpret_cast<const float4 *>(xi + k);
+        const float4 q = *reinterpret_cast<const float4 *>(yj + k);
+        float d = p.x - q.x; d2 = fmaf(d, d, d2);
+        d = p.y - q.y; d2 = fmaf(d, d, d2);
+        d = p.z - q.z; d2 = fmaf(d, d, d2);
+        d = p.w - q.w; d2 = fmaf(d, d, d2);
+      }
+      return d2;
+    }
+  }
+  for (int k = 0; k < D; ++k) { const float d = xi[k] - yj[k]; d2 = fmaf(d, d, d2); }
+  return d2;
+}
+
 // 16-row tiles per wave: three where the kernel stays within 256 VGPRs, else two.
-constexpr int kmin_split_tiles(int D, int K) { return K <= (D <= 32 ? 13 : (D <= 64 ? 12 : 4)) ? 3 : 2; }
+constexpr int kmin_split_tiles(int D, int K) { return K <= (D <= 32 ? 13 : (D <= 64 ? 12 : 3)) ? 3 : 2; }
+
+// Work-groups of eight waves (two per SIMD at the kernel's register count, so one
+// per CU): every y tile staged in LDS serves 16 * TI rows per wave, 128 * TI in all.
+constexpr int kSplitThreads = 512;
+constexpr int kSplitWaves = kSplitThreads / kWave;
 
 template <int D, int K>
 struct KminSplitShape {
   static constexpr int DP = (D + 31) / 32 * 32;    // coordinates padded to whole MFMA steps
   static constexpr int NS = DP / 32;               // MFMA steps per product
   static constexpr int RS = DP + 4;                // u32 per LDS record: DP/2 hi, DP/2 lo, 4 pad
-  static constexpr int TJ = 64;                    // j rows per LDS tile
+  static constexpr int TJ = 128;                   // j rows per LDS tile (four staging threads each)
   static constexpr int TI = kmin_split_tiles(D, K);
-  static constexpr int ROWS_WG = 4 * 16 * TI;      // rows per work-group
+  static constexpr int ROWS_WG = kSplitWaves * 16 * TI;   // rows per work-group
 };
 
 template <int D, int K>
-__global__ __launch_bounds__(kThreads) void kmin_mfma_split_kernel(KminArgs a) {
+__global__ __launch_bounds__(kSplitThreads) void kmin_mfma_split_kernel(KminArgs a) {
   using S = KminSplitShape<D, K>;
   constexpr int DP = S::DP, NS = S::NS, RS = S::RS, TJ = S::TJ, TI = S::TI;
-  static_assert(S::ROWS_WG <= kThreads, "one thread per row for the centre");
+  static_assert(S::ROWS_WG <= kSplitThreads, "one thread per row for the centre");
   __shared__ __attribute__((aligned(16))) unsigned sRec[2 * TJ * RS];   // double-buffered split y tiles
   __shared__ __attribute__((aligned(16))) float sNy[2 * TJ];            // |y_c|^2 per j (kPadU: padding)
-  __shared__ float sRed[2 * D * (kThreads / kWave) + 8];
+  __shared__ float sRed[2 * D * kSplitWaves + 8];
   __shared__ float sCen[D];
 
   const int tid = threadIdx.x;
@@ -93,14 +122,20 @@ __global__ __launch_bounds__(kThreads) void kmin_mfma_split_kernel(KminArgs a) {
       if (lane == 0) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          if (d0 + q < D) { sRed[(2 * (d0 + q)) * 4 + wid] = lo[q]; sRed[(2 * (d0 + q) + 1) * 4 + wid] = hi[q]; }
+          if (d0 + q < D) {
+            sRed[(2 * (d0 + q)) * kSplitWaves + wid] = lo[q];
+            sRed[(2 * (d0 + q) + 1) * kSplitWaves + wid] = hi[q];
+          }
       }
     }
     __syncthreads();
-    for (int d = tid; d < D; d += kThreads) {
-      float l = sRed[(2 * d) * 4], h = sRed[(2 * d + 1) * 4];
+    for (int d = tid; d < D; d += kSplitThreads) {
+      float l = sRed[(2 * d) * kSplitWaves], h = sRed[(2 * d + 1) * kSplitWaves];
 #pragma unroll
-      for (int w = 1; w < kThreads / kWave; ++w) { l = fminf(l, sRed[(2 * d) * 4 + w]); h = fmaxf(h, sRed[(2 * d + 1) * 4 + w]); }
+      for (int w = 1; w < kSplitWaves; ++w) {
+        l = fminf(l, sRed[(2 * d) * kSplitWaves + w]);
+        h = fmaxf(h, sRed[(2 * d + 1) * kSplitWaves + w]);
+      }
       sCen[d] = 0.5f * l + 0.5f * h;
     }
     __syncthreads();
@@ -137,6 +172,7 @@ __global__ __launch_bounds__(kThreads) void kmin_mfma_split_kernel(KminArgs a) {
     ax[t] = sqrtf(n);
   }
   const float mcoef = kmin_split_margin_coef(DP);
+  const bool v4 = ((reinterpret_cast<uintptr_t>(a.x) | reinterpret_cast<uintptr_t>(a.y)) & 15u) == 0;
 
   // Prefilter thresholds stay below kPadU, the value padded j carry, so padding
   // never passes; rows beyond M get -inf and never pass either.
@@ -156,7 +192,7 @@ __global__ __launch_bounds__(kThreads) void kmin_mfma_split_kernel(KminArgs a) {
 
   // tile staging: thread (sj = tid/4, sg = tid%4) owns the 8-coordinate chunks
   // c = 4q + sg (q < NS) of column sj, i.e. coordinates 32q + 8sg + e
-  static_assert(TJ * 4 == kThreads, "four staging threads per j");
+  static_assert(TJ * 4 == kSplitThreads, "four staging threads per j");
   const int sj = tid >> 2, sg = tid & 3;
   float ry[NS][8];
   auto load_tile = [&](int64_t jt) {
@@ -246,10 +282,7 @@ __global__ __launch_bounds__(kThreads) void kmin_mfma_split_kernel(KminArgs a) {
           for (int r = 0; r < 4; ++r) {
             const int64_t j = jt + j16 + 4 * lgrp + r;
             if (u[t][r] < thr[t] && j < je && row[t] < M) {
-              const float *xi = a.x + row[t] * D;
-              const float *yj = a.y + j * D;
-              float d2 = 0.0f;
-              for (int k = 0; k < D; ++k) { const float d = xi[k] - yj[k]; d2 = fmaf(d, d, d2); }
+              const float d2 = exact_sq_dist<D>(a.x + row[t] * D, a.y + j * D, v4);
               if (d2 < bd[t][K - 1]) {
                 kmin_insert<K>(bd[t], bi[t], d2, (int)j);
                 const float kth = bd[t][K - 1];
@@ -308,7 +341,7 @@ __global__ __launch_bounds__(kThreads) void kmin_mfma_split_kernel(KminArgs a) {
 
 template <int D, int K>
 void launch_kmin_mfma_split_t(dim3 grid, const KminArgs &a, hipStream_t st) {
-  hipLaunchKernelGGL((kmin_mfma_split_kernel<D, K>), grid, dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((kmin_mfma_split_kernel<D, K>), grid, dim3(kSplitThreads), 0, st, a);
 }
 
 }  // namespace kmi
