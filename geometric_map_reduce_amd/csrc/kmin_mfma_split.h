@@ -56,7 +56,7 @@ __device__ __forceinline__ float exact_sq_dist(const float *xi, const float *yj,
   float d2 = 0.0f;
   if constexpr (D % 4 == 0) {
     if (v4) {
-#pragma unroll
+#pragma unroll 4
       for (int k = 0; k < D; k += 4) {
         const float4 p = *reinterpret_cast<const float4 *>(xi + k);
         const float4 q = *reinterpret_cast<const float4 *>(yj + k);
@@ -72,27 +72,37 @@ __device__ __forceinline__ float exact_sq_dist(const float *xi, const float *yj,
   return d2;
 }
 
-// 16-row tiles per wave: three where the kernel stays within 256 VGPRs, else two.
-constexpr int kmin_split_tiles(int D, int K) { return K <= (D <= 32 ? 13 : (D <= 64 ? 12 : 3)) ? 3 : 2; }
+// Work-group shape.  Twelve waves (768 threads, three waves per SIMD at <= 168
+// VGPRs) with two 16-row tiles per wave where the K-lists are short enough to fit
+// without spills; else eight waves (two per SIMD, <= 256 VGPRs) with three tiles
+// per wave where that still fits, else two.  Both main forms hold 384 rows
+// (12 x 2 x 16, 8 x 3 x 16).  At D = 64 the twelve-wave form ran K = 1 in 416
+// against 563 ms and K = 4 in 522 against 584 ms; at K = 10 it spilled and ran
+// 840 against 785 ms.
+constexpr bool kmin_split_wide(int D, int K) { return D <= 32 ? K <= 6 : (D <= 50 ? K <= 5 : (D <= 64 ? K <= 4 : false)); }
+constexpr int kmin_split_threads(int D, int K) { return kmin_split_wide(D, K) ? 768 : 512; }
+constexpr int kmin_split_tiles(int D, int K) {
+  return kmin_split_wide(D, K) ? 2 : (K <= (D <= 32 ? 13 : (D <= 64 ? 12 : 1)) ? 3 : 2);
+}
 
-// Work-groups of eight waves (two per SIMD at the kernel's register count, so one
-// per CU): every y tile staged in LDS serves 16 * TI rows per wave, 128 * TI in all.
-constexpr int kSplitThreads = 512;
-constexpr int kSplitWaves = kSplitThreads / kWave;
+// One work-group per CU: every y tile staged in LDS serves 16 * TI rows per wave.
 
 template <int D, int K>
 struct KminSplitShape {
   static constexpr int DP = (D + 31) / 32 * 32;    // coordinates padded to whole MFMA steps
   static constexpr int NS = DP / 32;               // MFMA steps per product
   static constexpr int RS = DP + 4;                // u32 per LDS record: DP/2 hi, DP/2 lo, 4 pad
-  static constexpr int TJ = 128;                   // j rows per LDS tile (four staging threads each)
+  static constexpr int NT = kmin_split_threads(D, K);   // threads per work-group
+  static constexpr int NW = NT / kWave;               // waves per work-group
+  static constexpr int TJ = NT / 4;                   // j rows per LDS tile (four staging threads each)
   static constexpr int TI = kmin_split_tiles(D, K);
-  static constexpr int ROWS_WG = kSplitWaves * 16 * TI;   // rows per work-group
+  static constexpr int ROWS_WG = NW * 16 * TI;        // rows per work-group
 };
 
 template <int D, int K>
-__global__ __launch_bounds__(kSplitThreads) void kmin_mfma_split_kernel(KminArgs a) {
+__global__ __launch_bounds__(kmin_split_threads(D, K)) void kmin_mfma_split_kernel(KminArgs a) {
   using S = KminSplitShape<D, K>;
+  constexpr int kSplitThreads = S::NT, kSplitWaves = S::NW;
   constexpr int DP = S::DP, NS = S::NS, RS = S::RS, TJ = S::TJ, TI = S::TI;
   static_assert(S::ROWS_WG <= kSplitThreads, "one thread per row for the centre");
   __shared__ __attribute__((aligned(16))) unsigned sRec[2 * TJ * RS];   // double-buffered split y tiles
@@ -341,7 +351,7 @@ __global__ __launch_bounds__(kSplitThreads) void kmin_mfma_split_kernel(KminArgs
 
 template <int D, int K>
 void launch_kmin_mfma_split_t(dim3 grid, const KminArgs &a, hipStream_t st) {
-  hipLaunchKernelGGL((kmin_mfma_split_kernel<D, K>), grid, dim3(kSplitThreads), 0, st, a);
+  hipLaunchKernelGGL((kmin_mfma_split_kernel<D, K>), grid, dim3(KminSplitShape<D, K>::NT), 0, st, a);
 }
 
 }  // namespace kmi
