@@ -10,10 +10,14 @@
 //   <y, -2x> ~ <y_hi, (-2x)_hi> + <y_hi, (-2x)_lo> + <y_lo, (-2x)_hi>
 // with three v_mfma_f32_16x16x32_bf16 per 32 coordinates (products exact in
 // fp32, fp32 accumulation), and |y_c|^2 entering as the instruction's C input.
-// The dropped product y_lo (-2x)_lo and the rounding of the lo parts are each
-// below 2^-18 |y_k| |2x_k|, so the whole split error is below 1.6 * 2^-18 of
-// (2|x_c| + sqrt(K-th distance))^2; the pass margin adds 2^-16 of that to the
-// accumulation bound of the fp32 form over 3 * 32 * ceil(D / 32) products.  A
+// bf16 keeps 8 significant bits, so |v - v_hi| <= 2^-8 |v| and the rounding of
+// the lo part is below 2^-16 |v|.  The dropped product y_lo (-2x)_lo and the two
+// lo roundings are then each below about 2^-16 |y_k| |2x_k|, and the split error
+// is below 3.01 * 2^-16 sum_k |y_k| |2x_k| <= 1.51 * 2^-16 (2|x_c| + sqrt(kth))^2
+// (kth: the row's K-th distance, with |y_c| <= |x_c| + sqrt(kth) for every
+// candidate that matters).  The pass margin adds 2^-14 of that square, 2.66
+// times the bound, to the accumulation bound of the fp32 form over
+// 3 * 32 * ceil(D / 32) products.  A
 // candidate whose exact distance could be below the row's K-th therefore
 // always passes; passing candidates get the exact direct-form fp32 distance
 // from raw coordinates and the same register insertion, lane-group threshold
@@ -45,8 +49,8 @@ __device__ __forceinline__ void split_bf16x2(float v0, float v1, unsigned &hi, u
 }
 
 // Pass margin coefficient of the split form (see the header comment): the fp32
-// form's bound taken over the 3 * DP products, plus 2^-16 for the split.
-__device__ __forceinline__ float kmin_split_margin_coef(int DP) { return kmin_margin_coef(3 * DP) + 1.52587890625e-5f; }
+// form's bound taken over the 3 * DP products, plus 2^-14 for the split.
+__device__ __forceinline__ float kmin_split_margin_coef(int DP) { return kmin_margin_coef(3 * DP) + 6.103515625e-5f; }
 
 // Exact direct-form squared distance sum_k (x_k - y_k)^2 in fp32, in coordinate
 // order (the same arithmetic as every other K-min kernel); 16-byte loads when D
