@@ -444,7 +444,10 @@ def test_workload_laplace_1M():
 
 KMIN_SMALL = [(1, 1, 1, 1), (5, 40, 3, 10), (300, 1000, 3, 10), (257, 513, 2, 16), (100, 3000, 4, 32),
               (70, 600, 8, 7), (64, 300, 16, 5), (40, 500, 32, 10), (30, 200, 50, 3), (25, 300, 64, 10),
-              (10, 128, 100, 2), (200, 900, 5, 1), (129, 129, 3, 12)]
+              (10, 128, 100, 2), (200, 900, 5, 1), (129, 129, 3, 12),
+              # matrix-core prefilter shapes: several twelve-wave work-groups with ragged rows
+              # and j, eight waves of three tiles, K = N, N below one 16-j step, D = 100 at K = 1
+              (800, 1000, 64, 4), (500, 777, 50, 12), (20, 16, 64, 16), (33, 7, 32, 7), (400, 300, 100, 1)]
 
 
 @pytest.mark.parametrize("case", KMIN_SMALL, ids=lambda c: "M%d_N%d_D%d_K%d" % c)
