@@ -17,9 +17,8 @@
 // (kth: the row's K-th distance, with |y_c| <= |x_c| + sqrt(kth) for every
 // candidate that matters).  The pass margin adds 2^-14 of that square, 2.66
 // times the bound, to the accumulation bound of the fp32 form over
-// 3 * 32 * ceil(D / 32) products.  A
-// candidate whose exact distance could be below the row's K-th therefore
-// always passes; passing candidates get the exact direct-form fp32 distance
+// 3 * 32 * ceil(D / 32) products.  A candidate whose exact distance could be
+// below the row's K-th therefore always passes; passing candidates get the exact direct-form fp32 distance
 // from raw coordinates and the same register insertion, lane-group threshold
 // sharing and final merge as the fp32-MFMA kernel, so the result is that of
 // the direct-form K-min in fp32, bit for bit.
@@ -82,7 +81,8 @@ __device__ __forceinline__ float exact_sq_dist(const float *xi, const float *yj,
 // per wave where that still fits, else two.  Both main forms hold 384 rows
 // (12 x 2 x 16, 8 x 3 x 16).  At D = 64 the twelve-wave form ran K = 1 in 416
 // against 563 ms and K = 4 in 522 against 584 ms; at K = 10 it spilled and ran
-// 840 against 785 ms.
+// 840 against 785 ms (all with an earlier, smaller pass margin; with the current
+// one the chosen forms take 418 / 531 / 797 ms at K = 1 / 4 / 10).
 constexpr bool kmin_split_wide(int D, int K) { return D <= 32 ? K <= 6 : (D <= 50 ? K <= 5 : (D <= 64 ? K <= 4 : false)); }
 constexpr int kmin_split_threads(int D, int K) { return kmin_split_wide(D, K) ? 768 : 512; }
 constexpr int kmin_split_tiles(int D, int K) {
