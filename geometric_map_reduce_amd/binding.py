@@ -68,7 +68,7 @@ def lib() -> ctypes.CDLL:
             L.keops_laplace_sum.argtypes = [P, P, P, i64, i64, i32, i32, f32, P, P]
             L.keops_gauss_max.argtypes = [P, P, P, i64, i64, i32, i32, f32, P, P, P]
             L.keops_gauss_min.argtypes = [P, P, P, i64, i64, i32, i32, f32, P, P, P]
-            L.keops_kmin.argtypes = [P, P, i64, i64, i32, i32, P, P, P]
+            L.keops_kmin.argtypes = [P, P, P, i64, i64, i32, i32, f32, P, P, P]
             L.keops_set_option.argtypes = [ctypes.c_int, i64]
             L.keops_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
             L.keops_status_string.argtypes = [ctypes.c_int]
@@ -317,7 +317,8 @@ def keops_kmin(x, y, K, out_d=None, out_idx=None, stream=None):
     out_d = _out(out_d, (M, K), dev, name="out_d")
     out_idx = _out(out_idx, (M, K), dev, dtype=torch.int64, name="out_idx")
     with torch.cuda.device(dev):
-        rc = lib().keops_kmin(_ptr(x), _ptr(y), M, N, D, int(K), _ptr(out_d), _ptr(out_idx),
+        # b and sigma of the uniform argument list are not read by K-min
+        rc = lib().keops_kmin(_ptr(x), _ptr(y), None, M, N, D, int(K), 1.0, _ptr(out_d), _ptr(out_idx),
                               _stream(stream, dev))
     _check("keops_kmin", rc)
     return out_d, out_idx

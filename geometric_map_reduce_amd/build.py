@@ -51,19 +51,31 @@ def _compile(src: str) -> tuple[str, str]:
     return obj, err
 
 
-def build(jobs: int | None = None, verbose: bool = False) -> str:
-    """Compile every source (always) and link the library; returns its path."""
+def _stale(src: str) -> bool:
+    """True when the object of ``src`` is missing or older than the source or any header."""
+    obj = os.path.join(OBJ, os.path.basename(src) + ".o")
+    if not os.path.exists(obj):
+        return True
+    deps = [src] + [os.path.join(d, f) for d in (CSRC, INCLUDE) for f in os.listdir(d) if f.endswith(".h")]
+    return os.path.getmtime(obj) < max(os.path.getmtime(p) for p in deps)
+
+
+def build(jobs: int | None = None, verbose: bool = False, incremental: bool = False) -> str:
+    """Compile every source (or, ``incremental``, those older than their inputs) and link
+    the library; returns its path."""
     os.makedirs(OBJ, exist_ok=True)
     srcs = sources()
-    jobs = jobs or min(len(srcs), max(1, os.cpu_count() or 1), 16)
+    todo = [s for s in srcs if _stale(s)] if incremental else srcs
+    jobs = jobs or min(max(len(todo), 1), max(1, os.cpu_count() or 1), 16)
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        results = list(ex.map(_compile, srcs))
+        results = list(ex.map(_compile, todo))
     if verbose:
         for _, err in results:
             if err.strip():
                 print(err, file=sys.stderr)
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + [o for o, _ in results]
+    objs = [os.path.join(OBJ, os.path.basename(s) + ".o") for s in srcs]
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stderr}")
@@ -72,4 +84,4 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, incremental="--incremental" in sys.argv[1:]))

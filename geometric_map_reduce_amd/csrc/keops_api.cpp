@@ -732,8 +732,8 @@ int keops_laplace_sum(const float *x, const float *y, const float *b, int64_t M,
   return gauss_entry(OP_LAPLACE, x, y, b, nullptr, M, N, D, E, sigma, out, stream);
 }
 
-int keops_kmin(const float *x, const float *y, int64_t M, int64_t N, int32_t D, int32_t K, float *out_d,
-               int64_t *out_idx, void *stream) {
+int keops_kmin(const float *x, const float *y, const float * /*b: not read*/, int64_t M, int64_t N, int32_t D,
+               int32_t K, float /*sigma: not read*/, float *out_d, int64_t *out_idx, void *stream) {
   if (M < 0 || N < 0 || D < 1 || K < 1) return KEOPS_ERR_INVALID_ARG;
   if ((int64_t)K > N) return KEOPS_ERR_INVALID_ARG;
   if (M > 0 && (!x || !out_d || !out_idx)) return KEOPS_ERR_INVALID_ARG;

@@ -199,10 +199,14 @@ int keops_gauss_cg(const float *x, const float *b, int64_t N, int32_t D, int32_t
  * K-min reductions): for each row i, the K smallest squared distances
  * |x_i - y_j|^2, ascending, and their indices j; equal distances are ordered
  * by smaller j first.  K = 1 is ArgMin.
- * out_d: [M, K] fp32; out_idx: [M, K] int64.  Requires 1 <= K <= N < 2^31.
+ * The argument list follows the other reductions, (x, y, b, ..., sigma, out,
+ * stream): b and sigma do not enter a nearest-neighbour search, are never read
+ * and are not validated (b may be NULL, sigma any value).
+ * out_d: [M, K] fp32; out_idx: [M, K] int64, 8-byte aligned.
+ * Requires 1 <= K <= N < 2^31.
  */
-int keops_kmin(const float *x, const float *y,
-               int64_t M, int64_t N, int32_t D, int32_t K,
+int keops_kmin(const float *x, const float *y, const float *b,
+               int64_t M, int64_t N, int32_t D, int32_t K, float sigma,
                float *out_d, int64_t *out_idx, void *stream);
 
 /* Human-readable name of a status code (static storage). */

@@ -434,6 +434,49 @@ def pin_solve_residual(lib=None):
         assert np.all(np.abs(r) <= bound + 1e-12), np.abs(r).max()
 
 
+def pin_system_residual(lib=None, residual=None):
+    """oracle.gauss_system_residual, the checker of the conjugate-gradient solver ([README]
+    feature list: conjugate gradient solver for kriging), against facts that do not come from
+    it: a = 0 leaves r = b exactly; far-apart points make K the identity, so r = b - (1 + lam) a
+    (exact on dyadic values); the dense solution leaves a rounding-level residual; a row
+    selection returns exactly those rows of the full residual.  ``residual`` replaces the
+    helper (planted mistakes in a copy of it must fail here)."""
+    res = residual or oracle.gauss_system_residual
+    rng = np.random.default_rng(64)
+    # a = 0: no product contributes
+    x = rng.standard_normal((30, 3)).astype(np.float32)
+    b = rng.standard_normal((30, 2)).astype(np.float32)
+    r0 = res(x, b, np.zeros((30, 2), np.float32), 0.7, 0.5, lib=lib)
+    assert r0.shape == (30, 2) and np.array_equal(r0, b.astype(np.float64))
+    # K = I (points 100 apart, sigma 1: exp(-1e4) is exactly 0 in double), dyadic a, b, lam
+    xf = (np.arange(16, dtype=np.float32)[:, None] * np.float32(100.0)).repeat(3, 1)
+    af = dyadic(rng, (16, 2))
+    bf = dyadic(rng, (16, 2))
+    for lam in (0.25, 0.0, 3.0):
+        rf = res(xf, bf, af, 1.0, lam, lib=lib)
+        assert np.array_equal(rf, bf.astype(np.float64) - (1.0 + lam) * af.astype(np.float64)), lam
+    # the dense solve, rounded to fp32, leaves a residual of fp32 rounding times (K + lam I)
+    for (N, D, E, sigma, lam) in [(50, 3, 1, 0.6, 0.2), (35, 4, 2, 1.2, 2.0)]:
+        xs = rng.standard_normal((N, D)).astype(np.float32)
+        bs = rng.standard_normal((N, E)).astype(np.float32)
+        a = oracle.gauss_solve(xs, bs, sigma, lam, lib=lib)
+        K = brute_K(xs, xs, sigma)
+        r = res(xs, bs, a.astype(np.float32), sigma, lam, lib=lib)
+        bound = 2.0 ** -23 * (K.sum(1, keepdims=True) + lam) * np.abs(a).max(0, keepdims=True)
+        assert r.shape == (N, E) and np.all(np.abs(r) <= bound + 1e-12), np.abs(r).max()
+        # a residual that is not small: a perturbed solution; its residual is (K + lam I) delta
+        delta = dyadic(rng, (N, E), -1.0, 1.0)
+        a2 = (a.astype(np.float32) + delta).astype(np.float32)
+        r2 = res(xs, bs, a2, sigma, lam, lib=lib)
+        expect = bs.astype(np.float64) - (K + lam * np.eye(N)) @ a2.astype(np.float64)
+        rel_close(r2, expect, 0, 1e-12 * (1 + np.abs(expect).max()))
+        # rows: exactly the selected rows of the full call, in the given order
+        rows = np.array([N - 1, 0, 7, 3], np.int64)
+        full = res(xs, bs, a2, sigma, lam, lib=lib)
+        sub = res(xs, bs, a2, sigma, lam, rows=rows, lib=lib)
+        assert sub.shape == (4, E) and np.array_equal(sub, full[rows])
+
+
 # --------------------------------------------------------------------------- block-sparse ranges
 def random_ranges(rng, M, N, n_row_ranges, max_j_ranges, cover=False):
     """Disjoint row ranges (a partition of [0, M) when ``cover``, else with gaps), each meeting

@@ -92,15 +92,16 @@ def test_transposed_gradients_validation(L):
 
 
 @pytest.mark.parametrize("args,rc", [
-    ((None, None, 0, 5, 3, 0, None, None, None), -1),       # K < 1
-    ((None, None, 0, 5, 3, 6, None, None, None), -1),       # K > N
-    ((None, FAKE, 0, 5, 0, 1, None, None, None), -1),       # D < 1
-    ((None, FAKE, 0, 100, 3, 17, None, None, None), -2),    # K not compiled
-    ((None, FAKE, 0, 5, 9, 2, None, None, None), -2),       # D not compiled
-    ((None, FAKE, 0, 1 << 31, 3, 2, None, None, None), -2),  # N >= 2^31
-    ((None, FAKE, 0, 5, 3, 5, None, None, None), 0),        # M = 0: no-op
-    ((FAKE, FAKE2, 4, 5, 3, 2, None, ctypes.c_void_p(0x900000), None), -1),   # out_d null
-    ((FAKE, FAKE2, 4, 5, 3, 2, ctypes.c_void_p(0x900000), ctypes.c_void_p(0x900004), None), -1),  # idx misaligned
+    ((None, None, None, 0, 5, 3, 0, 1.0, None, None, None), -1),       # K < 1
+    ((None, None, None, 0, 5, 3, 6, 1.0, None, None, None), -1),       # K > N
+    ((None, FAKE, None, 0, 5, 0, 1, 1.0, None, None, None), -1),       # D < 1
+    ((None, FAKE, None, 0, 100, 3, 17, 1.0, None, None, None), -2),    # K not compiled
+    ((None, FAKE, None, 0, 5, 9, 2, 1.0, None, None, None), -2),       # D not compiled
+    ((None, FAKE, None, 0, 1 << 31, 3, 2, 1.0, None, None, None), -2),  # N >= 2^31
+    ((None, FAKE, None, 0, 5, 3, 5, 1.0, None, None, None), 0),        # M = 0: no-op
+    ((None, FAKE, FAKE2, 0, 5, 3, 5, float("nan"), None, None, None), 0),   # b, sigma never read
+    ((FAKE, FAKE2, None, 4, 5, 3, 2, 1.0, None, ctypes.c_void_p(0x900000), None), -1),   # out_d null
+    ((FAKE, FAKE2, None, 4, 5, 3, 2, 1.0, ctypes.c_void_p(0x900000), ctypes.c_void_p(0x900004), None), -1),  # idx misaligned
 ])
 def test_kmin_validation(L, args, rc):
     assert L.keops_kmin(*args) == rc

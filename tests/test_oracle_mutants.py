@@ -91,3 +91,31 @@ def test_mutant_is_caught(name, tmp_path):
         except (AssertionError, ValueError, FloatingPointError):
             caught.append(pin.__name__)
     assert caught, f"mutant {name} survived every pin"
+
+
+# Planted mistakes in a copy of the Python checker of the conjugate-gradient solver
+# (oracle.gauss_system_residual); pin_system_residual must catch each one.
+RESIDUAL_MUTANTS = {
+    "residual_lam_sign": ("- float(lam) * a[sel]", "+ float(lam) * a[sel]"),
+    "residual_lam_dropped": ("- float(lam) * a[sel]", "- 0.0 * a[sel]"),
+    "residual_rows_ignored_in_product": ("gauss_sum(x[rows] if rows is not None else x, x, a",
+                                         "gauss_sum(x, x, a"),
+    "residual_rows_ignored_in_b": ("return b[sel] - Ka", "return b[:Ka.shape[0]] - Ka"),
+    "residual_product_sign": ("return b[sel] - Ka", "return b[sel] + Ka"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(RESIDUAL_MUTANTS))
+def test_residual_mutant_is_caught(name):
+    import inspect
+    import textwrap
+    old, new = RESIDUAL_MUTANTS[name]
+    src = textwrap.dedent(inspect.getsource(oracle.gauss_system_residual))
+    assert src.count(old) == 1, f"mutation site for {name} not found"
+    ns = dict(vars(oracle))
+    exec(compile(src.replace(old, new), f"<mutant {name}>", "exec"), ns)
+    try:
+        oracle_pins.pin_system_residual(residual=ns["gauss_system_residual"])
+    except (AssertionError, ValueError, IndexError):
+        return
+    pytest.fail(f"mutant {name} survived pin_system_residual")
