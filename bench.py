@@ -84,16 +84,17 @@ def is_stream(op, M, D):
 def roofline_of(op, M, D, E):
     """(bound, algorithmic units per pair, kernel name) of the dominant pass-1 kernel.
     MFMA sum: the contraction <x~, y~> of 2D flops per pair against the fp32 matrix peak
-    (the per-pair exp and accumulate are VALU work on top).  MFMA K-min: the split-bf16
-    prefilter's three bf16 products over D coordinates, 6D flops per pair, against the
-    bf16 matrix peak.  Few-rows sum: HBM bytes, priced per launch (y and b read once)
-    rather than per pair."""
+    (the per-pair exp and accumulate are VALU work on top).  MFMA K-min: the distance's
+    contraction, 2D algorithmic flops per pair, against the peak of the bf16 matrix pipe
+    the split-bf16 prefilter runs on (it executes three bf16 products, 6D flops, reported
+    beside it).  Few-rows sum: HBM bytes, priced per launch (y and b read once) rather
+    than per pair."""
     if is_stream(op, M, D):
         return "hbm", None, "gauss_stream_kernel"
     if uses_mfma(op, D):
         if op == "sum":
             return "mfma", 2 * D, "gauss_mfma_sum_kernel"
-        return "mfma_bf16", 6 * D, "kmin_mfma_split_kernel"
+        return "mfma_bf16", 2 * D, "kmin_mfma_split_kernel"
     # the transposed gradients run the row kernels with y as the rows
     kop = {"grad_y": "grad_x", "grad_b": "sum", "cg": "sum", "sum_ranges": "sum"}.get(op, op)
     if op == "laplace":
@@ -269,12 +270,72 @@ def copy_calibration(torch, args):
                       "read_bytes_per_launch": 4 * n, "write_bytes_per_launch": 4 * n}), flush=True)
 
 
+MICRO_PROBES = ["fma", "add", "exp", "fma_exp", "mfma_f32", "mfma_bf16", "mfma_fma_wave", "mfma_exp_wave",
+                "split_mfma", "split_valu", "split_both", "pair_valu", "pair_mfma"]
+
+
+def micro_rates(torch):
+    """Instruction rates of the chip (geometric_map_reduce_amd/micro/rates.hip): for each probe
+    the kernel time, the engine clock it ran at, the cycles one SIMD spends per wave64
+    instruction of each kind, and for the pair probes the Gaussian pair-evaluations per second.
+    Prints one JSON line."""
+    import ctypes
+
+    from geometric_map_reduce_amd import build as gbuild
+    lib = ctypes.CDLL(gbuild.MICRO_LIB)
+    lib.keops_micro_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_float),
+                                    ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
+    assert lib.keops_micro_count() == len(MICRO_PROBES)
+    torch.cuda.init()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    simds = 4 * cus
+    kinds = ["fma", "add", "exp", "mfma_f32", "mfma_bf16"]
+    res = {}
+    for pid, name in enumerate(MICRO_PROBES):
+        threads = 512 if name.startswith("split") else 256
+        blocks = cus * (4 if threads == 512 else 8)
+        iters = 64 if name.startswith("pair") else 2048
+        for _ in range(2):              # the first launch also loads the code object
+            ms, mhz = ctypes.c_float(0), ctypes.c_double(0)
+            cnt = (ctypes.c_double * 8)()
+            rc = lib.keops_micro_run(pid, blocks, iters, ctypes.byref(ms), ctypes.byref(mhz), cnt)
+            if rc != 0:
+                raise RuntimeError(f"micro probe {name}: status {rc}")
+        t = ms.value * 1e-3
+        simd_cycles = t * mhz.value * 1e6 * simds      # SIMD-cycles available during the launch
+        waves = cnt[5]
+        r = {"ms": round(ms.value, 4), "clock_mhz": round(mhz.value, 1), "blocks": blocks, "threads": threads,
+             "iters": iters}
+        instr = {k: cnt[q] * waves for q, k in enumerate(kinds) if cnt[q] > 0}
+        # cycles of one SIMD per wave64 instruction, all kinds of the probe together
+        tot = sum(instr.values())
+        if tot:
+            r["wave_instr"] = {k: v for k, v in instr.items()}
+            r["simd_cycles_per_wave_instr"] = round(simd_cycles / tot, 3)
+            if len(instr) == 1:
+                k = next(iter(instr))
+                per_s = instr[k] * 64 / t
+                if k.startswith("mfma"):
+                    flops = (16 * 16 * 4 * 2 if k == "mfma_f32" else 16 * 16 * 32 * 2) * instr[k] / t
+                    r["tflops"] = round(flops / 1e12, 2)
+                else:
+                    r["lane_ops_per_s"] = float(f"{per_s:.4g}")
+        if cnt[6]:
+            pairs = cnt[6] / t
+            r["pairs_per_s"] = float(f"{pairs:.4g}")
+            r["equiv_12flop_tflops"] = round(12 * pairs / 1e12, 2)
+            r["frac_fp32_vector_peak"] = round(12 * pairs / (PEAK_FP32_TFLOPS * 1e12), 4)
+            r["simd_cycles_per_64_pairs"] = round(simd_cycles / (cnt[6] / 64), 3)
+        res[name] = r
+    print(json.dumps({"workload": "micro", "cus": cus, "probes": res}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="sum", choices=sorted(BENCHES) + ["copycal"])
+    ap.add_argument("--workload", default="sum", choices=sorted(BENCHES) + ["copycal", "micro"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -290,6 +351,9 @@ def main():
 
     if args.workload == "copycal":
         copy_calibration(torch, args)
+        return
+    if args.workload == "micro":
+        micro_rates(torch)
         return
 
     import geometric_map_reduce_amd as gm
@@ -373,8 +437,9 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic}
         kinfo = {"flops_per_pair": fpp}
         if bound == "mfma_bf16":
-            # the same prefilter as an fp32 contraction (2D flops per pair) for comparison
-            kinfo["fp32_equivalent_TFLOP_s"] = round(2 * w.D * per_launch / (kern_avg_ms * 1e-3) / 1e12, 3)
+            # what the split-bf16 prefilter executes: three bf16 products over D, 6D flops per pair
+            kinfo["executed_flops_per_pair"] = 6 * w.D
+            kinfo["executed_TFLOP_s"] = round(6 * w.D * per_launch / (kern_avg_ms * 1e-3) / 1e12, 3)
 
     res = {
         "metric": METRIC if args.workload == "sum" else f"{op} G pair-evals/s @ {w.name}",

@@ -19,6 +19,9 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkeops_mi355x.so")
+# instruction-rate microbenchmarks: a library of their own, never linked into LIB
+MICRO_SRC = os.path.join(HERE, "micro", "rates.hip")
+MICRO_LIB = os.path.join(HERE, "libkeops_micro.so")
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -80,7 +83,18 @@ def build(jobs: int | None = None, verbose: bool = False, incremental: bool = Fa
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stderr}")
     os.replace(tmp, LIB)
+    build_micro()
     return LIB
+
+
+def build_micro() -> str:
+    """Compile the instruction-rate microbenchmarks into libkeops_micro.so (same flags)."""
+    tmp = MICRO_LIB + ".tmp%d" % os.getpid()
+    res = subprocess.run([HIPCC, *CFLAGS, "-shared", "-o", tmp, MICRO_SRC], capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {MICRO_SRC}:\n{res.stderr}")
+    os.replace(tmp, MICRO_LIB)
+    return MICRO_LIB
 
 
 if __name__ == "__main__":
