@@ -271,7 +271,8 @@ def copy_calibration(torch, args):
 
 
 MICRO_PROBES = ["fma", "add", "exp", "fma_exp", "mfma_f32", "mfma_bf16", "mfma_fma_wave", "mfma_exp_wave",
-                "split_mfma", "split_valu", "split_both", "pair_valu", "pair_mfma"]
+                "split_mfma", "split_valu", "split_both", "pair_valu", "pair_mfma", "bank_free", "bank_two",
+                "bank_three"]
 
 
 def micro_rates(torch):

@@ -19,7 +19,9 @@
 //                         three FMAs, one exp2 and one add per pair;
 //   pair_mfma             the same pairs with the exponent from one
 //                         v_mfma_f32_16x16x4f32 per 16 x 16 pairs (rows in the A
-//                         operand, LDS records in B), then exp2 and an FMA with b.
+//                         operand, LDS records in B), then exp2 and an FMA with b;
+//   bank_{free,two,three} v_fmac_f32 chains whose three VGPR reads sit in three, two or
+//                         one register bank (index mod 4).
 // Work per launch is returned to the host so that rates need no duplicated
 // constants: keops_micro_run fills per-wave instruction counts.
 #include <hip/hip_runtime.h>
@@ -324,6 +326,56 @@ __global__ __launch_bounds__(256) void k_pair_mfma(float *out, Clock *c, int ite
   clock_stop(c);
 }
 
+// VGPR bank probes: eight independent v_fmac_f32 chains (d = s0 * s1 + d reads three
+// VGPRs) with every operand pinned to a physical register, so that the register bank
+// (index mod 4) of the three reads is fixed: variant 0 puts them in three different
+// banks, variant 1 two of them in one bank, variant 2 all three in one bank.  The
+// rate difference is the cost of a bank conflict.  No memory access in the asm.
+#define KMI_BANK_BODY(A0, A1, A2, A3, A4, A5, A6, A7, X0, X1, X2, X3, X4, X5, X6, X7, Y0, Y1, Y2, Y3, Y4, Y5, Y6, Y7) \
+  asm volatile(                                                                                                  \
+      "v_fmac_f32 %0, %8, %16\n\tv_fmac_f32 %1, %9, %17\n\tv_fmac_f32 %2, %10, %18\n\t"                            \
+      "v_fmac_f32 %3, %11, %19\n\tv_fmac_f32 %4, %12, %20\n\tv_fmac_f32 %5, %13, %21\n\t"                          \
+      "v_fmac_f32 %6, %14, %22\n\tv_fmac_f32 %7, %15, %23"                                                        \
+      : "+{" A0 "}"(a[0]), "+{" A1 "}"(a[1]), "+{" A2 "}"(a[2]), "+{" A3 "}"(a[3]), "+{" A4 "}"(a[4]),            \
+        "+{" A5 "}"(a[5]), "+{" A6 "}"(a[6]), "+{" A7 "}"(a[7])                                                    \
+      : "{" X0 "}"(x[0]), "{" X1 "}"(x[1]), "{" X2 "}"(x[2]), "{" X3 "}"(x[3]), "{" X4 "}"(x[4]),                 \
+        "{" X5 "}"(x[5]), "{" X6 "}"(x[6]), "{" X7 "}"(x[7]), "{" Y0 "}"(y[0]), "{" Y1 "}"(y[1]),                 \
+        "{" Y2 "}"(y[2]), "{" Y3 "}"(y[3]), "{" Y4 "}"(y[4]), "{" Y5 "}"(y[5]), "{" Y6 "}"(y[6]), "{" Y7 "}"(y[7]))
+
+template <int V>
+__global__ void k_bank(float *out, Clock *c, int iters) {
+  clock_start(c);
+  float a[8], x[8], y[8];
+  // run-time operands, so that the compiler keeps them in their registers instead of
+  // re-creating constants before every asm block
+  for (int k = 0; k < 8; ++k) {
+    a[k] = 1e-3f * threadIdx.x + k;
+    x[k] = 0.999f - 1e-9f * (threadIdx.x + 7 * k);
+    y[k] = 1e-4f * (k + 1) + 1e-9f * threadIdx.x;
+  }
+  for (int i = 0; i < iters; ++i)
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (V == 0)   // acc bank b, s0 bank b+1, s1 bank b+2
+        KMI_BANK_BODY("v8", "v9", "v10", "v11", "v12", "v13", "v14", "v15",
+                      "v17", "v18", "v19", "v16", "v21", "v22", "v23", "v20",
+                      "v26", "v27", "v24", "v25", "v30", "v31", "v28", "v29");
+      else if (V == 1)   // acc and s0 in one bank, s1 in the next
+        KMI_BANK_BODY("v8", "v9", "v10", "v11", "v12", "v13", "v14", "v15",
+                      "v16", "v17", "v18", "v19", "v20", "v21", "v22", "v23",
+                      "v25", "v26", "v27", "v24", "v29", "v30", "v31", "v28");
+      else   // all three in one bank
+        KMI_BANK_BODY("v8", "v9", "v10", "v11", "v12", "v13", "v14", "v15",
+                      "v16", "v17", "v18", "v19", "v20", "v21", "v22", "v23",
+                      "v24", "v25", "v26", "v27", "v28", "v29", "v30", "v31");
+    }
+  float s = 0.0f;
+  for (int k = 0; k < 8; ++k) s += a[k];
+  sink(out, s);
+  clock_stop(c);
+}
+#undef KMI_BANK_BODY
+
 }  // namespace
 
 extern "C" {
@@ -331,7 +383,7 @@ extern "C" {
 // Probe ids, in the order listed at the top of this file.
 enum {
   P_FMA = 0, P_ADD, P_EXP, P_FMA_EXP, P_MFMA_F32, P_MFMA_BF16, P_MFMA_FMA_WAVE, P_MFMA_EXP_WAVE,
-  P_SPLIT_MFMA, P_SPLIT_VALU, P_SPLIT_BOTH, P_PAIR_VALU, P_PAIR_MFMA, P_COUNT
+  P_SPLIT_MFMA, P_SPLIT_VALU, P_SPLIT_BOTH, P_PAIR_VALU, P_PAIR_MFMA, P_BANK_FREE, P_BANK_TWO, P_BANK_THREE, P_COUNT
 };
 
 int keops_micro_count(void) { return P_COUNT; }
@@ -363,6 +415,7 @@ int keops_micro_run(int probe, int blocks, int iters, float *ms, double *clk_mhz
     case P_SPLIT_BOTH: threads = 512; counts[3] = n * kMf; counts[0] = n * kCh; counts[2] = n * kCh / 2; break;
     case P_PAIR_VALU: counts[6] = (double)blocks * 256 * 2 * 256 * iters; break;
     case P_PAIR_MFMA: counts[6] = (double)blocks * 4 * 64 * 256 * iters; break;
+    case P_BANK_FREE: case P_BANK_TWO: case P_BANK_THREE: counts[0] = n * 8; break;
   }
   // split probes: four waves of each role per work-group; the counts of split_both are
   // those of one MFMA wave plus one VALU wave
@@ -393,6 +446,9 @@ int keops_micro_run(int probe, int blocks, int iters, float *ms, double *clk_mhz
       case P_SPLIT_BOTH: hipLaunchKernelGGL(k_split, g, b, 0, nullptr, out, clk, iters, 3); break;
       case P_PAIR_VALU: hipLaunchKernelGGL(k_pair_valu, g, b, 0, nullptr, out, clk, iters); break;
       case P_PAIR_MFMA: hipLaunchKernelGGL(k_pair_mfma, g, b, 0, nullptr, out, clk, iters); break;
+      case P_BANK_FREE: hipLaunchKernelGGL(k_bank<0>, g, b, 0, nullptr, out, clk, iters); break;
+      case P_BANK_TWO: hipLaunchKernelGGL(k_bank<1>, g, b, 0, nullptr, out, clk, iters); break;
+      case P_BANK_THREE: hipLaunchKernelGGL(k_bank<2>, g, b, 0, nullptr, out, clk, iters); break;
     }
     (void)hipEventRecord(e1, nullptr);
     Clock h{};
