@@ -2,8 +2,8 @@
 //
 // With S splits of the j range, pass 1 leaves S partial results per row:
 //   sum / grad_x : partial sums,               combined as  sum_s p_s
-//   LogSumExp    : (m_s, s_s) in log2 units,   combined as  m = max_s m_s,
-//                  s = sum_s s_s 2^(m_s - m),  out = ln2 (m + log2 s)
+//   LogSumExp    : (m_s, s_s) in log2 units,   combined as  v_s = m_s + log2 s_s,
+//                  m = max_s v_s, out = ln2 (m + log2 sum_s 2^(v_s - m))
 //   K-min        : sorted (d^2, j) lists,      merged by (d^2, j) order;
 //   Max/ArgMax   : (value, j) pairs,           the largest value, then the smaller j.
 // Splits are visited in order, so results do not depend on scheduling.
@@ -24,68 +24,21 @@ __global__ __launch_bounds__(kThreads) void sum_combine_kernel(const float *__re
 }
 
 __global__ __launch_bounds__(kThreads) void lse_combine_kernel(const float *__restrict__ ws, int nsplit,
-                                                               int64_t M, int E, float thr, float *__restrict__ out) {
+                                                               int64_t M, int E, float *__restrict__ out) {
   const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (t >= M * E) return;
   const int64_t i = t / E;
   const int e = (int)(t - i * E);
   const int64_t stride = M * 2 * E;
   const float *p = ws + i * 2 * E + 2 * e;
-  float m = -3.0e38f;
-  for (int k = 0; k < nsplit; ++k) m = fmaxf(m, p[k * stride]);
-  float s = 0.0f;
-  for (int k = 0; k < nsplit; ++k) s += p[k * stride + 1] * exp2f(p[k * stride] - m);
-  // a sum below thr (fixed-shift partials: possibly lost to underflow) or NaN is
-  // left as NaN for the fix-up launch
-  out[t] = s >= thr ? kLn2 * (m + log2f(s)) : __int_as_float(0x7fc00000);
-}
-
-// Maximum of b (or of |b|) over b[0..n), NaN ignored, -inf if empty: stage 1 writes
-// one partial per work-group (grid-strided), stage 2 (one work-group) reduces them.
-__device__ float block_max_f(float m, float *red) {
-  red[threadIdx.x] = m;
-  __syncthreads();
-  for (int w = kThreads / 2; w > 0; w >>= 1) {
-    if (threadIdx.x < w) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + w]);
-    __syncthreads();
-  }
-  return red[0];
-}
-
-__global__ __launch_bounds__(kThreads) void bmax_kernel(const float *__restrict__ b, int64_t n, int absval,
-                                                        float *__restrict__ part) {
-  __shared__ float red[kThreads];
+  // each partial as one log2 value m_s + log2 s_s (a fixed-shift partial sum may be close
+  // to the top of the fp32 range, so the sums are not added in their own scale)
   float m = -INFINITY;
-  for (int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x; t < n; t += (int64_t)gridDim.x * kThreads)
-    m = fmaxf(m, absval ? fabsf(b[t]) : b[t]);
-  m = block_max_f(m, red);
-  if (threadIdx.x == 0) part[blockIdx.x] = m;
-}
-
-__global__ __launch_bounds__(kThreads) void bmax_final_kernel(const float *__restrict__ part, int nparts,
-                                                              float *__restrict__ out) {
-  __shared__ float red[kThreads];
-  float m = -INFINITY;
-  for (int t = threadIdx.x; t < nparts; t += kThreads) m = fmaxf(m, part[t]);
-  m = block_max_f(m, red);
-  if (threadIdx.x == 0) out[0] = m;
-}
-
-// Guarded sum / grad_x split launches: out[i][w] = (sum over splits of the unscaled
-// partials) times the row factor f[i]; a row with threshold t[i] >= 0 whose sum is
-// below it (or NaN) is written as NaN for the fix-up launch; t[i] < 0 marks a
-// direct-form row (factor, then 2^-64).
-__global__ __launch_bounds__(kThreads) void rows_combine_kernel(const float *__restrict__ ws, int nsplit, int64_t M,
-                                                                int W, const float *__restrict__ f,
-                                                                const float *__restrict__ t, float *__restrict__ out) {
-  const int64_t q = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (q >= M * W) return;
-  const int64_t i = q / W;
+  for (int k = 0; k < nsplit; ++k) m = fmaxf(m, p[k * stride] + log2f(p[k * stride + 1]));
   float s = 0.0f;
-  for (int k = 0; k < nsplit; ++k) s += ws[(int64_t)k * M * W + q];
-  const float ti = t[i];
-  if (ti >= 0.0f) out[q] = fabsf(s) >= ti ? s * f[i] : __int_as_float(0x7fc00000);
-  else out[q] = (s * f[i]) * exp2f(-kDirectOffset);
+  if (m > -INFINITY)
+    for (int k = 0; k < nsplit; ++k) s += exp2f(p[k * stride] + log2f(p[k * stride + 1]) - m);
+  out[t] = m > -INFINITY ? kLn2 * (m + log2f(s)) : -INFINITY;
 }
 
 template <int K>
@@ -131,11 +84,8 @@ __global__ __launch_bounds__(kThreads) void fill_kernel(float *__restrict__ out,
 
 // Max/ArgMax: for row i, column e, the split with the largest signed value
 // (NaN never wins), the smaller index among equal values; splits in order.
-// rf, rt (optional): guarded launches leave the values unscaled; as in rows_combine,
-// the row factor and threshold are applied here (a flagged row: NaN, index -1)
 __global__ __launch_bounds__(kThreads) void max_combine_kernel(const float *__restrict__ ws, int nsplit, int64_t M,
-                                                               int E, float sign, const float *__restrict__ rf,
-                                                               const float *__restrict__ rt, float *__restrict__ out,
+                                                               int E, float sign, float *__restrict__ out,
                                                                int64_t *__restrict__ out_idx) {
   const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (t >= M * E) return;
@@ -149,15 +99,6 @@ __global__ __launch_bounds__(kThreads) void max_combine_kernel(const float *__re
     const float v = p[k * stride];
     const int j = __float_as_int(p[k * stride + 1]);
     if (j >= 0 && (v > best || (v == best && (bi < 0 || j < bi)))) { best = v; bi = j; }
-  }
-  if (rt) {
-    const float ti = rt[i];
-    if (ti >= 0.0f && !(fabsf(best) >= ti)) {
-      out[t] = __int_as_float(0x7fc00000);
-      out_idx[t] = -1;
-      return;
-    }
-    best = ti >= 0.0f ? best * rf[i] : (best * rf[i]) * exp2f(-kDirectOffset);
   }
   out[t] = sign * best;
   out_idx[t] = (int64_t)bi;
@@ -180,22 +121,9 @@ void launch_sum_combine(const float *ws, int nsplit, int64_t count, float *out, 
   if (count > 0) hipLaunchKernelGGL(sum_combine_kernel, dim3(blocks_for(count)), dim3(kThreads), 0, st, ws, nsplit, count, out);
 }
 
-void launch_lse_combine(const float *ws, int nsplit, int64_t M, int E, float thr, float *out, hipStream_t st) {
+void launch_lse_combine(const float *ws, int nsplit, int64_t M, int E, float *out, hipStream_t st) {
   if (M * E > 0)
-    hipLaunchKernelGGL(lse_combine_kernel, dim3(blocks_for(M * E)), dim3(kThreads), 0, st, ws, nsplit, M, E, thr, out);
-}
-
-void launch_bmax(const float *b, int64_t n, bool absval, float *scratch, float *out, hipStream_t st) {
-  const int64_t want = (n + 16 * kThreads - 1) / (16 * kThreads);   // about 16 loads per thread
-  const int g = (int)std::max<int64_t>(1, std::min<int64_t>(kBmaxParts, want));
-  hipLaunchKernelGGL(bmax_kernel, dim3(g), dim3(kThreads), 0, st, b, n, absval ? 1 : 0, scratch);
-  hipLaunchKernelGGL(bmax_final_kernel, dim3(1), dim3(kThreads), 0, st, scratch, g, out);
-}
-
-void launch_rows_combine(const float *ws, int nsplit, int64_t M, int W, const float *f, const float *t, float *out,
-                         hipStream_t st) {
-  if (M * W > 0)
-    hipLaunchKernelGGL(rows_combine_kernel, dim3(blocks_for(M * W)), dim3(kThreads), 0, st, ws, nsplit, M, W, f, t, out);
+    hipLaunchKernelGGL(lse_combine_kernel, dim3(blocks_for(M * E)), dim3(kThreads), 0, st, ws, nsplit, M, E, out);
 }
 
 int launch_kmin_combine(const float *pd, const int32_t *pi, int nsplit, int64_t M, int K, float *out_d,
@@ -214,11 +142,11 @@ void launch_fill(float *out, int64_t count, float v, hipStream_t st) {
   if (count > 0) hipLaunchKernelGGL(fill_kernel, dim3(blocks_for(count)), dim3(kThreads), 0, st, out, count, v);
 }
 
-void launch_max_combine(const float *ws, int nsplit, int64_t M, int E, float sign, const float *rf, const float *rt,
-                        float *out, int64_t *out_idx, hipStream_t st) {
+void launch_max_combine(const float *ws, int nsplit, int64_t M, int E, float sign, float *out, int64_t *out_idx,
+                        hipStream_t st) {
   if (M * E > 0)
     hipLaunchKernelGGL(max_combine_kernel, dim3(blocks_for(M * E)), dim3(kThreads), 0, st, ws, nsplit, M, E, sign,
-                       rf, rt, out, out_idx);
+                       out, out_idx);
 }
 
 void launch_fill_i64(int64_t *out, int64_t count, int64_t v, hipStream_t st) {

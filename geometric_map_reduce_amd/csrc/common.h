@@ -57,30 +57,24 @@ struct GaussArgs {
   // Null for dense launches (rows from blockIdx.x, j from blockIdx.y).
   const BsItem *items;
   const int64_t *redr;
-  // Underflow guard of the expanded form (dense launches): the maximum of b
-  // (LogSumExp) or of |b| (sum, grad_x, Max), one float, null when off; ceil(log2 N).
-  // LogSumExp: a fixed per-row shift where the maximum allows; lse_thr is the
-  // smallest shifted row sum trusted against underflow.  Sum and grad_x: a row
-  // whose shifted accumulator falls below N max|b| 2^-109 (grad_x: times
-  // 32 sum_e |g_e|) may have lost terms to the floor of exp2.  Such rows are
-  // written as NaN and recomputed by the fix-up launch.
-  const float *bmax;
-  float log2n;
-  float lse_thr;
-  // Split launches of the sum and grad_x with the guard: the partials are left
-  // unscaled, and split 0 writes each row's factor and threshold (threshold -1:
-  // a direct-form row, whose factor is followed by 2^-64 and which is never
-  // flagged).  Null otherwise.
-  float *row_f;
-  float *row_t;
-  // Fix-up launch: a work-group returns at once unless one of its rows holds
-  // NaN; otherwise it recomputes its rows (direct form for the sum and grad_x,
-  // the running maximum for LogSumExp).
-  int fixup;
 };
 
-// Most work-groups of the max-of-b pre-pass (its scratch holds one float each).
-constexpr int kBmaxParts = 1024;
+// Range checks of one work-group's result, made by the work-group itself once its
+// j range is done (no pre-pass, no second launch):
+//  * underflow: the expanded form shifts each exponent by G, so a term below
+//    2^-126 in the shifted scale is flushed by v_exp_f32.  With nj terms of at
+//    most max|b| each, a shifted row result at or above nj max|b| 2^-109
+//    (grad_x: times 32 sum_e |g_e|; Max: max|b| 2^-109) has lost at most 2^-17 of
+//    itself; a row below it sends the work-group to the direct form.  LogSumExp
+//    with a fixed per-row shift: a row sum below nj 2^-110 goes back to the
+//    running maximum.
+//  * overflow: a non-finite result from finite inputs (the shifts scale the
+//    accumulators by up to 2^64) sends the work-group to the direct form with an
+//    exponent offset small enough for the sums it saw: 2^off nj max|b| (grad_x:
+//    times its coefficient bound) stays below 2^120.
+// Each work-group redoes its own rows at most once.
+constexpr float kGuardLoss = 109.0f;     // underflow threshold per term: 2^-109, 2^17 above the flush level
+constexpr float kOffsetRoom = 120.0f;    // log2 bound of a direct-form accumulator
 
 // Arguments of the few-rows sum kernel (j per lane, rows in LDS).
 struct StreamArgs {
@@ -185,5 +179,14 @@ __device__ __forceinline__ float block_min(float v, float *red) {
 }
 
 __device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
+
+// A value the caller knows to be the same in every lane, moved to scalar registers so
+// that the compiler can keep loop control on it off the VALU.
+__device__ __forceinline__ int64_t uniform_i64(int64_t v) {
+  const uint64_t u = (uint64_t)v;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 
 }  // namespace kmi

@@ -37,6 +37,8 @@
 //            K_ij by (2/sigma^2)|x - y| and can lift them into range).
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace kmi {
@@ -81,11 +83,12 @@ __device__ __forceinline__ float lane4(const float4 &v, int u) {
 // Exponent (log2 units) of the pair map for R rows and one j record, phase by
 // phase over the rows so that the R chains are independent.
 //   EXPANDED: q_r = <x'_r, 2y'> + c_j      (xs = x', record = (2y', c_j))
-//   DIRECT  : q_r = off - s^2 |x_r - y|^2  (xs = raw x, record = raw y); the
+//   DIRECT  : q_r = off_r - s^2 |x_r - y|^2  (xs = raw x, record = raw y); the
 //             differences are kept in d for the grad_x accumulation.
-//   LAPLACE : q_r = off - s2 |x_r - y|      (direct form only; s2 = log2 e / sigma)
+//   LAPLACE : q_r = off_r - s2 |x_r - y|      (direct form only; s2 = log2 e / sigma)
 template <bool FAST, int R, int D, int NV4, bool LAPLACE = false>
-__device__ __forceinline__ void pair_exponent(const float (&xs)[R][D], const float (&yv)[NV4], float s2, float off,
+__device__ __forceinline__ void pair_exponent(const float (&xs)[R][D], const float (&yv)[NV4], float s2,
+                                              const float (&off)[R],
                                               float (&q)[R], float (&d)[FAST ? 1 : R][D]) {
   if (FAST) {
 #pragma unroll
@@ -110,7 +113,7 @@ __device__ __forceinline__ void pair_exponent(const float (&xs)[R][D], const flo
       for (int r = 0; r < R; ++r) q[r] = __builtin_amdgcn_sqrtf(q[r]);   // v_sqrt_f32, about 1 ulp
     }
 #pragma unroll
-    for (int r = 0; r < R; ++r) q[r] = fmaf(-s2, q[r], off);
+    for (int r = 0; r < R; ++r) q[r] = fmaf(-s2, q[r], off[r]);
   }
 }
 
@@ -134,10 +137,11 @@ __device__ __forceinline__ void pipelined_records(const float4 *rec, int j0, int
 #pragma unroll
     for (int k = 0; k < 4 * NV; ++k) asm volatile("" : "+v"(yv[u][k]));
   }
+  const float nooff[R] = {};   // the expanded form reads no offset
   for (int jj = j0; jj < j1; jj += 4) {
     float q[4][R], dd[1][D];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) pair_exponent<true>(xs, yv[u], s2, 0.0f, q[u], dd);
+    for (int u = 0; u < 4; ++u) pair_exponent<true>(xs, yv[u], s2, nooff, q[u], dd);
     const int jn = jj + 4 < j1 ? jj + 4 : jj;
 #pragma unroll
     for (int u = 0; u < 4; ++u) load_rec<NV>(rec, jn + u, yv[u]);
@@ -158,15 +162,19 @@ __device__ __forceinline__ void gauss_jloop(const GaussArgs &a,
                                             float (*sPay)[GaussShape<OP, D, E>::PAY * GaussShape<OP, D, E>::TJ],
                                             int (*sIdx)[GaussShape<OP, D, E>::TJR], int (*sSeg)[4],
                                             const float (&xs)[R][D], const float (&gr)[R][E], const float (&cen)[D],
-                                            float G, float (&acc)[R][GaussShape<OP, D, E>::NACC],
-                                            int (&ix)[R][2 * E], int64_t jb, int64_t je) {
+                                            float G, const float (&off)[R],
+                                            float (&acc)[R][GaussShape<OP, D, E>::NACC], int (&ix)[R][2 * E],
+                                            float &bmx, int64_t jb, int64_t je) {
   using S = GaussShape<OP, D, E>;
   constexpr int NV = S::NV, PAY = S::PAY, TJ = S::TJ, NP = S::NPART;
   constexpr bool SPLIT = S::SPLIT && FAST;
   const int tid = threadIdx.x;
   const float s2 = a.scale * a.scale;
-  // exponent offset of the direct form (see the file comment); LSE tracks its own max
-  const float off = (FAST || OP == OP_LSE) ? 0.0f : kDirectOffset;
+  // off: each row's exponent offset in the direct form (not read by the expanded form;
+  // 0 for LogSumExp, which tracks its own maximum)
+  // the j range is uniform across the work-group: keep the tile loop's control scalar
+  jb = uniform_i64(jb);
+  je = uniform_i64(je);
 
   // raw tile registers (one j per thread for tid < TJ)
   float ry[D], rb[E];
@@ -193,6 +201,12 @@ __device__ __forceinline__ void gauss_jloop(const GaussArgs &a,
   };
   auto stage = [&](int buf, bool ok, int64_t jt_stage) {
     if (tid >= TJ) return;
+    // the largest |b| this work-group sees, for its range checks (once per j; padded
+    // j hold b = 0)
+    if (OP != OP_LSE) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) bmx = fmaxf(bmx, fabsf(rb[e]));
+    }
     if (SPLIT) {
       // record (2y', c_j + log2 |b|) at the j's place in its wave's segment: b > 0
       // first, then the rest (b <= 0, NaN, and padded j), in j order within each class
@@ -545,6 +559,14 @@ __device__ __forceinline__ void gauss_jloop(const GaussArgs &a,
   }
 }
 
+// Forms a work-group's j loop can take (uniform across the work-group).
+enum JMode : int {
+  JM_DIRECT = 0,   // raw differences, exponent offset `off`
+  JM_FAST = 1,     // expanded form, shift G = r2/2
+  JM_FIXED = 2,    // LogSumExp, expanded form, fixed per-row shift G - |x'|^2
+  JM_RUN = 3,      // LogSumExp, expanded form, running maximum (G = 0)
+};
+
 template <int OP, int D, int E, int R>
 __global__ __launch_bounds__(kThreads) void gauss_valu_kernel(GaussArgs a) {
   using S = GaussShape<OP, D, E>;
@@ -557,19 +579,6 @@ __global__ __launch_bounds__(kThreads) void gauss_valu_kernel(GaussArgs a) {
 
   // row blocks already computed by the MFMA kernel (uniform across the work-group)
   if (a.wg_flags && a.wg_flags[blockIdx.x]) return;
-  // fix-up launch: only work-groups with a row the first pass left as NaN
-  if ((OP == OP_LSE || OP == OP_SUM || OP == OP_GRAD || OP == OP_MAX) && a.fixup) {
-    constexpr int WO = OP == OP_GRAD ? D : E;
-    bool bad = false;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int64_t i = (int64_t)blockIdx.x * (kThreads * R) + (int64_t)r * kThreads + threadIdx.x;
-      if (i < a.M)
-#pragma unroll
-        for (int w = 0; w < WO; ++w) bad |= a.out[i * WO + w] != a.out[i * WO + w];
-    }
-    if (!__syncthreads_or(bad)) return;
-  }
 
   const int tid = threadIdx.x;
   const int wid = tid / kWave, lane = tid & (kWave - 1);
@@ -577,17 +586,34 @@ __global__ __launch_bounds__(kThreads) void gauss_valu_kernel(GaussArgs a) {
   const int64_t row0 = item ? item->row_lo : (int64_t)blockIdx.x * (kThreads * R);
   const int64_t row_end = item ? item->row_hi : a.M;
   const int64_t M = a.M;
+  // the j of this work-group: one split of a dense launch, or the item's ranges
+  const int64_t jb0 = (int64_t)blockIdx.y * a.j_per_split;
+  const int64_t je0 = (jb0 + a.j_per_split < a.N) ? jb0 + a.j_per_split : a.N;
+  int64_t nj = 0;
+  if (!item) {
+    nj = je0 - jb0;
+  } else {
+    for (int64_t k = item->k0; k <= item->k1; ++k) {
+      const int64_t jb = k == item->k0 ? item->j0 : a.redr[2 * k];
+      const int64_t je = k == item->k1 ? item->j1 : a.redr[2 * k + 1];
+      nj += je > jb ? je - jb : 0;
+    }
+  }
+  const float log2n = nj > 1 ? ceilf(log2f((float)nj)) : 0.0f;
 
   // ---- rows (raw), bounding-box centre of the work-group
   float xs[R][D];
   bool valid[R];
+  auto load_rows = [&]() {
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int64_t i = row0 + (int64_t)r * kThreads + tid;
-    valid[r] = i < row_end;
+    for (int r = 0; r < R; ++r) {
+      const int64_t i = row0 + (int64_t)r * kThreads + tid;
+      valid[r] = i < row_end;
 #pragma unroll
-    for (int k = 0; k < D; ++k) xs[r][k] = valid[r] ? a.x[i * D + k] : 0.0f;
-  }
+      for (int k = 0; k < D; ++k) xs[r][k] = valid[r] ? a.x[i * D + k] : 0.0f;
+    }
+  };
+  load_rows();
   float cen[D];
   {
     float lo[D], hi[D];
@@ -631,29 +657,11 @@ __global__ __launch_bounds__(kThreads) void gauss_valu_kernel(GaussArgs a) {
     nx[r] = n;
     if (valid[r]) r2 = fmaxf(r2, n);
   }
-  r2 = block_max(r2, sRed + 2 * D * (kThreads / kWave));
+  float *red = sRed + 2 * D * (kThreads / kWave);
+  r2 = block_max(r2, red);
   // the Laplacian kernel needs |x - y| itself, which the expanded form cannot give
   // accurately for close pairs: always the direct form
   const bool fast = OP != OP_LAPLACE && a.form == FORM_AUTO && r2 <= kFastR2;
-  // Offset folded into every j constant so that exp2 stays within range: the
-  // largest exponent is r2 - G and the smallest row factor exponent is -G.
-  // LogSumExp takes the fixed shift G - |x'|^2 + (max b) log2 e per row when the
-  // exponents, at most G + (max b) log2 e, keep the row sum of N terms below
-  // 2^120; else (and on the fix-up launch) it tracks a running maximum
-  bool lse_fixed = false;
-  float bm = 0.0f;   // max b (LogSumExp) or max |b| (sum, grad_x) when the guard is on
-  const bool guard = fast && a.bmax && !item && !a.fixup;
-  if (guard) bm = a.bmax[0];   // uniform load
-  if (OP == OP_LSE && guard) lse_fixed = 0.5f * r2 + bm * kLog2e + a.log2n <= 120.0f;
-  // sum, grad_x: below this a shifted accumulator may have lost terms to the floor
-  // (each flushed term is under 2^-126 max|b|, times |g| |x' - y'| < 32 |g| for grad_x);
-  // Max: a maximum below 2^-109 max|b| may be a flushed term's place
-  // (the sign-split tile folds log2 |b| into the exponent, so there a flushed term is
-  // under 2^-126 itself: max(1, max|b|) covers both forms)
-  const float bmg = (OP == OP_SUM || OP == OP_MAX || (OP == OP_GRAD && E == 1)) ? fmaxf(bm, 1.0f) : bm;
-  const float thr_base = !(guard && (OP == OP_SUM || OP == OP_GRAD || OP == OP_MAX)) ? 0.0f
-                         : (OP == OP_MAX ? exp2f(-109.0f) * bmg : exp2f(a.log2n - 109.0f) * bmg);
-  const float G = ((OP == OP_LSE && !lse_fixed) || !fast) ? 0.0f : 0.5f * r2;
   if (fast) {
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -662,156 +670,226 @@ __global__ __launch_bounds__(kThreads) void gauss_valu_kernel(GaussArgs a) {
   }
 
   float gr[R][E];
+  float gmax = 0.0f;   // grad_x: the largest sum_e |g_e| of the work-group's rows
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int64_t i = row0 + (int64_t)r * kThreads + tid;
-#pragma unroll
-    for (int e = 0; e < E; ++e) gr[r][e] = (OP == OP_GRAD && valid[r]) ? a.g[i * E + e] : 0.0f;
-  }
-
-  // ---- accumulators
-  float acc[R][S::NACC];
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int q = 0; q < S::NACC; ++q) acc[r][q] = 0.0f;
-  if (OP == OP_LSE) {
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int e = 0; e < E; ++e) acc[r][2 * e] = -3.0e38f;   // running max (finite: keeps u - m defined)
-  }
-  int ix[R][2 * E];
-#pragma unroll
-  for (int r = 0; r < R; ++r)
+    float gs = 0.0f;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      ix[r][e] = -1;
-      ix[r][E + e] = -1;
-      if (OP == OP_MAX) {
-        acc[r][e] = -INFINITY;      // best value (sign-split tile: best exponent of a positive product)
-        acc[r][E + e] = INFINITY;   // sign-split tile: least exponent of a non-positive product
-      }
+      gr[r][e] = (OP == OP_GRAD && valid[r]) ? a.g[i * E + e] : 0.0f;
+      gs += fabsf(gr[r][e]);
     }
+    gmax = fmaxf(gmax, gs);
+  }
+  if (OP == OP_GRAD) gmax = block_max(gmax, red);
+
   // the sign-split tile's index array only exists for Max (a 1 x 1 stand-in otherwise)
   int (*sIdxP)[S::TJR] = reinterpret_cast<int (*)[S::TJR]>(&sIdx[0][0]);
-
-  // ---- the j loop, specialised on the form (uniform across the work-group):
-  // one j split of a dense launch, or the item's j ranges in order
-  if (!item) {
-    const int64_t jb = (int64_t)blockIdx.y * a.j_per_split;
-    const int64_t je = (jb + a.j_per_split < a.N) ? jb + a.j_per_split : a.N;
-    if (OP == OP_LSE && lse_fixed) gauss_jloop<OP, D, E, R, true, true>(a, sRec, sPay, sIdxP, sSeg, xs, gr, cen, G, acc, ix, jb, je);
-    else if (fast) gauss_jloop<OP, D, E, R, true>(a, sRec, sPay, sIdxP, sSeg, xs, gr, cen, G, acc, ix, jb, je);
-    else gauss_jloop<OP, D, E, R, false>(a, sRec, sPay, sIdxP, sSeg, xs, gr, cen, G, acc, ix, jb, je);
-  } else {
-    for (int64_t k = item->k0; k <= item->k1; ++k) {
-      const int64_t jb = k == item->k0 ? item->j0 : a.redr[2 * k];
-      const int64_t je = k == item->k1 ? item->j1 : a.redr[2 * k + 1];
-      if (jb >= je) continue;
-      if (fast) gauss_jloop<OP, D, E, R, true>(a, sRec, sPay, sIdxP, sSeg, xs, gr, cen, G, acc, ix, jb, je);
-      else gauss_jloop<OP, D, E, R, false>(a, sRec, sPay, sIdxP, sSeg, xs, gr, cen, G, acc, ix, jb, je);
-    }
-  }
-
-  // sign-split Max: back from exponents to the value in the shifted scale -- the best
-  // positive product if there is one, else the least negative (or zero) one
-  if (OP == OP_MAX && S::SPLIT && fast) {
+  constexpr int W = (OP == OP_SUM || OP == OP_LAPLACE) ? E : ((OP == OP_LSE || OP == OP_MAX) ? (2 * E) : D);
+  float acc[R][S::NACC];
+  int ix[R][2 * E];
+  auto reset = [&]() {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const bool haspos = acc[r][0] > -INFINITY;
-      const bool hasneg = acc[r][1] < INFINITY;
-      acc[r][0] = haspos ? fast_exp2(acc[r][0]) : (hasneg ? -fast_exp2(acc[r][1]) : -INFINITY);
-      ix[r][0] = haspos ? ix[r][0] : (hasneg ? ix[r][1] : -1);
-    }
-  }
-
-  // ---- finalise and store
-  const bool partial = a.nsplit > 1;
-  constexpr int W = (OP == OP_SUM || OP == OP_LAPLACE) ? E : ((OP == OP_LSE || OP == OP_MAX) ? (2 * E) : D);
-  // Guarded sum / grad_x / Max: split launches leave their partials unscaled, and split
-  // 0 writes each row's factor and threshold (pass 2 applies both to the whole row);
-  // one split tests here.  Threshold -1 marks a direct-form row (never flagged).
-  const bool rowwise = (OP == OP_SUM || OP == OP_GRAD || OP == OP_MAX) && a.bmax && !item && !a.fixup;
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    if (!valid[r]) continue;
-    const int64_t i = row0 + (int64_t)r * kThreads + tid;
-    // row factor f1, then f2 = 2^-64 for the direct form's offset
+      for (int q = 0; q < S::NACC; ++q) acc[r][q] = 0.0f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        ix[r][e] = -1;
+        ix[r][E + e] = -1;
+        if (OP == OP_LSE) acc[r][2 * e] = -3.0e38f;   // running max (finite: keeps u - m defined)
+        if (OP == OP_MAX) {
+          acc[r][e] = -INFINITY;      // best value (sign-split tile: best exponent of a positive product)
+          acc[r][E + e] = INFINITY;   // sign-split tile: least exponent of a non-positive product
+        }
+      }
+    }
+  };
+  // The work-group's j loop in one form (FAST: expanded distance; FIXED: LogSumExp
+  // with a fixed per-row shift): one split of a dense launch, or the item's ranges.
+  auto jloop = [&](auto fast_c, auto fixed_c, float G, const float (&offv)[R], float &bmx) {
+    constexpr bool F = decltype(fast_c)::value, X = decltype(fixed_c)::value;
+    if (!item) {
+      gauss_jloop<OP, D, E, R, F, X>(a, sRec, sPay, sIdxP, sSeg, xs, gr, cen, G, offv, acc, ix, bmx, jb0, je0);
+    } else {
+      for (int64_t k = item->k0; k <= item->k1; ++k) {
+        const int64_t jb = k == item->k0 ? item->j0 : a.redr[2 * k];
+        const int64_t je = k == item->k1 ? item->j1 : a.redr[2 * k + 1];
+        if (jb < je) gauss_jloop<OP, D, E, R, F, X>(a, sRec, sPay, sIdxP, sSeg, xs, gr, cen, G, offv, acc, ix, bmx, jb, je);
+      }
+    }
+    // sign-split Max: back from exponents to the value in the shifted scale -- the best
+    // positive product if there is one, else the least negative (or zero) one
+    if constexpr (OP == OP_MAX && S::SPLIT && F) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const bool haspos = acc[r][0] > -INFINITY;
+        const bool hasneg = acc[r][1] < INFINITY;
+        acc[r][0] = haspos ? fast_exp2(acc[r][0]) : (hasneg ? -fast_exp2(acc[r][1]) : -INFINITY);
+        ix[r][0] = haspos ? ix[r][0] : (hasneg ? ix[r][1] : -1);
+      }
+    }
+  };
+  using T = std::integral_constant<bool, true>;
+  using Fa = std::integral_constant<bool, false>;
+
+  // The values row r stores after a pass in `mode` (G the shift of the expanded form,
+  // off the row's direct-form offset): sums and gradients scaled back, LogSumExp's
+  // (max, sum) pairs in log2 units, Max's (signed value, index bits) pairs.
+  auto finals = [&](int r, int md, float G, float off, float (&res)[W]) {
+    const bool fx = md != JM_DIRECT;
+    // row factor f1, then f2 = 2^-off for the direct form's offset
     float f1 = 1.0f;
-    const float f2 = fast ? 1.0f : exp2f(-kDirectOffset);
+    const float f2 = fx ? 1.0f : exp2f(-off);
     if (OP == OP_SUM || OP == OP_LAPLACE || OP == OP_MAX) {
-      f1 = fast ? exp2f(G - nx[r]) : 1.0f;
+      f1 = fx ? exp2f(G - nx[r]) : 1.0f;
     } else if (OP == OP_GRAD) {
       // expanded: G_k = -(2/sigma^2) (1/s) exp2(G - |x'|^2) sum_j K' <g, b> (x'_k - y'_k)
       // direct:   G_k = -(2/sigma^2) sum_j K <g, b> (x_k - y_k)
-      f1 = (fast ? exp2f(G - nx[r]) * a.grad_coef : a.grad_coef_direct) * (E == 1 ? gr[r][0] : 1.0f);
+      f1 = (fx ? exp2f(G - nx[r]) * a.grad_coef : a.grad_coef_direct) * (E == 1 ? gr[r][0] : 1.0f);
     }
-    // (LogSumExp and Max pairs are built here; the sum and grad_x scale each value
-    // as it is stored, so only the accumulators stay live)
-    float res[(OP == OP_LSE || OP == OP_MAX) ? W : 1];
     if (OP == OP_MAX) {
-      // (signed value, index) pairs; the row factor is positive, so the argmax is that of acc
+      // the row factor is positive, so the argmax is that of acc
 #pragma unroll
       for (int e = 0; e < E; ++e) { res[2 * e] = (acc[r][e] * f1) * f2; res[2 * e + 1] = __int_as_float(ix[r][e]); }
     } else if (OP == OP_LSE) {
-      // (max, sum) in log2 units; the fixed form's shift is G - |x'|^2 (the
-      // (max b) log2 e of the bound never enters the exponents)
-      const float off = fast ? nx[r] : 0.0f;
+      // the fixed form's shift is G - |x'|^2; the running maximum is relative to |x'|^2
+      const float offl = fx ? nx[r] : 0.0f;
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        res[2 * e] = lse_fixed ? G - nx[r] : acc[r][2 * e] - off;
+        res[2 * e] = md == JM_FIXED ? G - nx[r] : acc[r][2 * e] - offl;
         res[2 * e + 1] = acc[r][2 * e + 1];
-      }
-    }
-    // the guard's threshold for this row, and (one split) its verdict
-    float t = -1.0f;
-    if ((OP == OP_SUM || OP == OP_GRAD || OP == OP_MAX) && rowwise && fast) {
-      float gs = 32.0f;
-      if (OP == OP_GRAD && E > 1) {
-        gs = 0.0f;
-#pragma unroll
-        for (int e = 0; e < E; ++e) gs += fabsf(gr[r][e]);
-        gs *= 32.0f;
-      }
-      t = OP == OP_GRAD ? thr_base * gs : thr_base;
-    }
-    // one split: each value below the threshold (or NaN) is stored as NaN; the fix-up
-    // launch recomputes every row of a block that holds one
-    const bool test = (OP == OP_SUM || OP == OP_GRAD || OP == OP_MAX) && rowwise && !partial && t >= 0.0f;
-    if (partial) {
-      const int64_t slot = item ? item->slot : blockIdx.y;
-      float *dst = a.out + (slot * M + i) * W;
-      if ((OP == OP_SUM || OP == OP_GRAD || OP == OP_MAX) && rowwise) {
-#pragma unroll
-        for (int w = 0; w < W; ++w)
-          dst[w] = OP == OP_MAX ? ((w & 1) ? res[OP == OP_MAX ? w : 0] : acc[r][w / 2]) : acc[r][w];   // unscaled
-        if (blockIdx.y == 0) { a.row_f[i] = f1; a.row_t[i] = t; }
-      } else if (OP == OP_LSE || OP == OP_MAX) {
-#pragma unroll
-        for (int w = 0; w < W; ++w) dst[w] = res[(OP == OP_LSE || OP == OP_MAX) ? w : 0];
-      } else {
-#pragma unroll
-        for (int w = 0; w < W; ++w) dst[w] = (acc[r][w] * f1) * f2;
-      }
-    } else if (OP == OP_LSE) {
-      // a fixed-shift sum below the underflow threshold (or NaN) is left as NaN
-#pragma unroll
-      for (int e = 0; e < E; ++e)
-        a.out[i * E + e] = (lse_fixed && !(res[2 * e + 1] >= a.lse_thr)) ? __int_as_float(0x7fc00000)
-                                                                        : kLn2 * (res[2 * e] + log2f(res[2 * e + 1]));
-    } else if (OP == OP_MAX) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const bool low = test && !(fabsf(acc[r][e]) >= t);
-        a.out[i * E + e] = low ? __int_as_float(0x7fc00000) : a.max_sign * res[2 * e];
-        a.out_idx[i * E + e] = low ? -1 : (int64_t)__float_as_int(res[2 * e + 1]);
       }
     } else {
 #pragma unroll
-      for (int w = 0; w < W; ++w)
-        a.out[i * W + w] = (test && !(fabsf(acc[r][w]) >= t)) ? __int_as_float(0x7fc00000) : (acc[r][w] * f1) * f2;
+      for (int w = 0; w < W; ++w) res[w] = (acc[r][w] * f1) * f2;
     }
+  };
+  const bool partial = a.nsplit > 1;
+  auto put = [&](int r, const float (&res)[W]) {
+    const int64_t i = row0 + (int64_t)r * kThreads + tid;
+    if (partial) {
+      const int64_t slot = item ? item->slot : blockIdx.y;
+      float *dst = a.out + (slot * M + i) * W;
+#pragma unroll
+      for (int w = 0; w < W; ++w) dst[w] = res[w];
+    } else if (OP == OP_LSE) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) a.out[i * E + e] = kLn2 * (res[2 * e] + log2f(res[2 * e + 1]));
+    } else if (OP == OP_MAX) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        a.out[i * E + e] = a.max_sign * res[2 * e];
+        a.out_idx[i * E + e] = (int64_t)__float_as_int(res[2 * e + 1]);
+      }
+    } else {
+#pragma unroll
+      for (int w = 0; w < W; ++w) a.out[i * W + w] = res[w];
+    }
+  };
+
+  // ---- first pass: the expanded form where its precision condition holds (LogSumExp
+  // with a fixed per-row shift; shift G = r2/2: the largest exponent is r2 - G, the
+  // smallest row factor exponent -G), else the direct form with offset 2^64
+  const int mode = fast ? (OP == OP_LSE ? JM_FIXED : JM_FAST) : JM_DIRECT;
+  const float G = fast ? 0.5f * r2 : 0.0f;
+  float offr[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) offr[r] = OP == OP_LSE ? 0.0f : kDirectOffset;
+  float bmx = 0.0f;   // the largest |b| of the work-group's j (staging tracks it)
+  reset();
+  if (mode == JM_FIXED) jloop(T(), T(), G, offr, bmx);
+  else if (mode == JM_FAST) jloop(T(), Fa(), G, offr, bmx);
+  else jloop(Fa(), Fa(), 0.0f, offr, bmx);
+
+  // ---- range checks (see GaussArgs).  Every row stores its first-pass values now; rows
+  // that fail a check are computed once more (second pass) and overwrite them:
+  //   over[r]: non-finite from finite inputs -> direct form, offset off_safe;
+  //   low[r]:  below the expanded form's floor  -> direct form with the row's own offset:
+  //            its terms are below the threshold in the shifted scale, i.e. below
+  //            thr 2^(G - |x'|^2) in the true one, so 2^off times them stays below
+  //            2^kOffsetRoom for off up to kOffsetRoom - log2(thr) - G + |x'|^2 (at least
+  //            64, at most 127 so that exp2(off - s^2 d^2) itself is finite).  Kept only
+  //            if finite: a row that is low by cancellation of large terms keeps the
+  //            first pass.  LogSumExp: fixed-shift sum low or not finite -> running max.
+  if (OP != OP_LSE) bmx = block_max(bmx, red);
+  bool over[R], low[R];
+  bool any = false;
+  float off_safe = kDirectOffset;
+  {
+    const bool fx = mode != JM_DIRECT;
+    const bool inputs_finite = isfinite(bmx) && isfinite(gmax);
+    // direct-form offset that keeps this work-group's accumulators below 2^kOffsetRoom
+    float lim = log2f(fmaxf(bmx, 1e-30f)) + (OP == OP_MAX ? 0.0f : log2n);
+    if (OP == OP_GRAD) {
+      // |x - y| K <= 0.43 sigma and the factor 2/sigma^2: both ends of sigma bounded
+      const float ls = 0.5f * log2f(2.0f / fabsf(a.grad_coef_direct));   // log2 sigma
+      lim += log2f(fmaxf(gmax, 1.0f)) + fabsf(ls) + 1.0f;
+    }
+    off_safe = fminf(kDirectOffset, floorf(kOffsetRoom - lim));
+    // the underflow threshold of the expanded form (sign-split tile: log2 |b| is in the
+    // exponent, so a flushed term is under 2^-126 itself; max(1, max|b|) covers both)
+    const float bmg = (OP == OP_SUM || OP == OP_MAX || (OP == OP_GRAD && E == 1)) ? fmaxf(bmx, 1.0f) : bmx;
+    float thr = OP == OP_MAX ? exp2f(-kGuardLoss) * bmg : exp2f(log2n - kGuardLoss) * bmg;
+    if (OP == OP_GRAD) thr *= 32.0f * (E == 1 ? 1.0f : gmax);
+    const float lse_thr = exp2f(log2n - kGuardLoss - 1.0f);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      over[r] = false;
+      low[r] = false;
+      if (!valid[r]) continue;
+      float res[W];
+      finals(r, mode, G, offr[r], res);
+      put(r, res);
+      if (!inputs_finite) continue;
+      if (OP == OP_LSE) {
+        if (mode == JM_FIXED) {
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            const float sm = acc[r][2 * e + 1];
+            low[r] |= !(sm >= lse_thr) || !(sm < INFINITY);
+          }
+        }
+      } else {
+        constexpr int WA = OP == OP_MAX ? E : W;
+#pragma unroll
+        for (int w = 0; w < WA; ++w) {
+          const float v = res[OP == OP_MAX ? 2 * w : w];
+          over[r] |= !(fabsf(v) < INFINITY);
+          if (fx) low[r] |= !(fabsf(acc[r][w]) >= thr);
+        }
+        if (!fx) over[r] &= off_safe < kDirectOffset;   // a smaller offset would not help
+        // grad_x: the direct form's differences are raw, x - y = (x' - y') / s
+        const float lg = OP == OP_GRAD ? fmaxf(0.0f, -log2f(a.scale)) : 0.0f;
+        const float off_low = fminf(127.0f, fmaxf(kDirectOffset, floorf(kOffsetRoom - log2f(thr) - G + nx[r] - lg)));
+        offr[r] = over[r] ? off_safe : (low[r] ? off_low : kDirectOffset);
+      }
+      any |= over[r] || low[r];
+    }
+  }
+  if (!__syncthreads_or(any)) return;
+
+  // ---- second pass over the same j
+  reset();
+  if (OP == OP_LSE) {
+    jloop(T(), Fa(), 0.0f, offr, bmx);   // running maximum, expanded form (G = 0)
+  } else {
+    load_rows();                         // raw coordinates for the direct form
+    jloop(Fa(), Fa(), 0.0f, offr, bmx);
+  }
+  const int mode2 = OP == OP_LSE ? JM_RUN : JM_DIRECT;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (!valid[r] || !(over[r] || low[r])) continue;
+    float res[W];
+    finals(r, mode2, 0.0f, offr[r], res);
+    bool fin = true;
+    if (OP != OP_LSE) {
+#pragma unroll
+      for (int w = 0; w < W; ++w) fin &= fabsf(res[w]) < INFINITY || (OP == OP_MAX && (w & 1));
+    }
+    if (over[r] || fin) put(r, res);
   }
 }
 

@@ -31,11 +31,12 @@ int gauss_dispatch_sum_stream(int D, int E, int mr, VariantInfo *info, dim3 grid
 // out[r] = sum over the nparts partials part[p][r], in order of p, in double:
 // one work-group per output, each thread a strided share, then a fixed-shape
 // tree over the work-group (deterministic for a given nparts).
-// Underflow guard (g.row_fac set): an expanded-form row whose sum is below
+// Range checks: an expanded-form row (g.row_fac set) whose sum is below
 // N max|b| 2^-109 times its factor may have lost its terms to the floor of exp2
-// (each flushed term is under 2^-126 max|b| before the factor); the work-group
-// then recomputes that output in the direct form, exp2(64 - s^2 |x - y|^2) b with
-// the 2^-64 applied at the end, accumulated in double.
+// (each flushed term is under 2^-126 max|b| before the factor), and a sum that is
+// not finite overflowed in a shifted fp32 accumulator; the work-group then
+// recomputes that output in the direct form, exp2(64 - s^2 |x - y|^2) b with the
+// 2^-64 applied at the end, accumulated in double.
 __device__ double stream_block_sum(double v, double *red) {
   red[threadIdx.x] = v;
   __syncthreads();
@@ -64,32 +65,37 @@ __global__ __launch_bounds__(kThreads) void stream_combine_kernel(const float *p
                                                                   float *out, StreamGuard g) {
   __shared__ double red[kThreads];
   const int64_t r = blockIdx.x;
+  const int64_t i = r / g.E;
+  const int e = (int)(r - i * g.E);
   double v = 0.0;
   for (int p = threadIdx.x; p < nparts; p += kThreads) v += (double)part[(int64_t)p * count + r];
   double total = stream_block_sum(v, red);
-  if (g.row_fac) {
-    const int64_t i = r / g.E;
-    const int e = (int)(r - i * g.E);
+  // uniform: every thread holds the same total
+  bool redo = !isfinite(total);   // a shifted partial overflowed
+  if (!redo && g.row_fac) {
     const float fac = g.row_fac[i];
     if (fac >= 0.0f) {
       float bm = -INFINITY;
       for (int t = threadIdx.x; t < g.nparts; t += kThreads) bm = fmaxf(bm, g.chunk_bmax[t]);
       bm = (float)stream_block_max(bm, red);
-      const double thr = exp2((double)g.log2n - 109.0) * (double)bm * (double)fac;
-      if (!(fabs(total) >= thr)) {   // uniform: every thread holds the same total
-        const float s2 = g.scale * g.scale;
-        double acc = 0.0;
-        for (int64_t j = threadIdx.x; j < g.N; j += kThreads) {
-          float d2 = 0.0f;
-          for (int k = 0; k < g.D; ++k) {
-            const float d = g.x[i * g.D + k] - g.y[j * g.D + k];
-            d2 = fmaf(d, d, d2);
-          }
-          acc += (double)exp2f(fmaf(-s2, d2, kDirectOffset)) * (double)g.b[j * g.E + e];
-        }
-        total = stream_block_sum(acc, red) * exp2(-(double)kDirectOffset);
-      }
+      const double thr = exp2((double)g.log2n - (double)kGuardLoss) * (double)bm * (double)fac;
+      redo = !(fabs(total) >= thr);
     }
+  }
+  if (redo) {
+    // exp2(64 - s^2 |x - y|^2) is at most 2^64 in fp32; the products and the sum are
+    // taken in double, so neither the floor nor the range of fp32 is reached
+    const float s2 = g.scale * g.scale;
+    double acc = 0.0;
+    for (int64_t j = threadIdx.x; j < g.N; j += kThreads) {
+      float d2 = 0.0f;
+      for (int k = 0; k < g.D; ++k) {
+        const float d = g.x[i * g.D + k] - g.y[j * g.D + k];
+        d2 = fmaf(d, d, d2);
+      }
+      acc += (double)exp2f(fmaf(-s2, d2, kDirectOffset)) * (double)g.b[j * g.E + e];
+    }
+    total = stream_block_sum(acc, red) * exp2(-(double)kDirectOffset);
   }
   if (threadIdx.x == 0) out[r] = (float)total;
 }

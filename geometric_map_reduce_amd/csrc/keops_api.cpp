@@ -225,17 +225,19 @@ int gauss_stream_entry(const float *x, const float *y, const float *b, int64_t M
   a.j_per_wg = jpw;
   a.part = ws;
   a.form = form == 1 ? FORM_DIRECT : FORM_AUTO;
+  // pass 2 recomputes an output directly when the guard flags it, or when the sum of
+  // its partials is not finite (the shifted accumulators can overflow)
   StreamGuard g{};
+  g.x = x; g.y = y; g.b = b;
+  g.N = N; g.D = D; g.E = E;
+  g.scale = a.scale;
+  g.nparts = (int)wgs;
+  g.log2n = (float)std::ceil(std::log2((double)N));
   if (guard) {
     a.row_fac = (float *)((char *)ws + part_bytes);
     a.chunk_bmax = (float *)((char *)ws + part_bytes + fac_bytes);
     g.row_fac = a.row_fac;
     g.chunk_bmax = a.chunk_bmax;
-    g.nparts = (int)wgs;
-    g.log2n = (float)std::ceil(std::log2((double)N));
-    g.x = x; g.y = y; g.b = b;
-    g.N = N; g.D = D; g.E = E;
-    g.scale = a.scale;
   }
   const int prof = prof_begin(st);
   gauss_dispatch_sum_stream(D, E, info.rows_per_wg, nullptr, dim3((unsigned)wgs, (unsigned)groups), &a, st);
@@ -324,23 +326,14 @@ int gauss_entry(int op, const float *x, const float *y, const float *b, const fl
   a.out_idx = out_idx;
   a.max_sign = max_sign;
 
-  // Underflow guard of the expanded form (VALU kernels): LogSumExp, sum and grad_x
-  // take a pre-pass over b, and rows the guard flags are recomputed by a fix-up
-  // launch.  The form switch KEOPS_OPT_FORM = 1 (direct everywhere) needs none.
-  const bool guard = !use_mfma && form == 0 && (op == OP_LSE || op == OP_SUM || op == OP_GRAD || op == OP_MAX);
-  const bool rowwise = guard && op != OP_LSE && p.nsplit > 1;
-
-  // workspace: split-j partials, then (MFMA path) one form flag per row block,
-  // then (guard) the partial maxima of b, then (guarded split sum / grad_x) the
-  // row factors and thresholds
+  // workspace: split-j partials, then (MFMA path) one form flag per row block.  The
+  // range checks of the expanded and direct forms happen inside each work-group.
   float *ws = nullptr;
   const int PW = (op == OP_SUM || op == OP_LAPLACE) ? E : ((op == OP_LSE || op == OP_MAX) ? 2 * E : D);
   auto al = [](size_t v) { return (v + 255) / 256 * 256; };
   const size_t part_bytes = p.nsplit > 1 ? al((size_t)p.nsplit * M * PW * sizeof(float)) : 0;
   const size_t flag_bytes = use_mfma ? al((size_t)p.nblk * sizeof(int)) : 0;
-  const size_t bmax_bytes = guard ? al((kBmaxParts + 1) * sizeof(float)) : 0;   // scratch, then the maximum
-  const size_t row_bytes = rowwise ? al((size_t)M * sizeof(float)) : 0;
-  const size_t ws_bytes = part_bytes + flag_bytes + bmax_bytes + 2 * row_bytes;
+  const size_t ws_bytes = part_bytes + flag_bytes;
   if (ws_bytes > 0) {
     if (hipMallocAsync((void **)&ws, ws_bytes, st) != hipSuccess || !ws) {
       (void)hipGetLastError();
@@ -349,22 +342,6 @@ int gauss_entry(int op, const float *x, const float *y, const float *b, const fl
   }
   a.out = p.nsplit > 1 ? ws : out;
   const dim3 grid((unsigned)p.nblk, (unsigned)p.nsplit);
-  // LogSumExp: fixed per-row shift where the range allows (bound from max b); rows
-  // whose shifted sum falls below lse_thr are recomputed.  Each lost term is below
-  // 2^-126, so what the threshold trusts is within N 2^-126 / thr = 2^-16 of the sum.
-  // Sum / grad_x: the kernel derives its thresholds from max |b| the same way.
-  const int log2n = (int)std::ceil(std::log2((double)N));
-  if (guard) {
-    float *bm = (float *)((char *)ws + part_bytes + flag_bytes);
-    launch_bmax(b, N * E, op != OP_LSE, bm, bm + kBmaxParts, st);
-    a.bmax = bm + kBmaxParts;
-    a.log2n = (float)log2n;
-    a.lse_thr = std::ldexp(1.0f, log2n + 16 - 126);
-    if (rowwise) {
-      a.row_f = (float *)((char *)ws + part_bytes + flag_bytes + bmax_bytes);
-      a.row_t = (float *)((char *)ws + part_bytes + flag_bytes + bmax_bytes + row_bytes);
-    }
-  }
   const int prof = prof_begin(st);
   if (use_mfma) {
     a.wg_flags = (int *)((char *)ws + part_bytes);
@@ -378,25 +355,9 @@ int gauss_entry(int op, const float *x, const float *y, const float *b, const fl
     prof_end(prof, st);
   }
   if (p.nsplit > 1) {
-    if (op == OP_LSE) launch_lse_combine(ws, p.nsplit, M, E, a.lse_thr, out, st);
-    else if (op == OP_MAX) launch_max_combine(ws, p.nsplit, M, E, max_sign, a.row_f, a.row_t, out, out_idx, st);
-    else if (rowwise) launch_rows_combine(ws, p.nsplit, M, PW, a.row_f, a.row_t, out, st);
+    if (op == OP_LSE) launch_lse_combine(ws, p.nsplit, M, E, out, st);
+    else if (op == OP_MAX) launch_max_combine(ws, p.nsplit, M, E, max_sign, out, out_idx, st);
     else launch_sum_combine(ws, p.nsplit, M * PW, out, st);
-  }
-  if (guard) {
-    // rows left as NaN: their 256-row blocks again, one row per lane, whole j range
-    // (LogSumExp with the running maximum, sum and grad_x in the direct form); every
-    // other work-group returns at once
-    GaussArgs f = a;
-    f.out = out;
-    f.nsplit = 1;
-    f.j_per_split = N;
-    f.bmax = nullptr;
-    f.row_f = nullptr;
-    f.row_t = nullptr;
-    f.fixup = 1;
-    if (op != OP_LSE) f.form = FORM_DIRECT;
-    fn(D, E, 0, nullptr, dim3((unsigned)((M + narrow_info.rows_per_wg - 1) / narrow_info.rows_per_wg), 1), &f, st);
   }
   if (ws) (void)hipFreeAsync(ws, st);
   return check_launch();
@@ -562,7 +523,7 @@ int gauss_ranges_entry(int op, const float *x, const float *y, const float *b, c
   fn(D, E, wide ? 1 : 0, nullptr, dim3((unsigned)items.size(), 1), &a, st);
   prof_end(prof, st);
   if (smax > 1) {
-    if (op == OP_LSE) launch_lse_combine(part, (int)smax, M, E, 0.0f, out, st);
+    if (op == OP_LSE) launch_lse_combine(part, (int)smax, M, E, out, st);
     else launch_sum_combine(part, (int)smax, M * PW, out, st);
   }
   (void)hipFreeAsync(ws, st);

@@ -46,13 +46,7 @@ KMI_DECLARE_KMIN(kmin_dispatch_mfma_split)
 #undef KMI_DECLARE_KMIN
 
 void launch_sum_combine(const float *ws, int nsplit, int64_t count, float *out, hipStream_t st);
-// thr: merged sums below it (or NaN) are written as NaN (0 keeps every finite value)
-void launch_lse_combine(const float *ws, int nsplit, int64_t M, int E, float thr, float *out, hipStream_t st);
-// max of b[0..n) (or of |b|) into out[0]; scratch holds kBmaxParts floats
-void launch_bmax(const float *b, int64_t n, bool absval, float *scratch, float *out, hipStream_t st);
-// pass 2 of guarded sum / grad_x split launches (row factors f, thresholds t)
-void launch_rows_combine(const float *ws, int nsplit, int64_t M, int W, const float *f, const float *t, float *out,
-                         hipStream_t st);
+void launch_lse_combine(const float *ws, int nsplit, int64_t M, int E, float *out, hipStream_t st);
 int launch_kmin_combine(const float *pd, const int32_t *pi, int nsplit, int64_t M, int K, float *out_d,
                         int64_t *out_i, hipStream_t st);
 void launch_fill(float *out, int64_t count, float v, hipStream_t st);
@@ -60,11 +54,11 @@ void launch_fill2(float *out, int64_t pairs, float v0, float v1, hipStream_t st)
 void launch_fill_i64(int64_t *out, int64_t count, int64_t v, hipStream_t st);
 // Max/ArgMax pass 2: partials [nsplit][M][E] of (signed value, index bits); the
 // largest value wins, the smaller index on ties; out = sign * value.
-void launch_max_combine(const float *ws, int nsplit, int64_t M, int E, float sign, const float *rf, const float *rt,
-                        float *out, int64_t *out_idx, hipStream_t st);
-// Underflow guard of the few-rows sum's pass 2 (row_fac null: off): the rows' factors
-// from pass 1, the partial maxima of |b|, ceil(log2 N), and what a direct recompute
-// of a flagged output needs.
+void launch_max_combine(const float *ws, int nsplit, int64_t M, int E, float sign, float *out, int64_t *out_idx,
+                        hipStream_t st);
+// Range checks of the few-rows sum's pass 2: the rows' factors from pass 1 and the
+// partial maxima of |b| (row_fac null: no underflow check, the direct form throughout),
+// ceil(log2 N), and what a direct recompute of a flagged output needs.
 struct StreamGuard {
   const float *row_fac;
   const float *chunk_bmax;   // [nparts] maxima of |b| per j chunk
