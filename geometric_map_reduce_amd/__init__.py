@@ -6,6 +6,8 @@ never stored, run as hand-written gfx950 HIP kernels behind the C ABI of
 ``geometric_map_reduce_amd.build``):
 
 * ``keops_gauss_sum``    -- a_i = sum_j K_ij b_j
+* ``keops_gauss_sum_noalloc`` -- the same with its workspace in a fixed device
+  scratch of the library (no allocation during the call)
 * ``keops_gauss_lse``    -- log sum_j exp(-|x_i - y_j|^2/sigma^2 + b_j)
 * ``keops_gauss_grad_x`` -- gradient of the sum with respect to x
 * ``keops_gauss_grad_y``, ``keops_gauss_grad_b`` -- gradients with respect to y
@@ -23,5 +25,5 @@ from .binding import (KEOPS_OPT_FORM, KEOPS_OPT_MFMA, KEOPS_OPT_PROFILE, KEOPS_O
                       KEOPS_OPT_WG_TARGET, KeopsError, keops_gauss_cg, keops_gauss_grad_b, keops_gauss_grad_x,
                       keops_gauss_grad_x_ranges, keops_gauss_grad_y, keops_gauss_lse, keops_gauss_lse_ranges,
                       keops_gauss_max, keops_gauss_min, keops_laplace_sum,
-                      keops_gauss_sum, keops_gauss_sum_ranges, keops_kmin, keops_profile_read,
+                      keops_gauss_sum, keops_gauss_sum_noalloc, keops_gauss_sum_ranges, keops_kmin, keops_profile_read,
                       keops_set_option, keops_version, lib, status_string)

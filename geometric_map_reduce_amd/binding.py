@@ -27,6 +27,7 @@ KEOPS_ERR_INVALID_ARG = -1
 KEOPS_ERR_UNSUPPORTED = -2
 KEOPS_ERR_ALLOC = -3
 KEOPS_ERR_HIP = -4
+KEOPS_ERR_SCRATCH = -5
 KEOPS_OPT_SPLIT_J = 1
 KEOPS_OPT_FORM = 2
 KEOPS_OPT_ROWS = 3
@@ -56,6 +57,7 @@ def lib() -> ctypes.CDLL:
             L = ctypes.CDLL(LIB_PATH)
             P, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
             L.keops_gauss_sum.argtypes = [P, P, P, i64, i64, i32, i32, f32, P, P]
+            L.keops_gauss_sum_noalloc.argtypes = [P, P, P, i64, i64, i32, i32, f32, P, P]
             L.keops_gauss_lse.argtypes = [P, P, P, i64, i64, i32, i32, f32, P, P]
             L.keops_gauss_grad_x.argtypes = [P, P, P, P, i64, i64, i32, i32, f32, P, P]
             L.keops_gauss_grad_y.argtypes = [P, P, P, P, i64, i64, i32, i32, f32, P, P]
@@ -73,8 +75,8 @@ def lib() -> ctypes.CDLL:
             L.keops_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
             L.keops_status_string.argtypes = [ctypes.c_int]
             L.keops_status_string.restype = ctypes.c_char_p
-            for f in ("keops_gauss_sum", "keops_gauss_lse", "keops_gauss_grad_x", "keops_gauss_grad_y",
-                      "keops_gauss_grad_b", "keops_gauss_cg", "keops_gauss_sum_ranges", "keops_gauss_lse_ranges",
+            for f in ("keops_gauss_sum", "keops_gauss_sum_noalloc", "keops_gauss_lse", "keops_gauss_grad_x",
+                      "keops_gauss_grad_y", "keops_gauss_grad_b", "keops_gauss_cg", "keops_gauss_sum_ranges", "keops_gauss_lse_ranges",
                       "keops_gauss_grad_x_ranges", "keops_gauss_max", "keops_gauss_min", "keops_laplace_sum",
                       "keops_kmin",
                       "keops_set_option", "keops_version", "keops_profile_read"):
@@ -148,6 +150,12 @@ def _gauss(fn_name, x, y, b, sigma, out, stream, g=None):
 def keops_gauss_sum(x, y, b, sigma, out=None, stream=None):
     """out[i, e] = sum_j exp(-|x_i - y_j|^2 / sigma^2) b[j, e]   (x [M,D], y [N,D], b [N,E])."""
     return _gauss("keops_gauss_sum", x, y, b, sigma, out, stream)
+
+
+def keops_gauss_sum_noalloc(x, y, b, sigma, out=None, stream=None):
+    """keops_gauss_sum with its workspace in the library's fixed device scratch (no device
+    allocation inside the call; pass ``out`` to allocate nothing at all here either)."""
+    return _gauss("keops_gauss_sum_noalloc", x, y, b, sigma, out, stream)
 
 
 def keops_gauss_lse(x, y, b, sigma, out=None, stream=None):

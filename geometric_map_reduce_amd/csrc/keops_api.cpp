@@ -15,6 +15,14 @@
 #include "keops_mi355x.h"
 #include "launch.h"
 
+// Device scratch of keops_gauss_sum_noalloc (split-j partials and form flags): a
+// fixed array in the library's code object, one copy per GPU, held until the process
+// ends.  Host code never passes `scratch` itself to a kernel or a copy: on the host
+// the name stands for a shadow, not a device address; the address of each GPU's copy
+// comes from hipGetSymbolAddress (scratch_of_device below).
+static constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
 namespace kmi {
 namespace {
 
@@ -76,6 +84,39 @@ int device_setup(int *cus) {
   *cus = c;
   return KEOPS_OK;
 }
+
+// Address of this device's copy of `scratch`, looked up once per device with that
+// device current (each GPU holds its own copy at its own address).
+std::mutex g_scratch_mu;
+std::atomic<char *> g_scratch_ptr[kMaxDevices];
+
+int scratch_of_device(char **ptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KEOPS_ERR_HIP;
+  char *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      void *q = nullptr;
+      if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) {
+        (void)hipGetLastError();
+        return KEOPS_ERR_HIP;
+      }
+      p = (char *)q;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return KEOPS_OK;
+}
+
+// Workspace of one call: allocated stream-ordered (arena null), or carved from a
+// fixed device buffer of `cap` bytes (the no-allocation entry point).
+struct Arena {
+  char *base;
+  size_t cap;
+};
 
 bool overlaps(const void *a, int64_t abytes, const void *b, int64_t bbytes) {
   if (!a || !b || abytes <= 0 || bbytes <= 0) return false;
@@ -149,7 +190,7 @@ struct Plan {
 // size is not a multiple of the resident capacity leaves CUs idle, and at a
 // handful of work-groups per CU that tail costs several per cent.
 Plan make_plan(int64_t M, int64_t N, int cus, int64_t rows_wide, int64_t rows_narrow, int tile_j,
-               int64_t wgs_per_cu, int64_t wide_min_rows) {
+               int64_t wgs_per_cu, int64_t wide_min_rows, int64_t max_split = 65535) {
   const int64_t target = g_opt_wg_target.load();
   if (target > 0) wgs_per_cu = target;
   if (rows_wide < 1) rows_wide = 1;
@@ -174,6 +215,7 @@ Plan make_plan(int64_t M, int64_t N, int cus, int64_t rows_wide, int64_t rows_na
     if (s > max_s) s = max_s;
   }
   if (s > ntiles) s = ntiles;
+  if (s > max_split) s = max_split;
   if (s < 1) s = 1;
   if (s > 65535) s = 65535;
   const int64_t tiles_per = (ntiles + s - 1) / s;
@@ -191,8 +233,12 @@ constexpr int64_t kStreamMaxRows = 64;
 constexpr int64_t kStreamWgsPerCu = 8;
 constexpr int64_t kStreamMaxSteps = 128;
 
+// Returns kStreamNoFit (nothing enqueued) when `arena` cannot hold its workspace.
+constexpr int kStreamNoFit = 1;
+
 int gauss_stream_entry(const float *x, const float *y, const float *b, int64_t M, int64_t N, int D, int E,
-                       float sigma, float *out, hipStream_t st, int cus, const VariantInfo &info, int form) {
+                       float sigma, float *out, hipStream_t st, int cus, const VariantInfo &info, int form,
+                       const Arena *arena) {
   const int64_t step = info.tile_j;
   const int64_t groups = (M + info.rows_per_wg - 1) / info.rows_per_wg;
   const int64_t nsteps = (N + step - 1) / step;
@@ -214,7 +260,10 @@ int gauss_stream_entry(const float *x, const float *y, const float *b, int64_t M
   const size_t part_bytes = ((size_t)wgs * M * E * sizeof(float) + 255) / 256 * 256;
   const size_t fac_bytes = guard ? ((size_t)M * sizeof(float) + 255) / 256 * 256 : 0;
   const size_t bmax_bytes = guard ? (size_t)wgs * sizeof(float) : 0;
-  if (hipMallocAsync((void **)&ws, part_bytes + fac_bytes + bmax_bytes, st) != hipSuccess || !ws) {
+  if (arena) {
+    if (part_bytes + fac_bytes + bmax_bytes > arena->cap) return kStreamNoFit;
+    ws = (float *)arena->base;
+  } else if (hipMallocAsync((void **)&ws, part_bytes + fac_bytes + bmax_bytes, st) != hipSuccess || !ws) {
     (void)hipGetLastError();
     return KEOPS_ERR_ALLOC;
   }
@@ -243,13 +292,13 @@ int gauss_stream_entry(const float *x, const float *y, const float *b, int64_t M
   gauss_dispatch_sum_stream(D, E, info.rows_per_wg, nullptr, dim3((unsigned)wgs, (unsigned)groups), &a, st);
   prof_end(prof, st);
   launch_stream_combine(ws, (int)wgs, M * E, out, g, st);
-  (void)hipFreeAsync(ws, st);
+  if (!arena) (void)hipFreeAsync(ws, st);
   return check_launch();
 }
 
 int gauss_entry(int op, const float *x, const float *y, const float *b, const float *g, int64_t M, int64_t N,
                 int32_t D, int32_t E, float sigma, float *out, void *stream, int64_t *out_idx = nullptr,
-                float max_sign = 1.0f) {
+                float max_sign = 1.0f, bool no_alloc = false) {
   // ---- validation (host only)
   if (M < 0 || N < 0 || D < 1 || E < 1) return KEOPS_ERR_INVALID_ARG;
   if (!std::isfinite(sigma) || !(sigma > 0.0f)) return KEOPS_ERR_INVALID_ARG;
@@ -281,11 +330,21 @@ int gauss_entry(int op, const float *x, const float *y, const float *b, const fl
   const int64_t form = g_opt_form.load();
   const bool use_mfma = op == OP_SUM && D >= 32 && form == 0 && g_opt_mfma.load() == 0 &&
                         gauss_dispatch_sum_mfma(D, E, 0, &mfma_info, dim3(), nullptr, nullptr) == 0;
+  // no-allocation calls: the MFMA path's one form flag per 256-row block must fit the
+  // scratch (split-j partials are then sized to what is left)
+  if (no_alloc && use_mfma &&
+      (size_t)((M + mfma_info.rows_per_wg - 1) / mfma_info.rows_per_wg) * sizeof(int) + 1024 > kNoAllocScratchBytes)
+    return KEOPS_ERR_SCRATCH;
   if (M == 0) return KEOPS_OK;
 
   // ---- device work
   hipStream_t st = (hipStream_t)stream;
   (void)hipGetLastError();
+  Arena arena{nullptr, 0};
+  if (no_alloc) {
+    if (int rc = scratch_of_device(&arena.base)) return rc;
+    arena.cap = kNoAllocScratchBytes;
+  }
   if (N == 0) {
     launch_fill(out, M * W, op == OP_LSE ? -INFINITY : (op == OP_MAX ? -max_sign * INFINITY : 0.0f), st);
     if (op == OP_MAX) launch_fill_i64(out_idx, M * E, -1, st);
@@ -299,15 +358,30 @@ int gauss_entry(int op, const float *x, const float *y, const float *b, const fl
     const int mr = M <= 4 ? 4 : stream_rows_large(D, E);
     if ((rows_opt == 3 || (rows_opt == 0 && M <= kStreamMaxRows)) &&
         gauss_dispatch_sum_stream(D, E, mr, &sinfo, dim3(), nullptr, nullptr) == 0 &&
-        (M + sinfo.rows_per_wg - 1) / sinfo.rows_per_wg <= 65535)
-      return gauss_stream_entry(x, y, b, M, N, D, E, sigma, out, st, cus, sinfo, (int)form);
+        (M + sinfo.rows_per_wg - 1) / sinfo.rows_per_wg <= 65535) {
+      const int rc = gauss_stream_entry(x, y, b, M, N, D, E, sigma, out, st, cus, sinfo, (int)form,
+                                        no_alloc ? &arena : nullptr);
+      if (rc != kStreamNoFit) return rc;   // else: the row-per-lane layout below
+    }
   }
   // The MFMA kernel and its direct-form companion both use 256-row work-groups
   // (the narrow VALU variant) and j-splits on the larger of the two tiles.
-  const Plan p = use_mfma ? make_plan(M, N, cus, mfma_info.rows_per_wg, mfma_info.rows_per_wg,
-                                      std::max(mfma_info.tile_j, narrow_info.tile_j), kMfmaSumWgsPerCu, 0)
-                          : make_plan(M, N, cus, wide_info.rows_per_wg, narrow_info.rows_per_wg, wide_info.tile_j,
-                                      kGaussWgsPerCu, op == OP_GRAD ? wide_info.rows_per_wg * cus : kWideMinRows);
+  const int PW = (op == OP_SUM || op == OP_LAPLACE) ? E : ((op == OP_LSE || op == OP_MAX) ? 2 * E : D);
+  auto al = [](size_t v) { return (v + 255) / 256 * 256; };
+  auto plan = [&](int64_t max_split) {
+    return use_mfma ? make_plan(M, N, cus, mfma_info.rows_per_wg, mfma_info.rows_per_wg,
+                                std::max(mfma_info.tile_j, narrow_info.tile_j), kMfmaSumWgsPerCu, 0, max_split)
+                    : make_plan(M, N, cus, wide_info.rows_per_wg, narrow_info.rows_per_wg, wide_info.tile_j,
+                                kGaussWgsPerCu, op == OP_GRAD ? wide_info.rows_per_wg * cus : kWideMinRows, max_split);
+  };
+  Plan p = plan(65535);
+  const size_t flag_bytes = use_mfma ? al((size_t)p.nblk * sizeof(int)) : 0;
+  if (no_alloc && p.nsplit > 1 && al((size_t)p.nsplit * M * PW * sizeof(float)) + flag_bytes > arena.cap) {
+    // as many j-splits as the scratch holds partials for (one: no partials at all)
+    const size_t avail = arena.cap > flag_bytes + 256 ? arena.cap - flag_bytes - 256 : 0;
+    const int64_t fit = (int64_t)(avail / ((size_t)M * PW * sizeof(float)));
+    p = plan(fit >= 2 ? fit : 1);
+  }
 
   const double s2 = (double)sigma * (double)sigma;
   // Laplacian: scale^2 = log2(e) / sigma multiplies |x - y|
@@ -329,13 +403,13 @@ int gauss_entry(int op, const float *x, const float *y, const float *b, const fl
   // workspace: split-j partials, then (MFMA path) one form flag per row block.  The
   // range checks of the expanded and direct forms happen inside each work-group.
   float *ws = nullptr;
-  const int PW = (op == OP_SUM || op == OP_LAPLACE) ? E : ((op == OP_LSE || op == OP_MAX) ? 2 * E : D);
-  auto al = [](size_t v) { return (v + 255) / 256 * 256; };
   const size_t part_bytes = p.nsplit > 1 ? al((size_t)p.nsplit * M * PW * sizeof(float)) : 0;
-  const size_t flag_bytes = use_mfma ? al((size_t)p.nblk * sizeof(int)) : 0;
   const size_t ws_bytes = part_bytes + flag_bytes;
   if (ws_bytes > 0) {
-    if (hipMallocAsync((void **)&ws, ws_bytes, st) != hipSuccess || !ws) {
+    if (no_alloc) {
+      if (ws_bytes > arena.cap) return KEOPS_ERR_SCRATCH;
+      ws = (float *)arena.base;
+    } else if (hipMallocAsync((void **)&ws, ws_bytes, st) != hipSuccess || !ws) {
       (void)hipGetLastError();
       return KEOPS_ERR_ALLOC;
     }
@@ -359,7 +433,7 @@ int gauss_entry(int op, const float *x, const float *y, const float *b, const fl
     else if (op == OP_MAX) launch_max_combine(ws, p.nsplit, M, E, max_sign, out, out_idx, st);
     else launch_sum_combine(ws, p.nsplit, M * PW, out, st);
   }
-  if (ws) (void)hipFreeAsync(ws, st);
+  if (ws && !no_alloc) (void)hipFreeAsync(ws, st);
   return check_launch();
 }
 
@@ -540,6 +614,11 @@ extern "C" {
 int keops_gauss_sum(const float *x, const float *y, const float *b, int64_t M, int64_t N, int32_t D, int32_t E,
                     float sigma, float *out, void *stream) {
   return gauss_entry(OP_SUM, x, y, b, nullptr, M, N, D, E, sigma, out, stream);
+}
+
+int keops_gauss_sum_noalloc(const float *x, const float *y, const float *b, int64_t M, int64_t N, int32_t D,
+                            int32_t E, float sigma, float *out, void *stream) {
+  return gauss_entry(OP_SUM, x, y, b, nullptr, M, N, D, E, sigma, out, stream, nullptr, 1.0f, true);
 }
 
 int keops_gauss_lse(const float *x, const float *y, const float *b, int64_t M, int64_t N, int32_t D, int32_t E,
@@ -764,6 +843,7 @@ const char *keops_status_string(int status) {
     case KEOPS_ERR_UNSUPPORTED: return "unsupported D, E or K";
     case KEOPS_ERR_ALLOC: return "workspace allocation failed";
     case KEOPS_ERR_HIP: return "HIP error";
+    case KEOPS_ERR_SCRATCH: return "the call needs more device scratch than the no-allocation entry point holds";
     default: return "unknown status";
   }
 }

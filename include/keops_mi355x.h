@@ -61,6 +61,8 @@ extern "C" {
 #define KEOPS_ERR_UNSUPPORTED (-2)  /* D, E or K outside the compiled set; N >= 2^31 for K-min */
 #define KEOPS_ERR_ALLOC (-3)        /* workspace allocation failed                 */
 #define KEOPS_ERR_HIP (-4)          /* a HIP call or kernel launch failed          */
+#define KEOPS_ERR_SCRATCH (-5)      /* keops_gauss_sum_noalloc: the call needs more device
+                                       scratch than the library holds                 */
 
 /*
  * Gaussian kernel sum ([KO-GPU] §1 "Target operation"; [README] K_ij.sum(dim=1)):
@@ -70,6 +72,27 @@ extern "C" {
 int keops_gauss_sum(const float *x, const float *y, const float *b,
                     int64_t M, int64_t N, int32_t D, int32_t E, float sigma,
                     float *out, void *stream);
+
+/*
+ * keops_gauss_sum without any allocation, for callers that cannot allocate device
+ * memory during the call: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid hipMalloc.  Arguments, layouts, results and errors are those
+ * of keops_gauss_sum (the same kernels run); the difference is the workspace.  Instead
+ * of stream-ordered allocations, the split-j partial results (and, at D >= 32, one
+ * form flag per 256 rows) go to a fixed 64 MiB device array inside the library, one
+ * copy per GPU, allocated when the library's code is first loaded on that GPU and
+ * held until the process ends.  When the partials of the usual launch plan do not
+ * fit, the call uses fewer j-splits (at the fewest, none: then no scratch is used),
+ * which changes only the fp32 rounding order.  KEOPS_ERR_SCRATCH: the form flags
+ * alone exceed the array (D >= 32 with M above about 4e9 rows); nothing is enqueued.
+ * Every call on one GPU uses that GPU's same array, which keeps the last call's
+ * contents: calls that overlap in time on one GPU (different streams or threads,
+ * not ordered by the caller) race on it and give undefined results.  Nothing in the
+ * array needs to start at zero.
+ */
+int keops_gauss_sum_noalloc(const float *x, const float *y, const float *b,
+                            int64_t M, int64_t N, int32_t D, int32_t E, float sigma,
+                            float *out, void *stream);
 
 /*
  * LogSumExp reduction ([KO-GPU] §2 reductions list; [README] .logsumexp()):

@@ -148,3 +148,17 @@ def test_max_validation(L):
     assert L.keops_gauss_min(FAKE, FAKE2, FAKE2, 5, 7, 99, 1, 1.0, out, idx, None) == -2           # D
     assert L.keops_gauss_max(None, None, None, 0, 0, 3, 1, 1.0, None, None, None) == 0
 
+
+
+def test_noalloc_validation(L):
+    out = ctypes.c_void_p(0x900000)
+    # the same argument rules as keops_gauss_sum
+    assert L.keops_gauss_sum_noalloc(FAKE, FAKE2, FAKE2, 5, 7, 3, 1, 0.0, out, None) == -1
+    assert L.keops_gauss_sum_noalloc(None, None, None, 0, 0, 9, 1, 1.0, None, None) == -2
+    assert L.keops_gauss_sum_noalloc(None, None, None, 0, 0, 3, 1, 1.0, None, None) == 0
+    # D >= 32 with more rows than the scratch has form flags for: rejected before any HIP call
+    M = 1 << 36
+    x, y, o = ctypes.c_void_p(1 << 40), ctypes.c_void_p(1 << 48), ctypes.c_void_p(1 << 52)
+    assert L.keops_gauss_sum_noalloc(x, y, y, M, 10, 50, 1, 1.0, o, None) == -5
+    from geometric_map_reduce_amd import binding
+    assert "scratch" in binding.status_string(-5)
