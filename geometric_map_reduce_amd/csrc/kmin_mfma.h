@@ -222,11 +222,23 @@ __global__ __launch_bounds__(kThreads) void kmin_mfma_kernel(KminArgs a) {
         // threshold bounds its own K-th distance.  A candidate that fails the
         // least of the four trails K candidates of that group, so it cannot
         // be among the row's K smallest: the groups share the least threshold.
+        // Tighter still: every group's Q-th smallest distance (Q = ceil(K/4))
+        // is at most their largest, so the four lists hold 4Q >= K distances no
+        // larger than it, and a candidate beyond it cannot reach the row's final
+        // K smallest (the final merge of the four lists decides the result).
         // (All lanes run this: the branch above is wave-uniform.)
+        constexpr int Q = (K + 3) / 4;
 #pragma unroll
         for (int t = 0; t < TI; ++t) {
           thr[t] = fminf(thr[t], __shfl_xor(thr[t], 16));
           thr[t] = fminf(thr[t], __shfl_xor(thr[t], 32));
+          float q = bd[t][Q - 1];
+          q = fmaxf(q, __shfl_xor(q, 16));
+          q = fmaxf(q, __shfl_xor(q, 32));
+          if (q < INFINITY) {
+            const float sm = 2.0f * ax[t] + sqrtf(q);
+            thr[t] = fminf(thr[t], (q - nx[t]) + mcoef * sm * sm);
+          }
         }
       }
     }

@@ -52,55 +52,65 @@ __device__ __forceinline__ void split_bf16x2(float v0, float v1, unsigned &hi, u
 __device__ __forceinline__ float kmin_split_margin_coef(int DP) { return kmin_margin_coef(3 * DP) + 6.103515625e-5f; }
 
 // Exact direct-form squared distance sum_k (x_k - y_k)^2 in fp32, in coordinate
-// order (the same arithmetic as every other K-min kernel); 16-byte loads when D
-// is a multiple of 4 and both arrays are 16-byte aligned.
+// order (the same arithmetic as every other K-min kernel), from raw rows staged in
+// LDS (16-byte aligned, padded to whole float4).
 template <int D>
-__device__ __forceinline__ float exact_sq_dist(const float *xi, const float *yj, bool v4) {
+__device__ __forceinline__ float exact_sq_dist_lds(const float *xi, const float *yj) {
   float d2 = 0.0f;
-  if constexpr (D % 4 == 0) {
-    if (v4) {
-#pragma unroll 4
-      for (int k = 0; k < D; k += 4) {
-        const float4 p = *reinterpret_cast<const float4 *>(xi + k);
-        const float4 q = *reinterpret_cast<const float4 *>(yj + k);
-        float d = p.x - q.x; d2 = fmaf(d, d, d2);
-        d = p.y - q.y; d2 = fmaf(d, d, d2);
-        d = p.z - q.z; d2 = fmaf(d, d, d2);
-        d = p.w - q.w; d2 = fmaf(d, d, d2);
-      }
-      return d2;
-    }
+#pragma unroll
+  for (int k = 0; k < D / 4 * 4; k += 4) {
+    const float4 p = *reinterpret_cast<const float4 *>(xi + k);
+    const float4 q = *reinterpret_cast<const float4 *>(yj + k);
+    float d = p.x - q.x; d2 = fmaf(d, d, d2);
+    d = p.y - q.y; d2 = fmaf(d, d, d2);
+    d = p.z - q.z; d2 = fmaf(d, d, d2);
+    d = p.w - q.w; d2 = fmaf(d, d, d2);
   }
-  for (int k = 0; k < D; ++k) { const float d = xi[k] - yj[k]; d2 = fmaf(d, d, d2); }
+#pragma unroll
+  for (int k = D / 4 * 4; k < D; ++k) { const float d = xi[k] - yj[k]; d2 = fmaf(d, d, d2); }
   return d2;
 }
 
 // Work-group shape.  Twelve waves (768 threads, three waves per SIMD at <= 168
-// VGPRs) with two 16-row tiles per wave where the K-lists are short enough to fit
-// without spills; else eight waves (two per SIMD, <= 256 VGPRs) with three tiles
-// per wave where that still fits, else two.  Both main forms hold 384 rows
-// (12 x 2 x 16, 8 x 3 x 16).  At D = 64 the twelve-wave form ran K = 1 in 416
-// against 563 ms and K = 4 in 522 against 584 ms; at K = 10 it spilled and ran
-// 840 against 785 ms (all with an earlier, smaller pass margin; with the current
-// one the chosen forms take 418 / 531 / 797 ms at K = 1 / 4 / 10).
-constexpr bool kmin_split_wide(int D, int K) { return D <= 32 ? K <= 6 : (D <= 50 ? K <= 5 : (D <= 64 ? K <= 4 : false)); }
+// VGPRs) with two 16-row tiles per wave up to K = 15 at D = 32 and K = 10 at
+// D <= 64 (beyond, the K-lists spill; at D = 64 the compiler spills 2 to 8
+// registers from K = 8 to 10, and that form still ran faster than eight waves:
+// 558 against 624 ms at K = 10); else eight waves (two per SIMD, <= 256 VGPRs)
+// with three tiles per wave where that still fits, else two.  Both main forms
+// hold 384 rows (12 x 2 x 16, 8 x 3 x 16).
+constexpr bool kmin_split_wide(int D, int K) { return D <= 32 ? K <= 15 : (D <= 64 ? K <= 10 : false); }
 constexpr int kmin_split_threads(int D, int K) { return kmin_split_wide(D, K) ? 768 : 512; }
 constexpr int kmin_split_tiles(int D, int K) {
-  return kmin_split_wide(D, K) ? 2 : (K <= (D <= 32 ? 13 : (D <= 64 ? 12 : 1)) ? 3 : 2);
+  return kmin_split_wide(D, K) ? 2 : (K <= (D <= 32 ? 13 : (D <= 64 ? 12 : 0)) ? 3 : 2);
 }
 
 // One work-group per CU: every y tile staged in LDS serves 16 * TI rows per wave.
+// Besides the split tiles, LDS holds the raw fp32 rows of the work-group's x and of
+// the current y tile, so that the exact distance of a passing candidate is read at
+// LDS latency (from HBM it took four dependent rounds of global loads, and that
+// recheck was over half the kernel's time at K = 10).  The y tile is the largest
+// multiple of 16 j that fits beside them (80 at D = 64, 192 at D = 32), single
+// buffered for the raw rows: a double-buffered raw tile leaves room for 48 j at
+// D = 64 and ran slower.  Measured at 1M x 1M, D = 64, K = 10: 797 ms with
+// rechecks from HBM and 128-j tiles, 624 ms with 64-j LDS tiles in the eight-wave
+// form, 558 ms in the twelve-wave form, 530 ms with 80-j tiles.
 
 template <int D, int K>
 struct KminSplitShape {
   static constexpr int DP = (D + 31) / 32 * 32;    // coordinates padded to whole MFMA steps
   static constexpr int NS = DP / 32;               // MFMA steps per product
   static constexpr int RS = DP + 4;                // u32 per LDS record: DP/2 hi, DP/2 lo, 4 pad
+  static constexpr int DX = (D + 3) / 4 * 4;       // floats per raw row in LDS
   static constexpr int NT = kmin_split_threads(D, K);   // threads per work-group
   static constexpr int NW = NT / kWave;               // waves per work-group
-  static constexpr int TJ = NT / 4;                   // j rows per LDS tile (four staging threads each)
   static constexpr int TI = kmin_split_tiles(D, K);
   static constexpr int ROWS_WG = NW * 16 * TI;        // rows per work-group
+  static constexpr int FIXED_FLOATS = ROWS_WG * DX + D + 64;
+  static constexpr int TJ_FIT = (40960 - FIXED_FLOATS) / (2 * RS + 2 + DX) / 16 * 16;
+  static constexpr int TJ = TJ_FIT < NT / 4 ? TJ_FIT : NT / 4;   // j rows per LDS tile (four staging threads each)
+  static constexpr int LDS_BYTES = 4 * (TJ * (2 * RS + 2 + DX) + FIXED_FLOATS);
+  static_assert(LDS_BYTES <= 160 * 1024, "split K-min work-group exceeds the LDS of a CU");
+  static_assert(4 * TJ <= NT, "four staging threads per j");
 };
 
 template <int D, int K>
@@ -109,10 +119,17 @@ __global__ __launch_bounds__(kmin_split_threads(D, K)) void kmin_mfma_split_kern
   constexpr int kSplitThreads = S::NT, kSplitWaves = S::NW;
   constexpr int DP = S::DP, NS = S::NS, RS = S::RS, TJ = S::TJ, TI = S::TI;
   static_assert(S::ROWS_WG <= kSplitThreads, "one thread per row for the centre");
+  static_assert(TJ % 16 == 0, "whole groups of 16 j per tile");
+  constexpr int DX = S::DX;
   __shared__ __attribute__((aligned(16))) unsigned sRec[2 * TJ * RS];   // double-buffered split y tiles
   __shared__ __attribute__((aligned(16))) float sNy[2 * TJ];            // |y_c|^2 per j (kPadU: padding)
-  __shared__ float sRed[2 * D * kSplitWaves + 8];
+  __shared__ __attribute__((aligned(16))) float sYr[TJ * DX];           // raw y of the current tile
+  __shared__ __attribute__((aligned(16))) float sXr[S::ROWS_WG * DX];   // raw x of the work-group's rows
   __shared__ float sCen[D];
+  // the centre's per-wave extremes go to the raw y buffer, which is free until the
+  // first tile is staged
+  float *sRed = sYr;
+  static_assert(2 * D * kSplitWaves <= TJ * DX, "centre scratch fits the raw y buffer");
 
   const int tid = threadIdx.x;
   const int wid = tid / kWave, lane = tid & (kWave - 1);
@@ -155,14 +172,25 @@ __global__ __launch_bounds__(kmin_split_threads(D, K)) void kmin_mfma_split_kern
     __syncthreads();
   }
 
+  // ---- raw x rows of the work-group in LDS (rows beyond M hold zeros; never read)
+  for (int f = tid; f < S::ROWS_WG * DX; f += kSplitThreads) {
+    const int r = f / DX, k = f - r * DX;
+    const int64_t i = wg_row0 + r;
+    sXr[f] = (i < M && k < D) ? a.x[i * D + k] : 0.0f;
+  }
+  // (the first barrier of the j loop orders these writes before any read)
+
   // ---- B operands: split -2 x_c of row t*16 + l%16, coordinates 32s + 8(l/16) + e
   u32x4s xh[TI][NS], xl[TI][NS];
-  float nx[TI], ax[TI];
-  int64_t row[TI];
+  // local row index of tile t (the loop keeps only 32-bit local rows, and |x_c| is
+  // recomputed where needed, to stay within three waves per SIMD)
+  const int lrows = (int)(M - wg_row0 < S::ROWS_WG ? M - wg_row0 : S::ROWS_WG);   // rows of this work-group
+  auto lrow_of = [&](int t) { return wid * (16 * TI) + t * 16 + lrow; };
+  float nx[TI];
 #pragma unroll
   for (int t = 0; t < TI; ++t) {
-    row[t] = wg_row0 + wid * (16 * TI) + t * 16 + lrow;
-    const bool ok = row[t] < M;
+    const int64_t row = wg_row0 + lrow_of(t);
+    const bool ok = lrow_of(t) < lrows;
     float n = 0.0f;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
@@ -170,7 +198,7 @@ __global__ __launch_bounds__(kmin_split_threads(D, K)) void kmin_mfma_split_kern
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int k = 32 * s + 8 * lgrp + e;
-        const float c = (ok && k < D) ? a.x[row[t] * D + k] - sCen[k < D ? k : 0] : 0.0f;
+        const float c = (ok && k < D) ? a.x[row * D + k] - sCen[k < D ? k : 0] : 0.0f;
         n = fmaf(c, c, n);
         v[e] = -2.0f * c;
       }
@@ -183,10 +211,8 @@ __global__ __launch_bounds__(kmin_split_threads(D, K)) void kmin_mfma_split_kern
     n += __shfl_xor(n, 16);
     n += __shfl_xor(n, 32);
     nx[t] = n;
-    ax[t] = sqrtf(n);
   }
   const float mcoef = kmin_split_margin_coef(DP);
-  const bool v4 = ((reinterpret_cast<uintptr_t>(a.x) | reinterpret_cast<uintptr_t>(a.y)) & 15u) == 0;
 
   // Prefilter thresholds stay below kPadU, the value padded j carry, so padding
   // never passes; rows beyond M get -inf and never pass either.
@@ -196,7 +222,7 @@ __global__ __launch_bounds__(kmin_split_threads(D, K)) void kmin_mfma_split_kern
   float thr[TI];
 #pragma unroll
   for (int t = 0; t < TI; ++t) {
-    thr[t] = row[t] < M ? kThrCap : -INFINITY;
+    thr[t] = lrow_of(t) < lrows ? kThrCap : -INFINITY;
 #pragma unroll
     for (int k = 0; k < K; ++k) { bd[t][k] = INFINITY; bi[t][k] = -1; }
   }
@@ -206,12 +232,12 @@ __global__ __launch_bounds__(kmin_split_threads(D, K)) void kmin_mfma_split_kern
 
   // tile staging: thread (sj = tid/4, sg = tid%4) owns the 8-coordinate chunks
   // c = 4q + sg (q < NS) of column sj, i.e. coordinates 32q + 8sg + e
-  static_assert(TJ * 4 == kSplitThreads, "four staging threads per j");
   const int sj = tid >> 2, sg = tid & 3;
+  const bool stager = tid < 4 * TJ;
   float ry[NS][8];
   auto load_tile = [&](int64_t jt) {
     const int64_t j = jt + sj;
-    const bool ok = j < je;
+    const bool ok = stager && j < je;
 #pragma unroll
     for (int q = 0; q < NS; ++q)
 #pragma unroll
@@ -221,6 +247,7 @@ __global__ __launch_bounds__(kmin_split_threads(D, K)) void kmin_mfma_split_kern
       }
   };
   auto stage_tile = [&](int buf, int64_t jt) {
+    if (!stager) return;
     const bool ok = jt + sj < je;
     float ny = 0.0f;
     unsigned *rec = sRec + (buf * TJ + sj) * RS;
@@ -244,10 +271,22 @@ __global__ __launch_bounds__(kmin_split_threads(D, K)) void kmin_mfma_split_kern
     ny += __shfl_xor(ny, 2);
     if (sg == 0) sNy[buf * TJ + sj] = ok ? ny : kPadU;   // padded j: u ~ kPadU, never passes
   };
+  // raw coordinates of the tile (those the staging thread loaded) for the exact distance
+  auto stage_raw = [&]() {
+    if (!stager) return;
+#pragma unroll
+    for (int q = 0; q < NS; ++q)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int k = 32 * q + 8 * sg + e;
+        if (k < D) sYr[sj * DX + k] = ry[q][e];
+      }
+  };
 
   if (jb < je) {
     load_tile(jb);
     stage_tile(0, jb);
+    stage_raw();
   }
   __syncthreads();
   int buf = 0;
@@ -295,28 +334,46 @@ __global__ __launch_bounds__(kmin_split_threads(D, K)) void kmin_mfma_split_kern
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int64_t j = jt + j16 + 4 * lgrp + r;
-            if (u[t][r] < thr[t] && j < je && row[t] < M) {
-              const float d2 = exact_sq_dist<D>(a.x + row[t] * D, a.y + j * D, v4);
+            if (u[t][r] < thr[t] && j < je && lrow_of(t) < lrows) {
+              const float d2 = exact_sq_dist_lds<D>(sXr + lrow_of(t) * DX,
+                                                    sYr + (j16 + 4 * lgrp + r) * DX);
               if (d2 < bd[t][K - 1]) {
                 kmin_insert<K>(bd[t], bi[t], d2, (int)j);
                 const float kth = bd[t][K - 1];
-                const float sm = 2.0f * ax[t] + sqrtf(kth);
+                const float sm = 2.0f * sqrtf(nx[t]) + sqrtf(kth);
                 thr[t] = fminf((kth - nx[t]) + mcoef * sm * sm, kThrCap);
               }
             }
           }
-        // The four lane groups of a row see disjoint j; a candidate that fails
-        // the least of their thresholds trails K candidates of that group, so
-        // the groups share it.  (All lanes run this: the branch is wave-uniform.)
+        // The four lane groups of a row see disjoint j and keep a list each.  A
+        // candidate that fails the least of their thresholds trails K candidates
+        // of that group; tighter still, every group's Q-th smallest distance
+        // (Q = ceil(K/4)) is at most their largest, so the four lists together hold
+        // 4Q >= K distances no larger than it: a candidate beyond that largest one
+        // cannot reach the row's final K smallest, and only the final merge of the
+        // four lists decides the result.  (All lanes run this: the branch is
+        // wave-uniform.)
+        constexpr int Q = (K + 3) / 4;
 #pragma unroll
         for (int t = 0; t < TI; ++t) {
           thr[t] = fminf(thr[t], __shfl_xor(thr[t], 16));
           thr[t] = fminf(thr[t], __shfl_xor(thr[t], 32));
+          float q = bd[t][Q - 1];
+          q = fmaxf(q, __shfl_xor(q, 16));
+          q = fmaxf(q, __shfl_xor(q, 32));
+          if (q < INFINITY) {
+            const float sm = 2.0f * sqrtf(nx[t]) + sqrtf(q);
+            thr[t] = fminf(thr[t], (q - nx[t]) + mcoef * sm * sm);
+          }
         }
       }
     }
     if (has_next) stage_tile(buf ^ 1, jt + TJ);
-    __syncthreads();
+    __syncthreads();   // every wave past this tile's raw y
+    if (has_next) {
+      stage_raw();
+      __syncthreads();
+    }
     buf ^= 1;
   }
 
@@ -337,16 +394,17 @@ __global__ __launch_bounds__(kmin_split_threads(D, K)) void kmin_mfma_split_kern
     const bool partial = a.nsplit > 1;
 #pragma unroll
     for (int t = 0; t < TI; ++t) {
-      if (row[t] >= M) continue;
+      if (lrow_of(t) >= lrows) continue;
+      const int64_t row = wg_row0 + lrow_of(t);
 #pragma unroll
       for (int k = 0; k < K; ++k) {
         if (partial) {
-          const int64_t base = ((int64_t)blockIdx.y * M + row[t]) * K;
+          const int64_t base = ((int64_t)blockIdx.y * M + row) * K;
           a.out_d[base + k] = bd[t][k];
           a.part_idx[base + k] = bi[t][k];
         } else {
-          a.out_d[row[t] * K + k] = bd[t][k];
-          a.out_idx[row[t] * K + k] = (int64_t)bi[t][k];
+          a.out_d[row * K + k] = bd[t][k];
+          a.out_idx[row * K + k] = (int64_t)bi[t][k];
         }
       }
     }

@@ -703,18 +703,22 @@ def test_workload_sum_grad_10k():
     check_grad(G2, G2_ref, nu2)
 
 
-def test_workload_sum_lse_1M():
+@pytest.mark.parametrize("op", ["sum", "lse"])
+def test_workload_sum_lse_1M(op):
+    """M = N = 1e6, D = 3, sigma = 0.1: 4,096 seeded rows, each over all 1e6 j."""
     w = workloads.WORKLOADS["sum_lse_1M"]
-    say(f"workload {w.name}")
+    say(f"workload {w.name}: {op}")
     x, y, b = workloads.make_inputs(w)
     X, Y, B = dev(x), dev(y), dev(b)
-    rows = _sample(w.M, 2048)
-    a = host(gm.keops_gauss_sum(X, Y, B, w.sigma))
-    a_ref, n_ref = oracle.gauss_sum(x, y, b, w.sigma, rows=rows)
-    err_sum = check_sum(a[rows], a_ref, n_ref)
-    l = host(gm.keops_gauss_lse(X, Y, B, w.sigma))
-    err_lse = check_lse(l[rows], oracle.gauss_lse(x, y, b, w.sigma, rows=rows))
-    say(json.dumps({"workload": w.name, "sum_max_norm_err": err_sum, "lse_max_abs_err": err_lse}))
+    rows = _sample(w.M, 4096)
+    if op == "sum":
+        a = host(gm.keops_gauss_sum(X, Y, B, w.sigma))
+        a_ref, n_ref = oracle.gauss_sum(x, y, b, w.sigma, rows=rows)
+        err = check_sum(a[rows], a_ref, n_ref)
+    else:
+        l = host(gm.keops_gauss_lse(X, Y, B, w.sigma))
+        err = check_lse(l[rows], oracle.gauss_lse(x, y, b, w.sigma, rows=rows))
+    say(json.dumps({"workload": w.name, "op": op, "rows_checked": len(rows), "max_err": err}))
 
 
 def test_workload_solver_matvec():
@@ -725,10 +729,10 @@ def test_workload_solver_matvec():
     a = host(gm.keops_gauss_sum(X, Y, B, w.sigma))
     del X, Y, B
     torch.cuda.empty_cache()
-    rows = _sample(w.M, 96)
+    rows = _sample(w.M, 512)
     a_ref, n_ref = oracle.gauss_sum(x, y, b, w.sigma, rows=rows)
     err = check_sum(a[rows], a_ref, n_ref)
-    say(json.dumps({"workload": w.name, "sum_max_norm_err": err}))
+    say(json.dumps({"workload": w.name, "rows_checked": len(rows), "sum_max_norm_err": err}))
 
 
 def test_workload_stream_16_x_100M():
@@ -778,12 +782,13 @@ def test_workload_krige_100k():
 
 @pytest.mark.parametrize("name", ["kmin10_1M_d3", "kmin10_1M_d64"])
 def test_workload_kmin(name):
+    """K-min at M = N = 1e6: 4,096 seeded rows at D = 3, 2,048 at D = 64, each over all 1e6 j."""
     w = workloads.WORKLOADS[name]
     say(f"workload {w.name}")
     x, y, _ = workloads.make_inputs(w)
     d, i = gm.keops_kmin(dev(x), dev(y), w.K)
     d, i = host(d), host(i)
-    rows = _sample(w.M, 2048 if w.D <= 8 else 256)
+    rows = _sample(w.M, 4096 if w.D <= 8 else 2048)
     d_ref, i_ref = oracle.kmin(x, y, w.K, rows=rows)
     nswap = check_kmin(x, y, rows, d[rows], i[rows], d_ref, i_ref)
     say(json.dumps({"workload": w.name, "rows_checked": len(rows), "near_tie_swaps": nswap}))
