@@ -115,8 +115,16 @@ KERNEL_SOURCES = {
     "lse": ["gauss_kernel.h", "dispatch_gauss.h", "gauss_lse_small.hip"],
     "grad_x": ["gauss_kernel.h", "dispatch_gauss.h", "gauss_grad_small.hip"],
     "kmin": ["kmin_kernel.h", "dispatch_kmin.h", "kmin_d1_4.hip"],
+    "kmin_split": ["kmin_kernel.h", "kmin_mfma_split.h", "kmin_mfma_split.hip"],
     "stream": ["gauss_stream.h", "gauss_stream.hip"],
 }
+# the kernel whose HBM traffic each workload records (rocprofv3's kernel name)
+TRAFFIC_KERNELS = {
+    "sum": ("sum", "gauss_valu_kernel<0, 3, 1, 2>"),
+    "stream": ("stream", "gauss_stream_kernel<3, 1, 16>"),
+    "kmin64": ("kmin_split", "kmin_mfma_split_kernel<64, 10>"),
+}
+COPY_KNOWN_KIB = 262144.0          # the calibration copy reads and writes 256 MiB per launch
 
 
 def kernel_source_hash(op):
@@ -138,6 +146,53 @@ def recorded_traffic(bench_name, op):
     if rec.get("kernel_sources_sha256") != kernel_source_hash(op):
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def _counter_per_dispatch(csv_path, kernel):
+    """Per-dispatch sums (over XCDs and instances) of the one counter in a rocprofv3
+    --pmc CSV, for the dispatches whose kernel name contains ``kernel``."""
+    import csv
+    agg = {}
+    with open(csv_path) as fh:
+        for r in csv.DictReader(fh):
+            if kernel in r["Kernel_Name"]:
+                agg[r["Dispatch_Id"]] = agg.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    return [agg[k] for k in sorted(agg, key=int)]
+
+
+def record_traffic(workload, fetch_csv, write_csv, cal_fetch_csv, cal_write_csv):
+    """Write profiles/traffic_<workload>.json from four rocprofv3 --pmc runs (FETCH_SIZE and
+    WRITE_SIZE, each of this workload and of --workload copycal).  The counters read KiB
+    per dispatch; each is scaled by what it reads for the copy kernel of known size (the
+    copy's first dispatch, a warm-up that also pages in, is left out)."""
+    import statistics
+    src_key, kernel = TRAFFIC_KERNELS[workload]
+    cf = _counter_per_dispatch(cal_fetch_csv, "elementwise")[1:]
+    cw = _counter_per_dispatch(cal_write_csv, "elementwise")[1:]
+    f = _counter_per_dispatch(fetch_csv, kernel)
+    w = _counter_per_dispatch(write_csv, kernel)
+    if not (cf and cw and f and w):
+        raise SystemExit(f"no dispatches of {kernel!r} or of the copy kernel in the given CSVs")
+    ff, wf = COPY_KNOWN_KIB / statistics.mean(cf), COPY_KNOWN_KIB / statistics.mean(cw)
+    fb, wb = round(statistics.mean(f) * 1024 * ff), round(statistics.mean(w) * 1024 * wf)
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    rec = json.load(open(path)) if os.path.exists(path) else {}
+    rec.update({
+        "kernel": rec.get("kernel", kernel),
+        "fetch_size_kib_per_dispatch": f,
+        "write_size_kib_per_dispatch": w,
+        "copy_calibration": {"kernel": "torch neg elementwise, 256 MiB read + 256 MiB written",
+                             "fetch_size_kib": cf, "write_size_kib": cw,
+                             "fetch_factor": round(ff, 4), "write_factor": round(wf, 4)},
+        "hbm_fetch_bytes_per_launch": fb,
+        "hbm_write_bytes_per_launch": wb,
+        "hbm_bytes_per_launch": fb + wb,
+        "kernel_sources_sha256": kernel_source_hash(src_key),
+    })
+    with open(path, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps({"workload": workload, "kernel": kernel, "hbm_fetch_bytes": fb, "hbm_write_bytes": wb,
+                      "fetch_factor": round(ff, 4), "write_factor": round(wf, 4)}))
 
 
 def run_op(gm, op, X, Y, B, G, sigma, K, out, lam=0.0, ranges=None):
@@ -339,7 +394,12 @@ def main():
     ap.add_argument("--workload", default="sum", choices=sorted(BENCHES) + ["copycal", "micro"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--record-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="no GPU: write profiles/traffic_<workload>.json from rocprofv3 --pmc CSVs")
     args = ap.parse_args()
+    if args.record_traffic:
+        record_traffic(args.workload, *args.record_traffic)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -423,7 +483,8 @@ def main():
     value = pairs / (ms_step * 1e-3) / 1e9
     bound, fpp, kname = roofline_of(op, w.M, w.D, w.E)
     kern_avg_ms = kern_ms / max(launches, 1)
-    src_key = "stream" if bound == "hbm" else {"grad_y": "grad_x", "grad_b": "sum"}.get(op, op)
+    src_key = ("stream" if bound == "hbm" else "kmin_split" if bound == "mfma_bf16" and op == "kmin"
+               else {"grad_y": "grad_x", "grad_b": "sum"}.get(op, op))
     traffic = recorded_traffic(args.workload, src_key)
     if bound == "hbm":
         achieved = stream_bytes(w) / (kern_avg_ms * 1e-3) / 1e9
