@@ -21,9 +21,9 @@ never stored, run as hand-written gfx950 HIP kernels behind the C ABI of
 
 PyTorch supplies device memory and streams only.
 """
-from .binding import (KEOPS_OPT_FORM, KEOPS_OPT_MFMA, KEOPS_OPT_PROFILE, KEOPS_OPT_ROWS, KEOPS_OPT_SPLIT_J,  # noqa: F401
-                      KEOPS_OPT_WG_TARGET, KeopsError, keops_gauss_cg, keops_gauss_grad_b, keops_gauss_grad_x,
-                      keops_gauss_grad_x_ranges, keops_gauss_grad_y, keops_gauss_lse, keops_gauss_lse_ranges,
-                      keops_gauss_max, keops_gauss_min, keops_laplace_sum,
-                      keops_gauss_sum, keops_gauss_sum_noalloc, keops_gauss_sum_ranges, keops_kmin, keops_profile_read,
-                      keops_set_option, keops_version, lib, status_string)
+from .binding import (KEOPS_OPT_FAIL_ALLOC, KEOPS_OPT_FORM, KEOPS_OPT_MFMA, KEOPS_OPT_PROFILE,  # noqa: F401
+                      KEOPS_OPT_ROWS, KEOPS_OPT_SPLIT_J, KEOPS_OPT_WG_TARGET, KEOPS_OPT_WS_CACHE, KeopsError,
+                      keops_gauss_cg, keops_gauss_grad_b, keops_gauss_grad_x, keops_gauss_grad_x_ranges,
+                      keops_gauss_grad_y, keops_gauss_lse, keops_gauss_lse_ranges, keops_gauss_max, keops_gauss_min,
+                      keops_laplace_sum, keops_gauss_sum, keops_gauss_sum_noalloc, keops_gauss_sum_ranges,
+                      keops_kmin, keops_profile_read, keops_set_option, keops_version, lib, status_string)

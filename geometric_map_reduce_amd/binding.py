@@ -34,6 +34,8 @@ KEOPS_OPT_ROWS = 3
 KEOPS_OPT_PROFILE = 4
 KEOPS_OPT_WG_TARGET = 5
 KEOPS_OPT_MFMA = 6
+KEOPS_OPT_WS_CACHE = 7
+KEOPS_OPT_FAIL_ALLOC = 8
 
 _lock = threading.Lock()
 _lib = None
@@ -48,6 +50,8 @@ class KeopsError(RuntimeError):
 def lib() -> ctypes.CDLL:
     """The loaded library (raises if it has not been built)."""
     global _lib
+    if _lib is not None:
+        return _lib
     with _lock:
         if _lib is None:
             if not os.path.exists(LIB_PATH):
@@ -106,6 +110,26 @@ def _mat(t, name, device=None):
     return t
 
 
+class _on_device:
+    """Makes ``dev`` the current device for the call, switching only when it is not
+    already (torch.cuda.device always switches and back, a few microseconds per call)."""
+    __slots__ = ("idx", "prev")
+
+    def __init__(self, dev):
+        self.idx = dev.index
+        self.prev = None
+
+    def __enter__(self):
+        cur = torch.cuda.current_device()
+        if self.idx is not None and cur != self.idx:
+            self.prev = cur
+            torch.cuda.set_device(self.idx)
+
+    def __exit__(self, *exc):
+        if self.prev is not None:
+            torch.cuda.set_device(self.prev)
+
+
 def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else None
 
@@ -141,7 +165,7 @@ def _gauss(fn_name, x, y, b, sigma, out, stream, g=None):
             raise ValueError(f"g must be [M, E] = [{M}, {E}]")
         args.append(_ptr(g))
     out = _out(out, (M, D if g is not None else E), dev)
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         rc = getattr(lib(), fn_name)(*args, M, N, D, E, float(sigma), _ptr(out), _stream(stream, dev))
     _check(fn_name, rc)
     return out
@@ -183,7 +207,7 @@ def keops_gauss_grad_y(x, y, b, g, sigma, out=None, stream=None):
     if y.shape != (N, D) or g.shape != (M, E):
         raise ValueError(f"need y [N, D] = [{N}, {D}] and g [M, E] = [{M}, {E}]")
     out = _out(out, (N, D), dev)
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         rc = lib().keops_gauss_grad_y(_ptr(x), _ptr(y), _ptr(b), _ptr(g), M, N, D, E, float(sigma), _ptr(out),
                                       _stream(stream, dev))
     _check("keops_gauss_grad_y", rc)
@@ -201,7 +225,7 @@ def keops_gauss_grad_b(x, y, g, sigma, out=None, stream=None):
     if y.shape != (N, D) or g.shape[0] != M:
         raise ValueError(f"need y [N, {D}] and g [M, E] with M = {M}")
     out = _out(out, (N, E), dev)
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         rc = lib().keops_gauss_grad_b(_ptr(x), _ptr(y), _ptr(g), M, N, D, E, float(sigma), _ptr(out),
                                       _stream(stream, dev))
     _check("keops_gauss_grad_b", rc)
@@ -224,7 +248,7 @@ def keops_gauss_cg(x, b, sigma, lam, rtol=1e-5, max_iter=1000, out=None, stream=
     out = _out(out, (N, E), dev)
     it = ctypes.c_int32(0)
     res = (ctypes.c_float * max(E, 1))()
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         rc = lib().keops_gauss_cg(_ptr(x), _ptr(b), N, D, E, float(sigma), float(lam), float(rtol), int(max_iter),
                                   _ptr(out), ctypes.byref(it), res, _stream(stream, dev))
     _check("keops_gauss_cg", rc)
@@ -262,7 +286,7 @@ def _gauss_ranges(fn_name, x, y, b, sigma, ranges, out, stream, g=None):
         args.append(_ptr(g))
     out = _out(out, (M, D if g is not None else E), dev)
     hp = lambda a: a.ctypes.data_as(ctypes.c_void_p) if a.size else None  # noqa: E731
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         rc = getattr(lib(), fn_name)(*args, M, N, D, E, float(sigma), hp(ri), ri.shape[0], hp(si), hp(rj),
                                      rj.shape[0], _ptr(out), _stream(stream, dev))
     _check(fn_name, rc)
@@ -296,7 +320,7 @@ def _gauss_extremum(fn_name, x, y, b, sigma, out, out_idx, stream):
         raise ValueError(f"y must be [N, D] = [{N}, {D}], got {tuple(y.shape)}")
     out = _out(out, (M, E), dev)
     out_idx = _out(out_idx, (M, E), dev, dtype=torch.int64, name="out_idx")
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         rc = getattr(lib(), fn_name)(_ptr(x), _ptr(y), _ptr(b), M, N, D, E, float(sigma), _ptr(out), _ptr(out_idx),
                                      _stream(stream, dev))
     _check(fn_name, rc)
@@ -324,7 +348,7 @@ def keops_kmin(x, y, K, out_d=None, out_idx=None, stream=None):
         raise ValueError("x and y must have the same number of columns")
     out_d = _out(out_d, (M, K), dev, name="out_d")
     out_idx = _out(out_idx, (M, K), dev, dtype=torch.int64, name="out_idx")
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         # b and sigma of the uniform argument list are not read by K-min
         rc = lib().keops_kmin(_ptr(x), _ptr(y), None, M, N, D, int(K), 1.0, _ptr(out_d), _ptr(out_idx),
                               _stream(stream, dev))

@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <memory>
 #include <mutex>
 #include <vector>
 
@@ -27,7 +28,7 @@ namespace kmi {
 namespace {
 
 std::atomic<int64_t> g_opt_split{0}, g_opt_form{0}, g_opt_rows{0}, g_opt_profile{0}, g_opt_wg_target{0},
-    g_opt_mfma{0};
+    g_opt_mfma{0}, g_opt_ws_cache{1}, g_opt_fail_alloc{0};
 
 // ---- pass-1 timing (KEOPS_OPT_PROFILE)
 struct EventPair { hipEvent_t start, stop; };
@@ -118,6 +119,145 @@ struct Arena {
   size_t cap;
 };
 
+// ---- workspace cache
+// Each (device, stream, slot) keeps one grow-only device buffer, which the calls on
+// that stream reuse in stream order: after the first call of a given size a call
+// neither allocates nor waits on the host (a stream-ordered allocation and free per
+// call made every small call wait for the GPU).  Growing or evicting an idle buffer
+// frees it with hipFree, which waits for the device's pending work first.  A buffer
+// held by another host thread's call on the same stream is never shared (the two
+// calls' kernels could interleave): such a call allocates its own for the occasion.
+// Slot 0: the reductions' split partials; slot 1: the CG solver's vectors (its
+// products take slot 0 on the same stream).  KEOPS_OPT_WS_CACHE = 0 allocates per
+// call instead and frees the idle cached buffers.
+struct WsEntry {
+  int dev;
+  hipStream_t st;
+  int slot;
+  char *ptr;
+  size_t cap;
+  int busy;
+  uint64_t tick;
+};
+std::mutex g_ws_mu;
+std::vector<std::unique_ptr<WsEntry>> g_ws;
+uint64_t g_ws_tick = 0;
+constexpr size_t kWsMaxEntries = 32;
+
+// Frees every cached buffer no call holds (caller holds g_ws_mu).
+void ws_trim_locked() {
+  for (size_t k = 0; k < g_ws.size();) {
+    if (g_ws[k]->busy == 0) {
+      int cur = 0;
+      (void)hipGetDevice(&cur);
+      (void)hipSetDevice(g_ws[k]->dev);
+      (void)hipFree(g_ws[k]->ptr);
+      (void)hipSetDevice(cur);
+      g_ws.erase(g_ws.begin() + (ptrdiff_t)k);
+    } else {
+      ++k;
+    }
+  }
+  (void)hipGetLastError();
+}
+
+class Workspace {
+ public:
+  Workspace() = default;
+  Workspace(const Workspace &) = delete;
+  Workspace &operator=(const Workspace &) = delete;
+  ~Workspace() { release(); }
+
+  // A device buffer of at least `bytes` for work enqueued on `st` (null for 0 bytes).
+  // Returns KEOPS_OK or KEOPS_ERR_ALLOC (nothing enqueued).
+  int acquire(hipStream_t st, int slot, size_t bytes) {
+    release();
+    if (bytes == 0) return KEOPS_OK;
+    if (g_opt_fail_alloc.load(std::memory_order_relaxed) == 1) return KEOPS_ERR_ALLOC;
+    bytes = (bytes + 255) / 256 * 256;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return KEOPS_ERR_ALLOC;
+    }
+    if (g_opt_ws_cache.load(std::memory_order_relaxed) == 1) {
+      std::lock_guard<std::mutex> lk(g_ws_mu);
+      WsEntry *e = nullptr;
+      for (auto &u : g_ws)
+        if (u->dev == dev && u->st == st && u->slot == slot) { e = u.get(); break; }
+      if (!e && g_ws.size() >= kWsMaxEntries) {
+        // evict the least recently used idle buffer
+        size_t lru = g_ws.size();
+        for (size_t k = 0; k < g_ws.size(); ++k)
+          if (g_ws[k]->busy == 0 && (lru == g_ws.size() || g_ws[k]->tick < g_ws[lru]->tick)) lru = k;
+        if (lru < g_ws.size()) {
+          (void)hipSetDevice(g_ws[lru]->dev);
+          (void)hipFree(g_ws[lru]->ptr);
+          (void)hipSetDevice(dev);
+          g_ws.erase(g_ws.begin() + (ptrdiff_t)lru);
+        }
+      }
+      if (!e && g_ws.size() < kWsMaxEntries) {
+        g_ws.push_back(std::unique_ptr<WsEntry>(new WsEntry{dev, st, slot, nullptr, 0, 0, 0}));
+        e = g_ws.back().get();
+      }
+      if (e && e->busy == 0) {
+        if (e->cap < bytes) {
+          const size_t cap = std::max(bytes, (e->cap + e->cap / 4 + 255) / 256 * 256);
+          if (e->ptr) (void)hipFree(e->ptr);
+          e->ptr = nullptr;
+          e->cap = 0;
+          if (hipMalloc((void **)&e->ptr, cap) != hipSuccess || !e->ptr) {
+            (void)hipGetLastError();
+            e->ptr = nullptr;
+            // an empty entry is dropped again; the per-call allocation below may still fit
+            for (size_t k = 0; k < g_ws.size(); ++k)
+              if (g_ws[k].get() == e) { g_ws.erase(g_ws.begin() + (ptrdiff_t)k); break; }
+            e = nullptr;
+          } else {
+            e->cap = cap;
+          }
+        }
+        if (e) {
+          e->busy = 1;
+          e->tick = ++g_ws_tick;
+          entry_ = e;
+          ptr_ = e->ptr;
+          return KEOPS_OK;
+        }
+      }
+    }
+    if (hipMallocAsync((void **)&ptr_, bytes, st) != hipSuccess || !ptr_) {
+      (void)hipGetLastError();
+      ptr_ = nullptr;
+      return KEOPS_ERR_ALLOC;
+    }
+    owned_ = true;
+    st_ = st;
+    return KEOPS_OK;
+  }
+
+  char *ptr() const { return ptr_; }
+
+ private:
+  void release() {
+    if (owned_ && ptr_) (void)hipFreeAsync(ptr_, st_);
+    if (entry_) {
+      std::lock_guard<std::mutex> lk(g_ws_mu);
+      entry_->busy = 0;
+      if (g_opt_ws_cache.load(std::memory_order_relaxed) != 1) ws_trim_locked();
+    }
+    ptr_ = nullptr;
+    entry_ = nullptr;
+    owned_ = false;
+  }
+
+  char *ptr_ = nullptr;
+  hipStream_t st_ = nullptr;
+  WsEntry *entry_ = nullptr;
+  bool owned_ = false;
+};
+
 bool overlaps(const void *a, int64_t abytes, const void *b, int64_t bbytes) {
   if (!a || !b || abytes <= 0 || bbytes <= 0) return false;
   const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
@@ -173,6 +313,8 @@ constexpr int64_t kKminMfmaWgsPerCu = 4;
 // per lane until the wide variant fills every CU: it was the faster one up to
 // 200k rows.
 constexpr int64_t kWideMinRows = 40000;
+// below this many work-groups per CU, the j split may go down to one tile per split
+constexpr int64_t kSmallGridWgsPerCu = 8;
 
 struct Plan {
   int wide;
@@ -210,8 +352,11 @@ Plan make_plan(int64_t M, int64_t N, int cus, int64_t rows_wide, int64_t rows_na
     s = forced;
   } else if (p.nblk < want_wgs) {
     s = (want_wgs + p.nblk - 1) / p.nblk;
-    // at least 4 j tiles per split: with 2-3, the CG solve at 100k x 100k ran 2 % slower
-    const int64_t max_s = ntiles / 4 > 1 ? ntiles / 4 : 1;
+    // at least 4 j tiles per split (with 2-3, the CG solve at 100k x 100k ran 2 %
+    // slower), unless that leaves fewer than kSmallGridWgsPerCu work-groups per CU:
+    // then down to one tile per split (1k x 1k sum: 13 against 31 us)
+    int64_t max_s = ntiles / 4 > 1 ? ntiles / 4 : 1;
+    if (p.nblk * max_s < (int64_t)cus * kSmallGridWgsPerCu) max_s = ntiles;
     if (s > max_s) s = max_s;
   }
   if (s > ntiles) s = ntiles;
@@ -260,12 +405,13 @@ int gauss_stream_entry(const float *x, const float *y, const float *b, int64_t M
   const size_t part_bytes = ((size_t)wgs * M * E * sizeof(float) + 255) / 256 * 256;
   const size_t fac_bytes = guard ? ((size_t)M * sizeof(float) + 255) / 256 * 256 : 0;
   const size_t bmax_bytes = guard ? (size_t)wgs * sizeof(float) : 0;
+  Workspace wsp;
   if (arena) {
     if (part_bytes + fac_bytes + bmax_bytes > arena->cap) return kStreamNoFit;
     ws = (float *)arena->base;
-  } else if (hipMallocAsync((void **)&ws, part_bytes + fac_bytes + bmax_bytes, st) != hipSuccess || !ws) {
-    (void)hipGetLastError();
-    return KEOPS_ERR_ALLOC;
+  } else {
+    if (int rc = wsp.acquire(st, 0, part_bytes + fac_bytes + bmax_bytes)) return rc;
+    ws = (float *)wsp.ptr();
   }
   StreamArgs a{};
   a.x = x; a.y = y; a.b = b;
@@ -292,7 +438,6 @@ int gauss_stream_entry(const float *x, const float *y, const float *b, int64_t M
   gauss_dispatch_sum_stream(D, E, info.rows_per_wg, nullptr, dim3((unsigned)wgs, (unsigned)groups), &a, st);
   prof_end(prof, st);
   launch_stream_combine(ws, (int)wgs, M * E, out, g, st);
-  if (!arena) (void)hipFreeAsync(ws, st);
   return check_launch();
 }
 
@@ -405,13 +550,14 @@ int gauss_entry(int op, const float *x, const float *y, const float *b, const fl
   float *ws = nullptr;
   const size_t part_bytes = p.nsplit > 1 ? al((size_t)p.nsplit * M * PW * sizeof(float)) : 0;
   const size_t ws_bytes = part_bytes + flag_bytes;
+  Workspace wsp;
   if (ws_bytes > 0) {
     if (no_alloc) {
       if (ws_bytes > arena.cap) return KEOPS_ERR_SCRATCH;
       ws = (float *)arena.base;
-    } else if (hipMallocAsync((void **)&ws, ws_bytes, st) != hipSuccess || !ws) {
-      (void)hipGetLastError();
-      return KEOPS_ERR_ALLOC;
+    } else {
+      if (int rc = wsp.acquire(st, 0, ws_bytes)) return rc;
+      ws = (float *)wsp.ptr();
     }
   }
   a.out = p.nsplit > 1 ? ws : out;
@@ -433,7 +579,6 @@ int gauss_entry(int op, const float *x, const float *y, const float *b, const fl
     else if (op == OP_MAX) launch_max_combine(ws, p.nsplit, M, E, max_sign, out, out_idx, st);
     else launch_sum_combine(ws, p.nsplit, M * PW, out, st);
   }
-  if (ws && !no_alloc) (void)hipFreeAsync(ws, st);
   return check_launch();
 }
 
@@ -556,20 +701,16 @@ int gauss_ranges_entry(int op, const float *x, const float *y, const float *b, c
   const size_t ib = (items.size() * sizeof(BsItem) + 255) / 256 * 256;
   const size_t rb = ((size_t)nrj * 2 * sizeof(int64_t) + 255) / 256 * 256;
   const size_t pb = smax > 1 ? (size_t)smax * M * PW * sizeof(float) : 0;
-  char *ws = nullptr;
-  if (hipMallocAsync((void **)&ws, ib + rb + pb, st) != hipSuccess || !ws) {
-    (void)hipGetLastError();
-    return KEOPS_ERR_ALLOC;
-  }
+  Workspace wsp;
+  if (int rc = wsp.acquire(st, 0, ib + rb + pb)) return rc;
+  char *ws = wsp.ptr();
   std::vector<char> host(ib + rb);
   std::memcpy(host.data(), items.data(), items.size() * sizeof(BsItem));
   if (nrj > 0) std::memcpy(host.data() + ib, redranges_j, (size_t)nrj * 2 * sizeof(int64_t));
   // the host copy must outlive the transfer: wait for it
   if (hipMemcpyAsync(ws, host.data(), ib + rb, hipMemcpyHostToDevice, st) != hipSuccess ||
-      hipStreamSynchronize(st) != hipSuccess) {
-    (void)hipFreeAsync(ws, st);
+      hipStreamSynchronize(st) != hipSuccess)
     return KEOPS_ERR_HIP;
-  }
   float *part = smax > 1 ? (float *)(ws + ib + rb) : nullptr;
   // rows outside every kept range (and slots a row range does not use) hold the empty reduction
   if (smax > 1) {
@@ -600,7 +741,6 @@ int gauss_ranges_entry(int op, const float *x, const float *y, const float *b, c
     if (op == OP_LSE) launch_lse_combine(part, (int)smax, M, E, out, st);
     else launch_sum_combine(part, (int)smax, M * PW, out, st);
   }
-  (void)hipFreeAsync(ws, st);
   return check_launch();
 }
 
@@ -674,11 +814,9 @@ int keops_gauss_cg(const float *x, const float *b, int64_t N, int32_t D, int32_t
   const size_t vec = ((size_t)N * E * sizeof(float) + 255) / 256 * 256;
   const size_t part_bytes = (size_t)kCgBlocks * E * sizeof(double);
   const size_t scal_bytes = 5 * 4 * sizeof(double);
-  char *ws = nullptr;
-  if (hipMallocAsync((void **)&ws, 3 * vec + part_bytes + scal_bytes, st) != hipSuccess || !ws) {
-    (void)hipGetLastError();
-    return KEOPS_ERR_ALLOC;
-  }
+  Workspace wsp;
+  if (int rc = wsp.acquire(st, 1, 3 * vec + part_bytes + scal_bytes)) return rc;
+  char *ws = wsp.ptr();
   float *r = (float *)ws, *p = (float *)(ws + vec), *q = (float *)(ws + 2 * vec);
   double *part = (double *)(ws + 3 * vec);
   double *sc = (double *)(ws + 3 * vec + part_bytes);
@@ -729,7 +867,6 @@ int keops_gauss_cg(const float *x, const float *b, int64_t N, int32_t D, int32_t
     }
   }
   if (iters) *iters = it;
-  (void)hipFreeAsync(ws, st);
   if (rc == KEOPS_OK) rc = check_launch();
   if (rc == KEOPS_OK && hipStreamSynchronize(st) != hipSuccess) rc = KEOPS_ERR_HIP;
   return rc;
@@ -813,15 +950,12 @@ int keops_kmin(const float *x, const float *y, const float * /*b: not read*/, in
   a.x = x; a.y = y; a.M = M; a.N = N;
   a.j_per_split = p.jps;
   a.nsplit = p.nsplit;
-  void *ws = nullptr;
+  Workspace wsp;
   if (p.nsplit > 1) {
     const size_t n = (size_t)p.nsplit * M * K;
-    if (hipMallocAsync(&ws, n * (sizeof(float) + sizeof(int32_t)), st) != hipSuccess || !ws) {
-      (void)hipGetLastError();
-      return KEOPS_ERR_ALLOC;
-    }
-    a.out_d = (float *)ws;
-    a.part_idx = (int32_t *)((float *)ws + n);
+    if (int rc = wsp.acquire(st, 0, n * (sizeof(float) + sizeof(int32_t)))) return rc;
+    a.out_d = (float *)wsp.ptr();
+    a.part_idx = (int32_t *)((float *)wsp.ptr() + n);
   } else {
     a.out_d = out_d;
     a.out_idx = out_idx;
@@ -831,7 +965,6 @@ int keops_kmin(const float *x, const float *y, const float * /*b: not read*/, in
   prof_end(prof, st);
   if (p.nsplit > 1) {
     launch_kmin_combine(a.out_d, a.part_idx, p.nsplit, M, K, out_d, out_idx, st);
-    (void)hipFreeAsync(ws, st);
   }
   return check_launch();
 }
@@ -873,6 +1006,19 @@ int keops_set_option(int option, int64_t value) {
     case KEOPS_OPT_MFMA:
       if (value < 0 || value > 2) return KEOPS_ERR_INVALID_ARG;
       g_opt_mfma.store(value);
+      return KEOPS_OK;
+    case KEOPS_OPT_WS_CACHE:
+      // 0 = 1 here: the cache is on unless switched off
+      if (value < 0 || value > 2) return KEOPS_ERR_INVALID_ARG;
+      g_opt_ws_cache.store(value == 2 ? 0 : 1);
+      if (value == 2) {
+        std::lock_guard<std::mutex> lk(g_ws_mu);
+        ws_trim_locked();
+      }
+      return KEOPS_OK;
+    case KEOPS_OPT_FAIL_ALLOC:
+      if (value < 0 || value > 1) return KEOPS_ERR_INVALID_ARG;
+      g_opt_fail_alloc.store(value);
       return KEOPS_OK;
     default:
       return KEOPS_ERR_INVALID_ARG;

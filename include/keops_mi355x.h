@@ -29,8 +29,15 @@
  *             The library keeps no reference after returning, except through
  *             work queued on `stream`; the caller keeps the buffers alive
  *             until the stream has passed that work.  Outputs must not overlap
- *             inputs.  Split-j workspace is allocated by the library in
- *             stream order (hipMallocAsync / hipFreeAsync on `stream`).
+ *             inputs.  Split-j workspace belongs to the library: one device
+ *             buffer per (device, stream), allocated on first need, grown
+ *             when a call needs more, and reused in stream order by later
+ *             calls on that stream, so that a call allocates nothing once
+ *             its stream has seen a call of its size.  A buffer is freed
+ *             (with hipFree) when it grows, when more than 32 are held, or
+ *             when KEOPS_OPT_WS_CACHE is set to 2.  Destroy a stream only
+ *             after its calls' work has completed: a stream created later
+ *             may reuse the handle, and with it the buffer.
  *  Stream:    `stream` is a hipStream_t passed as void* (NULL = the default
  *             stream).  Calls only enqueue work and never synchronise; kernel
  *             faults surface at the caller's next synchronisation.
@@ -254,6 +261,13 @@ const char *keops_status_string(int status);
  *                          2 = the K-min prefilter at D >= 32 takes the fp32
  *                          MFMA form instead of the split-bf16 one (the same
  *                          results; the sum is unaffected)
+ *   KEOPS_OPT_WS_CACHE  -- 2 = no workspace cache: every call allocates and
+ *                          frees its workspace in stream order
+ *                          (hipMallocAsync / hipFreeAsync); setting it also
+ *                          frees the cached buffers no call holds
+ *   KEOPS_OPT_FAIL_ALLOC -- test switch: 1 = every workspace allocation fails,
+ *                          so that a call needing workspace returns
+ *                          KEOPS_ERR_ALLOC with nothing enqueued
  * Returns KEOPS_OK, or KEOPS_ERR_INVALID_ARG for an unknown option or value.
  */
 #define KEOPS_OPT_SPLIT_J 1
@@ -262,6 +276,8 @@ const char *keops_status_string(int status);
 #define KEOPS_OPT_PROFILE 4   /* 1 = record HIP events around each pass-1 launch */
 #define KEOPS_OPT_WG_TARGET 5
 #define KEOPS_OPT_MFMA 6
+#define KEOPS_OPT_WS_CACHE 7
+#define KEOPS_OPT_FAIL_ALLOC 8
 int keops_set_option(int option, int64_t value);
 
 /*

@@ -118,7 +118,11 @@ def test_options(L):
     assert L.keops_set_option(6, 3) == -1
     assert L.keops_set_option(6, 2) == 0
     assert L.keops_set_option(6, 1) == 0
-    for opt in (1, 2, 3, 5, 6):
+    assert L.keops_set_option(7, 3) == -1         # workspace cache: 0 automatic, 1 on, 2 off
+    assert L.keops_set_option(7, 1) == 0
+    assert L.keops_set_option(8, 2) == -1         # forced allocation failure: 0 / 1
+    assert L.keops_set_option(8, 1) == 0
+    for opt in (1, 2, 3, 5, 6, 7, 8):
         assert L.keops_set_option(opt, 0) == 0
     assert L.keops_version() >= 100
 
