@@ -50,8 +50,8 @@ struct GaussArgs {
   int64_t j_per_split;  // multiple of kTileJ
   int nsplit;
   int form;             // Form
-  // Per row-block form decisions of the MFMA kernel (1 = done there); when set,
-  // the VALU kernel skips those blocks.  Null otherwise.
+  // Per work-group decisions of the MFMA kernels, [row block][j split] (1 = results
+  // stored there); when set, the VALU kernel skips those work-groups.  Null otherwise.
   int *wg_flags;
   // Block-sparse launches: work item blockIdx.x and the [nrj][2] j ranges.
   // Null for dense launches (rows from blockIdx.x, j from blockIdx.y).
@@ -179,6 +179,11 @@ __device__ __forceinline__ float block_min(float v, float *red) {
 }
 
 __device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
+
+// Component u (0..3) of a float4, u known at compile time after unrolling.
+__device__ __forceinline__ float lane4(const float4 &v, int u) {
+  return u == 0 ? v.x : (u == 1 ? v.y : (u == 2 ? v.z : v.w));
+}
 
 // A value the caller knows to be the same in every lane, moved to scalar registers so
 // that the compiler can keep loop control on it off the VALU.

@@ -76,10 +76,6 @@ __device__ __forceinline__ void load_rec(const float4 *rec, int j, float (&yv)[4
   }
 }
 
-__device__ __forceinline__ float lane4(const float4 &v, int u) {
-  return u == 0 ? v.x : (u == 1 ? v.y : (u == 2 ? v.z : v.w));
-}
-
 // Exponent (log2 units) of the pair map for R rows and one j record, phase by
 // phase over the rows so that the R chains are independent.
 //   EXPANDED: q_r = <x'_r, 2y'> + c_j      (xs = x', record = (2y', c_j))
@@ -577,8 +573,8 @@ __global__ __launch_bounds__(kThreads) void gauss_valu_kernel(GaussArgs a) {
   __shared__ int sIdx[S::SPLIT && OP == OP_MAX ? 2 : 1][S::SPLIT && OP == OP_MAX ? S::TJR : 1];   // j of each record
   __shared__ int sSeg[2][4];                                                                     // class sizes per wave
 
-  // row blocks already computed by the MFMA kernel (uniform across the work-group)
-  if (a.wg_flags && a.wg_flags[blockIdx.x]) return;
+  // work-groups whose results the MFMA kernel has stored (uniform across the work-group)
+  if (a.wg_flags && a.wg_flags[(int64_t)blockIdx.x * gridDim.y + blockIdx.y]) return;
 
   const int tid = threadIdx.x;
   const int wid = tid / kWave, lane = tid & (kWave - 1);

@@ -14,7 +14,7 @@ int gauss_dispatch_sum_mfma(int D, int E, int wide, VariantInfo *info, dim3 grid
       info->tile_j = MfmaShape<DD>::TJ;                                \
       return 0;                                                        \
     }                                                                  \
-    launch_gauss_mfma_sum_t<DD, EE>(grid, *args, st);                  \
+    launch_gauss_mfma_t<OP_SUM, DD, EE>(grid, *args, st);              \
     return 0;                                                          \
   }
 #define KMI_MFMA_E(DD) KMI_MFMA_CASE(DD, 1) KMI_MFMA_CASE(DD, 2) KMI_MFMA_CASE(DD, 3) KMI_MFMA_CASE(DD, 4)

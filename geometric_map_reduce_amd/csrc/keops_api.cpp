@@ -471,12 +471,16 @@ int gauss_entry(int op, const float *x, const float *y, const float *b, const fl
   GaussDispatch fn = nullptr;
   if (gauss_find(op, D, E, 1, &wide_info, &fn) || gauss_find(op, D, E, 0, &narrow_info, &fn))
     return KEOPS_ERR_UNSUPPORTED;
-  // fp32-MFMA cross term where the contraction is large enough (D >= 32), unless switched off
+  // fp32-MFMA cross term where the contraction is large enough (D >= 32), unless
+  // switched off: the sum, the LogSumExp and (D <= 64) the gradient with respect to x
   const int64_t form = g_opt_form.load();
-  const bool use_mfma = op == OP_SUM && D >= 32 && form == 0 && g_opt_mfma.load() == 0 &&
-                        gauss_dispatch_sum_mfma(D, E, 0, &mfma_info, dim3(), nullptr, nullptr) == 0;
-  // no-allocation calls: the MFMA path's one form flag per 256-row block must fit the
-  // scratch (split-j partials are then sized to what is left)
+  const GaussDispatch mfma_fn = op == OP_SUM ? gauss_dispatch_sum_mfma
+                                : (op == OP_LSE ? gauss_dispatch_lse_mfma
+                                                : (op == OP_GRAD ? gauss_dispatch_grad_mfma : nullptr));
+  const bool use_mfma = mfma_fn && D >= 32 && form == 0 && g_opt_mfma.load() == 0 &&
+                        mfma_fn(D, E, 0, &mfma_info, dim3(), nullptr, nullptr) == 0;
+  // no-allocation calls: the MFMA path's work-group flags (one per 256-row block and
+  // j split) must fit the scratch (split-j partials are then sized to what is left)
   if (no_alloc && use_mfma &&
       (size_t)((M + mfma_info.rows_per_wg - 1) / mfma_info.rows_per_wg) * sizeof(int) + 1024 > kNoAllocScratchBytes)
     return KEOPS_ERR_SCRATCH;
@@ -519,14 +523,15 @@ int gauss_entry(int op, const float *x, const float *y, const float *b, const fl
                     : make_plan(M, N, cus, wide_info.rows_per_wg, narrow_info.rows_per_wg, wide_info.tile_j,
                                 kGaussWgsPerCu, op == OP_GRAD ? wide_info.rows_per_wg * cus : kWideMinRows, max_split);
   };
+  auto flag_bytes_of = [&](const Plan &q) { return use_mfma ? al((size_t)q.nblk * q.nsplit * sizeof(int)) : 0; };
   Plan p = plan(65535);
-  const size_t flag_bytes = use_mfma ? al((size_t)p.nblk * sizeof(int)) : 0;
-  if (no_alloc && p.nsplit > 1 && al((size_t)p.nsplit * M * PW * sizeof(float)) + flag_bytes > arena.cap) {
-    // as many j-splits as the scratch holds partials for (one: no partials at all)
-    const size_t avail = arena.cap > flag_bytes + 256 ? arena.cap - flag_bytes - 256 : 0;
-    const int64_t fit = (int64_t)(avail / ((size_t)M * PW * sizeof(float)));
+  if (no_alloc && p.nsplit > 1 && al((size_t)p.nsplit * M * PW * sizeof(float)) + flag_bytes_of(p) > arena.cap) {
+    // as many j-splits as the scratch holds partials and flags for (one: no partials)
+    const size_t per = (size_t)M * PW * sizeof(float) + (use_mfma ? (size_t)p.nblk * sizeof(int) : 0);
+    const int64_t fit = (int64_t)((arena.cap > 1024 ? arena.cap - 1024 : 0) / per);
     p = plan(fit >= 2 ? fit : 1);
   }
+  const size_t flag_bytes = flag_bytes_of(p);
 
   const double s2 = (double)sigma * (double)sigma;
   // Laplacian: scale^2 = log2(e) / sigma multiplies |x - y|
@@ -545,8 +550,8 @@ int gauss_entry(int op, const float *x, const float *y, const float *b, const fl
   a.out_idx = out_idx;
   a.max_sign = max_sign;
 
-  // workspace: split-j partials, then (MFMA path) one form flag per row block.  The
-  // range checks of the expanded and direct forms happen inside each work-group.
+  // workspace: split-j partials, then (MFMA path) one flag per work-group.  The range
+  // checks of the expanded and direct forms happen inside each work-group.
   float *ws = nullptr;
   const size_t part_bytes = p.nsplit > 1 ? al((size_t)p.nsplit * M * PW * sizeof(float)) : 0;
   const size_t ws_bytes = part_bytes + flag_bytes;
@@ -565,9 +570,9 @@ int gauss_entry(int op, const float *x, const float *y, const float *b, const fl
   const int prof = prof_begin(st);
   if (use_mfma) {
     a.wg_flags = (int *)((char *)ws + part_bytes);
-    gauss_dispatch_sum_mfma(D, E, 0, nullptr, grid, &a, st);
+    mfma_fn(D, E, 0, nullptr, grid, &a, st);
     prof_end(prof, st);
-    GaussArgs b2 = a;            // direct-form VALU pass over the blocks the MFMA kernel left
+    GaussArgs b2 = a;            // direct-form VALU pass over the work-groups the MFMA kernel left
     b2.form = FORM_DIRECT;
     fn(D, E, 0, nullptr, grid, &b2, st);
   } else {

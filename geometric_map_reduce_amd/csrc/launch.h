@@ -26,6 +26,8 @@ KMI_DECLARE_GAUSS(gauss_dispatch_max_large)
 KMI_DECLARE_GAUSS(laplace_dispatch_sum_small)
 KMI_DECLARE_GAUSS(laplace_dispatch_sum_large)
 KMI_DECLARE_GAUSS(gauss_dispatch_sum_mfma)
+KMI_DECLARE_GAUSS(gauss_dispatch_lse_mfma)
+KMI_DECLARE_GAUSS(gauss_dispatch_grad_mfma)
 #undef KMI_DECLARE_GAUSS
 
 // Few-rows sum with row groups of mr = 4 or stream_rows_large(D, E) rows (rows_per_wg =

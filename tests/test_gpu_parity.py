@@ -820,6 +820,61 @@ def test_mfma_vs_valu(D, E):
                     "mfma_vs_valu": dev_paths}))
 
 
+@pytest.mark.parametrize("D", [32, 50, 64, 100])
+@pytest.mark.parametrize("E", [1, 3])
+@pytest.mark.parametrize("op", ["lse", "grad_x"])
+def test_mfma_lse_grad_vs_valu(op, D, E):
+    """LogSumExp and grad_x with the fp32-MFMA cross term (automatic at D >= 32; grad_x
+    up to D = 64) and on the VALU (matrix cores switched off) both match the oracle."""
+    M, N, sigma = 700, 2300, 0.9 * np.sqrt(D / 3.0)
+    say(f"mfma {op} vs valu D={D} E={E}")
+    x, y, b, g = rand_case(150 + D + E, M, N, D, E, scale=1.0)
+    X, Y, B, G = dev(x), dev(y), dev(b), dev(g)
+    s32 = float(np.float32(sigma))
+    run = (lambda: gm.keops_gauss_lse(X, Y, B, sigma)) if op == "lse" else \
+        (lambda: gm.keops_gauss_grad_x(X, Y, B, G, sigma))
+    r_mfma = host(run())
+    gm.keops_set_option(gm.KEOPS_OPT_MFMA, 1)
+    r_valu = host(run())
+    if op == "lse":
+        ref = oracle.gauss_lse(x, y, b, s32)
+        e1, e2 = check_lse(r_mfma, ref), check_lse(r_valu, ref)
+    else:
+        G_ref, nu = oracle.gauss_grad_x(x, y, b, g, s32)
+        e1, e2 = check_grad(r_mfma, G_ref, nu), check_grad(r_valu, G_ref, nu)
+    say(json.dumps({"op": op, "D": D, "E": E, "mfma_err": e1, "valu_err": e2}))
+
+
+@pytest.mark.parametrize("split", [0, 1, 4])
+@pytest.mark.parametrize("op", ["lse", "grad_x"])
+def test_mfma_lse_grad_mixed_blocks(op, split):
+    """One call where some work-groups stay on the matrix cores and others go to the
+    direct-form VALU kernel: a row block spread beyond the expansion's range bound, and
+    (LogSumExp) rows so far from every y that their terms flush to zero, which the
+    work-group's underflow check hands over."""
+    say(f"mfma {op} mixed blocks split={split}")
+    rng = np.random.default_rng(78)
+    D, E, sigma = 50, 2, 0.6
+    x = (rng.standard_normal((700, D)) * 0.05).astype(np.float32)
+    x[256:512] *= np.float32(40.0)                 # second row block: beyond the range bound
+    x[600:610] += np.float32(1.2)                  # third block: ten rows far from every y
+    y = np.concatenate([x[:600:2] + np.float32(0.01) * rng.standard_normal((300, D)).astype(np.float32),
+                        (rng.standard_normal((900, D)) * 0.05).astype(np.float32)])
+    b = rng.standard_normal((y.shape[0], E)).astype(np.float32)
+    g = rng.standard_normal((x.shape[0], E)).astype(np.float32)
+    gm.keops_set_option(gm.KEOPS_OPT_SPLIT_J, split)
+    s32 = float(np.float32(sigma))
+    if op == "lse":
+        l = host(gm.keops_gauss_lse(dev(x), dev(y), dev(b), sigma))
+        ref = oracle.gauss_lse(x, y, b, s32)
+        assert np.all(ref[600:610] < -50.0)        # the far rows' terms are far below 2^-126
+        check_lse(l, ref)
+    else:
+        G = host(gm.keops_gauss_grad_x(dev(x), dev(y), dev(b), dev(g), sigma))
+        G_ref, nu = oracle.gauss_grad_x(x, y, b, g, s32)
+        check_grad(G, G_ref, nu)
+
+
 @pytest.mark.parametrize("split", [0, 1, 4])
 def test_mfma_mixed_blocks(split):
     """Row blocks within the expansion's range run on MFMA, the others on the direct-form
