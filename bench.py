@@ -51,6 +51,8 @@ BENCHES = {
     "sum10k": ("sum", "sum_grad_10k"),
     "sum1k": ("sum", "sum_1k"),
     "solver": ("sum", "solver_matvec_100k_x_10M"),
+    "solver_lse": ("lse", "solver_matvec_100k_x_10M"),
+    "solver_grad": ("grad_x", "solver_matvec_100k_x_10M"),
     "kmin3": ("kmin", "kmin10_1M_d3"),
     "kmin64": ("kmin", "kmin10_1M_d64"),
     "stream": ("sum", "stream_16_x_100M"),
@@ -72,8 +74,8 @@ def flops_per_pair(op, D, E):
 
 
 def uses_mfma(op, D):
-    """Ops whose pair map runs the -2<x, y> cross term on fp32 MFMA (D >= 32)."""
-    return D >= 32 and op in ("sum", "kmin")
+    """Ops whose pair map runs the -2<x, y> cross term on MFMA (D >= 32; grad_x up to 64)."""
+    return D >= 32 and (op in ("sum", "lse", "kmin") or (op == "grad_x" and D <= 64))
 
 
 def is_stream(op, M, D):
@@ -83,8 +85,9 @@ def is_stream(op, M, D):
 
 def roofline_of(op, M, D, E):
     """(bound, algorithmic units per pair, kernel name) of the dominant pass-1 kernel.
-    MFMA sum: the contraction <x~, y~> of 2D flops per pair against the fp32 matrix peak
-    (the per-pair exp and accumulate are VALU work on top).  MFMA K-min: the distance's
+    MFMA sum and LogSumExp: the contraction <x~, y~> of 2D flops per pair against the
+    fp32 matrix peak (the per-pair exp and accumulate are VALU work on top).  MFMA
+    grad_x: that contraction and the weighted sum of y, 4D flops per pair.  MFMA K-min: the distance's
     contraction, 2D algorithmic flops per pair, against the peak of the bf16 matrix pipe
     the split-bf16 prefilter runs on (it executes three bf16 products, 6D flops, reported
     beside it).  Few-rows sum: HBM bytes, priced per launch (y and b read once) rather
@@ -93,7 +96,11 @@ def roofline_of(op, M, D, E):
         return "hbm", None, "gauss_stream_kernel"
     if uses_mfma(op, D):
         if op == "sum":
-            return "mfma", 2 * D, "gauss_mfma_sum_kernel"
+            return "mfma", 2 * D, "gauss_mfma_kernel<sum>"
+        if op == "lse":
+            return "mfma", 2 * D, "gauss_mfma_kernel<lse>"
+        if op == "grad_x":
+            return "mfma", 4 * D, "gauss_mfma_grad_kernel"
         return "mfma_bf16", 2 * D, "kmin_mfma_split_kernel"
     # the transposed gradients run the row kernels with y as the rows
     kop = {"grad_y": "grad_x", "grad_b": "sum", "cg": "sum", "sum_ranges": "sum"}.get(op, op)
@@ -309,6 +316,21 @@ def cpu_baseline(op, w, x, y, b, g, target_s, gpu_out, ranges=None):
         check = {"rows": len(rows), "max_err_over_norm": float(np.max(np.abs(gpu - ref) / np.maximum(nrm, 1e-300)))}
     elif op == "lse":
         check = {"rows": len(rows), "max_abs_err": float(np.max(np.abs(gpu_out[rows].astype(np.float64) - res)))}
+    elif op == "kmin":
+        # index lists equal to the oracle's, or differing only among candidates whose
+        # distances lie within 1e-5 relative of each other (near ties)
+        d_ref, i_ref = res
+        d_gpu, i_gpu = gpu_out
+        i_gpu = i_gpu[rows]
+        same = np.all(i_gpu == i_ref, axis=1)
+        swaps = bad = 0
+        for r in np.flatnonzero(~same):
+            dx = ((x[rows[r]].astype(np.float64) - y[i_gpu[r]].astype(np.float64)) ** 2).sum(axis=1)
+            if np.all(np.abs(np.sort(dx) - d_ref[r]) <= 1e-5 * np.maximum(d_ref[r], 1e-30)):
+                swaps += 1
+            else:
+                bad += 1
+        check = {"rows": len(rows), "exact_rows": int(same.sum()), "near_tie_swaps": swaps, "mismatches": bad}
     return base, check
 
 
@@ -526,7 +548,8 @@ def main():
     if bs_info is not None:
         res["block_sparse"] = bs_info
     if not args.no_cpu_baseline:
-        gpu_out = (out[0] if op in ("kmin", "max") else out).cpu().numpy()
+        gpu_out = ((out[0].cpu().numpy(), out[1].cpu().numpy()) if op == "kmin"
+                   else (out[0] if op == "max" else out).cpu().numpy())
         base, check = cpu_baseline(op, w, x, y, b, g, args.cpu_seconds, gpu_out, ranges)
         res["cpu_baseline"] = base
         if check is not None:

@@ -39,9 +39,14 @@ constexpr size_t kMaxProfiled = 4096;
 // Records the start event when profiling is on; returns the pair index or -1.
 int prof_begin(hipStream_t st) {
   if (g_opt_profile.load(std::memory_order_relaxed) != 1) return -1;
+  // timing-only events: no system-scope fence (its cache write-back and invalidation
+  // cost a few microseconds of GPU time per event, visible on small calls)
   EventPair e{};
-  if (hipEventCreate(&e.start) != hipSuccess) return -1;
-  if (hipEventCreate(&e.stop) != hipSuccess) { (void)hipEventDestroy(e.start); return -1; }
+  if (hipEventCreateWithFlags(&e.start, hipEventDisableSystemFence) != hipSuccess) return -1;
+  if (hipEventCreateWithFlags(&e.stop, hipEventDisableSystemFence) != hipSuccess) {
+    (void)hipEventDestroy(e.start);
+    return -1;
+  }
   std::lock_guard<std::mutex> lk(g_prof_mu);
   if (g_prof_events.size() >= kMaxProfiled) {
     (void)hipEventDestroy(e.start);
