@@ -89,6 +89,9 @@ struct StreamArgs {
   // and the maximum of |b| over each j chunk (written by row group 0).  Null when off.
   float *row_fac;
   float *chunk_bmax;
+  // gradient with respect to x: the cotangent [M][E] and -(2 / sigma^2)
+  const float *g;
+  float coef;
 };
 
 // Arguments of the K-min pass-1 kernel.

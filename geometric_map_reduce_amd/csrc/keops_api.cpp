@@ -386,9 +386,9 @@ constexpr int64_t kStreamMaxSteps = 128;
 // Returns kStreamNoFit (nothing enqueued) when `arena` cannot hold its workspace.
 constexpr int kStreamNoFit = 1;
 
-int gauss_stream_entry(const float *x, const float *y, const float *b, int64_t M, int64_t N, int D, int E,
-                       float sigma, float *out, hipStream_t st, int cus, const VariantInfo &info, int form,
-                       const Arena *arena) {
+int gauss_stream_entry(int op, const float *x, const float *y, const float *b, const float *gv, int64_t M, int64_t N,
+                       int D, int E, float sigma, float *out, hipStream_t st, int cus, const VariantInfo &info,
+                       int form, const Arena *arena) {
   const int64_t step = info.tile_j;
   const int64_t groups = (M + info.rows_per_wg - 1) / info.rows_per_wg;
   const int64_t nsteps = (N + step - 1) / step;
@@ -403,11 +403,12 @@ int gauss_stream_entry(const float *x, const float *y, const float *b, int64_t M
   const int64_t jpw = (nsteps + wgs - 1) / wgs * step;
   wgs = (N + jpw - 1) / jpw;
 
-  // workspace: partials, then (underflow guard, expanded form allowed) the row
+  // workspace: partials, then (sum: underflow guard, expanded form allowed) the row
   // factors and the maxima of |b| per j chunk (taken by pass 1 from the b it streams)
-  const bool guard = form == 0;
+  const bool guard = op == OP_SUM && form == 0;
+  const int PW = op == OP_SUM ? E : (op == OP_LSE ? 2 * E : D);
   float *ws = nullptr;
-  const size_t part_bytes = ((size_t)wgs * M * E * sizeof(float) + 255) / 256 * 256;
+  const size_t part_bytes = ((size_t)wgs * M * PW * sizeof(float) + 255) / 256 * 256;
   const size_t fac_bytes = guard ? ((size_t)M * sizeof(float) + 255) / 256 * 256 : 0;
   const size_t bmax_bytes = guard ? (size_t)wgs * sizeof(float) : 0;
   Workspace wsp;
@@ -425,6 +426,8 @@ int gauss_stream_entry(const float *x, const float *y, const float *b, int64_t M
   a.j_per_wg = jpw;
   a.part = ws;
   a.form = form == 1 ? FORM_DIRECT : FORM_AUTO;
+  a.g = gv;
+  a.coef = (float)(-2.0 / ((double)sigma * (double)sigma));
   // pass 2 recomputes an output directly when the guard flags it, or when the sum of
   // its partials is not finite (the shifted accumulators can overflow)
   StreamGuard g{};
@@ -433,16 +436,23 @@ int gauss_stream_entry(const float *x, const float *y, const float *b, int64_t M
   g.scale = a.scale;
   g.nparts = (int)wgs;
   g.log2n = (float)std::ceil(std::log2((double)N));
+  g.g = gv;
+  g.coef = a.coef;
   if (guard) {
     a.row_fac = (float *)((char *)ws + part_bytes);
     a.chunk_bmax = (float *)((char *)ws + part_bytes + fac_bytes);
     g.row_fac = a.row_fac;
     g.chunk_bmax = a.chunk_bmax;
   }
+  const dim3 grid((unsigned)wgs, (unsigned)groups);
   const int prof = prof_begin(st);
-  gauss_dispatch_sum_stream(D, E, info.rows_per_wg, nullptr, dim3((unsigned)wgs, (unsigned)groups), &a, st);
+  if (op == OP_SUM) gauss_dispatch_sum_stream(D, E, info.rows_per_wg, nullptr, grid, &a, st);
+  else if (op == OP_LSE) gauss_dispatch_lse_stream(D, E, info.rows_per_wg, nullptr, grid, &a, st);
+  else gauss_dispatch_grad_stream(D, E, info.rows_per_wg, nullptr, grid, &a, st);
   prof_end(prof, st);
-  launch_stream_combine(ws, (int)wgs, M * E, out, g, st);
+  if (op == OP_SUM) launch_stream_combine(ws, (int)wgs, M * E, out, g, st);
+  else if (op == OP_LSE) launch_lse_combine(ws, (int)wgs, M, E, out, st);
+  else launch_stream_grad_combine(ws, (int)wgs, M, out, g, st);
   return check_launch();
 }
 
@@ -506,14 +516,17 @@ int gauss_entry(int op, const float *x, const float *y, const float *b, const fl
   }
   int cus = 0;
   if (int rc = device_setup(&cus)) return rc;
-  if (op == OP_SUM && !use_mfma) {
+  // few rows (sum, LogSumExp, gradient; D <= 8): lanes own j, the rows sit in LDS
+  if ((op == OP_SUM || op == OP_LSE || op == OP_GRAD) && !use_mfma) {
     VariantInfo sinfo{};
     const int64_t rows_opt = g_opt_rows.load();
-    const int mr = M <= 4 ? 4 : stream_rows_large(D, E);
+    const int mr = M <= 4 ? 4 : (op == OP_GRAD ? stream_grad_mr_large(D) : stream_rows_large(D, E));
+    const auto sfn = op == OP_SUM ? gauss_dispatch_sum_stream
+                                  : (op == OP_LSE ? gauss_dispatch_lse_stream : gauss_dispatch_grad_stream);
     if ((rows_opt == 3 || (rows_opt == 0 && M <= kStreamMaxRows)) &&
-        gauss_dispatch_sum_stream(D, E, mr, &sinfo, dim3(), nullptr, nullptr) == 0 &&
+        sfn(D, E, mr, &sinfo, dim3(), nullptr, nullptr) == 0 &&
         (M + sinfo.rows_per_wg - 1) / sinfo.rows_per_wg <= 65535) {
-      const int rc = gauss_stream_entry(x, y, b, M, N, D, E, sigma, out, st, cus, sinfo, (int)form,
+      const int rc = gauss_stream_entry(op, x, y, b, g, M, N, D, E, sigma, out, st, cus, sinfo, (int)form,
                                         no_alloc ? &arena : nullptr);
       if (rc != kStreamNoFit) return rc;   // else: the row-per-lane layout below
     }

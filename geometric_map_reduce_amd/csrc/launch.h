@@ -35,6 +35,9 @@ KMI_DECLARE_GAUSS(gauss_dispatch_grad_mfma)
 constexpr int stream_rows_large(int D, int E) {
   return D <= 4 ? (E == 1 ? 16 : (E == 2 ? 8 : 4)) : (E == 1 ? 8 : 4);
 }
+// Rows per row group of the large few-rows gradient variant: its accumulators, MR x D,
+// stay at 32 registers.
+constexpr int stream_grad_mr_large(int D) { return D <= 2 ? 16 : (D <= 4 ? 8 : 4); }
 int gauss_dispatch_sum_stream(int D, int E, int mr, VariantInfo *info, dim3 grid, const StreamArgs *args,
                               hipStream_t st);
 
@@ -70,9 +73,22 @@ struct StreamGuard {
   int64_t N;
   int D, E;
   float scale;
+  const float *g;   // gradient: the cotangent [M][E] and -(2 / sigma^2)
+  float coef;
 };
 void launch_stream_combine(const float *part, int nparts, int64_t count, float *out, const StreamGuard &g,
                            hipStream_t st);
+// Few-rows LogSumExp and gradient (gauss_stream_ops.h); `mr` is 4 or the large
+// variant's rows (stream_rows_large(D, E) for LogSumExp, stream_grad_mr_large(D) for
+// the gradient).
+int gauss_dispatch_lse_stream(int D, int E, int mr, VariantInfo *info, dim3 grid, const StreamArgs *args,
+                              hipStream_t st);
+int gauss_dispatch_grad_stream(int D, int E, int mr, VariantInfo *info, dim3 grid, const StreamArgs *args,
+                               hipStream_t st);
+// Gradient pass 2: out[i][d] = sum over the nparts partials in double; a non-finite
+// total (an overflow of the offset accumulators) is recomputed in double.
+void launch_stream_grad_combine(const float *part, int nparts, int64_t M, float *out, const StreamGuard &g,
+                                hipStream_t st);
 
 // Conjugate-gradient vector kernels (E <= 4 columns).  Each launcher that
 // reduces writes kCgBlocks x E double partials to `part` and their sums to

@@ -127,6 +127,56 @@ def test_stream_layout(case, form):
         check_sum(host(a), a_ref, n_ref)
 
 
+@pytest.mark.parametrize("form", [0, 1], ids=["auto", "direct"])
+@pytest.mark.parametrize("case", STREAM, ids=lambda c: "M%d_N%d_D%d_E%d_s%g" % c)
+def test_stream_layout_lse_grad(case, form):
+    """LogSumExp and grad_x in the few-rows layout (online LogSumExp per lane; the
+    gradient in the direct form) against the oracle, every row, for one long j range
+    per work-group, the default, and many short ones."""
+    M, N, D, E, sigma = case
+    say(f"stream lse/grad M={M} N={N} D={D} E={E} sigma={sigma} form={form}")
+    x, y, b, g = rand_case(400 + M + D, M, N, D, E)
+    sigma = float(np.float32(sigma))
+    l_ref = oracle.gauss_lse(x, y, b, sigma)
+    G_ref, nu = oracle.gauss_grad_x(x, y, b, g, sigma)
+    X, Y, B, Gt = dev(x), dev(y), dev(b), dev(g)
+    gm.keops_set_option(gm.KEOPS_OPT_ROWS, 3)
+    gm.keops_set_option(gm.KEOPS_OPT_FORM, form)
+    for target in (0, 1, 64):
+        gm.keops_set_option(gm.KEOPS_OPT_WG_TARGET, target)
+        check_lse(host(gm.keops_gauss_lse(X, Y, B, sigma)), l_ref)
+        check_grad(host(gm.keops_gauss_grad_x(X, Y, B, Gt, sigma)), G_ref, nu)
+
+
+@pytest.mark.parametrize("M", [1, 16, 40])
+def test_workload_few_rows_lse_grad_1M(M):
+    """M in {1, 16, 40} rows against N = 1e6 points (x, y ~ U[0,1)^3, b ~ N(0,1),
+    sigma = 0.1): LogSumExp and grad_x, chosen automatically in the few-rows layout,
+    every row against the oracle."""
+    say(f"few rows lse/grad M={M} N=1e6")
+    x, y, b = workloads.make_points("uniform", M, 1_000_000, 3, 1, seed=20 + M)
+    g = np.random.default_rng(M).standard_normal((M, 1)).astype(np.float32)
+    X, Y, B, Gt = dev(x), dev(y), dev(b), dev(g)
+    check_lse(host(gm.keops_gauss_lse(X, Y, B, 0.1)), oracle.gauss_lse(x, y, b, 0.1))
+    G_ref, nu = oracle.gauss_grad_x(x, y, b, g, 0.1)
+    check_grad(host(gm.keops_gauss_grad_x(X, Y, B, Gt, 0.1)), G_ref, nu)
+
+
+@pytest.mark.parametrize("M", [1, 16, 40])
+def test_stream_far_rows_lse_grad(M):
+    """Few-rows LogSumExp and grad_x with rows spread over 18 sigma and every y at one
+    end: the far rows' terms are far below 2^-126, which the running maximum of the
+    LogSumExp absorbs."""
+    say(f"stream far rows lse/grad M={M}")
+    x, y, b = _far_rows_case(491 + M, 1)
+    x = x[np.argsort(x[:, 0])][np.linspace(0, x.shape[0] - 1, M).astype(int)]
+    g = np.random.default_rng(M).standard_normal((M, 1)).astype(np.float32)
+    gm.keops_set_option(gm.KEOPS_OPT_ROWS, 3)
+    check_lse(host(gm.keops_gauss_lse(dev(x), dev(y), dev(b), 1.0)), oracle.gauss_lse(x, y, b, 1.0))
+    G_ref, nu = oracle.gauss_grad_x(x, y, b, g, 1.0)
+    check_grad(host(gm.keops_gauss_grad_x(dev(x), dev(y), dev(b), dev(g), 1.0)), G_ref, nu)
+
+
 def test_far_from_origin_and_spread():
     """Data far from the origin (centring) and spread out (direct-form fallback)."""
     say("far/spread")
