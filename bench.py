@@ -405,6 +405,25 @@ def micro_rates(torch):
             r["frac_fp32_vector_peak"] = round(12 * pairs / (PEAK_FP32_TFLOPS * 1e12), 4)
             r["simd_cycles_per_64_pairs"] = round(simd_cycles / (cnt[6] / 64), 3)
         res[name] = r
+    # HBM read rate: a 1.6 GB buffer read once per launch (the few-rows workload's y and
+    # b), grid-stride and one contiguous chunk per work-group, best of five launches
+    lib.keops_micro_hbm.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                    ctypes.POINTER(ctypes.c_float)]
+    n = 400_000_000
+    buf = torch.ones(n, device="cuda:0")
+    hbm = {}
+    for mode, label in ((0, "grid_stride"), (1, "chunk_per_wg")):
+        for blocks in (1024, 2048, 4096, 8192, 16384):
+            sink = torch.empty(blocks * 256, device="cuda:0")
+            best = None
+            for _ in range(6):
+                ms = ctypes.c_float(0)
+                if lib.keops_micro_hbm(ctypes.c_void_p(buf.data_ptr()), n, ctypes.c_void_p(sink.data_ptr()),
+                                       blocks, mode, ctypes.byref(ms)) != 0:
+                    raise RuntimeError("keops_micro_hbm failed")
+                best = ms.value if best is None else min(best, ms.value)
+            hbm[f"{label}_{blocks}"] = {"ms": round(best, 4), "GB_s": round(4 * n / (best * 1e-3) / 1e9, 1)}
+    res["hbm_read"] = hbm
     print(json.dumps({"workload": "micro", "cus": cus, "probes": res}), flush=True)
 
 

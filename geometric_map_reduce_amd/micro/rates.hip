@@ -376,9 +376,68 @@ __global__ void k_bank(float *out, Clock *c, int iters) {
 }
 #undef KMI_BANK_BODY
 
+
+// HBM read probe: float4 loads, four in flight per thread, summed into registers;
+// one float written per thread.  mode 0: grid-stride over the whole buffer; mode 1:
+// work-group w reads its own contiguous chunk, threads striding by the work-group
+// (the access pattern of the few-rows kernels, which stream y and b that way).
+__global__ __launch_bounds__(256) void k_hbm_read(const float4 *__restrict__ buf, int64_t n4, int64_t chunk4,
+                                                  int mode, float *sink) {
+  int64_t i, end, stride;
+  if (mode == 0) {
+    i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    end = n4;
+    stride = (int64_t)gridDim.x * blockDim.x;
+  } else {
+    i = (int64_t)blockIdx.x * chunk4 + threadIdx.x;
+    end = (int64_t)(blockIdx.x + 1) * chunk4 < n4 ? (int64_t)(blockIdx.x + 1) * chunk4 : n4;
+    stride = blockDim.x;
+  }
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (; i + 3 * stride < end; i += 4 * stride) {
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = buf[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) { acc.x += v[u].x; acc.y += v[u].y; acc.z += v[u].z; acc.w += v[u].w; }
+  }
+  for (; i < end; i += stride) {
+    const float4 v = buf[i];
+    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+  }
+  sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = acc.x + acc.y + acc.z + acc.w;
+}
+
 }  // namespace
 
 extern "C" {
+
+// Reads the device buffer `buf` of n floats (n a multiple of 4, 16-byte aligned)
+// once with `blocks` work-groups of 256 threads in `mode` (see k_hbm_read); `sink`
+// holds blocks * 256 floats.  *ms = kernel time (HIP events).  Returns 0, -1 for
+// invalid arguments, -4 on a HIP error.
+int keops_micro_hbm(const float *buf, int64_t n, float *sink, int blocks, int mode, float *ms) {
+  if (!buf || !sink || !ms || n < 4 || (n & 3) || ((uintptr_t)buf & 15) || blocks < 1 || mode < 0 || mode > 1)
+    return -1;
+  const int64_t n4 = n / 4;
+  const int64_t chunk4 = (n4 + blocks - 1) / blocks;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  int rc = 0;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+    rc = -4;
+  } else {
+    (void)hipEventRecord(e0, nullptr);
+    hipLaunchKernelGGL(k_hbm_read, dim3((unsigned)blocks), dim3(256), 0, nullptr,
+                       reinterpret_cast<const float4 *>(buf), n4, chunk4, mode, sink);
+    (void)hipEventRecord(e1, nullptr);
+    if (hipGetLastError() != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+        hipEventElapsedTime(ms, e0, e1) != hipSuccess)
+      rc = -4;
+  }
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  return rc;
+}
 
 // Probe ids, in the order listed at the top of this file.
 enum {
