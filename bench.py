@@ -74,8 +74,8 @@ def flops_per_pair(op, D, E):
 
 
 def uses_mfma(op, D):
-    """Ops whose pair map runs the -2<x, y> cross term on MFMA (D >= 32; grad_x up to 64)."""
-    return D >= 32 and (op in ("sum", "lse", "kmin") or (op == "grad_x" and D <= 64))
+    """Ops whose pair map runs the -2<x, y> cross term on MFMA (D >= 32)."""
+    return D >= 32 and op in ("sum", "lse", "kmin", "grad_x")
 
 
 def is_stream(op, M, D):

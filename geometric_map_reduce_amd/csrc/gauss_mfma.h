@@ -33,10 +33,11 @@
 // and is applied at the end).
 //
 // Work-group: 256 threads = 4 waves; each wave owns 4 row tiles (64 rows), i.e. 256
-// rows per work-group; four independent MFMA chains per wave.  j tiles of TJ = 64
-// rows are staged in LDS (double-buffered, one barrier per tile) in a permuted y~
-// layout that lets each lane read its k-slice with ds_read_b128; all 256 threads
-// build it, four per column.
+// rows per work-group; four independent MFMA chains per wave (the gradient at D > 64:
+// eight waves of two row tiles, the same 256 rows).  j tiles of TJ = 64 rows are
+// staged in LDS (double-buffered, one barrier per tile) in a permuted y~ layout that
+// lets each lane read its k-slice with ds_read_b128; 256 threads build it, four per
+// column.
 //
 // Range conditions, each decided by the work-group for its (row block, j split):
 //  * the expansion's precision condition of the VALU expanded form, max |x'_i|^2 <=
@@ -70,13 +71,40 @@ struct MfmaShape {
   static constexpr int YTS = TJ + 4;               // floats per coordinate row of the coordinate-major y'
 };
 
-// Bounding-box centre of the work-group's rows (thread t scans row wg_row0 + t) into
-// sCen.  Contains barriers: every thread of the work-group calls it.
+// The gradient's work-group: 256 rows like the sum's (the VALU kernel that takes over
+// failed work-groups uses the same blocks), as four waves of four row tiles, or at
+// D > 64 eight waves of two (four tiles' x~ slices and 16-coordinate accumulator tiles
+// would not fit one wave's registers there); the first 256 threads stage the tiles.
 template <int D>
+struct MfmaGradShape : MfmaShape<D> {
+  static constexpr int NW = D > 64 ? 8 : 4;        // waves per work-group
+  static constexpr int TI = D > 64 ? 2 : 4;        // 16-row tiles per wave
+  static constexpr int NT = NW * kWave;            // threads per work-group
+  static constexpr int ROWS_WG = NW * 16 * TI;
+  static_assert(ROWS_WG == 256, "the VALU kernel's 256-row blocks");
+};
+
+// Work-group maximum over NW waves; `red` holds NW floats.  Contains barriers.
+template <int NW>
+__device__ __forceinline__ float block_max_w(float v, float *red) {
+  v = wave_max(v);
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int k = 1; k < NW; ++k) r = fmaxf(r, red[k]);
+  return r;
+}
+
+// Bounding-box centre of the work-group's ROWS rows (thread t < ROWS scans row
+// wg_row0 + t) into sCen; NW waves, sRed holds 2 D NW floats.  Contains barriers:
+// every thread of the work-group calls it.
+template <int D, int NW, int ROWS>
 __device__ __forceinline__ void mfma_centre(const float *x, int64_t M, int64_t wg_row0, float *sRed, float *sCen) {
   const int tid = threadIdx.x, wid = tid / kWave, lane = tid & (kWave - 1);
   const int64_t i = wg_row0 + tid;
-  const bool ok = i < M;
+  const bool ok = tid < ROWS && i < M;
   for (int d0 = 0; d0 < D; d0 += 4) {
     float lo[4], hi[4];
 #pragma unroll
@@ -89,33 +117,32 @@ __device__ __forceinline__ void mfma_centre(const float *x, int64_t M, int64_t w
     if (lane == 0) {
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        if (d0 + q < D) { sRed[(2 * (d0 + q)) * 4 + wid] = lo[q]; sRed[(2 * (d0 + q) + 1) * 4 + wid] = hi[q]; }
+        if (d0 + q < D) { sRed[(2 * (d0 + q)) * NW + wid] = lo[q]; sRed[(2 * (d0 + q) + 1) * NW + wid] = hi[q]; }
     }
   }
   __syncthreads();
-  for (int d = tid; d < D; d += kThreads) {
-    float l = sRed[(2 * d) * 4], h = sRed[(2 * d + 1) * 4];
+  for (int d = tid; d < D; d += NW * kWave) {
+    float l = sRed[(2 * d) * NW], h = sRed[(2 * d + 1) * NW];
 #pragma unroll
-    for (int w = 1; w < kThreads / kWave; ++w) { l = fminf(l, sRed[(2 * d) * 4 + w]); h = fmaxf(h, sRed[(2 * d + 1) * 4 + w]); }
+    for (int w = 1; w < NW; ++w) { l = fminf(l, sRed[(2 * d) * NW + w]); h = fmaxf(h, sRed[(2 * d + 1) * NW + w]); }
     sCen[d] = 0.5f * l + 0.5f * h;
   }
   __syncthreads();
 }
 
-// x~ slices of the wave's row tiles: lane l holds x~[row t*16 + l%16][k = 4s + l/16];
-// nrow[t] gets |x'|^2 of row t*16 + l%16 (whole, in all four lanes of the row).
-// Returns the largest |x'|^2 over the wave's rows below M.
-template <int D>
+// x~ slices of the wave's TI row tiles (wave w owns rows w*16*TI ...): lane l holds
+// x~[row t*16 + l%16][k = 4s + l/16]; nrow[t] gets |x'|^2 of row t*16 + l%16 (whole, in
+// all four lanes of the row).  Returns the largest |x'|^2 over the wave's rows below M.
+template <int D, int TI>
 __device__ __forceinline__ float mfma_rows(const GaussArgs &a, int64_t wg_row0, const float *sCen,
-                                           float (&xa)[MfmaShape<D>::TI][MfmaShape<D>::KS],
-                                           float (&nrow)[MfmaShape<D>::TI]) {
+                                           float (&xa)[TI][MfmaShape<D>::KS], float (&nrow)[TI]) {
   using S = MfmaShape<D>;
   const int tid = threadIdx.x, wid = tid / kWave, lane = tid & (kWave - 1);
   const int lrow = lane & 15, lgrp = lane >> 4;
   float r2 = 0.0f;
 #pragma unroll
-  for (int t = 0; t < S::TI; ++t) {
-    const int64_t i = wg_row0 + wid * 64 + t * 16 + lrow;
+  for (int t = 0; t < TI; ++t) {
+    const int64_t i = wg_row0 + wid * (16 * TI) + t * 16 + lrow;
     const bool ok = i < a.M;
     float n = 0.0f;
 #pragma unroll
@@ -192,10 +219,10 @@ __global__ __launch_bounds__(kThreads) void gauss_mfma_kernel(GaussArgs a) {
   const int64_t flag_at = (int64_t)blockIdx.x * gridDim.y + blockIdx.y;
   float *red = sRed + 2 * D * (kThreads / kWave);
 
-  mfma_centre<D>(a.x, M, wg_row0, sRed, sCen);
+  mfma_centre<D, 4, S::ROWS_WG>(a.x, M, wg_row0, sRed, sCen);
   float xa[TI][KS];
   float nrow[TI];
-  const float r2 = block_max(mfma_rows<D>(a, wg_row0, sCen, xa, nrow), red);
+  const float r2 = block_max(mfma_rows<D, TI>(a, wg_row0, sCen, xa, nrow), red);
 
   const int64_t jb = (int64_t)blockIdx.y * a.j_per_split;
   const int64_t je = (jb + a.j_per_split < N) ? jb + a.j_per_split : N;
@@ -399,13 +426,14 @@ __global__ __launch_bounds__(kThreads) void gauss_mfma_kernel(GaussArgs a) {
 
 // ---------------------------------------------------------------- gradient
 template <int D, int E>
-__global__ __launch_bounds__(kThreads) void gauss_mfma_grad_kernel(GaussArgs a) {
-  using S = MfmaShape<D>;
+__global__ __launch_bounds__(MfmaGradShape<D>::NT) void gauss_mfma_grad_kernel(GaussArgs a) {
+  using S = MfmaGradShape<D>;
   constexpr int KS = S::KS, KSP = S::KSP, JS = S::JSTRIDE, TJ = S::TJ, TI = S::TI, DT = S::DT, YTS = S::YTS;
+  constexpr int NW = S::NW, NT = S::NT;
   __shared__ __attribute__((aligned(16))) float sY[2][TJ * JS];         // permuted y~, double-buffered
   __shared__ __attribute__((aligned(16))) float sYT[2][16 * DT * YTS];  // y' coordinate-major [d][j]
   __shared__ __attribute__((aligned(16))) float sB[2][E * TJ];          // payload of the tile, [e][j]
-  __shared__ float sRed[2 * D * (kThreads / kWave) + 8];
+  __shared__ float sRed[2 * D * NW + NW];
   __shared__ float sCen[D];
 
   const int tid = threadIdx.x;
@@ -414,19 +442,19 @@ __global__ __launch_bounds__(kThreads) void gauss_mfma_grad_kernel(GaussArgs a) 
   const int64_t M = a.M, N = a.N;
   const int64_t wg_row0 = (int64_t)blockIdx.x * S::ROWS_WG;
   const int64_t flag_at = (int64_t)blockIdx.x * gridDim.y + blockIdx.y;
-  float *red = sRed + 2 * D * (kThreads / kWave);
+  float *red = sRed + 2 * D * NW;
 
-  mfma_centre<D>(a.x, M, wg_row0, sRed, sCen);
+  mfma_centre<D, NW, S::ROWS_WG>(a.x, M, wg_row0, sRed, sCen);
   float xa[TI][KS];
   float nrow[TI];
-  const float r2 = block_max(mfma_rows<D>(a, wg_row0, sCen, xa, nrow), red);
+  const float r2 = block_max_w<NW>(mfma_rows<D, TI>(a, wg_row0, sCen, xa, nrow), red);
   // g of row t*16 + l%16 (several payload columns: it weights every pair; one: it
   // factors out and is applied at the end)
   float gi[TI][E];
   float gs = 0.0f;
 #pragma unroll
   for (int t = 0; t < TI; ++t) {
-    const int64_t i = wg_row0 + wid * 64 + t * 16 + lrow;
+    const int64_t i = wg_row0 + wid * (16 * TI) + t * 16 + lrow;
     float s = 0.0f;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
@@ -435,7 +463,7 @@ __global__ __launch_bounds__(kThreads) void gauss_mfma_grad_kernel(GaussArgs a) 
     }
     gs = fmaxf(gs, s);
   }
-  const float gmax = block_max(gs, red);
+  const float gmax = block_max_w<NW>(gs, red);
   const bool fast = a.form == FORM_AUTO && r2 <= kFastR2 && isfinite(gmax);
   if (!fast) {
     if (tid == 0 && a.wg_flags) a.wg_flags[flag_at] = 0;
@@ -446,7 +474,7 @@ __global__ __launch_bounds__(kThreads) void gauss_mfma_grad_kernel(GaussArgs a) 
 #pragma unroll
   for (int t = 0; t < TI; ++t) cin[t] = (floatx4){-nrow[t], -nrow[t], -nrow[t], -nrow[t]};
   // coordinates D .. 16 DT - 1 of the coordinate-major tiles stay 0
-  for (int f = tid; f < (16 * DT - D) * YTS; f += kThreads) {
+  for (int f = tid; f < (16 * DT - D) * YTS; f += NT) {
     sYT[0][D * YTS + f] = 0.0f;
     sYT[1][D * YTS + f] = 0.0f;
   }
@@ -454,14 +482,15 @@ __global__ __launch_bounds__(kThreads) void gauss_mfma_grad_kernel(GaussArgs a) 
   const int64_t jb = (int64_t)blockIdx.y * a.j_per_split;
   const int64_t je = (jb + a.j_per_split < N) ? jb + a.j_per_split : N;
 
-  static_assert(TJ * 4 == kThreads, "one k-group per thread");
+  static_assert(TJ * 4 <= NT, "four staging threads per j");
   const int sj = tid >> 2;
+  const bool stager = tid < 4 * TJ;
   float ry[KSP];
   float rb[E];
   float bmx = 0.0f;
   auto load_tile = [&](int64_t jt) {
     const int64_t j = jt + sj;
-    const bool ok = j < je;
+    const bool ok = stager && j < je;
     const int sg = tid & 3;
 #pragma unroll
     for (int q = 0; q < KSP; ++q) {
@@ -473,7 +502,7 @@ __global__ __launch_bounds__(kThreads) void gauss_mfma_grad_kernel(GaussArgs a) 
     for (int e = 0; e < E; ++e) rb[e] = (tid < TJ && jp < je) ? a.b[jp * E + e] : 0.0f;
   };
   auto stage_tile = [&](int buf, int64_t jt) {
-    mfma_stage_y<D>(sY[buf], sYT[buf], ry, sCen, a.scale, jt + sj < je, 0.0f);
+    if (stager) mfma_stage_y<D>(sY[buf], sYT[buf], ry, sCen, a.scale, jt + sj < je, 0.0f);
     if (tid < TJ) {
 #pragma unroll
       for (int e = 0; e < E; ++e) {
@@ -561,7 +590,7 @@ __global__ __launch_bounds__(kThreads) void gauss_mfma_grad_kernel(GaussArgs a) 
   // ---- sum_j w_ij (x'_i - y'_j) = x'_i W_i - O_i, checked and stored
   const int64_t nj = je - jb;
   const float log2n = nj > 1 ? ceilf(log2f((float)nj)) : 0.0f;
-  const float thr = exp2f(log2n - kGuardLoss) * fmaxf(block_max(bmx, red), 1.0f) * 32.0f * (E == 1 ? 1.0f : gmax);
+  const float thr = exp2f(log2n - kGuardLoss) * fmaxf(block_max_w<NW>(bmx, red), 1.0f) * 32.0f * (E == 1 ? 1.0f : gmax);
   const bool partial = a.nsplit > 1;
   bool low = false;
 #pragma unroll
@@ -574,7 +603,7 @@ __global__ __launch_bounds__(kThreads) void gauss_mfma_grad_kernel(GaussArgs a) 
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int il = t * 16 + 4 * lgrp + r;
-      const int64_t i = wg_row0 + wid * 64 + il;
+      const int64_t i = wg_row0 + wid * (16 * TI) + il;
       const float W = __shfl(ws[t], 4 * lgrp + r);
       if (i < M) {
         const float gf = a.grad_coef * (E == 1 ? a.g[i * E] : 1.0f);
@@ -602,7 +631,7 @@ void launch_gauss_mfma_t(dim3 grid, const GaussArgs &a, hipStream_t st) {
 
 template <int D, int E>
 void launch_gauss_mfma_grad_t(dim3 grid, const GaussArgs &a, hipStream_t st) {
-  hipLaunchKernelGGL((gauss_mfma_grad_kernel<D, E>), grid, dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((gauss_mfma_grad_kernel<D, E>), grid, dim3(MfmaGradShape<D>::NT), 0, st, a);
 }
 
 }  // namespace kmi

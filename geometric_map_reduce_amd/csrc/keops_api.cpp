@@ -487,7 +487,7 @@ int gauss_entry(int op, const float *x, const float *y, const float *b, const fl
   if (gauss_find(op, D, E, 1, &wide_info, &fn) || gauss_find(op, D, E, 0, &narrow_info, &fn))
     return KEOPS_ERR_UNSUPPORTED;
   // fp32-MFMA cross term where the contraction is large enough (D >= 32), unless
-  // switched off: the sum, the LogSumExp and (D <= 64) the gradient with respect to x
+  // switched off: the sum, the LogSumExp and the gradient with respect to x
   const int64_t form = g_opt_form.load();
   const GaussDispatch mfma_fn = op == OP_SUM ? gauss_dispatch_sum_mfma
                                 : (op == OP_LSE ? gauss_dispatch_lse_mfma
