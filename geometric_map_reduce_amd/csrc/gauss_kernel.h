@@ -384,8 +384,10 @@ __device__ __forceinline__ void gauss_jloop(const GaussArgs &a,
           }
         }
       }
-    } else if (OP == OP_LSE && FIXED && E == 1) {
-      // the payload is folded into the records' constant: exp2 and accumulate
+    } else if (OP == OP_LSE && FIXED && E == 1 && D <= 64) {
+      // the payload is folded into the records' constant: exp2 and accumulate (records
+      // read one group ahead; at D = 100 the four records in flight spilled 476
+      // registers, and the loop below reads them group by group)
       pipelined_records<NV>(rec, 0, cnt, xs, s2, [&](const float (&q)[R]) {
 #pragma unroll
         for (int r = 0; r < R; ++r) part[r][0] += fast_exp2(q[r]);

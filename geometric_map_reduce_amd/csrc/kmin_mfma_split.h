@@ -110,7 +110,7 @@ struct KminSplitShape {
   static constexpr int TJ = TJ_FIT < NT / 4 ? TJ_FIT : NT / 4;   // j rows per LDS tile (four staging threads each)
   static constexpr int LDS_BYTES = 4 * (TJ * (2 * RS + 2 + DX) + FIXED_FLOATS);
   static_assert(LDS_BYTES <= 160 * 1024, "split K-min work-group exceeds the LDS of a CU");
-  static_assert(4 * TJ <= NT, "four staging threads per j");
+  static_assert(4 * TJ <= NT, "at least four staging threads per j");
 };
 
 template <int D, int K>
@@ -230,20 +230,28 @@ __global__ __launch_bounds__(kmin_split_threads(D, K)) void kmin_mfma_split_kern
   const int64_t jb = (int64_t)blockIdx.y * a.j_per_split;
   const int64_t je = (jb + a.j_per_split < N) ? jb + a.j_per_split : N;
 
-  // tile staging: thread (sj = tid/4, sg = tid%4) owns the 8-coordinate chunks
-  // c = 4q + sg (q < NS) of column sj, i.e. coordinates 32q + 8sg + e
-  const int sj = tid >> 2, sg = tid & 3;
-  const bool stager = tid < 4 * TJ;
-  float ry[NS][8];
+  // tile staging: SPJ threads per column j; thread (sj = tid/SPJ, sg = tid%SPJ) owns the
+  // 8-coordinate chunks c = sg + SPJ m (m < CPT) of column sj, chunk c holding the
+  // coordinates 32 (c/4) + 8 (c%4) + e.  Eight threads per j where the work-group has
+  // them (the staging then spreads over ten of twelve waves instead of five), else four.
+  constexpr int SPJ = (NS >= 2 && 8 * TJ <= kSplitThreads) ? 8 : 4;
+  constexpr int CPT = 4 * NS / SPJ;
+  const int sj = tid / SPJ, sg = tid % SPJ;
+  const bool stager = tid < SPJ * TJ;
+  float ry[CPT][8];
+  auto chunk_k = [&](int m, int e) {
+    const int c = sg + SPJ * m;
+    return 32 * (c >> 2) + 8 * (c & 3) + e;
+  };
   auto load_tile = [&](int64_t jt) {
     const int64_t j = jt + sj;
     const bool ok = stager && j < je;
 #pragma unroll
-    for (int q = 0; q < NS; ++q)
+    for (int m = 0; m < CPT; ++m)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int k = 32 * q + 8 * sg + e;
-        ry[q][e] = (ok && k < D) ? a.y[j * D + k] : 0.0f;
+        const int k = chunk_k(m, e);
+        ry[m][e] = (ok && k < D) ? a.y[j * D + k] : 0.0f;
       }
   };
   auto stage_tile = [&](int buf, int64_t jt) {
@@ -252,34 +260,35 @@ __global__ __launch_bounds__(kmin_split_threads(D, K)) void kmin_mfma_split_kern
     float ny = 0.0f;
     unsigned *rec = sRec + (buf * TJ + sj) * RS;
 #pragma unroll
-    for (int q = 0; q < NS; ++q) {
+    for (int m = 0; m < CPT; ++m) {
       float v[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int k = 32 * q + 8 * sg + e;
-        v[e] = k < D ? ry[q][e] - sCen[k < D ? k : 0] : 0.0f;
+        const int k = chunk_k(m, e);
+        v[e] = k < D ? ry[m][e] - sCen[k < D ? k : 0] : 0.0f;
         ny = fmaf(v[e], v[e], ny);
       }
       unsigned h[4], l[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) split_bf16x2(v[2 * e], v[2 * e + 1], h[e], l[e]);
-      const int off = 16 * q + 4 * sg;
+      const int c = sg + SPJ * m;
+      const int off = 16 * (c >> 2) + 4 * (c & 3);
       *reinterpret_cast<u32x4s *>(rec + off) = (u32x4s){h[0], h[1], h[2], h[3]};
       *reinterpret_cast<u32x4s *>(rec + DP / 2 + off) = (u32x4s){l[0], l[1], l[2], l[3]};
     }
-    ny += __shfl_xor(ny, 1);
-    ny += __shfl_xor(ny, 2);
+#pragma unroll
+    for (int w = 1; w < SPJ; w *= 2) ny += __shfl_xor(ny, w);
     if (sg == 0) sNy[buf * TJ + sj] = ok ? ny : kPadU;   // padded j: u ~ kPadU, never passes
   };
   // raw coordinates of the tile (those the staging thread loaded) for the exact distance
   auto stage_raw = [&]() {
     if (!stager) return;
 #pragma unroll
-    for (int q = 0; q < NS; ++q)
+    for (int m = 0; m < CPT; ++m)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int k = 32 * q + 8 * sg + e;
-        if (k < D) sYr[sj * DX + k] = ry[q][e];
+        const int k = chunk_k(m, e);
+        if (k < D) sYr[sj * DX + k] = ry[m][e];
       }
   };
 
