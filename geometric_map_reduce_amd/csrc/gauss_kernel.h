@@ -392,7 +392,7 @@ __device__ __forceinline__ void gauss_jloop(const GaussArgs &a,
 #pragma unroll
         for (int r = 0; r < R; ++r) part[r][0] += fast_exp2(q[r]);
       });
-    } else if (OP == OP_LAPLACE && E == 1) {
+    } else if (OP == OP_LAPLACE && E == 1 && D <= 32) {
       // direct form with the records of the next group read ahead, as in
       // pipelined_records.  This group's b is read first, at the top, so that
       // waiting for it does not wait for the records in flight.

@@ -221,7 +221,7 @@ __global__ __launch_bounds__(kThreads) void kmin_valu_kernel(KminArgs a) {
     // least of the 4 prefilter values (v_min3 + v_min) is compared once, and the
     // lane masks are ORed in scalar registers: the CU's one scalar unit, shared by
     // its four SIMDs, sees one OR per row per group instead of one per pair.
-    auto filter_group = [&](const float4 (&g)[4][NV], int jj) {
+    auto filter_group = [&](auto &&fetch, int jj) {
       float t[4][R];
       uint64_t hit = 0;
 #pragma unroll
@@ -229,7 +229,7 @@ __global__ __launch_bounds__(kThreads) void kmin_valu_kernel(KminArgs a) {
         float yv[4 * NV];
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
-          const float4 q = g[u][v];
+          const float4 q = fetch(u, v);
           yv[4 * v] = q.x; yv[4 * v + 1] = q.y; yv[4 * v + 2] = q.z; yv[4 * v + 3] = q.w;
         }
 #pragma unroll
@@ -275,14 +275,21 @@ __global__ __launch_bounds__(kThreads) void kmin_valu_kernel(KminArgs a) {
         }
       }
     };
-    float4 ga[4][NV], gb[4][NV];
-    read_group(ga, 0);
-    for (int jj = 0; jj < cnt; jj += 8) {
-      read_group(gb, jj + 4);
-      filter_group(ga, jj);
-      if (jj + 4 < cnt) {   // wave-uniform
-        read_group(ga, jj + 8);
-        filter_group(gb, jj + 4);
+    if constexpr (NV > 4) {
+      // records of D > 15: read from LDS where they are used (two register buffers of
+      // four such records spilled hundreds of registers at D = 50)
+      for (int jj = 0; jj < cnt; jj += 4)
+        filter_group([&](int u, int v) { return rec[(jj + u) * NV + v]; }, jj);
+    } else {
+      float4 ga[4][NV], gb[4][NV];
+      read_group(ga, 0);
+      for (int jj = 0; jj < cnt; jj += 8) {
+        read_group(gb, jj + 4);
+        filter_group([&](int u, int v) { return ga[u][v]; }, jj);
+        if (jj + 4 < cnt) {   // wave-uniform
+          read_group(ga, jj + 8);
+          filter_group([&](int u, int v) { return gb[u][v]; }, jj + 4);
+        }
       }
     }
     if (has_next) stage(buf ^ 1, ok_next);
