@@ -932,6 +932,42 @@ int keops_laplace_sum(const float *x, const float *y, const float *b, int64_t M,
   return gauss_entry(OP_LAPLACE, x, y, b, nullptr, M, N, D, E, sigma, out, stream);
 }
 
+// Few-rows K-min: row groups x chunks of j, about kKminStreamWgsPerCu work-groups per
+// CU (three waves per SIMD fit; at 1e8 j, D = 3: 3 per CU ran fastest for K <= 16 and
+// 2 for K = 32, whose lists and merges are larger), each chunk at least
+// kKminStreamMinSteps steps; a chunk count of 8 or more is kept a multiple of 8, which
+// lets the kernel put the row groups of one chunk on one XCD.
+constexpr int64_t kKminStreamWgsPerCu = 3;
+constexpr int64_t kKminStreamWgsPerCuWideK = 2;
+constexpr int64_t kKminStreamMinSteps = 8;
+
+int kmin_stream_entry(const float *x, const float *y, int64_t M, int64_t N, int D, int K, float *out_d,
+                      int64_t *out_idx, hipStream_t st, int cus, const VariantInfo &info) {
+  const int64_t groups = (M + info.rows_per_wg - 1) / info.rows_per_wg;
+  const int64_t nsteps = (N + info.tile_j - 1) / info.tile_j;
+  const int64_t target = g_opt_wg_target.load() > 0 ? g_opt_wg_target.load()
+                                                    : (K > 16 ? kKminStreamWgsPerCuWideK : kKminStreamWgsPerCu);
+  int64_t C = ((int64_t)cus * target + groups - 1) / groups;
+  C = std::min(C, std::max<int64_t>(1, nsteps / kKminStreamMinSteps));
+  if (C >= 8) C = C / 8 * 8;
+  if (g_opt_split.load() > 0) C = g_opt_split.load();   // chunks past N stay empty
+  if (groups * C > 0x7fffffff) return KEOPS_ERR_UNSUPPORTED;
+  KminArgs a{};
+  a.x = x; a.y = y; a.M = M; a.N = N;
+  a.nsplit = (int)C;
+  a.j_per_split = (N + C - 1) / C;
+  const size_t n = (size_t)C * M * K;
+  Workspace wsp;
+  if (int rc = wsp.acquire(st, 0, n * (sizeof(float) + sizeof(int32_t)))) return rc;
+  a.out_d = (float *)wsp.ptr();
+  a.part_idx = (int32_t *)((float *)wsp.ptr() + n);
+  const int prof = prof_begin(st);
+  kmin_dispatch_stream(D, K, nullptr, dim3((unsigned)(groups * C)), &a, st);
+  prof_end(prof, st);
+  launch_kmin_stream_combine(a.out_d, a.part_idx, (int)C, M, K, out_d, out_idx, st);
+  return check_launch();
+}
+
 int keops_kmin(const float *x, const float *y, const float * /*b: not read*/, int64_t M, int64_t N, int32_t D,
                int32_t K, float /*sigma: not read*/, float *out_d, int64_t *out_idx, void *stream) {
   if (M < 0 || N < 0 || D < 1 || K < 1) return KEOPS_ERR_INVALID_ARG;
@@ -967,6 +1003,14 @@ int keops_kmin(const float *x, const float *y, const float * /*b: not read*/, in
   (void)hipGetLastError();
   int cus = 0;
   if (int rc = device_setup(&cus)) return rc;
+  // few rows: lanes own j, each keeps K-lists for a group of rows
+  {
+    VariantInfo sinfo{};
+    const int64_t rows_opt = g_opt_rows.load();
+    if ((rows_opt == 3 || (rows_opt == 0 && M <= kStreamMaxRows)) &&
+        kmin_dispatch_stream(D, K, &sinfo, dim3(), nullptr, nullptr) == 0)
+      return kmin_stream_entry(x, y, M, N, D, K, out_d, out_idx, st, cus, sinfo);
+  }
   const Plan p = make_plan(M, N, cus, info.rows_per_wg, info.rows_per_wg, info.tile_j,
                            (fn == kmin_dispatch_mfma || fn == kmin_dispatch_mfma_split) ? kKminMfmaWgsPerCu : kKminWgsPerCu, 0);
   KminArgs a{};

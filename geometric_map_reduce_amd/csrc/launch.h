@@ -48,12 +48,19 @@ KMI_DECLARE_KMIN(kmin_dispatch_d5_8)
 KMI_DECLARE_KMIN(kmin_dispatch_large)
 KMI_DECLARE_KMIN(kmin_dispatch_mfma)
 KMI_DECLARE_KMIN(kmin_dispatch_mfma_split)
+// few rows (lanes own j): rows_per_wg = rows per row group, tile_j = j per step;
+// the grid is one-dimensional, row groups x chunks (args->nsplit chunks)
+KMI_DECLARE_KMIN(kmin_dispatch_stream)
 #undef KMI_DECLARE_KMIN
 
 void launch_sum_combine(const float *ws, int nsplit, int64_t count, float *out, hipStream_t st);
 void launch_lse_combine(const float *ws, int nsplit, int64_t M, int E, float *out, hipStream_t st);
 int launch_kmin_combine(const float *pd, const int32_t *pi, int nsplit, int64_t M, int K, float *out_d,
                         int64_t *out_i, hipStream_t st);
+// The same merge for few rows: one work-group per row (the partial lists of all
+// splits merged by the work-group's threads together).
+int launch_kmin_stream_combine(const float *pd, const int32_t *pi, int nsplit, int64_t M, int K, float *out_d,
+                               int64_t *out_i, hipStream_t st);
 void launch_fill(float *out, int64_t count, float v, hipStream_t st);
 void launch_fill2(float *out, int64_t pairs, float v0, float v1, hipStream_t st);
 void launch_fill_i64(int64_t *out, int64_t count, int64_t v, hipStream_t st);

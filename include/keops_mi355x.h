@@ -251,9 +251,9 @@ const char *keops_status_string(int status);
  *                          condition holds)
  *   KEOPS_OPT_ROWS      -- 1 = one row per lane, 2 = the wide variant (several
  *                          rows per lane, for large M), 3 = the few-rows layout
- *                          of the sum, LogSumExp and gradient with respect to x
- *                          (j per lane, rows in LDS; chosen automatically for
- *                          M <= 64 at D <= 8)
+ *                          of the sum, LogSumExp, gradient with respect to x
+ *                          and K-min (j per lane, rows in LDS or registers;
+ *                          chosen automatically for M <= 64 at D <= 8)
  *   KEOPS_OPT_WG_TARGET -- work-groups per CU the automatic j-split aims for
  *                          (1..4096; ignored when KEOPS_OPT_SPLIT_J is set)
  *   KEOPS_OPT_MFMA      -- 1 = the Gaussian sum and K-min never use the

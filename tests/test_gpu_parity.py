@@ -528,6 +528,93 @@ def test_kmin_self_and_permutation():
     assert all(sorted(r) == list(range(16)) for r in i.tolist())
 
 
+# few-rows K-min (lanes own j): (M, N, D, K), rows from one to a full 64, ragged row
+# groups and chunks, K = 32 (two rows per group), N below one step and K = N
+KMIN_FEW = [(1, 5000, 3, 10), (3, 1000, 1, 1), (16, 20037, 3, 10), (40, 7777, 8, 16), (64, 3000, 2, 32),
+            (17, 300, 5, 7), (5, 10, 3, 10), (6, 2049, 4, 15), (64, 70000, 7, 2)]
+
+
+@pytest.mark.parametrize("split", [0, 1, 5, 16])
+@pytest.mark.parametrize("case", KMIN_FEW, ids=lambda c: "M%d_N%d_D%d_K%d" % c)
+def test_kmin_few_rows(case, split):
+    """The few-rows K-min equals the row-per-lane kernel bit for bit (both insert the same
+    direct-form fp32 distances by (d^2, j)) and matches the oracle."""
+    M, N, D, K = case
+    say(f"kmin few rows M={M} N={N} D={D} K={K} split={split}")
+    rng = np.random.default_rng(M * 13 + N + D * 7 + K)
+    x = rng.standard_normal((M, D)).astype(np.float32)
+    y = rng.standard_normal((N, D)).astype(np.float32)
+    if N > 4:
+        y[N - 1] = y[1]                       # an exact tie across the j range
+    X, Y = dev(x), dev(y)
+    gm.keops_set_option(gm.KEOPS_OPT_ROWS, 3)
+    gm.keops_set_option(gm.KEOPS_OPT_SPLIT_J, split)
+    d, i = gm.keops_kmin(X, Y, K)
+    gm.keops_set_option(gm.KEOPS_OPT_ROWS, 1)
+    gm.keops_set_option(gm.KEOPS_OPT_SPLIT_J, 0)
+    d1, i1 = gm.keops_kmin(X, Y, K)
+    d, i, d1, i1 = host(d), host(i), host(d1), host(i1)
+    assert np.array_equal(i, i1) and np.array_equal(d.view(np.uint32), d1.view(np.uint32))
+    d_ref, i_ref = oracle.kmin(x, y, K)
+    check_kmin(x, y, np.arange(M), d, i, d_ref, i_ref)
+
+
+@pytest.mark.parametrize("K", [1, 10, 32])
+@pytest.mark.parametrize("split", [0, 3])
+def test_kmin_few_rows_ties(K, split):
+    """Integer coordinates on a 3^3 grid: distances are exact in fp32 and nearly every
+    one is shared by hundreds of j, so each work-group's candidate set fills and the
+    order among equal distances decides every slot.  The picks must be the oracle's
+    exactly: ascending (d^2, j)."""
+    say(f"kmin few rows ties K={K} split={split}")
+    rng = np.random.default_rng(77 + K)
+    M, N, D = 24, 40000, 3
+    x = rng.integers(0, 3, (M, D)).astype(np.float32)
+    y = rng.integers(0, 3, (N, D)).astype(np.float32)
+    gm.keops_set_option(gm.KEOPS_OPT_ROWS, 3)
+    gm.keops_set_option(gm.KEOPS_OPT_SPLIT_J, split)
+    d, i = gm.keops_kmin(dev(x), dev(y), K)
+    d, i = host(d), host(i)
+    d_ref, i_ref = oracle.kmin(x, y, K)
+    assert np.array_equal(i, i_ref)
+    assert np.array_equal(d.astype(np.float64), d_ref)
+
+
+@pytest.mark.parametrize("K", [3, 10, 32])
+def test_kmin_few_rows_many_chunks(K):
+    """700 chunks: pass 2's threads each merge two or three partial lists, some of
+    whose tails rank after the K entries already kept."""
+    say(f"kmin few rows 700 chunks K={K}")
+    rng = np.random.default_rng(330 + K)
+    M, N, D = 5, 300_000, 3
+    x = rng.standard_normal((M, D)).astype(np.float32)
+    y = rng.standard_normal((N, D)).astype(np.float32)
+    X, Y = dev(x), dev(y)
+    gm.keops_set_option(gm.KEOPS_OPT_ROWS, 3)
+    gm.keops_set_option(gm.KEOPS_OPT_SPLIT_J, 700)
+    d, i = gm.keops_kmin(X, Y, K)
+    gm.keops_set_option(gm.KEOPS_OPT_ROWS, 1)
+    gm.keops_set_option(gm.KEOPS_OPT_SPLIT_J, 0)
+    d1, i1 = gm.keops_kmin(X, Y, K)
+    d, i, d1, i1 = host(d), host(i), host(d1), host(i1)
+    assert np.array_equal(i, i1) and np.array_equal(d.view(np.uint32), d1.view(np.uint32))
+    d_ref, i_ref = oracle.kmin(x, y, K)
+    check_kmin(x, y, np.arange(M), d, i, d_ref, i_ref)
+
+
+@pytest.mark.parametrize("M", [1, 16, 64])
+def test_workload_kmin_few_rows_1M(M):
+    """Few-rows K-min at N = 1e6 (D = 3, K = 10) in the launch configuration the library
+    picks: every row against the oracle over all j."""
+    say(f"kmin few rows M={M} N=1e6")
+    rng = np.random.default_rng(600 + M)
+    x = rng.standard_normal((M, 3)).astype(np.float32)
+    y = rng.standard_normal((1_000_000, 3)).astype(np.float32)
+    d, i = gm.keops_kmin(dev(x), dev(y), 10)
+    d_ref, i_ref = oracle.kmin(x, y, 10)
+    check_kmin(x, y, np.arange(M), host(d), host(i), d_ref, i_ref)
+
+
 @pytest.mark.parametrize("E", [1, 2])
 @pytest.mark.parametrize("rows", [1, 2], ids=["narrow", "wide"])
 @pytest.mark.parametrize("split", [0, 1, 3])
