@@ -76,12 +76,13 @@ __device__ __forceinline__ float exact_sq_dist_lds(const float *xi, const float 
 // D <= 64 (beyond, the K-lists spill; at D = 64 the compiler spills 2 to 8
 // registers from K = 8 to 10, and that form still ran faster than eight waves:
 // 558 against 624 ms at K = 10); else eight waves (two per SIMD, <= 256 VGPRs)
-// with three tiles per wave where that still fits, else two.  Both main forms
-// hold 384 rows (12 x 2 x 16, 8 x 3 x 16).
+// with three tiles per wave where that still fits, else two, and one at K = 32
+// (with two, the 128 registers of its lists were placed in scratch memory).  The
+// two main forms hold 384 rows (12 x 2 x 16, 8 x 3 x 16).
 constexpr bool kmin_split_wide(int D, int K) { return D <= 32 ? K <= 15 : (D <= 64 ? K <= 10 : false); }
 constexpr int kmin_split_threads(int D, int K) { return kmin_split_wide(D, K) ? 768 : 512; }
 constexpr int kmin_split_tiles(int D, int K) {
-  return kmin_split_wide(D, K) ? 2 : (K <= (D <= 32 ? 13 : (D <= 64 ? 12 : 0)) ? 3 : 2);
+  return kmin_split_wide(D, K) ? 2 : (K <= (D <= 32 ? 13 : (D <= 64 ? 12 : 0)) ? 3 : (K <= 16 ? 2 : 1));
 }
 
 // One work-group per CU: every y tile staged in LDS serves 16 * TI rows per wave.

@@ -1033,7 +1033,7 @@ def test_mfma_mixed_blocks(split):
 @pytest.mark.parametrize("D,K,data", [(32, 10, "mix"), (50, 3, "mix"), (64, 10, "mix"), (64, 16, "mix"), (100, 1, "mix"),
                                        (100, 10, "mix"), (64, 1, "mix"), (64, 32, "mix"), (64, 10, "dups"),
                                        (100, 16, "dups"), (32, 13, "dups"), (64, 10, "far"), (50, 4, "far"),
-                                       (100, 3, "mix")])
+                                       (100, 3, "mix"), (32, 32, "dups"), (100, 32, "mix"), (50, 32, "far")])
 def test_kmin_mfma_equals_valu(D, K, data):
     """Both MFMA-prefiltered K-min forms (split bf16, the default, and fp32) and the
     VALU K-min return the direct-form fp32 K-min: identical indices and
