@@ -56,6 +56,9 @@ BENCHES = {
     "kmin3": ("kmin", "kmin10_1M_d3"),
     "kmin64": ("kmin", "kmin10_1M_d64"),
     "stream": ("sum", "stream_16_x_100M"),
+    "stream_lse": ("lse", "stream_16_x_100M"),
+    "stream_grad": ("grad_x", "stream_16_x_100M"),
+    "stream_kmin": ("kmin", "kmin10_16_x_100M"),
     "cg": ("cg", "krige_100k"),
     "sum_bs": ("sum_ranges", "sum_lse_1M"),
     "max": ("max", "sum_lse_1M"),
@@ -64,7 +67,7 @@ BENCHES = {
 BS_VOXEL, BS_EPS = 0.1, 1e-5       # block-sparse bench: voxel side and truncation threshold
 CG_RTOL = 1e-4
 PEAK_HBM_GBS = 8000.0             # MI355X HBM3E peak
-STREAM_MAX_ROWS = 64              # the library's few-rows layout (j per lane) for the sum
+STREAM_MAX_ROWS = 64              # the library's few-rows layout (j per lane), D <= 8
 
 
 def flops_per_pair(op, D, E):
@@ -78,9 +81,14 @@ def uses_mfma(op, D):
     return D >= 32 and op in ("sum", "lse", "kmin", "grad_x")
 
 
+STREAM_KERNELS = {"sum": "gauss_stream_kernel", "lse": "gauss_stream_lse_kernel",
+                  "grad_x": "gauss_stream_grad_kernel", "kmin": "kmin_stream_kernel"}
+
+
 def is_stream(op, M, D):
-    """The sum at few rows runs the j-per-lane kernel, bound by streaming y and b from HBM."""
-    return op == "sum" and M <= STREAM_MAX_ROWS and D <= 8
+    """At few rows the sum, LogSumExp, grad_x and K-min run the j-per-lane kernels, whose
+    floor is streaming y (and b) from HBM once."""
+    return op in STREAM_KERNELS and M <= STREAM_MAX_ROWS and D <= 8
 
 
 def roofline_of(op, M, D, E):
@@ -90,10 +98,10 @@ def roofline_of(op, M, D, E):
     grad_x: that contraction and the weighted sum of y, 4D flops per pair.  MFMA K-min: the distance's
     contraction, 2D algorithmic flops per pair, against the peak of the bf16 matrix pipe
     the split-bf16 prefilter runs on (it executes three bf16 products, 6D flops, reported
-    beside it).  Few-rows sum: HBM bytes, priced per launch (y and b read once) rather
-    than per pair."""
+    beside it).  Few-rows kernels: HBM bytes, priced per launch (y and b read once)
+    rather than per pair."""
     if is_stream(op, M, D):
-        return "hbm", None, "gauss_stream_kernel"
+        return "hbm", None, STREAM_KERNELS[op]
     if uses_mfma(op, D):
         if op == "sum":
             return "mfma", 2 * D, "gauss_mfma_kernel<sum>"
@@ -110,9 +118,14 @@ def roofline_of(op, M, D, E):
     return "alu", flops_per_pair(op, D, E), name
 
 
-def stream_bytes(w):
-    """Algorithmic HBM bytes of one few-rows sum launch: x, y, b read once, out written once."""
-    return 4 * (w.N * (w.D + w.E) + w.M * w.D + w.M * w.E)
+def stream_bytes(w, op="sum"):
+    """Algorithmic HBM bytes of one few-rows launch: the inputs read once, the outputs
+    written once (K-min reads no b and writes K fp32 distances and int64 indices per row;
+    grad_x also reads the cotangent [M, E] and writes [M, D])."""
+    if op == "kmin":
+        return 4 * (w.N * w.D + w.M * w.D) + 12 * w.M * w.K
+    extra = w.M * w.E + w.M * w.D if op == "grad_x" else w.M * w.E
+    return 4 * (w.N * (w.D + w.E) + w.M * w.D + extra)
 
 
 # sources that define each benchmarked kernel and its launch plan
@@ -124,6 +137,8 @@ KERNEL_SOURCES = {
     "kmin": ["kmin_kernel.h", "dispatch_kmin.h", "kmin_d1_4.hip"],
     "kmin_split": ["kmin_kernel.h", "kmin_mfma_split.h", "kmin_mfma_split.hip"],
     "stream": ["gauss_stream.h", "gauss_stream.hip"],
+    "stream_ops": ["gauss_stream_ops.h", "gauss_stream_ops.hip"],
+    "kmin_stream": ["kmin_kernel.h", "kmin_stream.h", "kmin_stream.hip"],
 }
 # the kernel whose HBM traffic each workload records (rocprofv3's kernel name)
 TRAFFIC_KERNELS = {
@@ -524,14 +539,15 @@ def main():
     value = pairs / (ms_step * 1e-3) / 1e9
     bound, fpp, kname = roofline_of(op, w.M, w.D, w.E)
     kern_avg_ms = kern_ms / max(launches, 1)
-    src_key = ("stream" if bound == "hbm" else "kmin_split" if bound == "mfma_bf16" and op == "kmin"
+    src_key = ({"sum": "stream", "kmin": "kmin_stream"}.get(op, "stream_ops") if bound == "hbm"
+               else "kmin_split" if bound == "mfma_bf16" and op == "kmin"
                else {"grad_y": "grad_x", "grad_b": "sum"}.get(op, op))
     traffic = recorded_traffic(args.workload, src_key)
     if bound == "hbm":
-        achieved = stream_bytes(w) / (kern_avg_ms * 1e-3) / 1e9
+        achieved = stream_bytes(w, op) / (kern_avg_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic}
-        kinfo = {"bytes_per_launch": stream_bytes(w)}
+        kinfo = {"bytes_per_launch": stream_bytes(w, op)}
     else:
         per_launch = w.N * w.N if op == "cg" else pairs
         achieved = fpp * per_launch / (kern_avg_ms * 1e-3) / 1e12

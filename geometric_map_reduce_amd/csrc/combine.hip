@@ -41,6 +41,39 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(const float *__re
   out[t] = m > -INFINITY ? kLn2 * (m + log2f(s)) : -INFINITY;
 }
 
+// The same merge with one work-group per output, for few outputs over many splits
+// (the few-rows layout): the threads take the splits t, t + 256, ...; the maximum
+// and the sum go through fixed-shape work-group reductions (deterministic for a
+// given nsplit).  One thread per output looped over 2,048 splits with a dependent
+// load each, and took 1 ms at 16 rows.
+__global__ __launch_bounds__(kThreads) void lse_combine_rows_kernel(const float *__restrict__ ws, int nsplit,
+                                                                    int64_t M, int E, float *__restrict__ out) {
+  __shared__ float red[kThreads / kWave];
+  const int64_t t = blockIdx.x;
+  const int64_t i = t / E;
+  const int e = (int)(t - i * E);
+  const int64_t stride = M * 2 * E;
+  const float *p = ws + i * 2 * E + 2 * e;
+  float m = -INFINITY;
+  for (int k = threadIdx.x; k < nsplit; k += kThreads) m = fmaxf(m, p[k * stride] + log2f(p[k * stride + 1]));
+  m = block_max(m, red);
+  float s = 0.0f;
+  if (m > -INFINITY)
+    for (int k = threadIdx.x; k < nsplit; k += kThreads) s += exp2f(p[k * stride] + log2f(p[k * stride + 1]) - m);
+  s = row16_sum(s);
+  s += __shfl_xor(s, 16);
+  s += __shfl_xor(s, 32);
+  __syncthreads();   // every thread has read the maxima out of red
+  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float tot = red[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / kWave; ++w) tot += red[w];
+    out[t] = m > -INFINITY ? kLn2 * (m + log2f(tot)) : -INFINITY;
+  }
+}
+
 template <int K>
 __global__ __launch_bounds__(kThreads) void kmin_combine_kernel(const float *__restrict__ pd, const int32_t *__restrict__ pi,
                                                                 int nsplit, int64_t M, float *__restrict__ out_d,
@@ -124,6 +157,11 @@ void launch_sum_combine(const float *ws, int nsplit, int64_t count, float *out, 
 void launch_lse_combine(const float *ws, int nsplit, int64_t M, int E, float *out, hipStream_t st) {
   if (M * E > 0)
     hipLaunchKernelGGL(lse_combine_kernel, dim3(blocks_for(M * E)), dim3(kThreads), 0, st, ws, nsplit, M, E, out);
+}
+
+void launch_lse_combine_rows(const float *ws, int nsplit, int64_t M, int E, float *out, hipStream_t st) {
+  if (M * E > 0)
+    hipLaunchKernelGGL(lse_combine_rows_kernel, dim3((unsigned)(M * E)), dim3(kThreads), 0, st, ws, nsplit, M, E, out);
 }
 
 int launch_kmin_combine(const float *pd, const int32_t *pi, int nsplit, int64_t M, int K, float *out_d,

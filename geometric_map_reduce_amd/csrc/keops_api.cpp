@@ -451,7 +451,7 @@ int gauss_stream_entry(int op, const float *x, const float *y, const float *b, c
   else gauss_dispatch_grad_stream(D, E, info.rows_per_wg, nullptr, grid, &a, st);
   prof_end(prof, st);
   if (op == OP_SUM) launch_stream_combine(ws, (int)wgs, M * E, out, g, st);
-  else if (op == OP_LSE) launch_lse_combine(ws, (int)wgs, M, E, out, st);
+  else if (op == OP_LSE) launch_lse_combine_rows(ws, (int)wgs, M, E, out, st);
   else launch_stream_grad_combine(ws, (int)wgs, M, out, g, st);
   return check_launch();
 }

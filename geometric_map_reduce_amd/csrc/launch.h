@@ -55,6 +55,8 @@ KMI_DECLARE_KMIN(kmin_dispatch_stream)
 
 void launch_sum_combine(const float *ws, int nsplit, int64_t count, float *out, hipStream_t st);
 void launch_lse_combine(const float *ws, int nsplit, int64_t M, int E, float *out, hipStream_t st);
+// The same with one work-group per output (few outputs, many splits; M * E < 2^32).
+void launch_lse_combine_rows(const float *ws, int nsplit, int64_t M, int E, float *out, hipStream_t st);
 int launch_kmin_combine(const float *pd, const int32_t *pi, int nsplit, int64_t M, int K, float *out_d,
                         int64_t *out_i, hipStream_t st);
 // The same merge for few rows: one work-group per row (the partial lists of all

@@ -23,12 +23,14 @@ solver_matvec_100k_x_10M   1e5       1e7       50   E=1     1.0    x, y ~ N(0, I
 kmin10_1M_d3               1e6       1e6       3    K=10    --     16-component mixture
 kmin10_1M_d64              1e6       1e6       64   K=10    --     16-component mixture
 stream_16_x_100M           16        1e8       3    E=1     0.1    x, y ~ U[0,1)^3, b ~ N(0,1)
+kmin10_16_x_100M           16        1e8       3    K=10    --     x, y ~ U[0,1)^3
 krige_100k                 1e5       1e5       3    E=1     0.1    x ~ U[0,1)^3, b ~ N(0,1); lambda = 1
 =========================  ========  ========  ===  ======  =====  =========================
 
 stream_16_x_100M is the few-rows, many-j case (the Falkon issue's M << N taken
 to its end): 16 rows against 1e8 points, where streaming y and b from HBM
-once, not arithmetic, bounds the time.  krige_100k is the conjugate-gradient
+once, not arithmetic, bounds the time; kmin10_16_x_100M is the K-min over
+the same shape.  krige_100k is the conjugate-gradient
 solve of (K + lambda I) a = b on the points x (the README's kriging / spline
 use of the solver); its y draw is made, to keep the recipe's order, and unused.
 
@@ -85,7 +87,8 @@ WORKLOADS = {
         Workload("kmin10_1M_d64", 1_000_000, 1_000_000, 64, K=10, dist="mixture16",
                  ops=("kmin",)),
         Workload("stream_16_x_100M", 16, 100_000_000, 3, E=1, sigma=0.1, dist="uniform",
-                 ops=("sum",)),
+                 ops=("sum", "lse", "grad_x")),
+        Workload("kmin10_16_x_100M", 16, 100_000_000, 3, K=10, dist="uniform", ops=("kmin",)),
         Workload("krige_100k", 100_000, 100_000, 3, E=1, sigma=0.1, dist="uniform", ops=("cg",), lam=1.0),
     ]
 }

@@ -884,6 +884,17 @@ def test_workload_stream_16_x_100M():
     say(f"  max err / norm {err:.3g}")
 
 
+def test_workload_kmin10_16_x_100M():
+    """Few-rows K-min at 1e8 j: every row against the oracle, in the launch the library picks."""
+    w = workloads.WORKLOADS["kmin10_16_x_100M"]
+    say(f"workload {w.name}")
+    x, y, _ = workloads.make_inputs(w)
+    d, i = gm.keops_kmin(dev(x), dev(y), w.K)
+    d_ref, i_ref = oracle.kmin(x, y, w.K)
+    nswap = check_kmin(x, y, np.arange(w.M), host(d), host(i), d_ref, i_ref)
+    say(json.dumps({"workload": w.name, "rows_checked": w.M, "near_tie_swaps": nswap}))
+
+
 def test_workload_transposed_grads_1M():
     """grad_y and grad_b at M = N = 1e6 (D = 3, sigma = 0.1), sampled points against the oracle."""
     w = workloads.WORKLOADS["sum_lse_1M"]
