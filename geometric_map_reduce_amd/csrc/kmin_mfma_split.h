@@ -281,16 +281,21 @@ __global__ __launch_bounds__(kmin_split_threads(D, K)) void kmin_mfma_split_kern
     for (int w = 1; w < SPJ; w *= 2) ny += __shfl_xor(ny, w);
     if (sg == 0) sNy[buf * TJ + sj] = ok ? ny : kPadU;   // padded j: u ~ kPadU, never passes
   };
-  // raw coordinates of the tile (those the staging thread loaded) for the exact distance
+  // raw coordinates of the tile (those the staging thread loaded) for the exact
+  // distance, as float4 stores (a chunk is 8 consecutive coordinates, 32-byte
+  // aligned; coordinates past D are 0 and land in the row's padding, or are not
+  // stored where they would pass its end).  (Neither these stores, in place of
+  // scalar ones, nor rows padded to start on different banks changed the LDS
+  // bank-conflict count or the time at D = 64.)
   auto stage_raw = [&]() {
     if (!stager) return;
 #pragma unroll
-    for (int m = 0; m < CPT; ++m)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int k = chunk_k(m, e);
-        if (k < D) sYr[sj * DX + k] = ry[m][e];
-      }
+    for (int m = 0; m < CPT; ++m) {
+      const int k0 = chunk_k(m, 0);
+      float *dst = sYr + sj * DX + k0;
+      if (k0 + 4 <= DX) *reinterpret_cast<float4 *>(dst) = make_float4(ry[m][0], ry[m][1], ry[m][2], ry[m][3]);
+      if (k0 + 8 <= DX) *reinterpret_cast<float4 *>(dst + 4) = make_float4(ry[m][4], ry[m][5], ry[m][6], ry[m][7]);
+    }
   };
 
   if (jb < je) {
