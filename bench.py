@@ -145,6 +145,7 @@ TRAFFIC_KERNELS = {
     "sum": ("sum", "gauss_valu_kernel<0, 3, 1, 2>"),
     "stream": ("stream", "gauss_stream_kernel<3, 1, 16>"),
     "kmin64": ("kmin_split", "kmin_mfma_split_kernel<64, 10>"),
+    "stream_kmin": ("kmin_stream", "kmin_stream_kernel<3, 10, 4>"),
 }
 COPY_KNOWN_KIB = 262144.0          # the calibration copy reads and writes 256 MiB per launch
 
