@@ -113,7 +113,7 @@ __global__ __launch_bounds__(kThreads) void kmin_valu_kernel(KminArgs a) {
       hi[k] = -INFINITY;
 #pragma unroll
       for (int r = 0; r < R; ++r)
-        if (valid[r]) { lo[k] = fminf(lo[k], xr[r][k]); hi[k] = fmaxf(hi[k], xr[r][k]); }
+        if (valid[r] && isfinite(xr[r][k])) { lo[k] = fminf(lo[k], xr[r][k]); hi[k] = fmaxf(hi[k], xr[r][k]); }
       lo[k] = wave_min(lo[k]);
       hi[k] = wave_max(hi[k]);
     }
@@ -130,7 +130,9 @@ __global__ __launch_bounds__(kThreads) void kmin_valu_kernel(KminArgs a) {
         l = fminf(l, sRed[(2 * k) * 4 + w]);
         h = fmaxf(h, sRed[(2 * k + 1) * 4 + w]);
       }
-      cen[k] = 0.5f * l + 0.5f * h;
+      // finite coordinates only (an infinite one would make every row's centred
+      // coordinates infinite); 0 where the work-group has none
+      cen[k] = l <= h ? 0.5f * l + 0.5f * h : 0.0f;
     }
   }
   // -2 * centred coordinates, |x_c|^2, |x_c|

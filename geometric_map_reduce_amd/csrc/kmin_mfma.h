@@ -68,8 +68,9 @@ __global__ __launch_bounds__(kThreads) void kmin_mfma_kernel(KminArgs a) {
       for (int q = 0; q < 4; ++q) {
         const int d = d0 + q;
         const float v = (ok && d < D) ? a.x[i * D + d] : 0.0f;
-        lo[q] = wave_min((ok && d < D) ? v : INFINITY);
-        hi[q] = wave_max((ok && d < D) ? v : -INFINITY);
+        // finite coordinates only: an infinite one would put the centre at infinity
+        lo[q] = wave_min((ok && d < D && isfinite(v)) ? v : INFINITY);
+        hi[q] = wave_max((ok && d < D && isfinite(v)) ? v : -INFINITY);
       }
       if (lane == 0) {
 #pragma unroll
@@ -82,7 +83,7 @@ __global__ __launch_bounds__(kThreads) void kmin_mfma_kernel(KminArgs a) {
       float l = sRed[(2 * d) * 4], h = sRed[(2 * d + 1) * 4];
 #pragma unroll
       for (int w = 1; w < kThreads / kWave; ++w) { l = fminf(l, sRed[(2 * d) * 4 + w]); h = fmaxf(h, sRed[(2 * d + 1) * 4 + w]); }
-      sCen[d] = 0.5f * l + 0.5f * h;
+      sCen[d] = l <= h ? 0.5f * l + 0.5f * h : 0.0f;   // 0 where no row is finite
     }
     __syncthreads();
   }

@@ -148,8 +148,9 @@ __global__ __launch_bounds__(kmin_split_threads(D, K)) void kmin_mfma_split_kern
       for (int q = 0; q < 4; ++q) {
         const int d = d0 + q;
         const float v = (ok && d < D) ? a.x[i * D + d] : 0.0f;
-        lo[q] = wave_min((ok && d < D) ? v : INFINITY);
-        hi[q] = wave_max((ok && d < D) ? v : -INFINITY);
+        // finite coordinates only: an infinite one would put the centre at infinity
+        lo[q] = wave_min((ok && d < D && isfinite(v)) ? v : INFINITY);
+        hi[q] = wave_max((ok && d < D && isfinite(v)) ? v : -INFINITY);
       }
       if (lane == 0) {
 #pragma unroll
@@ -168,7 +169,7 @@ __global__ __launch_bounds__(kmin_split_threads(D, K)) void kmin_mfma_split_kern
         l = fminf(l, sRed[(2 * d) * kSplitWaves + w]);
         h = fmaxf(h, sRed[(2 * d + 1) * kSplitWaves + w]);
       }
-      sCen[d] = 0.5f * l + 0.5f * h;
+      sCen[d] = l <= h ? 0.5f * l + 0.5f * h : 0.0f;   // 0 where no row is finite
     }
     __syncthreads();
   }

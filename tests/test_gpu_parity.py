@@ -580,6 +580,78 @@ def test_kmin_few_rows_ties(K, split):
     assert np.array_equal(d.astype(np.float64), d_ref)
 
 
+@pytest.mark.parametrize("K", [1, 5])
+def test_kmin_few_rows_nonfinite(K):
+    """Non-finite coordinates: a NaN row and an infinite row get no neighbour (+inf, -1);
+    y points with a NaN or an infinite coordinate are never picked; the few-rows and
+    row-per-lane layouts agree bit for bit, and the finite rows match the oracle run on
+    the finite points alone."""
+    say(f"kmin few rows non-finite K={K}")
+    rng = np.random.default_rng(808 + K)
+    M, N, D = 6, 5000, 3
+    x = rng.standard_normal((M, D)).astype(np.float32)
+    y = rng.standard_normal((N, D)).astype(np.float32)
+    x[2, 0] = np.nan
+    x[4, 1] = np.inf
+    bad = np.array([10, 20, 30, 4999])
+    y[10, 1] = np.nan
+    y[20, 0] = np.inf
+    y[30, 2] = -np.inf
+    y[4999] = np.nan
+    X, Y = dev(x), dev(y)
+    gm.keops_set_option(gm.KEOPS_OPT_ROWS, 3)
+    d, i = gm.keops_kmin(X, Y, K)
+    gm.keops_set_option(gm.KEOPS_OPT_ROWS, 1)
+    d1, i1 = gm.keops_kmin(X, Y, K)
+    d, i, d1, i1 = host(d), host(i), host(d1), host(i1)
+    assert np.array_equal(i, i1) and np.array_equal(d.view(np.uint32), d1.view(np.uint32))
+    for r in (2, 4):
+        assert (i[r] == -1).all() and np.isinf(d[r]).all() and (d[r] > 0).all()
+    good = np.setdiff1d(np.arange(N), bad)
+    assert not np.isin(i, bad).any()
+    rows = np.array([0, 1, 3, 5])
+    d_ref, i_ref = oracle.kmin(x[rows], y[good], K)
+    check_kmin(x[rows], y[good], np.arange(len(rows)), d[rows], np.searchsorted(good, i[rows]), d_ref, i_ref)
+
+
+@pytest.mark.parametrize("rows", [0, 1], ids=["auto", "row_per_lane"])
+@pytest.mark.parametrize("M", [6, 600])
+def test_nonfinite_rows_leave_others_exact(M, rows):
+    """A NaN row and a row with an infinite coordinate share their work-group (or row
+    group) with finite rows: the finite rows' sum, LogSumExp, grad_x, Max and K-min
+    must still match the oracle (work-group centres and range checks take finite
+    coordinates only)."""
+    say(f"non-finite rows M={M} rows={rows}")
+    rng = np.random.default_rng(909 + M)
+    N, D, sigma, K = 3000, 3, 0.7, 4
+    x = rng.standard_normal((M, D)).astype(np.float32)
+    y = rng.standard_normal((N, D)).astype(np.float32)
+    b = rng.standard_normal((N, 1)).astype(np.float32)
+    g = rng.standard_normal((M, 1)).astype(np.float32)
+    x[1, 0] = np.nan
+    x[3, 2] = np.inf
+    fin = np.setdiff1d(np.arange(M), [1, 3])
+    X, Y, B, G = dev(x), dev(y), dev(b), dev(g)
+    gm.keops_set_option(gm.KEOPS_OPT_ROWS, rows)
+    a = host(gm.keops_gauss_sum(X, Y, B, sigma))
+    a_ref, n_ref = oracle.gauss_sum(x[fin], y, b, sigma)
+    check_sum(a[fin], a_ref, n_ref)
+    l = host(gm.keops_gauss_lse(X, Y, B, sigma))
+    check_lse(l[fin], oracle.gauss_lse(x[fin], y, b, sigma))
+    gr = host(gm.keops_gauss_grad_x(X, Y, B, G, sigma))
+    gr_ref, nu = oracle.gauss_grad_x(x[fin], y, b, g[fin], sigma)
+    check_grad(gr[fin], gr_ref, nu)
+    v, vi = gm.keops_gauss_max(X, Y, B, sigma)
+    v_ref, vi_ref = oracle.gauss_max(x[fin], y, b, sigma, 1)
+    check_max(x[fin], y, b, sigma, 1, np.arange(len(fin)), host(v)[fin], host(vi)[fin], v_ref, vi_ref)
+    d, i = gm.keops_kmin(X, Y, K)
+    d, i = host(d), host(i)
+    d_ref, i_ref = oracle.kmin(x[fin], y, K)
+    check_kmin(x[fin], y, np.arange(len(fin)), d[fin], i[fin], d_ref, i_ref)
+    for r in (1, 3):
+        assert (i[r] == -1).all() and np.isinf(d[r]).all()
+
+
 @pytest.mark.parametrize("K", [3, 10, 32])
 def test_kmin_few_rows_many_chunks(K):
     """700 chunks: pass 2's threads each merge two or three partial lists, some of
