@@ -615,15 +615,16 @@ def test_kmin_few_rows_nonfinite(K):
 
 
 @pytest.mark.parametrize("rows", [0, 1], ids=["auto", "row_per_lane"])
-@pytest.mark.parametrize("M", [6, 600])
-def test_nonfinite_rows_leave_others_exact(M, rows):
+@pytest.mark.parametrize("M,D", [(6, 3), (600, 3), (600, 64)])
+def test_nonfinite_rows_leave_others_exact(M, D, rows):
     """A NaN row and a row with an infinite coordinate share their work-group (or row
     group) with finite rows: the finite rows' sum, LogSumExp, grad_x, Max and K-min
     must still match the oracle (work-group centres and range checks take finite
-    coordinates only)."""
-    say(f"non-finite rows M={M} rows={rows}")
-    rng = np.random.default_rng(909 + M)
-    N, D, sigma, K = 3000, 3, 0.7, 4
+    coordinates only).  D = 64 runs the matrix-core kernels."""
+    say(f"non-finite rows M={M} D={D} rows={rows}")
+    rng = np.random.default_rng(909 + M + D)
+    N, K = 3000, 4
+    sigma = 0.7 * np.sqrt(D / 3.0)
     x = rng.standard_normal((M, D)).astype(np.float32)
     y = rng.standard_normal((N, D)).astype(np.float32)
     b = rng.standard_normal((N, 1)).astype(np.float32)
