@@ -653,6 +653,29 @@ def test_nonfinite_rows_leave_others_exact(M, D, rows):
         assert (i[r] == -1).all() and np.isinf(d[r]).all()
 
 
+@pytest.mark.parametrize("rows", [0, 1], ids=["auto", "row_per_lane"])
+@pytest.mark.parametrize("M,D", [(6, 3), (600, 3), (600, 64)])
+def test_lse_minus_inf_payloads(M, D, rows):
+    """LogSumExp with log-weights b = -inf: those j drop out (the result equals the
+    oracle over the other j), and where every b is -inf every row is -inf."""
+    say(f"lse -inf payloads M={M} D={D} rows={rows}")
+    rng = np.random.default_rng(1303 + M + D)
+    N = 3000
+    sigma = 0.7 * np.sqrt(D / 3.0)
+    x = rng.standard_normal((M, D)).astype(np.float32)
+    y = rng.standard_normal((N, D)).astype(np.float32)
+    b = rng.standard_normal((N, 1)).astype(np.float32)
+    drop = rng.random(N) < 0.3
+    b[drop] = -np.inf
+    gm.keops_set_option(gm.KEOPS_OPT_ROWS, rows)
+    l = host(gm.keops_gauss_lse(dev(x), dev(y), dev(b), sigma))
+    keep = ~drop
+    check_lse(l, oracle.gauss_lse(x, y[keep], b[keep], sigma))
+    b_all = np.full((N, 1), -np.inf, np.float32)
+    l_all = host(gm.keops_gauss_lse(dev(x), dev(y), dev(b_all), sigma))
+    assert np.all(l_all == -np.inf)
+
+
 @pytest.mark.parametrize("K", [3, 10, 32])
 def test_kmin_few_rows_many_chunks(K):
     """700 chunks: pass 2's threads each merge two or three partial lists, some of
