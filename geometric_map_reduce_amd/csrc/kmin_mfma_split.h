@@ -245,16 +245,38 @@ __global__ __launch_bounds__(kmin_split_threads(D, K)) void kmin_mfma_split_kern
     const int c = sg + SPJ * m;
     return 32 * (c >> 2) + 8 * (c & 3) + e;
   };
+  // A chunk's 8 coordinates are consecutive: where rows allow it (D a multiple of
+  // 4 or 2 and y aligned to match, a uniform test) they are read as float4 or
+  // float2, 2 or 4 loads per chunk instead of 8; the parts past D are 0.
+  constexpr int VW = D % 4 == 0 ? 4 : (D % 2 == 0 ? 2 : 1);
+  const bool yvec = VW > 1 && ((uintptr_t)a.y & (uintptr_t)(4 * VW - 1)) == 0;
   auto load_tile = [&](int64_t jt) {
     const int64_t j = jt + sj;
     const bool ok = stager && j < je;
+    if (yvec) {
 #pragma unroll
-    for (int m = 0; m < CPT; ++m)
+      for (int m = 0; m < CPT; ++m)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int k = chunk_k(m, e);
-        ry[m][e] = (ok && k < D) ? a.y[j * D + k] : 0.0f;
-      }
+        for (int e = 0; e < 8; e += VW) {
+          const int k = chunk_k(m, e);   // a multiple of VW, so k < D covers the whole group
+          const bool in = ok && k < D;
+          if constexpr (VW == 4) {
+            const float4 v = in ? *reinterpret_cast<const float4 *>(a.y + j * D + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+            ry[m][e] = v.x; ry[m][e + 1] = v.y; ry[m][e + 2] = v.z; ry[m][e + 3] = v.w;
+          } else if constexpr (VW == 2) {
+            const float2 v = in ? *reinterpret_cast<const float2 *>(a.y + j * D + k) : make_float2(0.f, 0.f);
+            ry[m][e] = v.x; ry[m][e + 1] = v.y;
+          }
+        }
+    } else {
+#pragma unroll
+      for (int m = 0; m < CPT; ++m)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int k = chunk_k(m, e);
+          ry[m][e] = (ok && k < D) ? a.y[j * D + k] : 0.0f;
+        }
+    }
   };
   auto stage_tile = [&](int buf, int64_t jt) {
     if (!stager) return;
