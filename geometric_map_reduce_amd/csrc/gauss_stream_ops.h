@@ -18,6 +18,15 @@
 //       v = <2x', y'> - |y'|^2 + b log2 e,  row constant -|x'|^2;
 //   direct: v = -s^2 |x - y|^2 + b log2 e.
 // The running maximum leaves no range condition on b or on the distance.
+// In the expanded form a first pass takes one shift per work-group and column
+// instead, folded into each j's constant, so that a pair costs the sum's three
+// FMAs, one exp and one add, without the running maximum:
+//   M = r2 / 2 + log2 e b0   (r2 = max |x'|^2 of the group, b0 = the largest b of
+// the chunk's first step).  The expanded v is at most |x'|^2 - |x' - y'|^2 + b log2 e,
+// so while every b of the chunk stays below b0 + 16 a term is below 2^(64 + 23.1)
+// and a sum of 2^31 of them below 2^119: no overflow.  The work-group runs the
+// online pass over its chunk instead when some b exceeds b0 + 16, or when a row's
+// shifted sum falls below 2^-60 (it may have lost terms below the fp32 range).
 //
 // Gradient: the direct form, exp2(64 - s^2 |x - y|^2) <g_i, b_j> (x - y) from raw
 // differences, accumulated per (row, coordinate) with the 2^64 offset (one payload
@@ -86,6 +95,7 @@ __global__ __launch_bounds__(kThreads) void gauss_stream_lse_kernel(StreamArgs a
   __shared__ float sCen[D];
   __shared__ float sN[MR];
   __shared__ int sFast;
+  __shared__ float sR2;
   __shared__ float sRed[kThreads / kWave][MR * E];
 
   const int tid = threadIdx.x;
@@ -95,6 +105,7 @@ __global__ __launch_bounds__(kThreads) void gauss_stream_lse_kernel(StreamArgs a
   if (tid == 0) {
     const float r2 = stream_ops_centre<D>(a.x, r0, nr, s, sCen, sN);
     const bool fast = a.form == FORM_AUTO && r2 <= kFastR2;
+    sR2 = r2;
     for (int i = 0; i < MR; ++i)
       for (int d = 0; d < DP; ++d) {
         float v = 0.0f;
@@ -115,17 +126,137 @@ __global__ __launch_bounds__(kThreads) void gauss_stream_lse_kernel(StreamArgs a
   for (int d = 0; d < D; ++d) cen[d] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sCen[d])));
 
   float m[MR][E], sm[MR][E];
-#pragma unroll
-  for (int i = 0; i < MR; ++i)
-#pragma unroll
-    for (int e = 0; e < E; ++e) { m[i][e] = -3.0e38f; sm[i][e] = 0.0f; }
 
   const int64_t jb = (int64_t)blockIdx.x * a.j_per_wg;
   const int cnt = (int)((jb + a.j_per_wg < a.N) ? a.j_per_wg : a.N - jb);   // >= 1 by the grid
   const float *yb = a.y + jb * D, *bb = a.b + jb * E;
   const float s2 = s * s;
+  const int wid = tid / kWave, lane = tid & (kWave - 1);
   float ty[J][D], tb[J][E];
   bool ok[J];
+
+  // ---- expanded form: one shift per work-group and column, M = r2 / 2 + log2 e b0
+  if (fast) {
+    __shared__ float sB0[E];
+    __shared__ int sRedo;
+    stream_ops_load<D, E, J>(yb, bb, cnt, 0, ty, tb, ok);
+    float bm[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      bm[e] = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < J; ++k) bm[e] = ok[k] ? fmaxf(bm[e], tb[k][e]) : bm[e];
+      const float w = wave_max(bm[e]);
+      if (lane == 0) sRed[wid][e] = w;
+    }
+    if (tid == 0) sRedo = 0;
+    __syncthreads();
+    if (tid < E) {
+      float w = sRed[0][tid];
+#pragma unroll
+      for (int q = 1; q < kThreads / kWave; ++q) w = fmaxf(w, sRed[q][tid]);
+      sB0[tid] = w;
+    }
+    __syncthreads();
+    float Ms[E], bcap[E];
+    bool finite = true;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float b0 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sB0[e])));
+      Ms[e] = fmaf(kLog2e, b0, 0.5f * sR2);
+      bcap[e] = b0 + 16.0f;
+      finite = finite && isfinite(Ms[e]);   // else (all -inf, or an infinite b): the online pass
+    }
+    if (finite) {   // uniform
+      bool over = false;   // some b of this lane above b0 + 16
+#pragma unroll
+      for (int i = 0; i < MR; ++i)
+#pragma unroll
+        for (int e = 0; e < E; ++e) sm[i][e] = 0.0f;
+      for (int off = 0; off < cnt; off += STEP) {
+        // per j: the centred y and its constant b log2 e - s^2 |y - c|^2 - M
+        float cj[J][E];
+        float u[J][D];
+#pragma unroll
+        for (int k = 0; k < J; ++k) {
+          float n = 0.0f;
+#pragma unroll
+          for (int d = 0; d < D; ++d) {
+            u[k][d] = ty[k][d] - cen[d];
+            n = fmaf(u[k][d], u[k][d], n);
+          }
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            cj[k][e] = ok[k] ? fmaf(kLog2e, tb[k][e], fmaf(-s2, n, -Ms[e])) : -INFINITY;
+            over = over || (ok[k] && !(tb[k][e] <= bcap[e]));   // NaN b too: the online pass decides
+          }
+        }
+        if (off + STEP < cnt) stream_ops_load<D, E, J>(yb, bb, cnt, off + STEP, ty, tb, ok);   // next step in flight
+        asm volatile("" ::: "memory");   // row records from LDS each step, not held in registers
+#pragma unroll
+        for (int i = 0; i < MR; ++i) {
+          float r[DP];
+          const float4 *src = reinterpret_cast<const float4 *>(sRow + i * DP);
+#pragma unroll
+          for (int q = 0; q < DP / 4; ++q) {
+            const float4 v = src[q];
+            r[4 * q] = v.x; r[4 * q + 1] = v.y; r[4 * q + 2] = v.z; r[4 * q + 3] = v.w;
+          }
+#pragma unroll
+          for (int k = 0; k < J; ++k) {
+            if (E == 1) {
+              float q = cj[k][0];
+#pragma unroll
+              for (int d = 0; d < D; ++d) q = fmaf(r[d], u[k][d], q);
+              sm[i][0] += fast_exp2(q);
+            } else {
+              float q = 0.0f;
+#pragma unroll
+              for (int d = 0; d < D; ++d) q = fmaf(r[d], u[k][d], q);
+#pragma unroll
+              for (int e = 0; e < E; ++e) sm[i][e] += fast_exp2(q + cj[k][e]);
+            }
+          }
+        }
+      }
+      // work-group sums; a row below 2^-60 sends the work-group to the online pass
+#pragma unroll
+      for (int i = 0; i < MR; ++i)
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          float v = row16_sum(sm[i][e]);
+          v += __shfl_xor(v, 16);
+          v += __shfl_xor(v, 32);
+          if (lane == 0) sRed[wid][i * E + e] = v;
+        }
+      if (over) sRedo = 1;
+      __syncthreads();
+      float tot = 0.0f;
+      if (tid < nr * E) {
+        tot = sRed[0][tid];
+#pragma unroll
+        for (int q = 1; q < kThreads / kWave; ++q) tot += sRed[q][tid];
+        if (!(tot >= 0x1p-60f)) sRedo = 1;
+      }
+      __syncthreads();
+      if (!sRedo) {   // uniform
+        if (tid < nr * E) {
+          const int i = tid / E, e = tid - i * E;
+          float *dst = a.part + (((int64_t)blockIdx.x * a.M + r0 + i) * E + e) * 2;
+          dst[0] = Ms[e] + sN[i];
+          dst[1] = tot;
+        }
+        return;
+      }
+      __syncthreads();   // sRed is reused below
+    }
+  }
+
+  // ---- online pass: a running maximum per (row, e) in each lane
+#pragma unroll
+  for (int i = 0; i < MR; ++i)
+#pragma unroll
+    for (int e = 0; e < E; ++e) { m[i][e] = -3.0e38f; sm[i][e] = 0.0f; }
   stream_ops_load<D, E, J>(yb, bb, cnt, 0, ty, tb, ok);
   for (int off = 0; off < cnt; off += STEP) {
     // this step's j: per-j constants (b log2 e, and -|y'|^2 for the expanded form)
@@ -190,7 +321,6 @@ __global__ __launch_bounds__(kThreads) void gauss_stream_lse_kernel(StreamArgs a
   }
 
   // ---- merge the lanes' (m, s) per (row, e): maximum, then the rescaled sums
-  const int wid = tid / kWave, lane = tid & (kWave - 1);
   __shared__ float sMax[MR * E];
 #pragma unroll
   for (int i = 0; i < MR; ++i)

@@ -653,6 +653,24 @@ def test_nonfinite_rows_leave_others_exact(M, D, rows):
         assert (i[r] == -1).all() and np.isinf(d[r]).all()
 
 
+@pytest.mark.parametrize("spike", [0.0, 12.0, 40.0])
+def test_stream_lse_shift_and_cap(spike):
+    """Few-rows LogSumExp's per-work-group shift comes from the first step's largest b:
+    a b far above it later in the chunk (40) sends the work-group to the online pass,
+    one within the cap (12) stays on the shifted pass; both must match the oracle."""
+    say(f"stream lse shift cap spike={spike}")
+    rng = np.random.default_rng(1401)
+    M, N, D, sigma = 12, 300_000, 3, 0.1
+    x = rng.uniform(0, 1, (M, D)).astype(np.float32)
+    y = rng.uniform(0, 1, (N, D)).astype(np.float32)
+    b = rng.standard_normal((N, 1)).astype(np.float32)
+    if spike:
+        b[rng.integers(N // 2, N, 40), 0] = spike
+    gm.keops_set_option(gm.KEOPS_OPT_ROWS, 3)
+    l = host(gm.keops_gauss_lse(dev(x), dev(y), dev(b), sigma))
+    check_lse(l, oracle.gauss_lse(x, y, b, sigma))
+
+
 @pytest.mark.parametrize("rows", [0, 1], ids=["auto", "row_per_lane"])
 @pytest.mark.parametrize("M,D", [(6, 3), (600, 3), (600, 64)])
 def test_lse_minus_inf_payloads(M, D, rows):
