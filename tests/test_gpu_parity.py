@@ -1155,6 +1155,31 @@ def test_mfma_mixed_blocks(split):
     check_sum(a, a_ref, n_ref)
 
 
+@pytest.mark.parametrize("D", [50, 64])
+def test_kmin_mfma_unaligned_y(D):
+    """y one float past a 16-byte boundary (the ABI asks for 4-byte alignment only): the
+    split-bf16 K-min reads y with scalar loads then, and must still equal the VALU
+    kernel bit for bit and match the oracle."""
+    say(f"kmin mfma unaligned y D={D}")
+    rng = np.random.default_rng(1500 + D)
+    M, N, K = 500, 2000, 10
+    x = rng.standard_normal((M, D)).astype(np.float32)
+    y = rng.standard_normal((N, D)).astype(np.float32)
+    buf = torch.empty(N * D + 4, dtype=torch.float32, device="cuda")
+    Y = buf[1:1 + N * D].view(N, D)
+    Y.copy_(torch.from_numpy(y))
+    assert Y.data_ptr() % 16 == 4
+    X = dev(x)
+    d1, i1 = gm.keops_kmin(X, Y, K)
+    gm.keops_set_option(gm.KEOPS_OPT_MFMA, 1)
+    d2, i2 = gm.keops_kmin(X, Y, K)
+    gm.keops_set_option(gm.KEOPS_OPT_MFMA, 0)
+    d1, i1, d2, i2 = host(d1), host(i1), host(d2), host(i2)
+    assert np.array_equal(i1, i2) and np.array_equal(d1.view(np.int32), d2.view(np.int32))
+    d_ref, i_ref = oracle.kmin(x, y, K)
+    check_kmin(x, y, np.arange(M), d1, i1, d_ref, i_ref)
+
+
 @pytest.mark.parametrize("D,K,data", [(32, 10, "mix"), (50, 3, "mix"), (64, 10, "mix"), (64, 16, "mix"), (100, 1, "mix"),
                                        (100, 10, "mix"), (64, 1, "mix"), (64, 32, "mix"), (64, 10, "dups"),
                                        (100, 16, "dups"), (32, 13, "dups"), (64, 10, "far"), (50, 4, "far"),
