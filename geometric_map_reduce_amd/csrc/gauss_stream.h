@@ -152,6 +152,20 @@ __device__ __forceinline__ void stream_jloop(const StreamArgs &a, const float *s
   }
 }
 
+// Work-group w of the one-dimensional grid of 8 G ceil(C / 8) work-groups (G row
+// groups, C chunks of j) -> (row group rg, chunk c).  Chunk c goes to XCD c % 8 (the
+// dispatcher hands out ids round-robin over the eight), and the G row groups of a
+// chunk get consecutive ids among that XCD's, so they run together and all but the
+// first read the chunk's y and b from the XCD's L2 (with the chunk's row groups far
+// apart in the grid, each read it from HBM).  Returns false for the padding ids
+// (c >= C), which exit at once.
+__device__ __forceinline__ bool stream_place(int64_t w, int64_t G, int64_t C, int64_t &rg, int64_t &c) {
+  const int64_t xcd = w & 7, k = w >> 3;
+  rg = k % G;
+  c = (k / G) * 8 + xcd;
+  return c < C;
+}
+
 template <int D, int E, int MR>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(stream_waves(D, E, MR))))
 void gauss_stream_kernel(StreamArgs a) {
@@ -165,7 +179,9 @@ void gauss_stream_kernel(StreamArgs a) {
   __shared__ float sBm[kThreads / kWave];
 
   const int tid = threadIdx.x;
-  const int64_t r0 = (int64_t)blockIdx.y * MR;
+  int64_t rg, c;
+  if (!stream_place(blockIdx.x, (a.M + MR - 1) / MR, (a.N + a.j_per_wg - 1) / a.j_per_wg, rg, c)) return;
+  const int64_t r0 = rg * MR;
   const int nr = (int)((a.M - r0) < MR ? (a.M - r0) : MR);   // >= 1 by the grid
 
   // ---- row group set-up: one thread, at most MR x D values
@@ -205,7 +221,7 @@ void gauss_stream_kernel(StreamArgs a) {
     }
     sG = G;
     sFast = fast ? 1 : 0;
-    if (a.row_fac && blockIdx.x == 0)
+    if (a.row_fac && c == 0)
       for (int i = 0; i < nr; ++i) a.row_fac[r0 + i] = fast ? sFac[i] : -1.0f;
   }
   __syncthreads();
@@ -221,7 +237,7 @@ void gauss_stream_kernel(StreamArgs a) {
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[i][e] = 0.0f;
 
-  const int64_t jb = (int64_t)blockIdx.x * a.j_per_wg;
+  const int64_t jb = c * a.j_per_wg;
   const int cnt = (int)((jb + a.j_per_wg < a.N) ? a.j_per_wg : a.N - jb);   // >= 1 by the grid
   float bmx = 0.0f;
   if (sFast) stream_jloop<D, E, MR, true>(a, sRow, cen, Gs, jb, cnt, acc, bmx);
@@ -241,23 +257,23 @@ void gauss_stream_kernel(StreamArgs a) {
       }
     }
   }
-  if (a.chunk_bmax && blockIdx.y == 0) {
+  if (a.chunk_bmax && rg == 0) {
     const float m = wave_max(bmx);
     if (lane == 0) sBm[wid] = m;
   }
   __syncthreads();
-  if (a.chunk_bmax && blockIdx.y == 0 && tid == 0) {
+  if (a.chunk_bmax && rg == 0 && tid == 0) {
     float m = sBm[0];
 #pragma unroll
     for (int w = 1; w < kThreads / kWave; ++w) m = fmaxf(m, sBm[w]);
-    a.chunk_bmax[blockIdx.x] = m;
+    a.chunk_bmax[c] = m;
   }
   if (tid < nr * E) {
     const int i = tid / E, e = tid - i * E;
     float v = sRed[0][tid];
 #pragma unroll
     for (int w = 1; w < kThreads / kWave; ++w) v += sRed[w][tid];
-    a.part[((int64_t)blockIdx.x * a.M + r0 + i) * E + e] = v * sFac[i];
+    a.part[(c * a.M + r0 + i) * E + e] = v * sFac[i];
   }
 }
 

@@ -99,7 +99,9 @@ __global__ __launch_bounds__(kThreads) void gauss_stream_lse_kernel(StreamArgs a
   __shared__ float sRed[kThreads / kWave][MR * E];
 
   const int tid = threadIdx.x;
-  const int64_t r0 = (int64_t)blockIdx.y * MR;
+  int64_t rg, c;
+  if (!stream_place(blockIdx.x, (a.M + MR - 1) / MR, (a.N + a.j_per_wg - 1) / a.j_per_wg, rg, c)) return;
+  const int64_t r0 = rg * MR;
   const int nr = (int)((a.M - r0) < MR ? (a.M - r0) : MR);   // >= 1 by the grid
   const float s = a.scale;
   if (tid == 0) {
@@ -127,7 +129,7 @@ __global__ __launch_bounds__(kThreads) void gauss_stream_lse_kernel(StreamArgs a
 
   float m[MR][E], sm[MR][E];
 
-  const int64_t jb = (int64_t)blockIdx.x * a.j_per_wg;
+  const int64_t jb = c * a.j_per_wg;
   const int cnt = (int)((jb + a.j_per_wg < a.N) ? a.j_per_wg : a.N - jb);   // >= 1 by the grid
   const float *yb = a.y + jb * D, *bb = a.b + jb * E;
   const float s2 = s * s;
@@ -242,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void gauss_stream_lse_kernel(StreamArgs a
       if (!sRedo) {   // uniform
         if (tid < nr * E) {
           const int i = tid / E, e = tid - i * E;
-          float *dst = a.part + (((int64_t)blockIdx.x * a.M + r0 + i) * E + e) * 2;
+          float *dst = a.part + ((c * a.M + r0 + i) * E + e) * 2;
           dst[0] = Ms[e] + sN[i];
           dst[1] = tot;
         }
@@ -353,7 +355,7 @@ __global__ __launch_bounds__(kThreads) void gauss_stream_lse_kernel(StreamArgs a
     float v = sRed[0][tid];
 #pragma unroll
     for (int q = 1; q < kThreads / kWave; ++q) v += sRed[q][tid];
-    float *dst = a.part + (((int64_t)blockIdx.x * a.M + r0 + i) * E + e) * 2;
+    float *dst = a.part + ((c * a.M + r0 + i) * E + e) * 2;
     dst[0] = sMax[tid] + sN[i];
     dst[1] = v;
   }
@@ -369,7 +371,9 @@ __global__ __launch_bounds__(kThreads) void gauss_stream_grad_kernel(StreamArgs 
   __shared__ float sRed[kThreads / kWave][MR * D];
 
   const int tid = threadIdx.x;
-  const int64_t r0 = (int64_t)blockIdx.y * MR;
+  int64_t rg, c;
+  if (!stream_place(blockIdx.x, (a.M + MR - 1) / MR, (a.N + a.j_per_wg - 1) / a.j_per_wg, rg, c)) return;
+  const int64_t r0 = rg * MR;
   const int nr = (int)((a.M - r0) < MR ? (a.M - r0) : MR);
   for (int f = tid; f < MR * DP; f += kThreads) {
     const int i = f / DP, d = f - i * DP;
@@ -387,7 +391,7 @@ __global__ __launch_bounds__(kThreads) void gauss_stream_grad_kernel(StreamArgs 
 #pragma unroll
     for (int d = 0; d < D; ++d) acc[i][d] = 0.0f;
 
-  const int64_t jb = (int64_t)blockIdx.x * a.j_per_wg;
+  const int64_t jb = c * a.j_per_wg;
   const int cnt = (int)((jb + a.j_per_wg < a.N) ? a.j_per_wg : a.N - jb);
   const float *yb = a.y + jb * D, *bb = a.b + jb * E;
   const float s2 = a.scale * a.scale;
@@ -459,7 +463,7 @@ __global__ __launch_bounds__(kThreads) void gauss_stream_grad_kernel(StreamArgs 
 #pragma unroll
     for (int q = 1; q < kThreads / kWave; ++q) v += sRed[q][tid];
     const float gf = a.coef * (E == 1 ? sG[i] : 1.0f);
-    a.part[((int64_t)blockIdx.x * a.M + r0 + i) * D + d] = (v * exp2f(-kDirectOffset)) * gf;
+    a.part[(c * a.M + r0 + i) * D + d] = (v * exp2f(-kDirectOffset)) * gf;
   }
 }
 

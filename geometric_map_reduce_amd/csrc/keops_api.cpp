@@ -399,9 +399,12 @@ int gauss_stream_entry(int op, const float *x, const float *y, const float *b, c
   wgs = std::max(lo, std::min(wgs, hi));
   if (wgs > nsteps) wgs = nsteps;
   if (wgs < 1) wgs = 1;
-  if (wgs > 0x7fffffff || groups > 65535) return KEOPS_ERR_UNSUPPORTED;
   const int64_t jpw = (nsteps + wgs - 1) / wgs * step;
   wgs = (N + jpw - 1) / jpw;
+  // one-dimensional grid, 8 x groups x ceil(wgs / 8) ids: the kernels place the row
+  // groups of one chunk together on one XCD (the padding ids exit at once)
+  const int64_t nblk = 8 * groups * ((wgs + 7) / 8);
+  if (nblk > 0x7fffffff) return KEOPS_ERR_UNSUPPORTED;
 
   // workspace: partials, then (sum: underflow guard, expanded form allowed) the row
   // factors and the maxima of |b| per j chunk (taken by pass 1 from the b it streams)
@@ -444,7 +447,7 @@ int gauss_stream_entry(int op, const float *x, const float *y, const float *b, c
     g.row_fac = a.row_fac;
     g.chunk_bmax = a.chunk_bmax;
   }
-  const dim3 grid((unsigned)wgs, (unsigned)groups);
+  const dim3 grid((unsigned)nblk);
   const int prof = prof_begin(st);
   if (op == OP_SUM) gauss_dispatch_sum_stream(D, E, info.rows_per_wg, nullptr, grid, &a, st);
   else if (op == OP_LSE) gauss_dispatch_lse_stream(D, E, info.rows_per_wg, nullptr, grid, &a, st);

@@ -36,8 +36,8 @@ constexpr int stream_rows_large(int D, int E) {
   return D <= 4 ? (E == 1 ? 16 : (E == 2 ? 8 : 4)) : (E == 1 ? 8 : 4);
 }
 // Rows per row group of the large few-rows gradient variant: its accumulators, MR x D,
-// stay at 32 registers.
-constexpr int stream_grad_mr_large(int D) { return D <= 2 ? 16 : (D <= 4 ? 8 : 4); }
+// stay at 48 registers (sixteen rows up to D = 3: 102 VGPRs, five waves per SIMD).
+constexpr int stream_grad_mr_large(int D) { return D <= 3 ? 16 : (D <= 4 ? 8 : 4); }
 int gauss_dispatch_sum_stream(int D, int E, int mr, VariantInfo *info, dim3 grid, const StreamArgs *args,
                               hipStream_t st);
 
