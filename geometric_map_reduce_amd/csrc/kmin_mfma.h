@@ -215,7 +215,7 @@ __global__ __launch_bounds__(kThreads) void kmin_mfma_kernel(KminArgs a) {
                 kmin_insert<K>(bd[t], bi[t], d2, (int)j);
                 const float kth = bd[t][K - 1];
                 const float sm = 2.0f * ax[t] + sqrtf(kth);
-                thr[t] = fminf((kth - nx[t]) + mcoef * sm * sm, kThrCap);
+                thr[t] = fminf(thr[t], fminf((kth - nx[t]) + mcoef * sm * sm, kThrCap));   // keep a tighter shared bound
               }
             }
           }

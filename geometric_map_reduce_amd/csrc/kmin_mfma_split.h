@@ -379,7 +379,7 @@ __global__ __launch_bounds__(kmin_split_threads(D, K)) void kmin_mfma_split_kern
                 kmin_insert<K>(bd[t], bi[t], d2, (int)j);
                 const float kth = bd[t][K - 1];
                 const float sm = 2.0f * sqrtf(nx[t]) + sqrtf(kth);
-                thr[t] = fminf((kth - nx[t]) + mcoef * sm * sm, kThrCap);
+                thr[t] = fminf(thr[t], fminf((kth - nx[t]) + mcoef * sm * sm, kThrCap));   // keep a tighter shared bound
               }
             }
           }
