@@ -148,15 +148,18 @@ def test_stream_layout_lse_grad(case, form):
         check_grad(host(gm.keops_gauss_grad_x(X, Y, B, Gt, sigma)), G_ref, nu)
 
 
-@pytest.mark.parametrize("M", [1, 16, 40])
+@pytest.mark.parametrize("M", [1, 16, 40, 64])
 def test_workload_few_rows_lse_grad_1M(M):
-    """M in {1, 16, 40} rows against N = 1e6 points (x, y ~ U[0,1)^3, b ~ N(0,1),
-    sigma = 0.1): LogSumExp and grad_x, chosen automatically in the few-rows layout,
-    every row against the oracle."""
-    say(f"few rows lse/grad M={M} N=1e6")
+    """M in {1, 16, 40, 64} rows against N = 1e6 points (x, y ~ U[0,1)^3, b ~ N(0,1),
+    sigma = 0.1): the sum, LogSumExp and grad_x, chosen automatically in the few-rows
+    layout (up to four row groups sharing each chunk of j), every row against the
+    oracle."""
+    say(f"few rows sum/lse/grad M={M} N=1e6")
     x, y, b = workloads.make_points("uniform", M, 1_000_000, 3, 1, seed=20 + M)
     g = np.random.default_rng(M).standard_normal((M, 1)).astype(np.float32)
     X, Y, B, Gt = dev(x), dev(y), dev(b), dev(g)
+    a_ref, n_ref = oracle.gauss_sum(x, y, b, 0.1)
+    check_sum(host(gm.keops_gauss_sum(X, Y, B, 0.1)), a_ref, n_ref)
     check_lse(host(gm.keops_gauss_lse(X, Y, B, 0.1)), oracle.gauss_lse(x, y, b, 0.1))
     G_ref, nu = oracle.gauss_grad_x(x, y, b, g, 0.1)
     check_grad(host(gm.keops_gauss_grad_x(X, Y, B, Gt, 0.1)), G_ref, nu)
