@@ -14,12 +14,23 @@
 
 namespace kmi {
 
+// The partials are added in split order; they are loaded eight at a time first, so
+// that a thread waits for one round of loads per eight splits rather than one per
+// split (at 10k rows, 40 splits: 9.3 us with the loads one at a time).
 __global__ __launch_bounds__(kThreads) void sum_combine_kernel(const float *__restrict__ ws, int nsplit,
                                                                int64_t count, float *__restrict__ out) {
   const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (t >= count) return;
+  constexpr int U = 8;
   float s = 0.0f;
-  for (int k = 0; k < nsplit; ++k) s += ws[(int64_t)k * count + t];
+  for (int k0 = 0; k0 < nsplit; k0 += U) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = k0 + u < nsplit ? ws[(int64_t)(k0 + u) * count + t] : 0.0f;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (k0 + u < nsplit) s += v[u];
+  }
   out[t] = s;
 }
 
