@@ -520,6 +520,26 @@ def test_kmin_small(case):
         check_kmin(x, y, np.arange(M), host(d), host(i), d_ref, i_ref)
 
 
+@pytest.mark.parametrize("D", [3, 50])
+def test_kmeans_assignment(D):
+    """k-means assignment (the pages' argmin reduction): 200,000 points of a 16-component
+    mixture against 64 centroids (a few j tiles, every row block of the grid), K = 1,
+    on the VALU kernel (D = 3) and the matrix-core prefilter (D = 50); 4,096 sampled
+    rows against the oracle, and every index a valid centroid."""
+    say(f"k-means assignment M=200000 N=64 D={D}")
+    x, _, _ = workloads.make_points("mixture16", 200_000, 1, D, 1, seed=70 + D)
+    rng = np.random.default_rng(71 + D)
+    cent = x[rng.choice(x.shape[0], 64, replace=False)] + np.float32(0.01) * rng.standard_normal((64, D)).astype(np.float32)
+    cent = np.ascontiguousarray(cent, dtype=np.float32)
+    d, i = gm.keops_kmin(dev(x), dev(cent), 1)
+    torch.cuda.synchronize()
+    d, i = host(d), host(i)
+    assert ((i >= 0) & (i < 64)).all()
+    rows = _sample(x.shape[0], 4096)
+    d_ref, i_ref = oracle.kmin(x[rows], cent, 1)
+    check_kmin(x, cent, rows, d[rows], i[rows], d_ref, i_ref)
+
+
 def test_kmin_self_and_permutation():
     say("kmin self-match and K = N")
     rng = np.random.default_rng(9)
