@@ -148,6 +148,36 @@ def test_stream_layout_lse_grad(case, form):
         check_grad(host(gm.keops_gauss_grad_x(X, Y, B, Gt, sigma)), G_ref, nu)
 
 
+def _random_stream_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        cases.append((int(rng.integers(1, 65)), int(rng.integers(1, 40000)), int(rng.integers(1, 9)),
+                      int(rng.integers(1, 5)), float(rng.choice([0.05, 0.1, 0.3, 1.0, 2.0])),
+                      int(rng.choice([0, 1, 3, 7, 64])), int(rng.integers(0, 2))))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_stream_cases(24, 2024), ids=lambda c: "M%d_N%d_D%d_E%d_s%g_t%d_f%d" % c)
+def test_stream_random_shapes(case):
+    """Seeded random few-rows shapes (M up to 64, N up to 4e4, D 1-8, E 1-4, work-group
+    targets from one chunk to many, both forms): sum, LogSumExp and grad_x against the
+    oracle, every row.  Covers row-group counts and chunk counts that are not multiples
+    of 8 in the XCD placement of the grid."""
+    M, N, D, E, sigma, target, form = case
+    say(f"stream random M={M} N={N} D={D} E={E} sigma={sigma} target={target} form={form}")
+    sigma = float(np.float32(sigma))
+    x, y, b, g = rand_case(500 + M + N, M, N, D, E)
+    gm.keops_set_option(gm.KEOPS_OPT_WG_TARGET, target)
+    gm.keops_set_option(gm.KEOPS_OPT_FORM, form)
+    X, Y, B, Gt = dev(x), dev(y), dev(b), dev(g)
+    a_ref, n_ref = oracle.gauss_sum(x, y, b, sigma)
+    check_sum(host(gm.keops_gauss_sum(X, Y, B, sigma)), a_ref, n_ref)
+    check_lse(host(gm.keops_gauss_lse(X, Y, B, sigma)), oracle.gauss_lse(x, y, b, sigma))
+    G_ref, nu = oracle.gauss_grad_x(x, y, b, g, sigma)
+    check_grad(host(gm.keops_gauss_grad_x(X, Y, B, Gt, sigma)), G_ref, nu)
+
+
 @pytest.mark.parametrize("M", [1, 16, 40, 64])
 def test_workload_few_rows_lse_grad_1M(M):
     """M in {1, 16, 40, 64} rows against N = 1e6 points (x, y ~ U[0,1)^3, b ~ N(0,1),
