@@ -362,10 +362,16 @@ __global__ __launch_bounds__(kThreads) void gauss_stream_lse_kernel(StreamArgs a
 }
 
 // ---------------------------------------------------------------- gradient
+// j per lane per step of the gradient: 2, where the sum takes 4 up to D + E = 8 (at 16
+// rows x 1e8, D = 3, pass 1 took 0.540 ms with 2, 0.550 with 4 and 0.557 with 8; at 64
+// rows 1.91, 1.99 and 2.09 ms): its 12 VALU instructions per pair already hide the
+// loads.  The launch plan keeps the sum's step (a multiple of this one).
+constexpr int stream_grad_j(int, int) { return 2; }
+
 template <int D, int E, int MR>
 __global__ __launch_bounds__(kThreads) void gauss_stream_grad_kernel(StreamArgs a) {
   constexpr int DP = stream_record_len<D>();
-  constexpr int J = stream_j(D, E), STEP = kThreads * J;
+  constexpr int J = stream_grad_j(D, E), STEP = kThreads * J;
   __shared__ __attribute__((aligned(16))) float sRow[MR * DP];
   __shared__ float sG[MR * E];
   __shared__ float sRed[kThreads / kWave][MR * D];
